@@ -1,0 +1,251 @@
+"""Seeded synthetic inputs for the attention-forward workloads.
+
+This module is shared by the tests, the benchmark and the oracle side. It holds
+none of the attention arithmetic: only how sequence lengths, q/k/v and the
+per-head ALiBi slopes (which callers pass in as an input) are drawn.
+
+Recipe (the same for every workload):
+  * lengths: ``numpy.random.default_rng(seed).integers(lo, hi, size=n,
+    endpoint=True)``;
+  * tensors: one ``torch.Generator('cpu').manual_seed(seed + 1)``, then
+    ``torch.randn(shape, dtype=float32)`` for q, k and v in that order, then a
+    cast to the workload's dtype (round to nearest even).  Everything is drawn
+    on the host, so a device copy and the oracle see identical bits;
+  * ALiBi slopes: ``2 ** (-8 (h + 1) / Hq)`` per query head, evaluated in
+    float64 and rounded to float32.
+
+Layouts are packed and row-major: q ``[Tq, Hq, D]``, k and v ``[Tk, Hkv, D]``,
+``seqstart_q`` / ``seqstart_k`` int32 ``[n + 1]``.  Query head ``h`` reads
+key/value head ``h // (Hq // Hkv)``.  A BMGHK tensor ``[B, M, G, Hq', K]``
+(the grouped-query layout of the xFormers tutorial page, section 5) is the same
+memory viewed as ``[B*M, G*Hq', K]``, so the BMGHK workload is generated in
+that shape and viewed packed.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+__all__ = [
+    "Workload", "Inputs", "WORKLOADS", "get_workload", "generate", "random_case",
+    "alibi_slopes", "seqstart_from_lengths", "sample_rows",
+]
+
+_DTYPES = {"fp16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One named workload: shapes, dtype, mask kind and how lengths are drawn."""
+
+    name: str
+    description: str
+    dtype: str                      # "fp16" | "bf16"
+    Hq: int
+    Hkv: int
+    D: int
+    causal: bool
+    alibi: bool
+    # exactly one of the following length recipes is used
+    seqlens: Optional[Tuple[int, ...]] = None        # fixed q = k lengths
+    num_seqs: int = 0                                # random lengths ...
+    len_lo: int = 0
+    len_hi: int = 0
+    decode: bool = False            # q length 1 per request, k length random
+    bmghk: Optional[Tuple[int, int, int, int]] = None  # (B, M, G, Hq per group)
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload(
+            name="packed_varlen_h8_d64_fp16",
+            description="packed varlen [37,120,8,200], 8 q/kv heads, D=64, fp16",
+            dtype="fp16", Hq=8, Hkv=8, D=64, causal=False, alibi=False,
+            seqlens=(37, 120, 8, 200)),
+        Workload(
+            name="bmghk_gqa_b2_m256_g2x4_d64_fp16",
+            description="BMGHK B=2 M=256 G=2 groups x 4 q heads, D=64, fp16, no mask",
+            dtype="fp16", Hq=8, Hkv=2, D=64, causal=False, alibi=False,
+            seqlens=(256, 256), bmghk=(2, 256, 2, 4)),
+        Workload(
+            name="causal_alibi_gqa_4x2048_h32kv8_d128_bf16",
+            description="4 x 2048 tokens, 32 q / 8 kv heads, D=128, bf16, causal + ALiBi",
+            dtype="bf16", Hq=32, Hkv=8, D=128, causal=True, alibi=True,
+            seqlens=(2048, 2048, 2048, 2048)),
+        Workload(
+            name="varlen_causal_gqa_64seq_h32kv8_d128_bf16",
+            description="64 packed sequences, lengths U[128,4096], 32 q / 8 kv heads, "
+                        "D=128, bf16, block-diagonal causal",
+            dtype="bf16", Hq=32, Hkv=8, D=128, causal=True, alibi=False,
+            num_seqs=64, len_lo=128, len_hi=4096),
+        Workload(
+            name="decode_splitkv_64req_h64kv8_d128_bf16",
+            description="64 requests x 1 query, KV lengths U[1024,32768], 64 q / 8 kv "
+                        "heads, D=128, bf16, split-KV + LSE combine",
+            dtype="bf16", Hq=64, Hkv=8, D=128, causal=False, alibi=False,
+            num_seqs=64, len_lo=1024, len_hi=32768, decode=True),
+    ]
+}
+
+
+def get_workload(name: str) -> Workload:
+    try:
+        return WORKLOADS[name]
+    except KeyError:
+        raise KeyError(f"unknown workload {name!r}; known: {sorted(WORKLOADS)}") from None
+
+
+@dataclasses.dataclass
+class Inputs:
+    """Host tensors for one call.  ``scale`` is a float32-representable float."""
+
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    seqstart_q: torch.Tensor        # int32 [n+1]
+    seqstart_k: torch.Tensor        # int32 [n+1]
+    seqlens_q: List[int]
+    seqlens_k: List[int]
+    Hq: int
+    Hkv: int
+    D: int
+    causal: bool
+    alibi_slopes: Optional[torch.Tensor]   # float32 [Hq] or None
+    scale: float
+    dtype: str
+    bmghk: Optional[Tuple[int, int, int, int]] = None
+
+    @property
+    def total_q(self) -> int:
+        return int(self.seqstart_q[-1])
+
+    @property
+    def total_k(self) -> int:
+        return int(self.seqstart_k[-1])
+
+    @property
+    def max_seqlen_q(self) -> int:
+        return max(self.seqlens_q) if self.seqlens_q else 0
+
+    @property
+    def max_seqlen_k(self) -> int:
+        return max(self.seqlens_k) if self.seqlens_k else 0
+
+
+def alibi_slopes(Hq: int) -> torch.Tensor:
+    """Per-query-head ALiBi slopes 2^(-8(h+1)/Hq), float64 rounded to float32."""
+    vals = [2.0 ** (-8.0 * (h + 1) / Hq) for h in range(Hq)]
+    return torch.tensor(vals, dtype=torch.float64).to(torch.float32)
+
+
+def default_scale(D: int) -> float:
+    """1/sqrt(D) rounded to float32 (the value the C entry point receives)."""
+    return float(np.float32(1.0 / math.sqrt(D)))
+
+
+def seqstart_from_lengths(lengths: Sequence[int]) -> torch.Tensor:
+    out = [0]
+    for L in lengths:
+        out.append(out[-1] + int(L))
+    return torch.tensor(out, dtype=torch.int32)
+
+
+def _lengths(w: Workload, seed: int) -> Tuple[List[int], List[int]]:
+    if w.seqlens is not None:
+        return list(w.seqlens), list(w.seqlens)
+    rng = np.random.default_rng(seed)
+    lk = [int(x) for x in rng.integers(w.len_lo, w.len_hi, size=w.num_seqs, endpoint=True)]
+    if w.decode:
+        return [1] * w.num_seqs, lk
+    return lk, list(lk)
+
+
+def _randn(g: torch.Generator, shape, dtype: torch.dtype) -> torch.Tensor:
+    return torch.randn(shape, generator=g, dtype=torch.float32).to(dtype)
+
+
+def generate(name_or_workload, seed: int = 0, *, causal: Optional[bool] = None,
+             alibi: Optional[bool] = None, num_seqs: Optional[int] = None) -> Inputs:
+    """Draw the inputs of one workload.
+
+    ``causal`` / ``alibi`` override the workload's mask choice (the pages run
+    the packed workload once without and once with the causal mask, and the
+    long varlen workload with and without ALiBi).  ``num_seqs`` keeps only the
+    first ``num_seqs`` sequences of a random-length workload (the same lengths
+    the full workload draws; the tensors are then drawn for that prefix only).
+    """
+    w = name_or_workload if isinstance(name_or_workload, Workload) else get_workload(name_or_workload)
+    lq, lk = _lengths(w, seed)
+    if num_seqs is not None:
+        lq, lk = lq[:num_seqs], lk[:num_seqs]
+    dt = _DTYPES[w.dtype]
+    g = torch.Generator("cpu").manual_seed(seed + 1)
+    Tq, Tk = sum(lq), sum(lk)
+    if w.bmghk is not None and num_seqs is None:
+        B, M, G, Hg = w.bmghk
+        q = _randn(g, (B, M, G, Hg, w.D), dt).view(B * M, G * Hg, w.D)
+        k = _randn(g, (B, M, G, 1, w.D), dt).view(B * M, G, w.D)
+        v = _randn(g, (B, M, G, 1, w.D), dt).view(B * M, G, w.D)
+    else:
+        q = _randn(g, (Tq, w.Hq, w.D), dt)
+        k = _randn(g, (Tk, w.Hkv, w.D), dt)
+        v = _randn(g, (Tk, w.Hkv, w.D), dt)
+    use_causal = w.causal if causal is None else causal
+    use_alibi = w.alibi if alibi is None else alibi
+    return Inputs(
+        q=q, k=k, v=v,
+        seqstart_q=seqstart_from_lengths(lq), seqstart_k=seqstart_from_lengths(lk),
+        seqlens_q=lq, seqlens_k=lk, Hq=w.Hq, Hkv=w.Hkv, D=w.D,
+        causal=use_causal, alibi_slopes=alibi_slopes(w.Hq) if use_alibi else None,
+        scale=default_scale(w.D), dtype=w.dtype, bmghk=w.bmghk if num_seqs is None else None)
+
+
+def random_case(seed: int, seqlens_q: Sequence[int], seqlens_k: Optional[Sequence[int]] = None,
+                Hq: int = 4, Hkv: int = 2, D: int = 64, dtype: str = "fp16",
+                causal: bool = False, alibi: bool = False, scale: Optional[float] = None,
+                slopes: Optional[torch.Tensor] = None, std: float = 1.0) -> Inputs:
+    """A free-form case for parity tests: given lengths, random N(0, std^2) q/k/v."""
+    lq = [int(x) for x in seqlens_q]
+    lk = list(lq) if seqlens_k is None else [int(x) for x in seqlens_k]
+    assert len(lq) == len(lk)
+    dt = _DTYPES[dtype] if isinstance(dtype, str) else dtype
+    g = torch.Generator("cpu").manual_seed(seed + 1)
+    Tq, Tk = sum(lq), sum(lk)
+    q = (torch.randn((Tq, Hq, D), generator=g) * std).to(dt)
+    k = (torch.randn((Tk, Hkv, D), generator=g) * std).to(dt)
+    v = (torch.randn((Tk, Hkv, D), generator=g) * std).to(dt)
+    if alibi and slopes is None:
+        slopes = alibi_slopes(Hq)
+    return Inputs(
+        q=q, k=k, v=v,
+        seqstart_q=seqstart_from_lengths(lq), seqstart_k=seqstart_from_lengths(lk),
+        seqlens_q=lq, seqlens_k=lk, Hq=Hq, Hkv=Hkv, D=D, causal=causal,
+        alibi_slopes=slopes if alibi else None,
+        scale=default_scale(D) if scale is None else float(np.float32(scale)),
+        dtype=dtype if isinstance(dtype, str) else {v_: k_ for k_, v_ in _DTYPES.items()}[dt])
+
+
+def sample_rows(inp: Inputs, count: int, seed: int = 0) -> List[Tuple[int, int]]:
+    """Deterministic (token, q head) picks for sampled checks at full size.
+
+    Always includes the first and last token of the first and last non-empty
+    sequence (the edges of the packing) and the last token of the longest one.
+    """
+    rng = np.random.default_rng(seed + 12345)
+    picks = set()
+    nonempty = [b for b, L in enumerate(inp.seqlens_q) if L > 0]
+    sq = inp.seqstart_q.tolist()
+    if nonempty:
+        longest = max(nonempty, key=lambda b: inp.seqlens_q[b])
+        for b in (nonempty[0], nonempty[-1], longest):
+            picks.add((sq[b], 0))
+            picks.add((sq[b + 1] - 1, inp.Hq - 1))
+    Tq = inp.total_q
+    while len(picks) < count and Tq > 0:
+        picks.add((int(rng.integers(0, Tq)), int(rng.integers(0, inp.Hq))))
+    return sorted(picks)

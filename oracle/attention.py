@@ -1,0 +1,152 @@
+"""Plain float64 attention over packed variable-length sequences (CPU oracle).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, ``__graft_entry__.smoke()``
+and ``bench.py``'s ``cpu_baseline`` leg, never by the product path.
+
+Sources (web pages; section names as printed on them):
+  [P1] "Cómo construir transformadores con memoria eficiente con xFormers usando
+       secuencias empaquetadas, GQA, ALiBi, SwiGLU y atención causal"
+       (7minutos.es) -- section 4, packed variable-length batch with
+       BlockDiagonalMask / BlockDiagonalCausalMask; section 5, grouped-query
+       attention in the 5-D BMGHK layout.
+  [P2] "How to Build Memory-Efficient Transformers with xFormers Using Packed
+       Sequences, GQA, ALiBi, SwiGLU, and Causal Attention" (yifor-blog) --
+       optimisation items 1 (packed sequences + block-diagonal mask), 2 (GQA),
+       3 (ALiBi: a different additive linear position penalty per head) and
+       5 (causal attention: implicit lower-triangular mask).
+  [P3] "multi query attention代码" (cidian.kuaisou.com) -- the self-attention
+       snippet: scores = Q K^T / sqrt(d_k), softmax, weighted sum of V.
+  [P5] "group query attention gqa" (cidian.kuaisou.com) -- GQA-G definition
+       (G groups, each sharing one K/V head; GQA-1 = MQA, GQA-H = MHA) and the
+       check that SDPA with enable_gqa equals SDPA after repeat_interleave of
+       the K/V heads along the head axis.
+
+Definition computed (for every sequence b and query head h):
+  L_q, L_k = lengths of sequence b; off = L_k - L_q;
+  g = h // (Hq // Hkv)                                     [P5; P1 section 5]
+  S[r, j] = scale * sum_d q[sq_b + r, h, d] * k[sk_b + j, g, d]      [P3]
+  with ALiBi:   S[r, j] -= slope_h * |(r + off) - j|              [P2 item 3]
+  with causal:  S[r, j] = -inf where j > r + off                  [P2 item 5]
+  keys of other sequences never enter row r            [P1 section 4; P2 item 1]
+  lse[h, sq_b + r] = ln sum_j exp(S[r, j])   (-inf for a row with no key)
+  out[sq_b + r, h, :] = sum_j exp(S[r, j] - lse) v[sk_b + j, g, :]  (0 if empty)
+
+Readings where the pages are silent (each is listed in the design notes):
+  * scale is applied to Q K^T before the bias is added, and the bias is not
+    scaled;
+  * ALiBi positions are local to each sequence; the penalty is
+    slope * distance, slopes given per query head;
+  * when L_q != L_k, query row r sits at key position r + off (queries are the
+    last L_q positions of the sequence; a single decode query sees its whole
+    KV history);
+  * a row with no allowed key has out = 0 and lse = -inf;
+  * lse is the natural-log normaliser of the scaled, biased, masked scores.
+Parity unpinned by the pages: the ALiBi slope values (an input here), the
+non-causal |i - j| form of ALiBi, the L_q != L_k causal alignment beyond the
+decode == last-prefill-row identity, and the empty-row convention.
+"""
+from __future__ import annotations
+
+from typing import List, Optional, Sequence, Tuple
+
+import torch
+
+__all__ = ["attention_forward", "attention_rows"]
+
+
+def _f64(x: torch.Tensor) -> torch.Tensor:
+    """Exact upcast of the given fp16/bf16/fp32 values to float64 on the CPU."""
+    return x.detach().to("cpu").to(torch.float64)
+
+
+def _starts(seqstart) -> List[int]:
+    return [int(s) for s in (seqstart.tolist() if torch.is_tensor(seqstart) else seqstart)]
+
+
+def _one_row_block(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, qpos: torch.Tensor,
+                   causal: bool, slope: Optional[float], scale: float
+                   ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Attention of query rows Q [R, D] (at key positions qpos [R]) over one
+    sequence's keys K, V [L_k, D].  Returns out [R, D] and lse [R]."""
+    L_k = K.shape[0]
+    kpos = torch.arange(L_k, dtype=torch.float64)
+    S = scale * (Q @ K.transpose(0, 1))                       # [P3]: scaled scores
+    if slope is not None:                                      # [P2 item 3]: ALiBi
+        S = S - slope * (qpos[:, None] - kpos[None, :]).abs()
+    if causal:                                                 # [P2 item 5]
+        S = S.masked_fill(kpos[None, :] > qpos[:, None], float("-inf"))
+    if L_k == 0:
+        lse = torch.full((Q.shape[0],), float("-inf"), dtype=torch.float64)
+    else:
+        lse = torch.logsumexp(S, dim=1)
+    empty = torch.isneginf(lse)
+    P = torch.exp(S - torch.where(empty, 0.0, lse)[:, None])  # softmax weights
+    P = torch.where(empty[:, None], 0.0, P)
+    out = P @ V
+    return out, lse
+
+
+def attention_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                      seqstart_q, seqstart_k, *, causal: bool = False,
+                      alibi_slopes: Optional[torch.Tensor] = None,
+                      scale: Optional[float] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Reference forward over packed sequences.
+
+    q [Tq, Hq, D], k and v [Tk, Hkv, D] (any float dtype, upcast exactly);
+    seqstart_q / seqstart_k: n+1 non-decreasing offsets starting at 0.
+    Returns out float64 [Tq, Hq, D] and lse float64 [Hq, Tq].  ``scale`` None
+    means 1/sqrt(D) [P3].  Slopes are taken at their given (float32) values.
+    """
+    Q64, K64, V64 = _f64(q), _f64(k), _f64(v)
+    Tq, Hq, D = Q64.shape
+    Tk, Hkv, Dk = K64.shape
+    assert Dk == D and tuple(V64.shape) == (Tk, Hkv, D) and Hq % Hkv == 0
+    if scale is None:
+        scale = D ** -0.5
+    slopes = None if alibi_slopes is None else [float(s) for s in _f64(alibi_slopes)]
+    sq, sk = _starts(seqstart_q), _starts(seqstart_k)
+    assert len(sq) == len(sk)
+    per_group = Hq // Hkv
+    out = torch.zeros((Tq, Hq, D), dtype=torch.float64)
+    lse = torch.full((Hq, Tq), float("-inf"), dtype=torch.float64)
+    for b in range(len(sq) - 1):
+        L_q, L_k = sq[b + 1] - sq[b], sk[b + 1] - sk[b]
+        if L_q == 0:
+            continue
+        qpos = torch.arange(L_q, dtype=torch.float64) + (L_k - L_q)
+        for h in range(Hq):
+            g = h // per_group                                  # [P5]: head grouping
+            o, l = _one_row_block(Q64[sq[b]:sq[b + 1], h, :], K64[sk[b]:sk[b + 1], g, :],
+                                  V64[sk[b]:sk[b + 1], g, :], qpos, causal,
+                                  None if slopes is None else slopes[h], float(scale))
+            out[sq[b]:sq[b + 1], h, :] = o
+            lse[h, sq[b]:sq[b + 1]] = l
+    return out, lse
+
+
+def attention_rows(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seqstart_q, seqstart_k,
+                   rows: Sequence[Tuple[int, int]], *, causal: bool = False,
+                   alibi_slopes: Optional[torch.Tensor] = None,
+                   scale: Optional[float] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The same definition evaluated for selected (packed token, query head)
+    rows only, for sampled checks on inputs too large to do whole.
+    Returns out float64 [len(rows), D] and lse float64 [len(rows)]."""
+    Tq, Hq, D = q.shape
+    Tk, Hkv, _ = k.shape
+    if scale is None:
+        scale = D ** -0.5
+    sq, sk = _starts(seqstart_q), _starts(seqstart_k)
+    per_group = Hq // Hkv
+    outs = torch.zeros((len(rows), D), dtype=torch.float64)
+    lses = torch.full((len(rows),), float("-inf"), dtype=torch.float64)
+    for n, (t, h) in enumerate(rows):
+        b = max(i for i in range(len(sq) - 1) if sq[i] <= t < sq[i + 1])
+        L_q, L_k = sq[b + 1] - sq[b], sk[b + 1] - sk[b]
+        g = h // per_group
+        qpos = torch.tensor([t - sq[b] + (L_k - L_q)], dtype=torch.float64)
+        slope = None if alibi_slopes is None else float(_f64(alibi_slopes)[h])
+        o, l = _one_row_block(_f64(q[t:t + 1, h, :]), _f64(k[sk[b]:sk[b + 1], g, :]),
+                              _f64(v[sk[b]:sk[b + 1], g, :]), qpos, causal, slope, float(scale))
+        outs[n] = o[0]
+        lses[n] = l[0]
+    return outs, lses
