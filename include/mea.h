@@ -1,0 +1,178 @@
+/*
+ * mea.h -- C ABI of the fused memory-efficient attention forward for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What is computed (for every packed sequence b and query head h):
+ *
+ *   out[t, h, :] = sum_j softmax_j(scale * q[t, h, :] . k[j, g(h), :] + bias) v[j, g(h), :]
+ *
+ * where j runs over the keys of sequence b only (block-diagonal mask over
+ * packed variable-length sequences: "Cómo construir transformadores con
+ * memoria eficiente con xFormers ..." (7minutos.es), section 4, and "How to
+ * Build Memory-Efficient Transformers with xFormers ..." (yifor-blog),
+ * optimisation item 1), the scores are the scaled dot products of the
+ * self-attention snippet on "multi query attention代码" (cidian.kuaisou.com),
+ * g(h) = h / (Hq / Hkv) is the shared key/value head of query head h
+ * (grouped-query attention: the GQA definition and the enable_gqa /
+ * repeat_interleave check on "group query attention gqa", and the BMGHK
+ * layout of the tutorial's section 5), and the bias is
+ *   - ALiBi (yifor-blog, item 3): -slope[h] * |(r + L_k - L_q) - j| for query
+ *     row r of the sequence, positions local to the sequence;
+ *   - causal (yifor-blog, item 5): -inf where j > r + L_k - L_q (the queries
+ *     are the last L_q positions of the sequence, so a single query sees its
+ *     whole key history).
+ * A row with no allowed key gets out = 0 and lse = -inf.
+ *
+ * The N x N score matrix is never written to memory: scores are produced
+ * tile by tile on the matrix cores and folded into an online softmax.  A call
+ * whose longest query sequence has one token (max_seqlen_q == 1, the decode
+ * case) splits each sequence's keys into chunks processed in parallel and
+ * merges the chunk results by their log-sum-exp (the split-K scheme named in
+ * section 1 of "大模型推理加速终极指南：xformers如何让Transformer性能飙升300%"
+ * (zizhi168.cn)).
+ *
+ * Layouts (row-major, contiguous, element = 16-bit float of `dtype`):
+ *   q, out       [total_q, Hq, D]
+ *   k, v         [total_k, Hkv, D]
+ *   lse          [Hq, total_q] float32 (natural log)
+ *   seqstart_q   int32 [num_seqs + 1]: sequence b owns query rows
+ *                seqstart_q[b] .. seqstart_q[b+1]-1; same for seqstart_k.
+ *   alibi_slopes float32 [Hq] (per query head) or NULL for no ALiBi.
+ *
+ * Ownership: every pointer argument is caller-owned DEVICE memory (q, k, v,
+ * out, lse, seqstart_q, seqstart_k, alibi_slopes, workspace).  The library
+ * allocates no memory, keeps no pointer after a call returns, and has no
+ * global mutable state apart from the thread-local error text.
+ *
+ * Execution: the work is enqueued on `stream` (a hipStream_t; NULL = the null
+ * stream) and the call returns without synchronising.  Faults during
+ * execution surface at the caller's next synchronisation, as for any HIP
+ * kernel.  Calls on different streams may run concurrently; calls sharing a
+ * workspace buffer must be ordered by the caller.
+ *
+ * Errors: arguments are validated before anything is enqueued; a non-OK
+ * status means nothing was launched and no output byte was written (except
+ * MEA_ERR_HIP, a launch failure reported by the HIP runtime).
+ * mea_last_error() returns a thread-local description of the last non-OK
+ * status of the calling thread.
+ */
+#ifndef MEA_H_
+#define MEA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MEA_ABI_VERSION 1
+
+#if defined(__GNUC__)
+#define MEA_EXPORT __attribute__((visibility("default")))
+#else
+#define MEA_EXPORT
+#endif
+
+typedef enum {
+  MEA_OK = 0,
+  MEA_ERR_INVALID = 1,      /* malformed argument (null pointer, bad sizes, workspace too small) */
+  MEA_ERR_UNSUPPORTED = 2,  /* well-formed but outside what the kernels implement */
+  MEA_ERR_HIP = 3           /* the HIP runtime refused a launch */
+} mea_status_t;
+
+typedef enum {
+  MEA_F16 = 0,   /* IEEE binary16 in and out; scores and softmax in float32 */
+  MEA_BF16 = 1   /* bfloat16 in and out; scores and softmax in float32 */
+} mea_dtype_t;
+
+/*
+ * mea_fwd -- attention forward over packed sequences (definition above).
+ *
+ *   q, k, v        device inputs, layouts above, 16-byte aligned.
+ *   out            device output [total_q, Hq, D], 16-byte aligned.  Rows of
+ *                  sequences with L_q = 0 do not exist; every other row is
+ *                  written.
+ *   lse            device output [Hq, total_q] float32, or NULL to skip it.
+ *   seqstart_q/k   device int32 [num_seqs + 1].  Preconditions (not checked:
+ *                  checking would need a device synchronisation):
+ *                  seqstart_*[0] == 0, non-decreasing, seqstart_q[num_seqs]
+ *                  == total_q, and every sequence length <= max_seqlen_q
+ *                  (resp. max_seqlen_k).  Violations read or write out of
+ *                  bounds.
+ *   num_seqs       >= 0; 0 (or total_q == 0) is a no-op returning MEA_OK.
+ *   total_q        number of packed query rows (the lse row stride).
+ *   max_seqlen_q/k upper bounds of the per-sequence lengths (sizes the grid).
+ *   Hq, Hkv        query / key-value heads; Hq % Hkv == 0.
+ *   D              head dimension, 64 or 128 (q, k and v share it).
+ *   dtype          MEA_F16 or MEA_BF16 (all of q, k, v, out).
+ *   causal         0 or 1.
+ *   alibi_slopes   device float32 [Hq] or NULL.
+ *   scale          finite and > 0 (1/sqrt(D) is the usual choice).
+ *   workspace      device scratch of at least mea_fwd_workspace_size(...)
+ *                  bytes, 256-byte aligned; may be NULL when that size is 0
+ *                  (every call with max_seqlen_q != 1).
+ *   stream         hipStream_t to enqueue on.
+ *
+ * Returns MEA_ERR_INVALID for: a NULL q/k/v/out/seqstart pointer; negative
+ * sizes; Hq or Hkv <= 0 or Hq % Hkv != 0; total_q > 0 with max_seqlen_q == 0;
+ * causal not 0/1; a workspace smaller than required.
+ * Returns MEA_ERR_UNSUPPORTED for: D not 64/128; dtype not listed; a
+ * non-finite or non-positive scale; a pointer not aligned as stated.
+ *
+ * Numerics: Q K^T runs on the matrix cores in the input dtype with float32
+ * accumulation; the softmax is float32; the softmax weights enter P V as
+ * IEEE half with V converted to half (exact for bfloat16 V with
+ * 2^-14 <= |v| <= 65504; larger magnitudes saturate, smaller lose bits
+ * below 2^-24); out is rounded to nearest even from float32.
+ */
+MEA_EXPORT mea_status_t mea_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                     const int32_t* seqstart_q, const int32_t* seqstart_k, int32_t num_seqs,
+                     int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq,
+                     int32_t Hkv, int32_t D, mea_dtype_t dtype, int32_t causal,
+                     const float* alibi_slopes, float scale, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
+ * mea_fwd_splitkv -- mea_fwd for the decode case (max_seqlen_q must be 1)
+ * with the key-chunk length forced to `chunk_keys` (a positive multiple of
+ * 128) instead of the library's choice.  The result does not depend on the
+ * chunk length beyond float32 rounding; this entry point exists to test that.
+ * Same arguments, ownership and errors as mea_fwd, plus MEA_ERR_INVALID for a
+ * bad chunk_keys or max_seqlen_q != 1.
+ */
+MEA_EXPORT mea_status_t mea_fwd_splitkv(const void* q, const void* k, const void* v, void* out, float* lse,
+                             const int32_t* seqstart_q, const int32_t* seqstart_k,
+                             int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
+                             int32_t max_seqlen_k, int32_t Hq, int32_t Hkv, int32_t D,
+                             mea_dtype_t dtype, int32_t causal, const float* alibi_slopes,
+                             float scale, void* workspace, size_t workspace_bytes, void* stream,
+                             int32_t chunk_keys);
+
+/*
+ * mea_fwd_workspace_size -- bytes of workspace mea_fwd (chunk_keys == 0) or
+ * mea_fwd_splitkv (chunk_keys > 0) needs for these sizes: 0 unless
+ * max_seqlen_q == 1, else num_seqs * ceil(max_seqlen_k / chunk) * Hq * (D + 1)
+ * * 4 (float32 partial outputs and log-sum-exps).  Returns 0 for arguments
+ * mea_fwd would reject.  Pure host function.
+ */
+MEA_EXPORT size_t mea_fwd_workspace_size(int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                              int32_t Hq, int32_t Hkv, int32_t D, int32_t chunk_keys);
+
+/* Key-chunk length mea_fwd picks for a decode call of these sizes. Pure host function. */
+MEA_EXPORT int32_t mea_default_chunk_keys(int32_t num_seqs, int32_t max_seqlen_k, int32_t Hkv);
+
+/* Static text for a status code. */
+MEA_EXPORT const char* mea_status_string(mea_status_t status);
+
+/* Thread-local detail for the calling thread's last non-OK status ("" if none). */
+MEA_EXPORT const char* mea_last_error(void);
+
+/* MEA_ABI_VERSION of the built library. */
+MEA_EXPORT int32_t mea_abi_version(void);
+
+#ifdef __cplusplus
+}  /* extern "C" */
+#endif
+
+#endif /* MEA_H_ */

@@ -1,0 +1,108 @@
+"""ctypes binding of the C ABI in ``include/mea.h`` (argument marshalling only).
+
+Every function here has the name and the argument order of the C entry point
+it wraps and passes plain integers (device addresses, sizes) straight
+through.  Loading fails loudly if ``libmea.so`` has not been built: there is
+no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+__all__ = [
+    "MEA_OK", "MEA_ERR_INVALID", "MEA_ERR_UNSUPPORTED", "MEA_ERR_HIP", "MEA_F16", "MEA_BF16",
+    "EXPORTED_SYMBOLS", "library_path", "load", "mea_fwd", "mea_fwd_splitkv",
+    "mea_fwd_workspace_size", "mea_default_chunk_keys", "mea_status_string", "mea_last_error",
+    "mea_abi_version",
+]
+
+MEA_OK, MEA_ERR_INVALID, MEA_ERR_UNSUPPORTED, MEA_ERR_HIP = 0, 1, 2, 3
+MEA_F16, MEA_BF16 = 0, 1
+
+EXPORTED_SYMBOLS = (
+    "mea_fwd", "mea_fwd_splitkv", "mea_fwd_workspace_size", "mea_default_chunk_keys",
+    "mea_status_string", "mea_last_error", "mea_abi_version",
+)
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+_lock = threading.Lock()
+_lib = None
+
+_i32, _sz, _vp, _f32 = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+_FWD_ARGS = [_vp, _vp, _vp, _vp, _vp,          # q k v out lse
+             _vp, _vp, _i32, _i32, _i32, _i32,  # seqstart_q seqstart_k num_seqs total_q max_q max_k
+             _i32, _i32, _i32, _i32, _i32,      # Hq Hkv D dtype causal
+             _vp, _f32, _vp, _sz, _vp]          # slopes scale workspace workspace_bytes stream
+
+
+def library_path() -> str:
+    return os.environ.get("MEA_LIBRARY", os.path.join(_PKG_DIR, "libmea.so"))
+
+
+def load() -> ctypes.CDLL:
+    """Load ``libmea.so`` (once).  Raises if it is missing or incomplete."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"HIP library {path} is not built; run `python -m memory_efficient_attention_amd.build` "
+                "(there is no CPU fallback)")
+        lib = ctypes.CDLL(path)
+        lib.mea_fwd.argtypes = _FWD_ARGS
+        lib.mea_fwd.restype = ctypes.c_int
+        lib.mea_fwd_splitkv.argtypes = _FWD_ARGS + [_i32]
+        lib.mea_fwd_splitkv.restype = ctypes.c_int
+        lib.mea_fwd_workspace_size.argtypes = [_i32] * 7
+        lib.mea_fwd_workspace_size.restype = _sz
+        lib.mea_default_chunk_keys.argtypes = [_i32] * 3
+        lib.mea_default_chunk_keys.restype = _i32
+        lib.mea_status_string.argtypes = [ctypes.c_int]
+        lib.mea_status_string.restype = ctypes.c_char_p
+        lib.mea_last_error.argtypes = []
+        lib.mea_last_error.restype = ctypes.c_char_p
+        lib.mea_abi_version.argtypes = []
+        lib.mea_abi_version.restype = _i32
+        _lib = lib
+        return lib
+
+
+def mea_fwd(q, k, v, out, lse, seqstart_q, seqstart_k, num_seqs, total_q, max_seqlen_q,
+            max_seqlen_k, Hq, Hkv, D, dtype, causal, alibi_slopes, scale, workspace,
+            workspace_bytes, stream) -> int:
+    return load().mea_fwd(q, k, v, out, lse, seqstart_q, seqstart_k, num_seqs, total_q,
+                          max_seqlen_q, max_seqlen_k, Hq, Hkv, D, dtype, causal, alibi_slopes,
+                          scale, workspace, workspace_bytes, stream)
+
+
+def mea_fwd_splitkv(q, k, v, out, lse, seqstart_q, seqstart_k, num_seqs, total_q, max_seqlen_q,
+                    max_seqlen_k, Hq, Hkv, D, dtype, causal, alibi_slopes, scale, workspace,
+                    workspace_bytes, stream, chunk_keys) -> int:
+    return load().mea_fwd_splitkv(q, k, v, out, lse, seqstart_q, seqstart_k, num_seqs, total_q,
+                                  max_seqlen_q, max_seqlen_k, Hq, Hkv, D, dtype, causal,
+                                  alibi_slopes, scale, workspace, workspace_bytes, stream,
+                                  chunk_keys)
+
+
+def mea_fwd_workspace_size(num_seqs, max_seqlen_q, max_seqlen_k, Hq, Hkv, D, chunk_keys=0) -> int:
+    return int(load().mea_fwd_workspace_size(num_seqs, max_seqlen_q, max_seqlen_k, Hq, Hkv, D, chunk_keys))
+
+
+def mea_default_chunk_keys(num_seqs, max_seqlen_k, Hkv) -> int:
+    return int(load().mea_default_chunk_keys(num_seqs, max_seqlen_k, Hkv))
+
+
+def mea_status_string(status: int) -> str:
+    return load().mea_status_string(status).decode()
+
+
+def mea_last_error() -> str:
+    return load().mea_last_error().decode()
+
+
+def mea_abi_version() -> int:
+    return int(load().mea_abi_version())

@@ -1,0 +1,259 @@
+"""Python front end: xFormers-style masks and the attention call.
+
+Marshalling only: shapes are checked and viewed packed, outputs and the
+decode workspace are allocated with torch (device memory and streams are all
+torch provides here), and every step of the computation runs in the HIP
+library through ``_native``.  The call surface follows the tutorial page
+"Cómo construir transformadores con memoria eficiente con xFormers ..."
+(7minutos.es): section 4 (``BlockDiagonalMask.from_seqlens``, the causal
+variant, ``memory_efficient_attention(q, k, v, attn_bias=...)`` on a packed
+``[1, total, H, K]`` batch, and ``mask.split(out)``), and section 5 (the
+5-D BMGHK grouped-query layout ``[B, M, G, Hq, K]`` with key/value heads
+``[B, M, G, 1, K]``).
+"""
+from __future__ import annotations
+
+import math
+from typing import List, Optional, Sequence, Tuple, Union
+
+import numpy as np
+import torch
+
+from . import _native
+
+__all__ = [
+    "BlockDiagonalMask", "BlockDiagonalCausalMask", "memory_efficient_attention",
+    "attention_packed", "MeaError",
+]
+
+
+class MeaError(RuntimeError):
+    """A non-OK status from the C entry point (its code is ``.status``)."""
+
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{_native.mea_status_string(status)}: {detail}")
+        self.status = status
+
+
+def _seqstart(lengths: Sequence[int]) -> List[int]:
+    out = [0]
+    for L in lengths:
+        out.append(out[-1] + int(L))
+    return out
+
+
+class BlockDiagonalMask:
+    """Attention only within each packed sequence (no padding between them).
+
+    ``q_seqlen[b]`` queries of sequence b attend to its ``kv_seqlen[b]``
+    keys; both are packed back to back along the token axis.
+    """
+
+    causal = False
+
+    def __init__(self, q_seqlen: Sequence[int], kv_seqlen: Optional[Sequence[int]] = None):
+        q = [int(x) for x in q_seqlen]
+        kv = list(q) if kv_seqlen is None else [int(x) for x in kv_seqlen]
+        if len(q) != len(kv):
+            raise ValueError(f"{len(q)} query lengths but {len(kv)} key lengths")
+        if any(x < 0 for x in q) or any(x < 0 for x in kv):
+            raise ValueError("sequence lengths must be non-negative")
+        self.q_seqlen: List[int] = q
+        self.kv_seqlen: List[int] = kv
+        self.q_seqstart: List[int] = _seqstart(q)
+        self.kv_seqstart: List[int] = _seqstart(kv)
+        self._dev = {}
+
+    @classmethod
+    def from_seqlens(cls, q_seqlen: Sequence[int], kv_seqlen: Optional[Sequence[int]] = None):
+        return cls(q_seqlen, kv_seqlen)
+
+    @property
+    def num_seqs(self) -> int:
+        return len(self.q_seqlen)
+
+    @property
+    def total_q(self) -> int:
+        return self.q_seqstart[-1]
+
+    @property
+    def total_kv(self) -> int:
+        return self.kv_seqstart[-1]
+
+    @property
+    def max_seqlen_q(self) -> int:
+        return max(self.q_seqlen, default=0)
+
+    @property
+    def max_seqlen_kv(self) -> int:
+        return max(self.kv_seqlen, default=0)
+
+    def seqstart_tensors(self, device) -> Tuple[torch.Tensor, torch.Tensor]:
+        """int32 device copies of the sequence offsets (cached per device)."""
+        key = str(torch.device(device))
+        if key not in self._dev:
+            self._dev[key] = (torch.tensor(self.q_seqstart, dtype=torch.int32, device=device),
+                              torch.tensor(self.kv_seqstart, dtype=torch.int32, device=device))
+        return self._dev[key]
+
+    def split(self, x: torch.Tensor) -> List[torch.Tensor]:
+        """Per-sequence views of a packed query-side tensor ``[1, total_q, ...]``
+        (or ``[total_q, ...]``): piece b is ``[1, q_seqlen[b], ...]``."""
+        return self._split(x, self.q_seqstart)
+
+    def split_kv(self, x: torch.Tensor) -> List[torch.Tensor]:
+        return self._split(x, self.kv_seqstart)
+
+    @staticmethod
+    def _split(x: torch.Tensor, starts: List[int]) -> List[torch.Tensor]:
+        packed = x[0] if (x.dim() >= 2 and x.shape[0] == 1 and x.shape[1] == starts[-1]) else x
+        if packed.shape[0] != starts[-1]:
+            raise ValueError(f"tensor has {packed.shape[0]} rows, mask covers {starts[-1]}")
+        return [packed[starts[b]:starts[b + 1]].unsqueeze(0) for b in range(len(starts) - 1)]
+
+
+class BlockDiagonalCausalMask(BlockDiagonalMask):
+    """Block-diagonal plus a causal mask inside each sequence.  When a
+    sequence has fewer queries than keys, its queries are its last positions."""
+
+    causal = True
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float16:
+        return _native.MEA_F16
+    if dt == torch.bfloat16:
+        return _native.MEA_BF16
+    raise TypeError(f"dtype {dt} is not supported (float16 or bfloat16)")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def attention_packed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                     seqstart_q: torch.Tensor, seqstart_k: torch.Tensor,
+                     max_seqlen_q: int, max_seqlen_k: int, *, causal: bool = False,
+                     alibi_slopes: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                     return_lse: bool = False, out: Optional[torch.Tensor] = None,
+                     lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                     chunk_keys: Optional[int] = None, stream: Optional[torch.cuda.Stream] = None):
+    """Packed call: q ``[Tq, Hq, D]``, k/v ``[Tk, Hkv, D]`` (contiguous device
+    tensors), int32 device ``seqstart_q/k`` ``[n + 1]``.  Returns ``out`` or
+    ``(out, lse)`` with lse ``[Hq, Tq]`` float32.  ``chunk_keys`` forces the
+    decode split length (only for max_seqlen_q == 1)."""
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("packed q, k, v must be [tokens, heads, D]")
+    Tq, Hq, D = q.shape
+    Tk, Hkv, Dk = k.shape
+    if Dk != D or tuple(v.shape) != (Tk, Hkv, D):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share a dtype")
+    dev = q.device
+    if dev.type != "cuda" or k.device != dev or v.device != dev:
+        raise ValueError("q, k and v must be on the same GPU")
+    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    if seqstart_q.dtype != torch.int32 or seqstart_k.dtype != torch.int32:
+        raise TypeError("seqstart tensors must be int32")
+    if seqstart_q.device != dev or seqstart_k.device != dev:
+        raise ValueError("seqstart tensors must be on the same GPU as q")
+    num_seqs = seqstart_q.numel() - 1
+    if seqstart_k.numel() != num_seqs + 1:
+        raise ValueError("seqstart_q and seqstart_k differ in length")
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((Hq, Tq), dtype=torch.float32, device=dev)
+    slopes = None
+    if alibi_slopes is not None:
+        slopes = alibi_slopes.to(device=dev, dtype=torch.float32).contiguous()
+        if slopes.numel() != Hq:
+            raise ValueError(f"alibi_slopes needs {Hq} values (one per query head)")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    scale = float(np.float32(scale))
+    ws_bytes = _native.mea_fwd_workspace_size(num_seqs, max_seqlen_q, max_seqlen_k, Hq, Hkv, D,
+                                              int(chunk_keys or 0))
+    if ws_bytes > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(seqstart_q), _ptr(seqstart_k),
+            num_seqs, Tq, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, D, _dtype_code(q.dtype),
+            int(bool(causal)), _ptr(slopes), scale, _ptr(workspace) if ws_bytes > 0 else None,
+            ws_bytes, stream.cuda_stream)
+    with torch.cuda.device(dev):
+        if chunk_keys is None:
+            st = _native.mea_fwd(*args)
+        else:
+            st = _native.mea_fwd_splitkv(*args, int(chunk_keys))
+    if st != _native.MEA_OK:
+        raise MeaError(st, _native.mea_last_error())
+    return (out, lse) if return_lse else out
+
+
+def _kv_heads_bmghk(k: torch.Tensor, hq: int) -> torch.Tensor:
+    """[B, M, G, Hk, K] key/value tensor with Hk == 1 (or broadcast along that
+    axis) -> [B, M, G, K]; Hk == hq (one K/V head per query head) -> [B, M, G*hq, K]."""
+    B, M, G, Hk, K = k.shape
+    if Hk == 1 or k.stride(3) == 0:
+        return k[:, :, :, 0, :]
+    if Hk == hq:
+        return k.reshape(B, M, G * Hk, K)
+    raise ValueError(f"BMGHK key/value head axis must be 1 or {hq}, got {Hk}")
+
+
+def memory_efficient_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                               attn_bias: Optional[BlockDiagonalMask] = None, *,
+                               scale: Optional[float] = None,
+                               alibi_slopes: Optional[torch.Tensor] = None,
+                               return_lse: bool = False):
+    """softmax(q k^T * scale + bias) v without materialising the scores.
+
+    Layouts: BMHK ``q [B, M, Hq, K]``, ``k/v [B, Mk, Hkv, K]`` with Hq a
+    multiple of Hkv (query head h reads key/value head h // (Hq/Hkv)); or BMGHK
+    ``q [B, M, G, Hq, K]``, ``k/v [B, Mk, G, 1, K]`` (G groups).  Without a
+    mask every batch element is attended on its own; with a
+    ``BlockDiagonalMask`` / ``BlockDiagonalCausalMask`` the batch must be 1
+    and the token axis is the packed sequences.  ``alibi_slopes`` (one per
+    query head, in the flattened head order) adds -slope * |i - j| with
+    sequence-local positions.  Returns a tensor shaped like ``q`` (and the
+    log-sum-exp ``[Hq_total, B*M]`` float32 if ``return_lse``).
+    """
+    if q.dim() == 5:
+        B, M, G, Hg, K = q.shape
+        qp = q.reshape(B * M, G * Hg, K)
+        kp = _kv_heads_bmghk(k, Hg)
+        vp = _kv_heads_bmghk(v, Hg)
+        Mk = kp.shape[1]
+        kp = kp.reshape(B * Mk, kp.shape[2], K)
+        vp = vp.reshape(B * Mk, vp.shape[2], K)
+    elif q.dim() == 4:
+        B, M, Hq, K = q.shape
+        Mk = k.shape[1]
+        qp = q.reshape(B * M, Hq, K)
+        kp = k.reshape(B * Mk, k.shape[2], K)
+        vp = v.reshape(B * Mk, v.shape[2], K)
+    else:
+        raise ValueError("q must be BMHK [B, M, H, K] or BMGHK [B, M, G, H, K]")
+    if tuple(k.shape) != tuple(v.shape):
+        raise ValueError("k and v must have the same shape")
+    if attn_bias is None:
+        mask = BlockDiagonalMask([M] * B, [Mk] * B)
+    else:
+        if not isinstance(attn_bias, BlockDiagonalMask):
+            raise TypeError(f"unsupported attn_bias {type(attn_bias).__name__}")
+        if B != 1:
+            raise ValueError("a block-diagonal mask needs batch size 1 (sequences packed along M)")
+        if attn_bias.total_q != M or attn_bias.total_kv != Mk:
+            raise ValueError(f"mask covers {attn_bias.total_q} queries / {attn_bias.total_kv} keys, "
+                             f"tensors have {M} / {Mk}")
+        mask = attn_bias
+    ssq, ssk = mask.seqstart_tensors(q.device)
+    res = attention_packed(qp, kp, vp, ssq, ssk, mask.max_seqlen_q, mask.max_seqlen_kv,
+                           causal=mask.causal, alibi_slopes=alibi_slopes, scale=scale,
+                           return_lse=return_lse)
+    if return_lse:
+        return res[0].view(q.shape), res[1]
+    return res.view(q.shape)

@@ -1,0 +1,191 @@
+// C ABI of the attention forward: argument validation, path choice, launch.
+// The contract (layouts, ownership, errors) is documented in include/mea.h.
+#include "mea.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdint>
+
+#include "mea_launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+mea_status_t fail(mea_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+int gcd_int(int x, int y) {
+  while (y != 0) {
+    const int t = x % y;
+    x = y;
+    y = t;
+  }
+  return x;
+}
+
+int32_t default_chunk(int32_t num_seqs, int32_t max_seqlen_k, int32_t Hkv) {
+  // Enough (sequence, chunk, kv-head) workgroups to fill 256 CUs several
+  // times over, but chunks long enough that the partials stay a small
+  // fraction of the K/V bytes.
+  const long long work = (long long)num_seqs * (long long)max_seqlen_k * (long long)Hkv;
+  long long c = (work + 2047) / 2048;
+  c = ((c + mea::kDcBN - 1) / mea::kDcBN) * mea::kDcBN;
+  if (c < mea::kDcBN) c = mea::kDcBN;
+  if (c > 1024) c = 1024;
+  return (int32_t)c;
+}
+
+size_t decode_ws_bytes(int32_t num_seqs, int32_t max_seqlen_k, int32_t Hq, int32_t D, int32_t chunk) {
+  const size_t nch = (size_t)((max_seqlen_k + chunk - 1) / chunk);
+  return (size_t)num_seqs * nch * (size_t)Hq * (size_t)(D + 1) * sizeof(float);
+}
+
+mea_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse,
+                      const int32_t* seqstart_q, const int32_t* seqstart_k, int32_t num_seqs,
+                      int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq,
+                      int32_t Hkv, int32_t D, mea_dtype_t dtype, int32_t causal,
+                      const float* alibi_slopes, float scale, void* workspace,
+                      size_t workspace_bytes, void* stream, int32_t chunk_keys, bool forced_split) {
+  g_last_error[0] = '\0';
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
+    return fail(MEA_ERR_INVALID, "q, k, v and out must be non-NULL device pointers");
+  if (seqstart_q == nullptr || seqstart_k == nullptr)
+    return fail(MEA_ERR_INVALID, "seqstart_q and seqstart_k must be non-NULL device pointers");
+  if (num_seqs < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+    return fail(MEA_ERR_INVALID, "negative size (num_seqs=%d total_q=%d max_seqlen_q=%d max_seqlen_k=%d)",
+                num_seqs, total_q, max_seqlen_q, max_seqlen_k);
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
+    return fail(MEA_ERR_INVALID, "need Hq > 0, Hkv > 0 and Hq %% Hkv == 0 (Hq=%d Hkv=%d)", Hq, Hkv);
+  if (causal != 0 && causal != 1) return fail(MEA_ERR_INVALID, "causal must be 0 or 1 (got %d)", causal);
+  if (total_q > 0 && max_seqlen_q == 0)
+    return fail(MEA_ERR_INVALID, "total_q=%d > 0 but max_seqlen_q == 0", total_q);
+  if (forced_split) {
+    if (max_seqlen_q != 1) return fail(MEA_ERR_INVALID, "mea_fwd_splitkv needs max_seqlen_q == 1 (got %d)", max_seqlen_q);
+    if (chunk_keys <= 0 || chunk_keys % mea::kDcBN != 0)
+      return fail(MEA_ERR_INVALID, "chunk_keys must be a positive multiple of %d (got %d)", mea::kDcBN, chunk_keys);
+  }
+  if (D != 64 && D != 128) return fail(MEA_ERR_UNSUPPORTED, "head dimension D=%d is not 64 or 128", D);
+  if (dtype != MEA_F16 && dtype != MEA_BF16) return fail(MEA_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(MEA_ERR_UNSUPPORTED, "scale must be finite and > 0 (got %g)", (double)scale);
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return fail(MEA_ERR_UNSUPPORTED, "q, k, v and out must be 16-byte aligned");
+  if ((lse != nullptr && !aligned(lse, 4)) || (alibi_slopes != nullptr && !aligned(alibi_slopes, 4)) ||
+      !aligned(seqstart_q, 4) || !aligned(seqstart_k, 4))
+    return fail(MEA_ERR_UNSUPPORTED, "lse, alibi_slopes and seqstart arrays must be 4-byte aligned");
+  if (num_seqs > 65535) return fail(MEA_ERR_UNSUPPORTED, "num_seqs=%d exceeds 65535", num_seqs);
+  if (num_seqs == 0 || total_q == 0) return MEA_OK;
+
+  mea::FwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.seqstart_q = seqstart_q;
+  a.seqstart_k = seqstart_k;
+  a.slopes = alibi_slopes;
+  a.scale_log2 = scale * mea::kLog2e;
+  a.num_seqs = num_seqs;
+  a.total_q = total_q;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.group = Hq / Hkv;
+  const bool bf16 = dtype == MEA_BF16;
+  const bool alibi = alibi_slopes != nullptr;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  hipError_t err;
+  if (max_seqlen_q == 1) {
+    const int32_t chunk = forced_split ? chunk_keys : default_chunk(num_seqs, max_seqlen_k, Hkv);
+    const size_t need = decode_ws_bytes(num_seqs, max_seqlen_k, Hq, D, chunk);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+      return fail(MEA_ERR_INVALID, "workspace of %zu bytes is smaller than the %zu bytes required", workspace_bytes, need);
+    if (need > 0 && !aligned(workspace, 256)) return fail(MEA_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+    a.chunk_keys = chunk;
+    a.max_chunks = (max_seqlen_k + chunk - 1) / chunk;
+    a.head_slices = (a.group + mea::kDcHeadsPerWg - 1) / mea::kDcHeadsPerWg;
+    a.heads_per_wg = mea::kDcHeadsPerWg;
+    a.ws_o = static_cast<float*>(workspace);
+    a.ws_lse = a.ws_o + (size_t)num_seqs * a.max_chunks * Hq * D;
+    if ((long long)Hkv * a.head_slices > 65535) return fail(MEA_ERR_UNSUPPORTED, "too many key/value head slices");
+    err = mea::launch_decode(a, D, bf16, alibi, s);
+  } else {
+    a.heads_per_wg = gcd_int(a.group, mea::kPfWaves);
+    a.head_slices = a.group / a.heads_per_wg;
+    const int bt = 32 * (mea::kPfWaves / a.heads_per_wg);
+    if ((max_seqlen_q + bt - 1) / bt > 65535)
+      return fail(MEA_ERR_UNSUPPORTED, "max_seqlen_q=%d needs more than 65535 query tiles", max_seqlen_q);
+    err = mea::launch_prefill(a, D, bf16, causal != 0, alibi, max_seqlen_q, s);
+  }
+  if (err != hipSuccess) return fail(MEA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+  return MEA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mea_status_t mea_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                     const int32_t* seqstart_q, const int32_t* seqstart_k, int32_t num_seqs,
+                     int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq,
+                     int32_t Hkv, int32_t D, mea_dtype_t dtype, int32_t causal,
+                     const float* alibi_slopes, float scale, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  return fwd_impl(q, k, v, out, lse, seqstart_q, seqstart_k, num_seqs, total_q, max_seqlen_q,
+                  max_seqlen_k, Hq, Hkv, D, dtype, causal, alibi_slopes, scale, workspace,
+                  workspace_bytes, stream, 0, false);
+}
+
+mea_status_t mea_fwd_splitkv(const void* q, const void* k, const void* v, void* out, float* lse,
+                             const int32_t* seqstart_q, const int32_t* seqstart_k,
+                             int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
+                             int32_t max_seqlen_k, int32_t Hq, int32_t Hkv, int32_t D,
+                             mea_dtype_t dtype, int32_t causal, const float* alibi_slopes,
+                             float scale, void* workspace, size_t workspace_bytes, void* stream,
+                             int32_t chunk_keys) {
+  return fwd_impl(q, k, v, out, lse, seqstart_q, seqstart_k, num_seqs, total_q, max_seqlen_q,
+                  max_seqlen_k, Hq, Hkv, D, dtype, causal, alibi_slopes, scale, workspace,
+                  workspace_bytes, stream, chunk_keys, true);
+}
+
+size_t mea_fwd_workspace_size(int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                              int32_t Hq, int32_t Hkv, int32_t D, int32_t chunk_keys) {
+  if (max_seqlen_q != 1 || num_seqs <= 0 || max_seqlen_k <= 0 || Hq <= 0 || Hkv <= 0 ||
+      Hq % Hkv != 0 || (D != 64 && D != 128) || chunk_keys < 0 ||
+      (chunk_keys > 0 && chunk_keys % mea::kDcBN != 0))
+    return 0;
+  const int32_t chunk = chunk_keys > 0 ? chunk_keys : default_chunk(num_seqs, max_seqlen_k, Hkv);
+  return decode_ws_bytes(num_seqs, max_seqlen_k, Hq, D, chunk);
+}
+
+int32_t mea_default_chunk_keys(int32_t num_seqs, int32_t max_seqlen_k, int32_t Hkv) {
+  return default_chunk(num_seqs < 0 ? 0 : num_seqs, max_seqlen_k < 0 ? 0 : max_seqlen_k, Hkv < 1 ? 1 : Hkv);
+}
+
+const char* mea_status_string(mea_status_t status) {
+  switch (status) {
+    case MEA_OK: return "MEA_OK";
+    case MEA_ERR_INVALID: return "MEA_ERR_INVALID: malformed argument";
+    case MEA_ERR_UNSUPPORTED: return "MEA_ERR_UNSUPPORTED: outside what the kernels implement";
+    case MEA_ERR_HIP: return "MEA_ERR_HIP: the HIP runtime refused a launch";
+  }
+  return "unknown mea_status_t";
+}
+
+const char* mea_last_error(void) { return g_last_error; }
+
+int32_t mea_abi_version(void) { return MEA_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,111 @@
+// Shared device helpers for the attention kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mea {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// Everything a launch needs; passed by value as the kernel argument.
+struct FwdArgs {
+  const uint16_t* q;         // [total_q, Hq, D]
+  const uint16_t* k;         // [total_k, Hkv, D]
+  const uint16_t* v;         // [total_k, Hkv, D]
+  uint16_t* out;             // [total_q, Hq, D]
+  float* lse;                // [Hq, total_q] or nullptr
+  const int32_t* seqstart_q; // [num_seqs + 1]
+  const int32_t* seqstart_k; // [num_seqs + 1]
+  const float* slopes;       // [Hq] or nullptr
+  float* ws_o;               // decode: [num_seqs, max_chunks, Hq, D] float32 partials
+  float* ws_lse;             // decode: [num_seqs, max_chunks, Hq] float32 (log2 units)
+  float scale_log2;          // scale * log2(e)
+  int32_t num_seqs;
+  int32_t total_q;
+  int32_t Hq;
+  int32_t Hkv;
+  int32_t group;             // Hq / Hkv
+  int32_t heads_per_wg;      // prefill: query heads of one group served per workgroup
+  int32_t head_slices;       // prefill: group / heads_per_wg; decode: ceil(group / 32)
+  int32_t chunk_keys;        // decode: keys per chunk
+  int32_t max_chunks;        // decode: ceil(max_seqlen_k / chunk_keys)
+};
+
+// 32x32x16 matrix-core products, float32 accumulate.  Lane l holds row (or
+// column) l % 32 of a 32 x 16 operand and the 8 consecutive k-values 8*(l/32)..+7;
+// the accumulator register r of lane l is element (8*(r/4) + 4*(l/32) + r%4, l%32).
+template <bool BF16>
+__device__ __forceinline__ f32x16 mfma_32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (BF16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+}
+
+// The other half-wave's value of x (lane l <-> lane l ^ 32), combined.
+__device__ __forceinline__ float halfwave_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                            __builtin_bit_cast(uint32_t, x), false, false);
+  return __builtin_fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]),
+                         __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float halfwave_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                            __builtin_bit_cast(uint32_t, x), false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Two float32 values to a packed pair of IEEE halves, round to nearest even.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  _Float16 a = (_Float16)lo, b = (_Float16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// Two float32 values to the output dtype, packed, round to nearest even.
+template <bool BF16>
+__device__ __forceinline__ uint32_t pack_out_x2(float lo, float hi) {
+  if constexpr (BF16) {
+    __bf16 a = (__bf16)lo, b = (__bf16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  } else {
+    return pack_f16x2(lo, hi);
+  }
+}
+
+// A packed pair of bfloat16 values re-encoded as a packed pair of IEEE halves.
+// Exact for magnitudes in [2^-14, 65504]; larger ones saturate (round toward 0).
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  float lo = __builtin_bit_cast(float, w << 16);
+  float hi = __builtin_bit_cast(float, w & 0xffff0000u);
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+}
+
+// MFMA accumulator row of register r in half-wave `hi` (32x32 layout).
+__device__ __forceinline__ constexpr int acc_row(int r, int hi) { return 8 * (r / 4) + 4 * hi + (r % 4); }
+
+// Key rows are fed to the Q.K^T product in a permuted order so that the 16
+// accumulator registers of a lane hold two runs of 8 consecutive keys, which
+// is exactly the k-operand layout of the following P.V product.  Row rho of
+// a 32-key block holds key swap_bits_2_3(rho).
+__device__ __forceinline__ constexpr int key_of_row(int rho) {
+  return (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1);
+}
+// Tile-local key (within a 32-key block) held by accumulator register r of half-wave hi.
+__device__ __forceinline__ constexpr int key_of_reg(int r, int hi) { return 16 * (r / 8) + 8 * hi + (r % 8); }
+
+}  // namespace mea

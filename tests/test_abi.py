@@ -1,0 +1,115 @@
+"""C-ABI library checks that need no GPU: it loads, exports every symbol the
+header declares, and rejects malformed calls before touching the device."""
+import os
+import re
+
+import pytest
+
+from memory_efficient_attention_amd import _native
+from memory_efficient_attention_amd._native import (MEA_BF16, MEA_ERR_INVALID, MEA_ERR_UNSUPPORTED,
+                                                    MEA_F16, MEA_OK)
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mea.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_native.library_path()),
+                                reason="libmea.so not built (run __graft_entry__.build())")
+
+
+def header_symbols():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"MEA_EXPORT\s+[\w\s\*]+?\b(mea_\w+)\s*\(", txt)))
+
+
+def test_header_declares_the_binding_symbols():
+    assert header_symbols() == sorted(_native.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _native.load()
+    for name in header_symbols():
+        assert hasattr(lib, name), name
+
+
+def test_only_declared_c_symbols_are_exported():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", _native.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    mea = sorted({ln.split()[-1] for ln in out.splitlines() if ln.split() and ln.split()[-1].startswith("mea_")})
+    assert mea == header_symbols()
+
+
+def test_version_and_strings():
+    assert _native.mea_abi_version() == 1
+    for st in range(4):
+        assert _native.mea_status_string(st).startswith("MEA_")
+    assert "unknown" in _native.mea_status_string(99)
+
+
+# Plausible, aligned fake device addresses: validation never dereferences them.
+P = 1 << 20
+
+
+def call(**kw):
+    a = dict(q=P, k=P, v=P, out=P, lse=None, seqstart_q=P, seqstart_k=P, num_seqs=4, total_q=365,
+             max_seqlen_q=200, max_seqlen_k=200, Hq=8, Hkv=8, D=64, dtype=MEA_F16, causal=0,
+             alibi_slopes=None, scale=0.125, workspace=None, workspace_bytes=0, stream=None)
+    chunk = kw.pop("chunk_keys", None)
+    a.update(kw)
+    if chunk is None:
+        return _native.mea_fwd(**a)
+    return _native.mea_fwd_splitkv(**a, chunk_keys=chunk)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(q=None), MEA_ERR_INVALID, "non-NULL"),
+    (dict(out=None), MEA_ERR_INVALID, "non-NULL"),
+    (dict(seqstart_k=None), MEA_ERR_INVALID, "seqstart"),
+    (dict(num_seqs=-1), MEA_ERR_INVALID, "negative"),
+    (dict(Hq=8, Hkv=3), MEA_ERR_INVALID, "Hq % Hkv"),
+    (dict(Hkv=0), MEA_ERR_INVALID, "Hkv > 0"),
+    (dict(causal=2), MEA_ERR_INVALID, "causal"),
+    (dict(max_seqlen_q=0), MEA_ERR_INVALID, "max_seqlen_q == 0"),
+    (dict(D=96), MEA_ERR_UNSUPPORTED, "D=96"),
+    (dict(D=256), MEA_ERR_UNSUPPORTED, "D=256"),
+    (dict(dtype=7), MEA_ERR_UNSUPPORTED, "dtype"),
+    (dict(scale=float("nan")), MEA_ERR_UNSUPPORTED, "scale"),
+    (dict(scale=float("inf")), MEA_ERR_UNSUPPORTED, "scale"),
+    (dict(scale=-0.5), MEA_ERR_UNSUPPORTED, "scale"),
+    (dict(q=P + 8), MEA_ERR_UNSUPPORTED, "16-byte"),
+    (dict(lse=P + 2), MEA_ERR_UNSUPPORTED, "4-byte"),
+    (dict(num_seqs=70000), MEA_ERR_UNSUPPORTED, "65535"),
+    # decode path (max_seqlen_q == 1) without the workspace it needs
+    (dict(num_seqs=4, total_q=4, max_seqlen_q=1, max_seqlen_k=5000), MEA_ERR_INVALID, "workspace"),
+    (dict(num_seqs=4, total_q=4, max_seqlen_q=1, max_seqlen_k=5000, workspace=P, workspace_bytes=100),
+     MEA_ERR_INVALID, "workspace"),
+    # forced split entry point
+    (dict(chunk_keys=100, total_q=4, max_seqlen_q=1), MEA_ERR_INVALID, "chunk_keys"),
+    (dict(chunk_keys=0, total_q=4, max_seqlen_q=1), MEA_ERR_INVALID, "chunk_keys"),
+    (dict(chunk_keys=256), MEA_ERR_INVALID, "max_seqlen_q == 1"),
+])
+def test_rejected_before_launch(kw, status, needle):
+    assert call(**kw) == status
+    assert needle in _native.mea_last_error()
+
+
+@pytest.mark.parametrize("kw", [dict(num_seqs=0, total_q=0), dict(total_q=0, max_seqlen_q=0)])
+def test_empty_problem_is_a_noop(kw):
+    assert call(**kw) == MEA_OK
+
+
+def test_workspace_size():
+    ws = _native.mea_fwd_workspace_size
+    assert ws(4, 200, 200, 8, 8, 64, 0) == 0                       # prefill needs none
+    c = _native.mea_default_chunk_keys(64, 32680, 8)
+    assert c == 1024
+    assert ws(64, 1, 32680, 64, 8, 128, 0) == 64 * 32 * 64 * 129 * 4
+    assert ws(64, 1, 32680, 64, 8, 128, 256) == 64 * 128 * 64 * 129 * 4
+    assert ws(64, 1, 32680, 64, 8, 128, 100) == 0                  # invalid chunk
+    assert ws(2, 1, 100, 6, 4, 128, 0) == 0                        # Hq % Hkv != 0
+    assert _native.mea_default_chunk_keys(1, 32768, 8) == 128
+    assert _native.mea_default_chunk_keys(1, 0, 8) == 128
+    assert _native.mea_default_chunk_keys(0, 0, 0) == 128
+    for n, L, h in [(1, 1000, 1), (8, 4096, 8), (200, 32768, 8), (3, 77, 2)]:
+        c = _native.mea_default_chunk_keys(n, L, h)
+        assert c % 128 == 0 and 128 <= c <= 1024

@@ -1,0 +1,49 @@
+"""Host-side logic of the Python binding (no GPU): masks, splitting, layouts."""
+import pytest
+import torch
+
+from memory_efficient_attention_amd import BlockDiagonalCausalMask, BlockDiagonalMask
+from memory_efficient_attention_amd.api import _kv_heads_bmghk
+
+
+def test_from_seqlens_offsets():
+    m = BlockDiagonalMask.from_seqlens([37, 120, 8, 200])
+    assert m.q_seqstart == [0, 37, 157, 165, 365] and m.kv_seqstart == m.q_seqstart
+    assert (m.num_seqs, m.total_q, m.max_seqlen_q, m.causal) == (4, 365, 200, False)
+    c = BlockDiagonalCausalMask.from_seqlens([1, 1], [10, 20])
+    assert c.causal and c.kv_seqstart == [0, 10, 30] and c.max_seqlen_kv == 20
+
+
+def test_split_shapes_match_the_tutorial():
+    """Packed [1, 365, 8, 64] output splits into [1, L_b, 8, 64] pieces
+    (tutorial page, section 4)."""
+    m = BlockDiagonalMask.from_seqlens([37, 120, 8, 200])
+    out = torch.arange(365 * 8 * 64, dtype=torch.float32).view(1, 365, 8, 64)
+    pieces = m.split(out)
+    assert [tuple(p.shape) for p in pieces] == [(1, 37, 8, 64), (1, 120, 8, 64), (1, 8, 8, 64), (1, 200, 8, 64)]
+    assert torch.equal(torch.cat(pieces, dim=1), out)
+    assert pieces[1].data_ptr() == out[0, 37].data_ptr()            # views, not copies
+    assert [tuple(p.shape) for p in m.split(out[0])] == [(1, 37, 8, 64), (1, 120, 8, 64), (1, 8, 8, 64), (1, 200, 8, 64)]
+
+
+def test_bad_masks():
+    with pytest.raises(ValueError):
+        BlockDiagonalMask.from_seqlens([1, 2], [3])
+    with pytest.raises(ValueError):
+        BlockDiagonalMask.from_seqlens([-1])
+    with pytest.raises(ValueError):
+        BlockDiagonalMask.from_seqlens([3, 4]).split(torch.zeros(1, 8, 2))
+
+
+def test_bmghk_kv_head_axis():
+    B, M, G, Hg, K = 2, 5, 2, 4, 8
+    k = torch.randn(B, M, G, 1, K)
+    kk = _kv_heads_bmghk(k, Hg)
+    assert kk.shape == (B, M, G, K) and torch.equal(kk, k[:, :, :, 0])
+    ke = _kv_heads_bmghk(k.expand(B, M, G, Hg, K), Hg)                # broadcast view
+    assert torch.equal(ke, kk)
+    full = torch.randn(B, M, G, Hg, K)
+    kf = _kv_heads_bmghk(full, Hg)
+    assert kf.shape == (B, M, G * Hg, K) and torch.equal(kf[:, :, 5], full[:, :, 1, 1])
+    with pytest.raises(ValueError):
+        _kv_heads_bmghk(torch.randn(B, M, G, 3, K), Hg)

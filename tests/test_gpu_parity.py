@@ -1,0 +1,157 @@
+"""GPU parity: the HIP path against the CPU float64 oracle on the same seeded
+inputs, element by element (or on sampled rows at full size)."""
+import sys
+
+import pytest
+import torch
+
+from mea_workloads import generate, random_case, sample_rows
+from parity import compare, compare_rows, oracle_full, run_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- the workloads
+@pytest.mark.parametrize("causal", [False, True])
+def test_packed_varlen_fp16(causal):
+    """Packed [37,120,8,200], 8 heads, D=64, fp16, block-diagonal (then causal)."""
+    from memory_efficient_attention_amd import (BlockDiagonalCausalMask, BlockDiagonalMask,
+                                                memory_efficient_attention)
+    inp = generate("packed_varlen_h8_d64_fp16", causal=causal)
+    _log(f"packed_varlen causal={causal}")
+    q, k, v = (x.cuda().unsqueeze(0) for x in (inp.q, inp.k, inp.v))   # BMHK [1, 365, 8, 64]
+    mask_cls = BlockDiagonalCausalMask if causal else BlockDiagonalMask
+    mask = mask_cls.from_seqlens(inp.seqlens_q)
+    out, lse = memory_efficient_attention(q, k, v, attn_bias=mask, scale=inp.scale, return_lse=True)
+    torch.cuda.synchronize()
+    assert out.shape == (1, 365, 8, 64)
+    ref_out, ref_lse = oracle_full(inp)
+    r = compare(out[0].cpu(), lse.cpu(), ref_out, ref_lse, "fp16", "packed_varlen")
+    _log(f"  {r}")
+    pieces = mask.split(out)
+    assert [tuple(p.shape) for p in pieces] == [(1, L, 8, 64) for L in (37, 120, 8, 200)]
+    # the first sequence alone gives the same rows as the packed call
+    s0 = inp.seqlens_q[0]
+    alone = memory_efficient_attention(q[:, :s0], k[:, :s0], v[:, :s0], scale=inp.scale,
+                                       attn_bias=mask_cls.from_seqlens([s0]))
+    assert torch.equal(alone, pieces[0])
+
+
+def test_bmghk_gqa_fp16():
+    """BMGHK q [2,256,2,4,64], k/v [2,256,2,1,64], fp16, no mask."""
+    from memory_efficient_attention_amd import memory_efficient_attention
+    inp = generate("bmghk_gqa_b2_m256_g2x4_d64_fp16")
+    _log("bmghk")
+    B, M, G, Hg = inp.bmghk
+    q = inp.q.cuda().view(B, M, G, Hg, 64)
+    k = inp.k.cuda().view(B, M, G, 1, 64)
+    v = inp.v.cuda().view(B, M, G, 1, 64)
+    out, lse = memory_efficient_attention(q, k, v, scale=inp.scale, return_lse=True)
+    torch.cuda.synchronize()
+    assert out.shape == (2, 256, 2, 4, 64)
+    ref_out, ref_lse = oracle_full(inp)
+    _log(f"  {compare(out.reshape(512, 8, 64).cpu(), lse.cpu(), ref_out, ref_lse, 'fp16', 'bmghk')}")
+    # broadcast (stride-0) key/value heads give the same result
+    out2 = memory_efficient_attention(q, k.expand(B, M, G, Hg, 64), v.expand(B, M, G, Hg, 64), scale=inp.scale)
+    assert torch.equal(out, out2)
+
+
+def test_causal_alibi_gqa_4x2048_bf16():
+    inp = generate("causal_alibi_gqa_4x2048_h32kv8_d128_bf16")
+    _log("causal_alibi_gqa_4x2048")
+    out, lse = run_gpu(inp)
+    ref_out, ref_lse = oracle_full(inp)
+    _log(f"  {compare(out, lse, ref_out, ref_lse, 'bf16', 'causal_alibi_4x2048')}")
+
+
+@pytest.mark.parametrize("alibi", [False, True])
+def test_varlen_causal_gqa_64seq_bf16_full_size_sampled(alibi):
+    """All 64 sequences (137,663 tokens) on the GPU; the oracle checks sampled rows."""
+    inp = generate("varlen_causal_gqa_64seq_h32kv8_d128_bf16", alibi=alibi)
+    _log(f"varlen_64seq alibi={alibi} T={inp.total_q}")
+    out, lse = run_gpu(inp)
+    assert not torch.isnan(out).any()
+    rows = sample_rows(inp, 160, seed=1 + int(alibi))
+    _log(f"  {compare_rows(out, lse, inp, rows, 'varlen_64seq sampled')}")
+
+
+@pytest.mark.parametrize("alibi", [False, True])
+def test_varlen_causal_gqa_first_sequences_full(alibi):
+    inp = generate("varlen_causal_gqa_64seq_h32kv8_d128_bf16", alibi=alibi, num_seqs=6)
+    _log(f"varlen first 6 seqs alibi={alibi} T={inp.total_q}")
+    out, lse = run_gpu(inp)
+    ref_out, ref_lse = oracle_full(inp)
+    _log(f"  {compare(out, lse, ref_out, ref_lse, 'bf16', 'varlen first 6')}")
+
+
+def test_decode_splitkv_full_size_sampled():
+    inp = generate("decode_splitkv_64req_h64kv8_d128_bf16")
+    _log(f"decode 64 requests, sum Lk={inp.total_k}")
+    out, lse = run_gpu(inp)
+    rows = [(t, h) for t in range(64) for h in (0, 7, 8, 31, 63)]
+    _log(f"  {compare_rows(out, lse, inp, rows, 'decode sampled')}")
+
+
+def test_decode_splitkv_subset_full_and_chunk_invariance():
+    inp = generate("decode_splitkv_64req_h64kv8_d128_bf16", num_seqs=5)
+    _log(f"decode 5 requests, Lk={inp.seqlens_k}")
+    dev = to_device(inp)
+    ref_out, ref_lse = oracle_full(inp)
+    outs = []
+    for ck in (None, 128, 384, 1024, 4096, 32768):
+        out, lse = run_gpu(inp, dev, chunk_keys=ck)
+        _log(f"  chunk={ck}: {compare(out, lse, ref_out, ref_lse, 'bf16', f'decode chunk={ck}')}")
+        outs.append(out)
+    for o in outs[1:]:
+        assert (o.double() - outs[0].double()).abs().max().item() <= 1e-2
+
+
+# ----------------------------------------------------------------------------- edge cases
+EDGE = [
+    # (seqlens_q, seqlens_k, Hq, Hkv, D, dtype, causal, alibi)
+    ([1, 31, 32, 33, 63, 64, 65, 127, 128, 129, 300], None, 8, 8, 64, "fp16", True, False),
+    ([1, 31, 32, 33, 63, 64, 65, 127, 128, 129, 300], None, 8, 2, 128, "bf16", True, True),
+    ([0, 5, 0, 70, 0], None, 4, 1, 64, "fp16", False, False),                  # empty sequences, MQA
+    ([200, 17], None, 12, 4, 128, "fp16", True, True),                         # 3 heads per group
+    ([97, 250], None, 6, 1, 64, "bf16", False, True),                          # 6 heads per group, |i-j|
+    ([40, 7, 90], [100, 7, 300], 8, 4, 128, "bf16", True, True),               # L_q < L_k, bottom-right
+    ([50, 20], [10, 0], 4, 2, 64, "fp16", True, False),                        # L_q > L_k: rows with no key
+    ([64, 64], [0, 64], 4, 4, 128, "bf16", False, False),                      # no keys at all
+    ([1000], None, 16, 16, 128, "fp16", True, False),                          # MHA, one long sequence
+    ([1, 1, 1, 1, 1], [1, 130, 0, 3000, 257], 64, 2, 128, "bf16", False, True),  # decode, 32 heads/group
+    ([1, 1, 1], [700, 1, 129], 40, 1, 64, "fp16", True, False),               # decode, 40 heads/group
+    ([1, 0, 1], [0, 5, 64], 8, 8, 128, "bf16", False, False),                  # decode with empty rows
+    ([2, 1], [500, 400], 8, 2, 128, "bf16", True, True),                       # L_q=2: prefill path
+]
+
+
+@pytest.mark.parametrize("ci", range(len(EDGE)))
+def test_edge_cases(ci):
+    lq, lk, Hq, Hkv, D, dt, causal, alibi = EDGE[ci]
+    inp = random_case(1000 + ci, lq, lk, Hq=Hq, Hkv=Hkv, D=D, dtype=dt, causal=causal, alibi=alibi)
+    _log(f"edge {ci}: {EDGE[ci]}")
+    out, lse = run_gpu(inp)
+    ref_out, ref_lse = oracle_full(inp)
+    _log(f"  {compare(out, lse, ref_out, ref_lse, dt, f'edge {ci}')}")
+
+
+def test_deterministic_and_lse_optional():
+    inp = random_case(7, [300, 129, 1000], Hq=32, Hkv=8, D=128, dtype="bf16", causal=True, alibi=True)
+    dev = to_device(inp)
+    o1, l1 = run_gpu(inp, dev)
+    o2, l2 = run_gpu(inp, dev)
+    o3, _ = run_gpu(inp, dev, return_lse=False)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(o1, o3)
+
+
+def test_scale_and_slopes_arguments():
+    """A non-default scale and arbitrary per-head slopes reach the kernel."""
+    inp = random_case(8, [77, 300], Hq=8, Hkv=2, D=64, dtype="fp16", causal=True, alibi=True,
+                      scale=0.05, slopes=torch.tensor([0.0, 0.01, 0.1, 0.5, 1.0, 2.0, 0.3, 0.07]))
+    out, lse = run_gpu(inp)
+    ref_out, ref_lse = oracle_full(inp)
+    compare(out, lse, ref_out, ref_lse, "fp16", "scale/slopes")
