@@ -1,0 +1,307 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention forward hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic inputs:
+  1. packed causal GQA prefill: 64 sequences with lengths U[128, 4096] from
+     seed 0 (137,663 tokens), 32 query / 8 key-value heads, D = 128, bf16,
+     block-diagonal causal mask, no ALiBi;
+  2. split-KV decode: 64 requests x 1 query, KV lengths U[1024, 32768] from
+     seed 0 (1,101,299 KV tokens), 64 query / 8 key-value heads, D = 128, bf16,
+     partial kernel + log-sum-exp combine.
+Inputs are drawn on the host and copied to HBM before the timed region.
+
+Prints one JSON line.  ``value`` is the prefill throughput in TFLOP/s counting
+only unmasked score FLOPs (4 * D per allowed (query, key, head) triple) over
+the prefill kernel's own time (HIP events on its launch stream); the decode
+figures (GB/s of algorithmic bytes Q + K + V + O + LSE) are in ``decode``.
+``roofline`` describes the prefill kernel against the bf16 dense MFMA peak,
+``decode.roofline`` the decode launches against HBM bandwidth, and
+``cpu_baseline`` times the CPU float64 oracle on a bounded sample of the
+prefill workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s (% MFMA peak) packed causal GQA; decode GB/s (% HBM)"
+PEAK_MFMA_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0            # HBM3E
+PREFILL = "varlen_causal_gqa_64seq_h32kv8_d128_bf16"
+DECODE = "decode_splitkv_64req_h64kv8_d128_bf16"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCES = ["fwd_prefill.hip", "fwd_decode.hip", "mea_common.h", "mea_tiles.h", "mea_launch.h"]
+
+
+def unmasked_flops(inp) -> int:
+    """4*D FLOPs per allowed (query row, key, query head) triple."""
+    total = 0
+    for Lq, Lk in zip(inp.seqlens_q, inp.seqlens_k):
+        if inp.causal:
+            off = Lk - Lq
+            pairs = sum(max(0, min(Lk, r + off + 1)) for r in range(Lq)) if Lq != Lk else Lq * (Lq + 1) // 2
+        else:
+            pairs = Lq * Lk
+        total += pairs
+    return 4 * inp.D * inp.Hq * total
+
+
+def algorithmic_bytes(inp, with_lse=True) -> int:
+    """Q + K + V + O (+ LSE): every input byte read once, every output written once."""
+    b = 2 * (inp.q.numel() * 2 + inp.k.numel() + inp.v.numel())
+    if with_lse:
+        b += inp.Hq * inp.total_q * 4
+    return b
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "memory_efficient_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("kernels", {}).get(kernel)
+
+
+class Call:
+    """Pre-bound launch of one workload (buffers allocated once, outside the timed region)."""
+
+    def __init__(self, inp, dev):
+        import torch
+        from memory_efficient_attention_amd import _native
+        self.inp = inp
+        self.q, self.k, self.v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+        self.ssq, self.ssk = inp.seqstart_q.to(dev), inp.seqstart_k.to(dev)
+        self.slopes = None if inp.alibi_slopes is None else inp.alibi_slopes.to(dev)
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty((inp.Hq, inp.total_q), dtype=torch.float32, device=dev)
+        self.ws_bytes = _native.mea_fwd_workspace_size(len(inp.seqlens_q), inp.max_seqlen_q,
+                                                       inp.max_seqlen_k, inp.Hq, inp.Hkv, inp.D, 0)
+        self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=dev)
+        self.dtype = _native.MEA_BF16 if inp.dtype == "bf16" else _native.MEA_F16
+        self.native = _native
+
+    def __call__(self, stream):
+        inp = self.inp
+        st = self.native.mea_fwd(
+            self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.out.data_ptr(),
+            self.lse.data_ptr(), self.ssq.data_ptr(), self.ssk.data_ptr(), len(inp.seqlens_q),
+            inp.total_q, inp.max_seqlen_q, inp.max_seqlen_k, inp.Hq, inp.Hkv, inp.D, self.dtype,
+            int(inp.causal), None if self.slopes is None else self.slopes.data_ptr(), inp.scale,
+            self.ws.data_ptr() if self.ws_bytes else None, self.ws_bytes, stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"mea_fwd: {self.native.mea_status_string(st)}: {self.native.mea_last_error()}")
+
+
+def cpu_baseline(pre_inp, gpu_out, gpu_lse, budget_s: float):
+    """Time the float64 CPU oracle on the first sequences of the prefill
+    workload (about budget_s seconds of work) and check the GPU rows there."""
+    import torch
+    import oracle
+    from mea_workloads import _lengths, get_workload, prefix, random_case
+    # threads: torch's default (OMP_NUM_THREADS), i.e. the host share this process was given
+    lens, _ = _lengths(get_workload(PREFILL), 0)
+    per_seq = [4 * 128 * 32 * L * (L + 1) // 2 for L in lens]
+    # calibrate the oracle's rate on the first sequence, then take the longest
+    # prefix of sequences whose unmasked work fits the budget
+    probe = random_case(0, [1024], Hq=32, Hkv=8, D=128, dtype="bf16", causal=True)
+    t0 = time.perf_counter()
+    oracle.attention_forward(probe.q, probe.k, probe.v, probe.seqstart_q, probe.seqstart_k,
+                             causal=True, scale=probe.scale)
+    rate = unmasked_flops(probe) / max(time.perf_counter() - t0, 1e-6)   # FLOP/s
+    n, acc = 0, 0
+    while n < len(per_seq) and (acc + per_seq[n]) / rate <= budget_s:
+        acc += per_seq[n]
+        n += 1
+    n = max(n, 1)
+    sample = prefix(pre_inp, n)
+    t0 = time.perf_counter()
+    ref_out, ref_lse = oracle.attention_forward(sample.q, sample.k, sample.v, sample.seqstart_q,
+                                                sample.seqstart_k, causal=True, scale=sample.scale)
+    dt = time.perf_counter() - t0
+    T = sample.total_q
+    err = (gpu_out[:T].double() - ref_out).abs().max().item()
+    lerr = (gpu_lse[:, :T].double() - ref_lse).abs().max().item()
+    return {
+        "value": unmasked_flops(sample) / dt / 1e12, "unit": "TFLOP/s",
+        "cores": torch.get_num_threads(), "kind": "oracle",
+        "sample": f"first {n} of 64 sequences of the prefill workload ({T} tokens, "
+                  f"{unmasked_flops(sample) / 1e9:.1f} unmasked GFLOP), float64, {dt:.1f} s",
+        "gpu_vs_oracle_on_sample": {"max_abs_out": err, "max_abs_lse": lerr},
+    }
+
+
+def run_part(args, dev):
+    """Time one half of the step on its own (profiling aid); prints a short JSON line."""
+    import torch
+    from mea_workloads import generate
+    name = PREFILL if args.part == "prefill" else DECODE
+    call = Call(generate(name, seed=args.seed), dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        call(stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        call(stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / max(args.steps, 1)
+    res = {"part": args.part, "workload": name, "ms": round(ms, 4)}
+    if args.part == "prefill":
+        res["tflops"] = round(unmasked_flops(call.inp) / (ms * 1e-3) / 1e12, 2)
+    else:
+        res["gbs"] = round(algorithmic_bytes(call.inp) / (ms * 1e-3) / 1e9, 1)
+    print(json.dumps(res), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle work")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-alibi-variant", action="store_true")
+    ap.add_argument("--part", choices=["all", "prefill", "decode"], default="all",
+                    help="run only one half of the step (for profiling); the JSON line is for 'all'")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs as a single process on one GPU", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from mea_workloads import generate
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.part != "all":
+        run_part(args, dev)
+        return
+
+    t_gen = time.perf_counter()
+    pre = generate(PREFILL, seed=args.seed)
+    dec = generate(DECODE, seed=args.seed)
+    pre_call, dec_call = Call(pre, dev), Call(dec, dev)
+    pre_alibi = None
+    if not args.no_alibi_variant:
+        pre_alibi = Call(generate(PREFILL, seed=args.seed, alibi=True), dev)
+    torch.cuda.synchronize()
+    print(f"[bench] inputs generated and resident in HBM in {time.perf_counter() - t_gen:.1f} s",
+          file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        pre_call(stream)
+        dec_call(stream)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        pre_call(stream)
+        ev[i][1].record(stream)
+        dec_call(stream)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    dec_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    print(f"[bench] {K} steps: prefill {pre_ms:.3f} ms, decode {dec_ms:.3f} ms per step",
+          file=sys.stderr, flush=True)
+
+    pre_flops = unmasked_flops(pre)
+    dec_bytes = algorithmic_bytes(dec)
+    tflops = pre_flops / (pre_ms * 1e-3) / 1e12
+    gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
+
+    alibi_res = None
+    if pre_alibi is not None:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        pre_alibi(stream)
+        e0.record(stream)
+        for _ in range(max(3, K // 3)):
+            pre_alibi(stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ams = e0.elapsed_time(e1) / max(3, K // 3)
+        atf = unmasked_flops(pre_alibi.inp) / (ams * 1e-3) / 1e12
+        alibi_res = {"ms": round(ams, 4), "tflops": round(atf, 2),
+                     "frac": round(atf / PEAK_MFMA_BF16_TFLOPS, 4)}
+
+    traffic_pre = measured_traffic("fwd_prefill")
+    traffic_dec = measured_traffic("fwd_decode")
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{PREFILL} + {DECODE}",
+            "prefill": {"seqs": 64, "tokens": pre.total_q, "Hq": 32, "Hkv": 8, "D": 128,
+                        "mask": "block-diagonal causal", "alibi": False,
+                        "unmasked_flops": pre_flops},
+            "decode": {"requests": 64, "kv_tokens": dec.total_k, "Hq": 64, "Hkv": 8, "D": 128,
+                       "algorithmic_bytes": dec_bytes,
+                       "chunk_keys": dec_call.native.mea_default_chunk_keys(64, dec.max_seqlen_k, 8)},
+            "seed": args.seed,
+        },
+        "roofline": {
+            "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_BF16_TFLOPS, 4),
+            "traffic": traffic_pre, "kernel": "fwd_prefill_kernel<128,bf16,causal>",
+            "launch_ms": round(pre_ms, 4),
+        },
+        "decode": {
+            "value": round(gbs, 1), "unit": "GB/s", "ms": round(dec_ms, 4),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": traffic_dec,
+                         "kernel": "fwd_decode_partial_kernel + fwd_decode_combine_kernel"},
+        },
+        "prefill_alibi": alibi_res,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(pre, pre_call.out.cpu(), pre_call.lse.cpu(), args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -32,7 +32,7 @@ import torch
 
 __all__ = [
     "Workload", "Inputs", "WORKLOADS", "get_workload", "generate", "random_case",
-    "alibi_slopes", "seqstart_from_lengths", "sample_rows",
+    "alibi_slopes", "seqstart_from_lengths", "sample_rows", "prefix",
 ]
 
 _DTYPES = {"fp16": torch.float16, "bf16": torch.bfloat16}
@@ -228,6 +228,16 @@ def random_case(seed: int, seqlens_q: Sequence[int], seqlens_k: Optional[Sequenc
         alibi_slopes=slopes if alibi else None,
         scale=default_scale(D) if scale is None else float(np.float32(scale)),
         dtype=dtype if isinstance(dtype, str) else {v_: k_ for k_, v_ in _DTYPES.items()}[dt])
+
+
+def prefix(inp: Inputs, n: int) -> Inputs:
+    """The first ``n`` sequences of ``inp`` as views of the same tensors (the
+    rows a call on the whole of ``inp`` produces for them are comparable)."""
+    sq, sk = inp.seqstart_q.tolist(), inp.seqstart_k.tolist()
+    return dataclasses.replace(
+        inp, q=inp.q[:sq[n]], k=inp.k[:sk[n]], v=inp.v[:sk[n]],
+        seqstart_q=inp.seqstart_q[:n + 1].clone(), seqstart_k=inp.seqstart_k[:n + 1].clone(),
+        seqlens_q=inp.seqlens_q[:n], seqlens_k=inp.seqlens_k[:n], bmghk=None)
 
 
 def sample_rows(inp: Inputs, count: int, seed: int = 0) -> List[Tuple[int, int]]:
