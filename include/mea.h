@@ -118,7 +118,9 @@ typedef enum {
  * sizes; Hq or Hkv <= 0 or Hq % Hkv != 0; total_q > 0 with max_seqlen_q == 0;
  * causal not 0/1; a workspace smaller than required.
  * Returns MEA_ERR_UNSUPPORTED for: D not 64/128; dtype not listed; a
- * non-finite or non-positive scale; a pointer not aligned as stated.
+ * non-finite or non-positive scale; a pointer not aligned as stated;
+ * num_seqs > 65535; max_seqlen_k * Hkv * D * 2 >= 2^31 (one sequence's
+ * key/value rows are addressed with 32-bit byte offsets).
  *
  * Numerics: Q K^T runs on the matrix cores in the input dtype with float32
  * accumulation; the softmax is float32; the softmax weights enter P V as

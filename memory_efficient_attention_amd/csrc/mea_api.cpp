@@ -85,6 +85,9 @@ mea_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, fl
       !aligned(seqstart_q, 4) || !aligned(seqstart_k, 4))
     return fail(MEA_ERR_UNSUPPORTED, "lse, alibi_slopes and seqstart arrays must be 4-byte aligned");
   if (num_seqs > 65535) return fail(MEA_ERR_UNSUPPORTED, "num_seqs=%d exceeds 65535", num_seqs);
+  // key/value rows of one sequence are addressed with 32-bit byte offsets
+  if ((long long)max_seqlen_k * Hkv * D * 2 >= (1ll << 31))
+    return fail(MEA_ERR_UNSUPPORTED, "max_seqlen_k * Hkv * D * 2 bytes must stay below 2^31");
   if (num_seqs == 0 || total_q == 0) return MEA_OK;
 
   mea::FwdArgs a{};
@@ -125,8 +128,12 @@ mea_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, fl
     a.heads_per_wg = gcd_int(a.group, mea::kPfWaves);
     a.head_slices = a.group / a.heads_per_wg;
     const int bt = 32 * (mea::kPfWaves / a.heads_per_wg);
-    if ((max_seqlen_q + bt - 1) / bt > 65535)
-      return fail(MEA_ERR_UNSUPPORTED, "max_seqlen_q=%d needs more than 65535 query tiles", max_seqlen_q);
+    const long long tiles = (max_seqlen_q + bt - 1) / bt;
+    const long long items = (long long)Hkv * a.head_slices * num_seqs * tiles;
+    if (items > (1ll << 31) - 8)
+      return fail(MEA_ERR_UNSUPPORTED, "%lld prefill work items exceed the grid limit", items);
+    a.pf_max_tiles = (int32_t)tiles;
+    a.pf_items = (int32_t)items;
     err = mea::launch_prefill(a, D, bf16, causal != 0, alibi, max_seqlen_q, s);
   }
   if (err != hipSuccess) return fail(MEA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));

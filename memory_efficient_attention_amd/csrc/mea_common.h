@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace mea {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -38,6 +40,8 @@ struct FwdArgs {
   int32_t head_slices;       // prefill: group / heads_per_wg; decode: ceil(group / 32)
   int32_t chunk_keys;        // decode: keys per chunk
   int32_t max_chunks;        // decode: ceil(max_seqlen_k / chunk_keys)
+  int32_t pf_max_tiles;      // prefill: query tiles of the longest sequence
+  int32_t pf_items;          // prefill: head slices * num_seqs * pf_max_tiles
 };
 
 // 32x32x16 matrix-core products, float32 accumulate.  Lane l holds row (or

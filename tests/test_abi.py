@@ -39,6 +39,14 @@ def test_only_declared_c_symbols_are_exported():
     assert mea == header_symbols()
 
 
+def test_every_kernel_stub_is_defined():
+    """A kernel whose host-side launch stub is missing would only fail at load time."""
+    import subprocess
+    out = subprocess.run(["nm", "-C", "--undefined-only", _native.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    assert "__device_stub__" not in out
+
+
 def test_version_and_strings():
     assert _native.mea_abi_version() == 1
     for st in range(4):
@@ -79,6 +87,7 @@ def call(**kw):
     (dict(q=P + 8), MEA_ERR_UNSUPPORTED, "16-byte"),
     (dict(lse=P + 2), MEA_ERR_UNSUPPORTED, "4-byte"),
     (dict(num_seqs=70000), MEA_ERR_UNSUPPORTED, "65535"),
+    (dict(max_seqlen_k=1 << 20, Hq=8, Hkv=8, D=128), MEA_ERR_UNSUPPORTED, "2^31"),
     # decode path (max_seqlen_q == 1) without the workspace it needs
     (dict(num_seqs=4, total_q=4, max_seqlen_q=1, max_seqlen_k=5000), MEA_ERR_INVALID, "workspace"),
     (dict(num_seqs=4, total_q=4, max_seqlen_q=1, max_seqlen_k=5000, workspace=P, workspace_bytes=100),
