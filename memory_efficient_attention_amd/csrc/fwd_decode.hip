@@ -1,33 +1,69 @@
 // Split-KV attention forward for one query per sequence (the decode case).
 //
+// This path is bound by HBM bandwidth: every K/V byte of a sequence is read
+// once, so the kernels are built to keep as many bytes in flight per CU as
+// possible and to spend little else.
+//
 // Partial kernel: a workgroup takes one sequence, one key/value head g (and up
-// to 32 of its query heads) and one chunk of the sequence's keys.  It streams
-// that chunk's K/V from HBM exactly once, in 128-key tiles staged through LDS,
-// and serves all query heads of the group from each tile: the heads are the
-// 32 columns of the matrix-core products, so GQA's sharing turns directly
-// into fewer HBM bytes.  Each of the 4 waves takes one 32-key block of a tile
-// with its own online-softmax state; the waves merge in LDS at the end and
-// write one normalised float32 partial output and its log-sum-exp per head.
+// to 16 of its query heads) and one chunk of the sequence's keys.  Its 4
+// waves stream interleaved 32-key blocks of the chunk independently (no
+// workgroup barrier until the end), each with its own online-softmax state:
+//   S^T = K Q^T   16x16x32 products; the query heads of the group are the 16
+//                 columns, so one K/V read serves every head of the group
+//                 (GQA's saving becomes fewer HBM bytes);
+//   O^T += V^T P^T  with V transposed through a per-wave LDS slot.
+// K goes from HBM straight into the product's operand registers; the loads of
+// block i+1 are in flight while block i is computed.  At the end the 4 waves
+// merge in LDS and write one normalised float32 partial output and its
+// log-sum-exp (log2 units) per head.
 //
 // Combine kernel: per (sequence, query head) the chunk partials are merged
 // by their log-sum-exps: lse = log sum_c exp(lse_c), out = sum_c exp(lse_c -
 // lse) o_c, then rounded to the output dtype.
 #include "mea_common.h"
 #include "mea_launch.h"
-#include "mea_tiles.h"
 
 namespace mea {
 
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <bool BF16>
+__device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+constexpr int kWaves = 4;
+constexpr int kBlk = 32;                  // keys per wave block
+constexpr int kVtStride = kBlk + 8;       // elements per V^T row in a wave's LDS slot
+
+}  // namespace
+
 template <int D, bool BF16, bool ALIBI>
-__global__ __launch_bounds__(256) void fwd_decode_partial_kernel(FwdArgs a) {
-  using L = TileLayout<D, kDcBN>;
-  using Stager = TileStager<D, kDcBN, 256, BF16>;
-  constexpr int kRedStride = D + 1;  // floats per query row in the merge buffer
-  static_assert(4 * 32 * kRedStride * 4 + 2 * 4 * 32 * 4 <= L::bufBytes, "merge buffer");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[L::bufElems];
+__global__ __launch_bounds__(256, 2) void fwd_decode_partial_kernel(FwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the body uses buffer-resource types that exist only for the GPU target
+  constexpr int KS = D / 32;              // k-steps of the 16x16x32 Q K^T product
+  constexpr int DB = D / 16;              // 16-feature blocks of O^T
+  constexpr int VCH = D / 64;             // 16-byte V chunks per lane per key
+  constexpr int kSlotElems = D * kVtStride;
+  constexpr int kRedStride = D + 1;       // floats per query column in the merge buffer
+  constexpr int kSmemBytes = kWaves * kSlotElems * 2 > kWaves * 16 * kRedStride * 4 + 2 * kWaves * 16 * 4
+                                 ? kWaves * kSlotElems * 2
+                                 : kWaves * 16 * kRedStride * 4 + 2 * kWaves * 16 * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, q = lane & 15, g4 = lane >> 4;
   const int chunk = blockIdx.x, b = blockIdx.y;
   const int g = blockIdx.z / a.head_slices, hs = blockIdx.z % a.head_slices;
 
@@ -38,128 +74,195 @@ __global__ __launch_bounds__(256) void fwd_decode_partial_kernel(FwdArgs a) {
   const int c1 = min(Lk, c0 + a.chunk_keys);
   const int qpos = Lk - 1;  // the single query is the sequence's last position
 
-  const int hl = hs * kDcHeadsPerWg + l32;  // query head within the group (= MFMA column)
+  const int hl = hs * 16 + q;  // query head within the group (= product column)
   const bool col_valid = hl < a.group;
   const int head = g * a.group + hl;
 
-  u32x4 qf[D / 16];
+  // Q^T operand: lane (q, g4) holds features (D/4)*g4 + 8*ks .. +7 at k-step ks
+  u32x4 qf[KS];
   {
-    const uint16_t* qrow = a.q + ((size_t)sq0 * a.Hq + head) * D + 8 * hi;
+    const uint16_t* qrow = a.q + ((size_t)sq0 * a.Hq + head) * D + (D / 4) * g4;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
+    for (int ks = 0; ks < KS; ++ks) {
       u32x4 x = {0u, 0u, 0u, 0u};
-      if (col_valid) x = *(const u32x4*)(qrow + 16 * s);
-      qf[s] = x;
+      if (col_valid) x = *(const u32x4*)(qrow + 8 * ks);
+      qf[ks] = x;
     }
   }
   const float c = a.scale_log2;
   float slope2 = 0.f;
   if constexpr (ALIBI) slope2 = col_valid ? a.slopes[head] * kLog2e : 0.f;
 
-  f32x16 o[D / 32];
+  // K/V rows of this sequence and head, bounded: rows past the end read zeros
+  const uint32_t rs_bytes = (uint32_t)a.Hkv * D * 2;
+  const uint32_t seq_bytes = (uint32_t)(Lk - 1) * rs_bytes + D * 2;
+  const size_t head_off = ((size_t)sk0 * a.Hkv + g) * D;
+  const __amdgpu_buffer_rsrc_t krs = rows_rsrc(a.k + head_off, seq_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = rows_rsrc(a.v + head_off, seq_bytes);
+  // K operand rows: sub-block bb row r = lane & 15 holds key 8*(r/4) + 4*bb + r%4,
+  // so that a lane's 8 scores are 8 consecutive keys (the P operand layout)
+  uint32_t k_off[2];
 #pragma unroll
-  for (int d = 0; d < D / 32; ++d) o[d] = f32x16{};
+  for (int bb = 0; bb < 2; ++bb)
+    k_off[bb] = (uint32_t)(8 * (q >> 2) + 4 * bb + (q & 3)) * rs_bytes + (uint32_t)((D / 4) * g4) * 2;
+  // V staging: lane (kq, cv) loads keys 4kq..4kq+3 x feature chunks cv + 8*x
+  const int kq = lane & 7, cv = lane >> 3;
+  const uint32_t v_off = (uint32_t)(4 * kq) * rs_bytes + (uint32_t)cv * 16u;
+  uint16_t* vt = reinterpret_cast<uint16_t*>(smem) + wave * kSlotElems;  // this wave's V^T [D][kVtStride]
+
+  struct Regs {
+    u32x4 k[2][KS];
+    u32x4 v[VCH][4];
+  };
+  auto load = [&](Regs& R, int j0) {
+    const int soff = j0 * (int)rs_bytes;
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        R.k[bb][ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, k_off[bb] + 16 * ks, soff, 0));
+#pragma unroll
+    for (int x = 0; x < VCH; ++x)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        R.v[x][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, v_off + i * rs_bytes + x * 128, soff, 0));
+  };
+
+  f32x4 o[DB];
+#pragma unroll
+  for (int d = 0; d < DB; ++d) o[d] = f32x4{};
   float m_run = kNegInf, l_run = 0.f;
 
-  Stager st;
-  st.load(a.k, a.v, sk0, c1, c0, g, a.Hkv, tid);
-  for (int j0 = c0; j0 < c1; j0 += kDcBN) {
-    __syncthreads();
-    st.store(smem, tid);
-    __syncthreads();
-    if (j0 + kDcBN < c1) st.load(a.k, a.v, sk0, c1, j0 + kDcBN, g, a.Hkv, tid);
-
-    const int jw = j0 + 32 * wave;  // first key of this wave's block
-    if (jw < c1) {
-      f32x16 s = f32x16{};
-      const uint16_t* kp = smem + (32 * wave + key_of_row(l32)) * L::kStride + 8 * hi;
+  auto compute = [&](Regs& R, int j0) {
+    // V block -> LDS, transposed (and re-encoded as IEEE half for bfloat16)
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) s = mfma_32x32x16<BF16>(*(const u32x4*)(kp + 16 * ks), qf[ks], s);
-
-      const bool need_mask = jw + 32 > c1;
-      const int jlane = jw + 8 * hi;
-      const float sb = slope2 * (float)(jlane - qpos);
-      float mx = kNegInf;
+    for (int x = 0; x < VCH; ++x) {
+      u32x4 a0 = R.v[x][0], a1 = R.v[x][1], a2 = R.v[x][2], a3 = R.v[x][3];
+      if constexpr (BF16) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int jl = key_of_reg(r, 0);
-        float x;
-        if constexpr (ALIBI) x = __builtin_fmaf(s[r], c, __builtin_fmaf(slope2, (float)jl, sb));
-        else x = s[r] * c;
-        if (need_mask && jlane + jl >= c1) x = kNegInf;
-        s[r] = x;
-        mx = __builtin_fmaxf(mx, x);
-      }
-      mx = halfwave_max(mx);
-      const float m_new = __builtin_fmaxf(m_run, mx);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      float lsum = 0.f;
-      u32x4 pf[2];
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = fast_exp2(s[r] - m_use);
-        const float p1 = fast_exp2(s[r + 1] - m_use);
-        lsum += p0 + p1;
-        pf[r / 8][(r % 8) / 2] = pack_f16x2(p0, p1);
-      }
-      l_run = l_run * alpha + lsum;
-      m_run = m_new;
-#pragma unroll
-      for (int d = 0; d < D / 32; ++d) o[d] *= alpha;
-      const uint16_t* Vt = smem + L::kElems;
-#pragma unroll
-      for (int ch = 0; ch < 2; ++ch) {
-#pragma unroll
-        for (int d = 0; d < D / 32; ++d) {
-          const u32x4 vf = *(const u32x4*)(Vt + (32 * d + l32) * L::vStride + 32 * wave + 16 * ch + 8 * hi);
-          o[d] = mfma_32x32x16<false>(vf, pf[ch], o[d]);
+        for (int w = 0; w < 4; ++w) {
+          a0[w] = bf16x2_to_f16x2(a0[w]);
+          a1[w] = bf16x2_to_f16x2(a1[w]);
+          a2[w] = bf16x2_to_f16x2(a2[w]);
+          a3[w] = bf16x2_to_f16x2(a3[w]);
         }
       }
+      const int d0 = 8 * (cv + 8 * x);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        u32x2 even, odd;
+        even[0] = __builtin_amdgcn_perm(a1[w], a0[w], 0x05040100u);
+        even[1] = __builtin_amdgcn_perm(a3[w], a2[w], 0x05040100u);
+        odd[0] = __builtin_amdgcn_perm(a1[w], a0[w], 0x07060302u);
+        odd[1] = __builtin_amdgcn_perm(a3[w], a2[w], 0x07060302u);
+        *(u32x2*)(vt + (d0 + 2 * w) * kVtStride + 4 * kq) = even;
+        *(u32x2*)(vt + (d0 + 2 * w + 1) * kVtStride + 4 * kq) = odd;
+      }
     }
+    // scores: lane (q, g4) gets keys j0 + 8*g4 + 0..7 of column q
+    f32x4 s[2];
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      s[bb] = f32x4{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) s[bb] = mfma_16x16x32<BF16>(R.k[bb][ks], qf[ks], s[bb]);
+    }
+    const int jlane = j0 + 8 * g4;
+    float x[8];
+    float mx = kNegInf;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float sc = s[e / 4][e % 4];
+      float v;
+      if constexpr (ALIBI) v = __builtin_fmaf(sc, c, slope2 * (float)(jlane + e - qpos));
+      else v = sc * c;
+      if (jlane + e >= c1) v = kNegInf;
+      x[e] = v;
+      mx = __builtin_fmaxf(mx, v);
+    }
+    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16));
+    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+    if (__any(mx > m_run + 8.f)) {
+      const float m_new = __builtin_fmaxf(m_run, mx);
+      const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < DB; ++d) o[d] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+    u32x4 pf;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const float p0 = fast_exp2(x[e] - m_use), p1 = fast_exp2(x[e + 1] - m_use);
+      l_run += p0 + p1;
+      pf[e / 2] = pack_f16x2(p0, p1);
+    }
+    // O^T += V^T P^T: V^T fragment of feature block d is row 16d + q, keys 8*g4..+7
+#pragma unroll
+    for (int d = 0; d < DB; ++d) {
+      const u32x4 vf = *(const u32x4*)(vt + (16 * d + q) * kVtStride + 8 * g4);
+      o[d] = mfma_16x16x32<false>(vf, pf, o[d]);
+    }
+  };
+
+  // this wave's blocks: j = c0 + 32 * (wave + 4 * i)
+  const int nblk = (c1 - c0 + kBlk - 1) / kBlk;
+  Regs ra, rb;
+  int i = wave;
+  if (i < nblk) load(ra, c0 + kBlk * i);
+  for (; i < nblk; i += 2 * kWaves) {
+    const int inext = i + kWaves;
+    if (inext < nblk) load(rb, c0 + kBlk * inext);
+    compute(ra, c0 + kBlk * i);
+    if (inext >= nblk) break;
+    if (inext + kWaves < nblk) load(ra, c0 + kBlk * (inext + kWaves));
+    compute(rb, c0 + kBlk * inext);
   }
 
   // ---- merge the 4 waves' partial states in LDS
-  const float l_tot = halfwave_sum(l_run);
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
   __syncthreads();
-  float* red = reinterpret_cast<float*>(smem);   // [4][32][kRedStride]
-  float* mred = red + 4 * 32 * kRedStride;       // [4][32]
-  float* lred = mred + 4 * 32;                   // [4][32]
+  float* red = reinterpret_cast<float*>(smem);   // [4][16][kRedStride]
+  float* mred = red + kWaves * 16 * kRedStride;  // [4][16]
+  float* lred = mred + kWaves * 16;              // [4][16]
 #pragma unroll
-  for (int d = 0; d < D / 32; ++d)
+  for (int d = 0; d < DB; ++d)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) red[(wave * 32 + l32) * kRedStride + 32 * d + acc_row(r, hi)] = o[d][r];
-  if (hi == 0) {
-    mred[wave * 32 + l32] = m_run;
-    lred[wave * 32 + l32] = l_tot;
+    for (int r = 0; r < 4; ++r) red[(wave * 16 + q) * kRedStride + 16 * d + 4 * g4 + r] = o[d][r];
+  if (g4 == 0) {
+    mred[wave * 16 + q] = m_run;
+    lred[wave * 16 + q] = l_run;
   }
   __syncthreads();
 
-  const int q = tid >> 3, part = tid & 7;  // 32 columns x 8 parts of D/8 features
-  if (hs * kDcHeadsPerWg + q >= a.group) return;
+  const int qc = tid >> 4, part = tid & 15;  // 16 columns x 16 parts of D/16 features
+  if (hs * 16 + qc >= a.group) return;
   float M = kNegInf;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) M = __builtin_fmaxf(M, mred[w * 32 + q]);
-  float wgt[4], Ls = 0.f;
+  for (int w = 0; w < kWaves; ++w) M = __builtin_fmaxf(M, mred[w * 16 + qc]);
+  float wgt[kWaves], Ls = 0.f;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const float mw = mred[w * 32 + q];
+  for (int w = 0; w < kWaves; ++w) {
+    const float mw = mred[w * 16 + qc];
     wgt[w] = (mw == kNegInf) ? 0.f : fast_exp2(mw - M);
-    Ls += wgt[w] * lred[w * 32 + q];
+    Ls += wgt[w] * lred[w * 16 + qc];
   }
   const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
-  const int hq = g * a.group + hs * kDcHeadsPerWg + q;
+  const int hq = g * a.group + hs * 16 + qc;
   const size_t prow = ((size_t)b * a.max_chunks + chunk) * a.Hq + hq;
-  float* dst = a.ws_o + prow * D + part * (D / 8);
+  float* dst = a.ws_o + prow * D + part * (D / 16);
 #pragma unroll
-  for (int e = 0; e < D / 8; ++e) {
-    const int d = part * (D / 8) + e;
+  for (int e = 0; e < D / 16; ++e) {
+    const int d = part * (D / 16) + e;
     float acc = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) acc += wgt[w] * red[(w * 32 + q) * kRedStride + d];
+    for (int w = 0; w < kWaves; ++w) acc += wgt[w] * red[(w * 16 + qc) * kRedStride + d];
     dst[e] = acc * inv;
   }
   if (part == 0) a.ws_lse[prow] = Ls > 0.f ? M + fast_log2(Ls) : kNegInf;
+#endif
 }
 
 template <int D, bool BF16>

@@ -9,12 +9,20 @@
 //   online softmax   per query row = per lane, in float32, in log2 units
 //   O^T += V^T P^T   32 features x 32 queries per product, P re-used from S^T's
 //                    registers without any data movement
+//
+// Software pipeline (one wave per SIMD, the whole register file per wave):
+// while the vector ALU turns tile t's scores into probabilities, the matrix
+// pipe already computes tile t+1's scores into a second score buffer; then
+// P V of tile t overlaps the staging of tile t+2.  K/V tiles rotate through
+// three LDS buffers, so every load has a full iteration to land and one
+// barrier per tile suffices.
+//
 // Key tiles run from the causal diagonal backwards, so the largest scores (and,
 // with ALiBi, the smallest distance penalties) come first and the running
-// maximum rarely has to move; O is rescaled only when some row's maximum
-// grows by more than 2^8.  The causal mask and the end of a sequence cost
-// element tests only on the tiles that straddle them; tiles entirely above
-// the diagonal are never loaded.
+// maximum rarely has to move; O is rescaled only when some row's maximum grows
+// by more than 2^8.  The causal mask and the end of a sequence cost element
+// tests only on the tiles that straddle them; tiles entirely above the
+// diagonal of the whole workgroup are never loaded.
 //
 // Staging: K tiles go HBM -> LDS directly (buffer loads with the LDS
 // destination, no registers); V tiles go through registers, where they are
@@ -33,6 +41,7 @@ namespace mea {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kBufs = 3;                  // LDS ring of K/V tiles
 constexpr float kRescaleThreshold = 8.f;  // log2 units: p may reach 2^8 before O is rescaled
 
 template <int D>
@@ -62,11 +71,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base
 }  // namespace
 
 template <int D, bool BF16, bool CAUSAL, bool ALIBI>
-__global__ __launch_bounds__(kThreads, 2) void fwd_prefill_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the body uses buffer-resource types that exist only for the GPU target
   using L = PfLayout<D>;
   constexpr int BN = L::BN;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * L::bufBytes];
+  constexpr int KS = D / 16;             // k-steps of the Q K^T product
+  constexpr int NV = 4 * (D / 32);       // products of P V per tile
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kBufs * L::bufBytes];
 
   // ---- work item: XCD-aware remap of the linear workgroup index
   const int per_xcd = (int)gridDim.x >> 3;
@@ -98,20 +109,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_prefill_kernel(FwdArgs a) {
   const bool row_valid = my_tok < Lq;
   const int qpos = my_tok + off;  // key position of this query row
 
-  int kv_end = Lk, wave_kv_end = Lk;
-  if constexpr (CAUSAL) {
-    kv_end = min(Lk, min(t0 + BT, Lq) + off);
-    wave_kv_end = min(Lk, min(tok0 + 32, Lq) + off);
-  }
-  if (tok0 >= Lq) wave_kv_end = 0;
+  int kv_end = Lk;
+  if constexpr (CAUSAL) kv_end = min(Lk, min(t0 + BT, Lq) + off);
   const int nkt = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
 
   // ---- Q^T operand: lane holds features 16*s + 8*hi .. +7 of its row
-  u32x4 qf[D / 16];
+  u32x4 qf[KS];
   {
     const uint16_t* qrow = a.q + ((size_t)(sq0 + my_tok) * a.Hq + head) * D + 8 * hi;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
+    for (int s = 0; s < KS; ++s) {
       u32x4 x = {0u, 0u, 0u, 0u};
       if (row_valid) x = *(const u32x4*)(qrow + 16 * s);
       qf[s] = x;
@@ -143,9 +150,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_prefill_kernel(FwdArgs a) {
   const uint32_t v_voff = (uint32_t)(4 * kq) * rs_bytes + (uint32_t)cv * 16u;
   u32x4 vr[4];
 
-  auto issue_loads = [&](int ti, int buf) {
-    const int soff = ti * BN * (int)rs_bytes;
-    uint8_t* kdst = smem + buf * L::bufBytes;
+  // tile index of pipeline step t (diagonal tile first) and its LDS buffer
+  auto tile_of = [&](int t) { return nkt - 1 - t; };
+  auto buf_of = [&](int t) { return smem + (t % kBufs) * L::bufBytes; };
+
+  auto issue_loads = [&](int t) {
+    const int soff = tile_of(t) * BN * (int)rs_bytes;
+    uint8_t* kdst = buf_of(t);
 #pragma unroll
     for (int i = 0; i < L::kLoads; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)(kdst + (i * 4 + wave) * 1024),
@@ -156,9 +167,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_prefill_kernel(FwdArgs a) {
         vr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, v_voff + i * rs_bytes, soff, 0));
     }
   };
-  auto store_v = [&](int buf) {
+  auto store_v = [&](int t) {
     if (!v_job) return;
-    uint16_t* vt = reinterpret_cast<uint16_t*>(smem + buf * L::bufBytes + L::kBytes);
+    uint16_t* vt = reinterpret_cast<uint16_t*>(buf_of(t) + L::kBytes);
     u32x4 a0 = vr[0], a1 = vr[1], a2 = vr[2], a3 = vr[3];
     if constexpr (BF16) {
 #pragma unroll
@@ -186,24 +197,40 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_prefill_kernel(FwdArgs a) {
   for (int d = 0; d < D / 32; ++d) o[d] = f32x16{};
   float m_run = kNegInf, l_run = 0.f;
 
-  // One 64-key tile: S^T = K Q^T, softmax update, O^T += V^T P^T.
-  auto tile_step = [&](const uint8_t* buf, int j0, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    const uint8_t* Kb = buf;
-    const uint16_t* Vt = reinterpret_cast<const uint16_t*>(buf + L::kBytes);
-    f32x16 s[2];
+  // S^T = K Q^T of step t into s (two 32-key blocks); LDS fragments are read
+  // two k-steps ahead of the products that use them.
+  auto qk = [&](int t, f32x16 (&s)[2]) {
+    const uint8_t* Kb = buf_of(t);
+    const int r0 = key_of_row(l32), r1 = 32 + r0;
+    const uint8_t* krow0 = Kb + r0 * (D * 2);
+    const uint8_t* krow1 = Kb + r1 * (D * 2);
+    auto kread = [&](const uint8_t* krow, int r, int ks) {
+      return *(const u32x4*)(krow + k_pos<D>(r, 2 * ks + hi) * 16);
+    };
+    u32x4 ka[2][2];
+    ka[0][0] = kread(krow0, r0, 0);
+    ka[0][1] = kread(krow1, r1, 0);
+    ka[1][0] = kread(krow0, r0, 1);
+    ka[1][1] = kread(krow1, r1, 1);
+    s[0] = f32x16{};
+    s[1] = f32x16{};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      const int r = 32 * kb + key_of_row(l32);
-      const uint8_t* krow = Kb + r * (D * 2);
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const u32x4 kf = *(const u32x4*)(krow + k_pos<D>(r, 2 * ks + hi) * 16);
-        s[kb] = mfma_32x32x16<BF16>(kf, qf[ks], s[kb]);
+    for (int ks = 0; ks < KS; ++ks) {
+      s[0] = mfma_32x32x16<BF16>(ka[ks & 1][0], qf[ks], s[0]);
+      s[1] = mfma_32x32x16<BF16>(ka[ks & 1][1], qf[ks], s[1]);
+      if (ks + 2 < KS) {
+        ka[ks & 1][0] = kread(krow0, r0, ks + 2);
+        ka[ks & 1][1] = kread(krow1, r1, ks + 2);
       }
     }
+  };
+
+  // Scores of step t -> log2 units with bias and masks, row maximum, and the
+  // (rare) rescale of O.
+  auto prepare = [&](int t, f32x16 (&s)[2]) {
+    const int j0 = tile_of(t) * BN;
     const int jlane = j0 + 8 * hi;  // key of register 0 in block 0
+    const bool need_mask = (j0 + BN > Lk) || (CAUSAL && j0 + BN - 1 > tok0 + off);
     float mx = kNegInf;
     if constexpr (ALIBI) {
       const float sb = slope2 * (float)(jlane - qpos);
@@ -212,30 +239,24 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_prefill_kernel(FwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int jl = 32 * kb + key_of_reg(r, 0);
-          float x;
-          if constexpr (CAUSAL) x = __builtin_fmaf(s[kb][r], c, __builtin_fmaf(slope2, (float)jl, sb));
-          else x = __builtin_fmaf(s[kb][r], c, -slope2 * __builtin_fabsf((float)(jlane + jl - qpos)));
-          if constexpr (MASK) {
-            const int j = jlane + jl;
-            if (j >= Lk || (CAUSAL && j > qpos)) x = kNegInf;
-          }
-          s[kb][r] = x;
-          mx = __builtin_fmaxf(mx, x);
+          if constexpr (CAUSAL) s[kb][r] = __builtin_fmaf(s[kb][r], c, __builtin_fmaf(slope2, (float)jl, sb));
+          else s[kb][r] = __builtin_fmaf(s[kb][r], c, -slope2 * __builtin_fabsf((float)(jlane + jl - qpos)));
         }
-    } else {
-      // scores stay unscaled here; the scale (> 0) is folded into the exponent
+    }
+    if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          if constexpr (MASK) {
-            const int j = jlane + 32 * kb + key_of_reg(r, 0);
-            if (j >= Lk || (CAUSAL && j > qpos)) s[kb][r] = kNegInf;
-          }
-          mx = __builtin_fmaxf(mx, s[kb][r]);
+          const int j = jlane + 32 * kb + key_of_reg(r, 0);
+          if (j >= Lk || (CAUSAL && j > qpos)) s[kb][r] = kNegInf;
         }
-      mx *= c;
     }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[kb][r]);
+    if constexpr (!ALIBI) mx *= c;  // unscaled scores: the scale (> 0) is folded into the exponent
     mx = halfwave_max(mx);
     if (__any(mx > m_run + kRescaleThreshold)) {
       const float m_new = __builtin_fmaxf(m_run, mx);
@@ -245,9 +266,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_prefill_kernel(FwdArgs a) {
       for (int d = 0; d < D / 32; ++d) o[d] *= alpha;
       m_run = m_new;
     }
+  };
+
+  // Probabilities of the prepared scores, packed as the P operand.
+  auto probs = [&](f32x16 (&s)[2], u32x4 (&pf)[4], float& lsum) {
     const float m_use = (m_run == kNegInf) ? 0.f : m_run;
-    float lsum = 0.f;
-    u32x4 pf[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -263,37 +286,79 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_prefill_kernel(FwdArgs a) {
         lsum += p0 + p1;
         pf[2 * kb + r / 8][(r % 8) / 2] = pack_f16x2(p0, p1);
       }
-    l_run += lsum;
+  };
+
+  // O^T += V^T P^T of step t; V^T fragments read four products ahead.
+  auto pv = [&](int t, const u32x4 (&pf)[4]) {
+    const uint16_t* Vt = reinterpret_cast<const uint16_t*>(buf_of(t) + L::kBytes);
+    auto vread = [&](int i) {
+      const int ch = i / (D / 32), d = i % (D / 32);
+      return *(const u32x4*)(Vt + (32 * d + l32) * L::vStride + 16 * ch + 8 * hi);
+    };
+    u32x4 va[4];
 #pragma unroll
-    for (int ch = 0; ch < 4; ++ch)
+    for (int i = 0; i < 4; ++i) va[i] = vread(i);
 #pragma unroll
-      for (int d = 0; d < D / 32; ++d) {
-        const u32x4 vf = *(const u32x4*)(Vt + (32 * d + l32) * L::vStride + 16 * ch + 8 * hi);
-        o[d] = mfma_32x32x16<false>(vf, pf[ch], o[d]);
+    for (int i = 0; i < NV; ++i) {
+      const int ch = i / (D / 32), d = i % (D / 32);
+      o[d] = mfma_32x32x16<false>(va[i & 3], pf[ch], o[d]);
+      if (i + 4 < NV) va[i & 3] = vread(i + 4);
+    }
+  };
+
+  // One pipeline step: scores of step t are in cur.  A full step also
+  // computes step t+1's scores into nxt while it finishes step t (the last
+  // step of a workgroup has no successor).
+  auto step = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2], auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    if (t + 2 < nkt) issue_loads(t + 2);
+    prepare(t, cur);
+    u32x4 pf[4];
+    float lsum = 0.f;
+    if constexpr (FULL) qk(t + 1, nxt);
+    probs(cur, pf, lsum);
+    if constexpr (FULL) {
+      // matrix pipe: 2*KS products of Q K^T; vector ALU: the exponentials in between
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * KS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+        if (i % 2 == 1 && i < 2 * KS - 4) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
+    }
+    l_run += lsum;
+    pv(t, pf);
+    if (t + 2 < nkt) {
+      __builtin_amdgcn_s_waitcnt(0);
+      store_v(t + 2);
+    }
+    __syncthreads();
   };
 
   if (nkt > 0) {
-    issue_loads(nkt - 1, 0);
+    issue_loads(0);
     __builtin_amdgcn_s_waitcnt(0);
     store_v(0);
-  }
-  __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int ti = nkt - 1 - kt;  // diagonal tile first
-    const int j0 = ti * BN;
-    const int cur = kt & 1;
-    if (kt + 1 < nkt) issue_loads(ti - 1, cur ^ 1);
-    if (j0 < wave_kv_end) {
-      const bool need_mask = (j0 + BN > Lk) || (CAUSAL && j0 + BN - 1 > tok0 + off);
-      if (need_mask) tile_step(smem + cur * L::bufBytes, j0, std::true_type{});
-      else tile_step(smem + cur * L::bufBytes, j0, std::false_type{});
-    }
-    if (kt + 1 < nkt) {
+    if (nkt > 1) {
+      issue_loads(1);
       __builtin_amdgcn_s_waitcnt(0);
-      store_v(cur ^ 1);
+      store_v(1);
     }
     __syncthreads();
+    f32x16 sa[2], sb[2];
+    qk(0, sa);
+    int t = 0;
+    for (; t + 2 < nkt; t += 2) {
+      step(t, sa, sb, std::true_type{});
+      step(t + 1, sb, sa, std::true_type{});
+    }
+    if (nkt - t == 2) {
+      step(t, sa, sb, std::true_type{});
+      step(t + 1, sb, sa, std::false_type{});
+    } else {
+      step(t, sa, sb, std::false_type{});
+    }
   }
 
   // ---- epilogue: normalise, round, stage the wave's 32 x D tile through LDS

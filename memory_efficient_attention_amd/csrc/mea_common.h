@@ -37,7 +37,7 @@ struct FwdArgs {
   int32_t Hkv;
   int32_t group;             // Hq / Hkv
   int32_t heads_per_wg;      // prefill: query heads of one group served per workgroup
-  int32_t head_slices;       // prefill: group / heads_per_wg; decode: ceil(group / 32)
+  int32_t head_slices;       // prefill: group / heads_per_wg; decode: ceil(group / 16)
   int32_t chunk_keys;        // decode: keys per chunk
   int32_t max_chunks;        // decode: ceil(max_seqlen_k / chunk_keys)
   int32_t pf_max_tiles;      // prefill: query tiles of the longest sequence

@@ -12,9 +12,9 @@ namespace mea {
 // query heads that share one key/value head.
 constexpr int kPfWaves = 4;
 constexpr int kPfBN = 64;          // keys per LDS tile
-// Decode: workgroups of 4 waves streaming 128-key tiles, one 32-key block per wave.
-constexpr int kDcBN = 128;
-constexpr int kDcHeadsPerWg = 32;  // query heads of one group served per workgroup
+// Decode: workgroups of 4 waves, each streaming its own 32-key blocks of a chunk.
+constexpr int kDcBN = 128;        // chunk granularity: 4 waves x 32-key blocks
+constexpr int kDcHeadsPerWg = 16;  // query heads of one group served per workgroup
 
 hipError_t launch_prefill(const FwdArgs& a, int D, bool bf16, bool causal, bool alibi,
                           int max_seqlen_q, hipStream_t stream);
