@@ -64,8 +64,10 @@ __global__ __launch_bounds__(256, 2) void fwd_decode_partial_kernel(FwdArgs a) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, q = lane & 15, g4 = lane >> 4;
-  const int chunk = blockIdx.x, b = blockIdx.y;
-  const int g = blockIdx.z / a.head_slices, hs = blockIdx.z % a.head_slices;
+  // grid: x = key/value head slice (fastest, so the heads of one chunk are
+  // read together and share DRAM pages), y = chunk, z = sequence
+  const int g = blockIdx.x / a.head_slices, hs = blockIdx.x % a.head_slices;
+  const int chunk = blockIdx.y, b = blockIdx.z;
 
   const int sq0 = a.seqstart_q[b], Lq = a.seqstart_q[b + 1] - sq0;
   const int sk0 = a.seqstart_k[b], Lk = a.seqstart_k[b + 1] - sk0;
@@ -78,14 +80,16 @@ __global__ __launch_bounds__(256, 2) void fwd_decode_partial_kernel(FwdArgs a) {
   const bool col_valid = hl < a.group;
   const int head = g * a.group + hl;
 
-  // Q^T operand: lane (q, g4) holds features (D/4)*g4 + 8*ks .. +7 at k-step ks
+  // Q^T operand: lane (q, g4) holds 16-byte feature chunk 4*ks + g4 at k-step
+  // ks (the K operand uses the same chunks, so a K load instruction reads 64
+  // contiguous bytes of each of its 16 rows)
   u32x4 qf[KS];
   {
-    const uint16_t* qrow = a.q + ((size_t)sq0 * a.Hq + head) * D + (D / 4) * g4;
+    const uint16_t* qrow = a.q + ((size_t)sq0 * a.Hq + head) * D + 8 * g4;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 x = {0u, 0u, 0u, 0u};
-      if (col_valid) x = *(const u32x4*)(qrow + 8 * ks);
+      if (col_valid) x = *(const u32x4*)(qrow + 32 * ks);
       qf[ks] = x;
     }
   }
@@ -104,7 +108,7 @@ __global__ __launch_bounds__(256, 2) void fwd_decode_partial_kernel(FwdArgs a) {
   uint32_t k_off[2];
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb)
-    k_off[bb] = (uint32_t)(8 * (q >> 2) + 4 * bb + (q & 3)) * rs_bytes + (uint32_t)((D / 4) * g4) * 2;
+    k_off[bb] = (uint32_t)(8 * (q >> 2) + 4 * bb + (q & 3)) * rs_bytes + (uint32_t)g4 * 16u;
   // V staging: lane (kq, cv) loads keys 4kq..4kq+3 x feature chunks cv + 8*x
   const int kq = lane & 7, cv = lane >> 3;
   const uint32_t v_off = (uint32_t)(4 * kq) * rs_bytes + (uint32_t)cv * 16u;
@@ -120,7 +124,7 @@ __global__ __launch_bounds__(256, 2) void fwd_decode_partial_kernel(FwdArgs a) {
     for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        R.k[bb][ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, k_off[bb] + 16 * ks, soff, 0));
+        R.k[bb][ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, k_off[bb] + 64 * ks, soff, 0));
 #pragma unroll
     for (int x = 0; x < VCH; ++x)
 #pragma unroll
@@ -296,7 +300,7 @@ __global__ __launch_bounds__(D) void fwd_decode_combine_kernel(FwdArgs a) {
 template <int D, bool BF16>
 static hipError_t launch_decode_d(const FwdArgs& a, bool alibi, hipStream_t stream) {
   if (a.max_chunks > 0) {
-    const dim3 grid(a.max_chunks, a.num_seqs, a.Hkv * a.head_slices);
+    const dim3 grid(a.Hkv * a.head_slices, a.max_chunks, a.num_seqs);
     if (alibi) hipLaunchKernelGGL((fwd_decode_partial_kernel<D, BF16, true>), grid, dim3(256), 0, stream, a);
     else hipLaunchKernelGGL((fwd_decode_partial_kernel<D, BF16, false>), grid, dim3(256), 0, stream, a);
     const hipError_t e = hipGetLastError();

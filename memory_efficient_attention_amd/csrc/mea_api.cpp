@@ -122,7 +122,7 @@ mea_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, fl
     a.heads_per_wg = mea::kDcHeadsPerWg;
     a.ws_o = static_cast<float*>(workspace);
     a.ws_lse = a.ws_o + (size_t)num_seqs * a.max_chunks * Hq * D;
-    if ((long long)Hkv * a.head_slices > 65535) return fail(MEA_ERR_UNSUPPORTED, "too many key/value head slices");
+    if (a.max_chunks > 65535) return fail(MEA_ERR_UNSUPPORTED, "more than 65535 key chunks per sequence");
     err = mea::launch_decode(a, D, bf16, alibi, s);
   } else {
     a.heads_per_wg = gcd_int(a.group, mea::kPfWaves);
