@@ -42,6 +42,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// Cache policy of the K/V stream loads (default: measured faster than the
+// non-temporal policy for this access pattern).
+constexpr int kStreamPolicy = 0;
+
 constexpr int kWaves = 4;
 constexpr int kBlk = 32;                  // keys per wave block
 constexpr int kVtStride = kBlk + 8;       // elements per V^T row in a wave's LDS slot
@@ -124,12 +128,12 @@ __global__ __launch_bounds__(256, 2) void fwd_decode_partial_kernel(FwdArgs a) {
     for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        R.k[bb][ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, k_off[bb] + 64 * ks, soff, 0));
+        R.k[bb][ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, k_off[bb] + 64 * ks, soff, kStreamPolicy));
 #pragma unroll
     for (int x = 0; x < VCH; ++x)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        R.v[x][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, v_off + i * rs_bytes + x * 128, soff, 0));
+        R.v[x][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, v_off + i * rs_bytes + x * 128, soff, kStreamPolicy));
   };
 
   f32x4 o[DB];
@@ -269,31 +273,69 @@ __global__ __launch_bounds__(256, 2) void fwd_decode_partial_kernel(FwdArgs a) {
 #endif
 }
 
+// One wave per (sequence, query head); a lane owns D/64 features.  The chunk
+// log-sum-exps are reduced across the wave first, then every lane sums its
+// features over the chunks with several partial rows in flight.
 template <int D, bool BF16>
-__global__ __launch_bounds__(D) void fwd_decode_combine_kernel(FwdArgs a) {
-  const int b = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+__global__ __launch_bounds__(256) void fwd_decode_combine_kernel(FwdArgs a) {
+  constexpr int F = D / 64;  // features per lane
+  const int lane = threadIdx.x & 63;
+  const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int b = blockIdx.y;
+  if (h >= a.Hq) return;
   const int sq0 = a.seqstart_q[b], Lq = a.seqstart_q[b + 1] - sq0;
   if (Lq == 0) return;
   const int Lk = a.seqstart_k[b + 1] - a.seqstart_k[b];
   const int nch = (Lk + a.chunk_keys - 1) / a.chunk_keys;
   const size_t row0 = (size_t)b * a.max_chunks * a.Hq + h;  // partial row of chunk 0
+  const float* lse_p = a.ws_lse + row0;                        // chunk c at [c * Hq]
   float M = kNegInf;
-  for (int ch = 0; ch < nch; ++ch) M = __builtin_fmaxf(M, a.ws_lse[row0 + (size_t)ch * a.Hq]);
-  float S = 0.f, acc = 0.f;
+  for (int ch = lane; ch < nch; ch += 64) M = __builtin_fmaxf(M, lse_p[(size_t)ch * a.Hq]);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) M = __builtin_fmaxf(M, __shfl_xor(M, m));
+  float S = 0.f;
+  float acc[F];
+#pragma unroll
+  for (int f = 0; f < F; ++f) acc[f] = 0.f;
   if (M != kNegInf) {
-    for (int ch = 0; ch < nch; ++ch) {
-      const float lc = a.ws_lse[row0 + (size_t)ch * a.Hq];
+    const float* o_p = a.ws_o + row0 * D + lane * F;             // chunk c at [c * Hq * D]
+    const size_t ostride = (size_t)a.Hq * D;
+    int ch = 0;
+    for (; ch + 4 <= nch; ch += 4) {
+      float lc[4], ov[4][F];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        lc[u] = lse_p[(size_t)(ch + u) * a.Hq];
+#pragma unroll
+        for (int f = 0; f < F; ++f) ov[u][f] = o_p[(size_t)(ch + u) * ostride + f];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float w = (lc[u] == kNegInf) ? 0.f : fast_exp2(lc[u] - M);
+        S += w;
+#pragma unroll
+        for (int f = 0; f < F; ++f) acc[f] += w * ov[u][f];
+      }
+    }
+    for (; ch < nch; ++ch) {
+      const float lc = lse_p[(size_t)ch * a.Hq];
       const float w = (lc == kNegInf) ? 0.f : fast_exp2(lc - M);
       S += w;
-      acc += w * a.ws_o[(row0 + (size_t)ch * a.Hq) * D + d];
+#pragma unroll
+      for (int f = 0; f < F; ++f) acc[f] += w * o_p[(size_t)ch * ostride + f];
     }
   }
-  const float val = S > 0.f ? acc / S : 0.f;
-  uint16_t bits;
-  if constexpr (BF16) bits = __builtin_bit_cast(uint16_t, (__bf16)val);
-  else bits = __builtin_bit_cast(uint16_t, (_Float16)val);
-  a.out[((size_t)sq0 * a.Hq + h) * D + d] = bits;
-  if (d == 0 && a.lse != nullptr)
+  const float inv = S > 0.f ? 1.f / S : 0.f;
+  uint16_t* dst = a.out + ((size_t)sq0 * a.Hq + h) * D + lane * F;
+  if constexpr (F == 2) {
+    *(uint32_t*)dst = pack_out_x2<BF16>(acc[0] * inv, acc[1] * inv);
+  } else {
+    uint16_t bits;
+    if constexpr (BF16) bits = __builtin_bit_cast(uint16_t, (__bf16)(acc[0] * inv));
+    else bits = __builtin_bit_cast(uint16_t, (_Float16)(acc[0] * inv));
+    *dst = bits;
+  }
+  if (lane == 0 && a.lse != nullptr)
     a.lse[(size_t)h * a.total_q + sq0] = S > 0.f ? (M + fast_log2(S)) * kLn2 : kNegInf;
 }
 
@@ -306,7 +348,7 @@ static hipError_t launch_decode_d(const FwdArgs& a, bool alibi, hipStream_t stre
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((fwd_decode_combine_kernel<D, BF16>), dim3(a.num_seqs, a.Hq), dim3(D), 0, stream, a);
+  hipLaunchKernelGGL((fwd_decode_combine_kernel<D, BF16>), dim3((a.Hq + 3) / 4, a.num_seqs), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -42,7 +42,7 @@ int32_t default_chunk(int32_t num_seqs, int32_t max_seqlen_k, int32_t Hkv) {
   long long c = (work + 2047) / 2048;
   c = ((c + mea::kDcBN - 1) / mea::kDcBN) * mea::kDcBN;
   if (c < mea::kDcBN) c = mea::kDcBN;
-  if (c > 1024) c = 1024;
+  if (c > 2048) c = 2048;
   return (int32_t)c;
 }
 

@@ -111,8 +111,8 @@ def test_workspace_size():
     ws = _native.mea_fwd_workspace_size
     assert ws(4, 200, 200, 8, 8, 64, 0) == 0                       # prefill needs none
     c = _native.mea_default_chunk_keys(64, 32680, 8)
-    assert c == 1024
-    assert ws(64, 1, 32680, 64, 8, 128, 0) == 64 * 32 * 64 * 129 * 4
+    assert c == 2048
+    assert ws(64, 1, 32680, 64, 8, 128, 0) == 64 * 16 * 64 * 129 * 4
     assert ws(64, 1, 32680, 64, 8, 128, 256) == 64 * 128 * 64 * 129 * 4
     assert ws(64, 1, 32680, 64, 8, 128, 100) == 0                  # invalid chunk
     assert ws(2, 1, 100, 6, 4, 128, 0) == 0                        # Hq % Hkv != 0
@@ -121,4 +121,4 @@ def test_workspace_size():
     assert _native.mea_default_chunk_keys(0, 0, 0) == 128
     for n, L, h in [(1, 1000, 1), (8, 4096, 8), (200, 32768, 8), (3, 77, 2)]:
         c = _native.mea_default_chunk_keys(n, L, h)
-        assert c % 128 == 0 and 128 <= c <= 1024
+        assert c % 128 == 0 and 128 <= c <= 2048
