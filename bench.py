@@ -94,7 +94,7 @@ class Call:
         self.slopes = None if inp.alibi_slopes is None else inp.alibi_slopes.to(dev)
         self.out = torch.empty_like(self.q)
         self.lse = torch.empty((inp.Hq, inp.total_q), dtype=torch.float32, device=dev)
-        self.ws_bytes = _native.mea_fwd_workspace_size(len(inp.seqlens_q), inp.max_seqlen_q,
+        self.ws_bytes = _native.mea_fwd_workspace_size(len(inp.seqlens_q), inp.total_k, inp.max_seqlen_q,
                                                        inp.max_seqlen_k, inp.Hq, inp.Hkv, inp.D, 0)
         self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=dev)
         self.dtype = _native.MEA_BF16 if inp.dtype == "bf16" else _native.MEA_F16
@@ -105,7 +105,7 @@ class Call:
         st = self.native.mea_fwd(
             self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.out.data_ptr(),
             self.lse.data_ptr(), self.ssq.data_ptr(), self.ssk.data_ptr(), len(inp.seqlens_q),
-            inp.total_q, inp.max_seqlen_q, inp.max_seqlen_k, inp.Hq, inp.Hkv, inp.D, self.dtype,
+            inp.total_q, inp.total_k, inp.max_seqlen_q, inp.max_seqlen_k, inp.Hq, inp.Hkv, inp.D, self.dtype,
             int(inp.causal), None if self.slopes is None else self.slopes.data_ptr(), inp.scale,
             self.ws.data_ptr() if self.ws_bytes else None, self.ws_bytes, stream.cuda_stream)
         if st != 0:

@@ -97,11 +97,12 @@ typedef enum {
  *   seqstart_q/k   device int32 [num_seqs + 1].  Preconditions (not checked:
  *                  checking would need a device synchronisation):
  *                  seqstart_*[0] == 0, non-decreasing, seqstart_q[num_seqs]
- *                  == total_q, and every sequence length <= max_seqlen_q
- *                  (resp. max_seqlen_k).  Violations read or write out of
- *                  bounds.
+ *                  == total_q, seqstart_k[num_seqs] == total_k, and every
+ *                  sequence length <= max_seqlen_q (resp. max_seqlen_k).
+ *                  Violations read or write out of bounds.
  *   num_seqs       >= 0; 0 (or total_q == 0) is a no-op returning MEA_OK.
  *   total_q        number of packed query rows (the lse row stride).
+ *   total_k        number of packed key/value rows (sizes the workspace).
  *   max_seqlen_q/k upper bounds of the per-sequence lengths (sizes the grid).
  *   Hq, Hkv        query / key-value heads; Hq % Hkv == 0.
  *   D              head dimension, 64 or 128 (q, k and v share it).
@@ -110,8 +111,8 @@ typedef enum {
  *   alibi_slopes   device float32 [Hq] or NULL.
  *   scale          finite and > 0 (1/sqrt(D) is the usual choice).
  *   workspace      device scratch of at least mea_fwd_workspace_size(...)
- *                  bytes, 256-byte aligned; may be NULL when that size is 0
- *                  (every call with max_seqlen_q != 1).
+ *                  bytes, 256-byte aligned; may be NULL when that size is 0.
+ *                  Its contents on entry do not matter and are clobbered.
  *   stream         hipStream_t to enqueue on.
  *
  * Returns MEA_ERR_INVALID for: a NULL q/k/v/out/seqstart pointer; negative
@@ -130,7 +131,7 @@ typedef enum {
  */
 MEA_EXPORT mea_status_t mea_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                      const int32_t* seqstart_q, const int32_t* seqstart_k, int32_t num_seqs,
-                     int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq,
+                     int32_t total_q, int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq,
                      int32_t Hkv, int32_t D, mea_dtype_t dtype, int32_t causal,
                      const float* alibi_slopes, float scale, void* workspace,
                      size_t workspace_bytes, void* stream);
@@ -145,7 +146,7 @@ MEA_EXPORT mea_status_t mea_fwd(const void* q, const void* k, const void* v, voi
  */
 MEA_EXPORT mea_status_t mea_fwd_splitkv(const void* q, const void* k, const void* v, void* out, float* lse,
                              const int32_t* seqstart_q, const int32_t* seqstart_k,
-                             int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
+                             int32_t num_seqs, int32_t total_q, int32_t total_k, int32_t max_seqlen_q,
                              int32_t max_seqlen_k, int32_t Hq, int32_t Hkv, int32_t D,
                              mea_dtype_t dtype, int32_t causal, const float* alibi_slopes,
                              float scale, void* workspace, size_t workspace_bytes, void* stream,
@@ -153,13 +154,17 @@ MEA_EXPORT mea_status_t mea_fwd_splitkv(const void* q, const void* k, const void
 
 /*
  * mea_fwd_workspace_size -- bytes of workspace mea_fwd (chunk_keys == 0) or
- * mea_fwd_splitkv (chunk_keys > 0) needs for these sizes: 0 unless
- * max_seqlen_q == 1, else num_seqs * ceil(max_seqlen_k / chunk) * Hq * (D + 1)
- * * 4 (float32 partial outputs and log-sum-exps).  Returns 0 for arguments
- * mea_fwd would reject.  Pure host function.
+ * mea_fwd_splitkv (chunk_keys > 0) needs for these sizes.  Pure host function;
+ * returns 0 for arguments mea_fwd would reject.
+ *   max_seqlen_q == 1 (decode): num_seqs * ceil(max_seqlen_k / chunk) * Hq *
+ *     (D + 1) * 4 -- float32 partial outputs and log-sum-exps of the key chunks;
+ *   max_seqlen_q > 1 (prefill): (total_k / 64 + num_seqs) * Hkv * D * 128 --
+ *     one transposed half-precision copy of every 64-key tile of V (0 when
+ *     total_k == 0).
  */
-MEA_EXPORT size_t mea_fwd_workspace_size(int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
-                              int32_t Hq, int32_t Hkv, int32_t D, int32_t chunk_keys);
+MEA_EXPORT size_t mea_fwd_workspace_size(int32_t num_seqs, int32_t total_k, int32_t max_seqlen_q,
+                                         int32_t max_seqlen_k, int32_t Hq, int32_t Hkv, int32_t D,
+                                         int32_t chunk_keys);
 
 /* Key-chunk length mea_fwd picks for a decode call of these sizes. Pure host function. */
 MEA_EXPORT int32_t mea_default_chunk_keys(int32_t num_seqs, int32_t max_seqlen_k, int32_t Hkv);

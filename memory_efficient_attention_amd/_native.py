@@ -31,8 +31,8 @@ _lock = threading.Lock()
 _lib = None
 
 _i32, _sz, _vp, _f32 = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
-_FWD_ARGS = [_vp, _vp, _vp, _vp, _vp,          # q k v out lse
-             _vp, _vp, _i32, _i32, _i32, _i32,  # seqstart_q seqstart_k num_seqs total_q max_q max_k
+_FWD_ARGS = [_vp, _vp, _vp, _vp, _vp,                # q k v out lse
+             _vp, _vp, _i32, _i32, _i32, _i32, _i32,  # seqstart_q seqstart_k num_seqs total_q total_k max_q max_k
              _i32, _i32, _i32, _i32, _i32,      # Hq Hkv D dtype causal
              _vp, _f32, _vp, _sz, _vp]          # slopes scale workspace workspace_bytes stream
 
@@ -57,7 +57,7 @@ def load() -> ctypes.CDLL:
         lib.mea_fwd.restype = ctypes.c_int
         lib.mea_fwd_splitkv.argtypes = _FWD_ARGS + [_i32]
         lib.mea_fwd_splitkv.restype = ctypes.c_int
-        lib.mea_fwd_workspace_size.argtypes = [_i32] * 7
+        lib.mea_fwd_workspace_size.argtypes = [_i32] * 8
         lib.mea_fwd_workspace_size.restype = _sz
         lib.mea_default_chunk_keys.argtypes = [_i32] * 3
         lib.mea_default_chunk_keys.restype = _i32
@@ -71,25 +71,27 @@ def load() -> ctypes.CDLL:
         return lib
 
 
-def mea_fwd(q, k, v, out, lse, seqstart_q, seqstart_k, num_seqs, total_q, max_seqlen_q,
+def mea_fwd(q, k, v, out, lse, seqstart_q, seqstart_k, num_seqs, total_q, total_k, max_seqlen_q,
             max_seqlen_k, Hq, Hkv, D, dtype, causal, alibi_slopes, scale, workspace,
             workspace_bytes, stream) -> int:
-    return load().mea_fwd(q, k, v, out, lse, seqstart_q, seqstart_k, num_seqs, total_q,
+    return load().mea_fwd(q, k, v, out, lse, seqstart_q, seqstart_k, num_seqs, total_q, total_k,
                           max_seqlen_q, max_seqlen_k, Hq, Hkv, D, dtype, causal, alibi_slopes,
                           scale, workspace, workspace_bytes, stream)
 
 
-def mea_fwd_splitkv(q, k, v, out, lse, seqstart_q, seqstart_k, num_seqs, total_q, max_seqlen_q,
-                    max_seqlen_k, Hq, Hkv, D, dtype, causal, alibi_slopes, scale, workspace,
-                    workspace_bytes, stream, chunk_keys) -> int:
+def mea_fwd_splitkv(q, k, v, out, lse, seqstart_q, seqstart_k, num_seqs, total_q, total_k,
+                    max_seqlen_q, max_seqlen_k, Hq, Hkv, D, dtype, causal, alibi_slopes, scale,
+                    workspace, workspace_bytes, stream, chunk_keys) -> int:
     return load().mea_fwd_splitkv(q, k, v, out, lse, seqstart_q, seqstart_k, num_seqs, total_q,
-                                  max_seqlen_q, max_seqlen_k, Hq, Hkv, D, dtype, causal,
+                                  total_k, max_seqlen_q, max_seqlen_k, Hq, Hkv, D, dtype, causal,
                                   alibi_slopes, scale, workspace, workspace_bytes, stream,
                                   chunk_keys)
 
 
-def mea_fwd_workspace_size(num_seqs, max_seqlen_q, max_seqlen_k, Hq, Hkv, D, chunk_keys=0) -> int:
-    return int(load().mea_fwd_workspace_size(num_seqs, max_seqlen_q, max_seqlen_k, Hq, Hkv, D, chunk_keys))
+def mea_fwd_workspace_size(num_seqs, total_k, max_seqlen_q, max_seqlen_k, Hq, Hkv, D,
+                           chunk_keys=0) -> int:
+    return int(load().mea_fwd_workspace_size(num_seqs, total_k, max_seqlen_q, max_seqlen_k, Hq,
+                                             Hkv, D, chunk_keys))
 
 
 def mea_default_chunk_keys(num_seqs, max_seqlen_k, Hkv) -> int:

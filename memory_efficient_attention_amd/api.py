@@ -173,14 +173,14 @@ def attention_packed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     scale = float(np.float32(scale))
-    ws_bytes = _native.mea_fwd_workspace_size(num_seqs, max_seqlen_q, max_seqlen_k, Hq, Hkv, D,
+    ws_bytes = _native.mea_fwd_workspace_size(num_seqs, Tk, max_seqlen_q, max_seqlen_k, Hq, Hkv, D,
                                               int(chunk_keys or 0))
     if ws_bytes > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(seqstart_q), _ptr(seqstart_k),
-            num_seqs, Tq, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, D, _dtype_code(q.dtype),
+            num_seqs, Tq, Tk, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, D, _dtype_code(q.dtype),
             int(bool(causal)), _ptr(slopes), scale, _ptr(workspace) if ws_bytes > 0 else None,
             ws_bytes, stream.cuda_stream)
     with torch.cuda.device(dev):

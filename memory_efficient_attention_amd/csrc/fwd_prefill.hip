@@ -24,11 +24,15 @@
 // tests only on the tiles that straddle them; tiles entirely above the
 // diagonal of the whole workgroup are never loaded.
 //
-// Staging: K tiles go HBM -> LDS directly (buffer loads with the LDS
-// destination, no registers); V tiles go through registers, where they are
-// transposed (and, for bfloat16 inputs, re-encoded as IEEE half) on the way
-// into LDS.  Both use buffer resources bounded by the sequence's rows, so a
-// tile that runs past the sequence's end reads zeros instead of neighbours.
+// Staging: both tiles go HBM -> LDS directly (buffer loads with the LDS
+// destination, no registers, no vector ALU work).  K is read from the packed
+// input with a buffer resource bounded by the sequence's rows, so a tile that
+// runs past the sequence's end reads zeros instead of its neighbours.  V is
+// read from V^T tile images that a small pre-pass kernel writes into the
+// workspace: each (key/value head, 64-key tile of a sequence) becomes one
+// D x 64 image of IEEE halves (bfloat16 V is re-encoded), laid out exactly as
+// the LDS tile, so the transposition and conversion happen once per tile
+// instead of once per workgroup that reads it.
 //
 // Grid: one linear index, remapped so that the 8 XCDs each take a contiguous
 // run of (head slice, sequence, tile) work items: the workgroups working on
@@ -47,13 +51,13 @@ constexpr float kRescaleThreshold = 8.f;  // log2 units: p may reach 2^8 before 
 template <int D>
 struct PfLayout {
   static constexpr int BN = kPfBN;                    // keys per tile
-  static constexpr int kBytes = BN * D * 2;           // K rows, 16-byte chunks XOR-swizzled
-  static constexpr int vStride = BN + 8;              // elements per V^T row (padded)
-  static constexpr int vBytes = D * vStride * 2;
+  static constexpr int kBytes = BN * D * 2;           // K rows [BN][D], 16-byte chunks XOR-swizzled
+  static constexpr int vBytes = D * BN * 2;           // V^T rows [D][BN], 16-byte chunks XOR-swizzled
   static constexpr int bufBytes = kBytes + vBytes;
   static constexpr int chunks = D / 8;                // 16-byte chunks per K row
   static constexpr int rowsPerKB = 1024 / (D * 2);    // K rows per 1 KB direct-load block
   static constexpr int kLoads = kBytes / (kThreads * 16);
+  static constexpr int vLoads = vBytes / (kThreads * 16);
 };
 
 // Position of 16-byte chunk c of K row r inside the row: rows that 16 lanes
@@ -63,6 +67,10 @@ __device__ __forceinline__ int k_pos(int r, int c) {
   if constexpr (D == 128) return c ^ (r & 15);
   else return c ^ ((r >> 1) & 7);
 }
+
+// Byte offset of keys 8c..8c+7 of feature row r in a V^T image / LDS tile
+// (rows of 64 keys = 128 bytes; two rows share a 256-byte bank line).
+__device__ __forceinline__ int vt_off(int r, int c) { return r * 128 + 16 * (c ^ ((r >> 1) & 7)); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, (int)bytes, 0x00020000);
@@ -133,7 +141,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
   const uint32_t seq_bytes = Lk > 0 ? (uint32_t)(Lk - 1) * rs_bytes + D * 2 : 0u;
   const size_t head_off = ((size_t)sk0 * a.Hkv + g) * D;
   const __amdgpu_buffer_rsrc_t krs = rows_rsrc(a.k + head_off, seq_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = rows_rsrc(a.v + head_off, seq_bytes);
   // K: direct loads, block q = i * 4 + wave of 1 KB (rowsPerKB rows) per instruction
   uint32_t k_voff[L::kLoads];
 #pragma unroll
@@ -143,52 +150,32 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
     const int pos = lane % L::chunks;
     k_voff[i] = (uint32_t)r * rs_bytes + (uint32_t)k_pos<D>(r, pos) * 16u;
   }
-  // V: thread (kq, cv) holds keys 4kq..4kq+3 x features 8cv..8cv+7
-  constexpr int V_JOBS = (BN / 4) * L::chunks;
-  const bool v_job = V_JOBS >= kThreads || tid < V_JOBS;
-  const int kq = tid % (BN / 4), cv = tid / (BN / 4);
-  const uint32_t v_voff = (uint32_t)(4 * kq) * rs_bytes + (uint32_t)cv * 16u;
-  u32x4 vr[4];
+  // V: V^T images of this sequence and head in the workspace (tile ti at
+  // ti * Hkv images from the first), loaded 1 KB per instruction per wave
+  constexpr int kImgBytes = L::vBytes;
+  const int ntk = (Lk + BN - 1) / BN;  // key tiles of the sequence
+  const __amdgpu_buffer_rsrc_t vrs = rows_rsrc(
+      a.ws_vt + ((size_t)((sk0 / BN) + b) * a.Hkv + g) * (kImgBytes / 2),
+      (uint32_t)ntk * a.Hkv * kImgBytes);
 
   // tile index of pipeline step t (diagonal tile first) and its LDS buffer
   auto tile_of = [&](int t) { return nkt - 1 - t; };
   auto buf_of = [&](int t) { return smem + (t % kBufs) * L::bufBytes; };
 
   auto issue_loads = [&](int t) {
-    const int soff = tile_of(t) * BN * (int)rs_bytes;
-    uint8_t* kdst = buf_of(t);
+    const int ti = tile_of(t);
+    const int soff = ti * BN * (int)rs_bytes;
+    uint8_t* dst = buf_of(t);
 #pragma unroll
     for (int i = 0; i < L::kLoads; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)(kdst + (i * 4 + wave) * 1024),
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)(dst + (i * 4 + wave) * 1024),
                                                16, k_voff[i], soff, 0, 0);
-    if (v_job) {
+    const int vsoff = ti * a.Hkv * kImgBytes;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        vr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, v_voff + i * rs_bytes, soff, 0));
-    }
-  };
-  auto store_v = [&](int t) {
-    if (!v_job) return;
-    uint16_t* vt = reinterpret_cast<uint16_t*>(buf_of(t) + L::kBytes);
-    u32x4 a0 = vr[0], a1 = vr[1], a2 = vr[2], a3 = vr[3];
-    if constexpr (BF16) {
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        a0[x] = bf16x2_to_f16x2(a0[x]);
-        a1[x] = bf16x2_to_f16x2(a1[x]);
-        a2[x] = bf16x2_to_f16x2(a2[x]);
-        a3[x] = bf16x2_to_f16x2(a3[x]);
-      }
-    }
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      u32x2 even, odd;
-      even[0] = __builtin_amdgcn_perm(a1[x], a0[x], 0x05040100u);
-      even[1] = __builtin_amdgcn_perm(a3[x], a2[x], 0x05040100u);
-      odd[0] = __builtin_amdgcn_perm(a1[x], a0[x], 0x07060302u);
-      odd[1] = __builtin_amdgcn_perm(a3[x], a2[x], 0x07060302u);
-      *(u32x2*)(vt + (8 * cv + 2 * x) * L::vStride + 4 * kq) = even;
-      *(u32x2*)(vt + (8 * cv + 2 * x + 1) * L::vStride + 4 * kq) = odd;
+    for (int i = 0; i < L::vLoads; ++i) {
+      const int blk = i * 4 + wave;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)(dst + L::kBytes + blk * 1024),
+                                               16, (uint32_t)(blk * 1024 + lane * 16), vsoff, 0, 0);
     }
   };
 
@@ -197,31 +184,24 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
   for (int d = 0; d < D / 32; ++d) o[d] = f32x16{};
   float m_run = kNegInf, l_run = 0.f;
 
-  // S^T = K Q^T of step t into s (two 32-key blocks); LDS fragments are read
-  // two k-steps ahead of the products that use them.
-  auto qk = [&](int t, f32x16 (&s)[2]) {
+  // K fragments of step t for S^T = K Q^T: block kb, k-step ks.
+  auto read_k = [&](int t, u32x4 (&kf)[2][KS]) {
     const uint8_t* Kb = buf_of(t);
-    const int r0 = key_of_row(l32), r1 = 32 + r0;
-    const uint8_t* krow0 = Kb + r0 * (D * 2);
-    const uint8_t* krow1 = Kb + r1 * (D * 2);
-    auto kread = [&](const uint8_t* krow, int r, int ks) {
-      return *(const u32x4*)(krow + k_pos<D>(r, 2 * ks + hi) * 16);
-    };
-    u32x4 ka[2][2];
-    ka[0][0] = kread(krow0, r0, 0);
-    ka[0][1] = kread(krow1, r1, 0);
-    ka[1][0] = kread(krow0, r0, 1);
-    ka[1][1] = kread(krow1, r1, 1);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int r = 32 * kb + key_of_row(l32);
+      const uint8_t* krow = Kb + r * (D * 2);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kf[kb][ks] = *(const u32x4*)(krow + k_pos<D>(r, 2 * ks + hi) * 16);
+    }
+  };
+  auto qk = [&](const u32x4 (&kf)[2][KS], f32x16 (&s)[2]) {
     s[0] = f32x16{};
     s[1] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      s[0] = mfma_32x32x16<BF16>(ka[ks & 1][0], qf[ks], s[0]);
-      s[1] = mfma_32x32x16<BF16>(ka[ks & 1][1], qf[ks], s[1]);
-      if (ks + 2 < KS) {
-        ka[ks & 1][0] = kread(krow0, r0, ks + 2);
-        ka[ks & 1][1] = kread(krow1, r1, ks + 2);
-      }
+      s[0] = mfma_32x32x16<BF16>(kf[0][ks], qf[ks], s[0]);
+      s[1] = mfma_32x32x16<BF16>(kf[1][ks], qf[ks], s[1]);
     }
   };
 
@@ -288,21 +268,20 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
       }
   };
 
-  // O^T += V^T P^T of step t; V^T fragments read four products ahead.
-  auto pv = [&](int t, const u32x4 (&pf)[4]) {
-    const uint16_t* Vt = reinterpret_cast<const uint16_t*>(buf_of(t) + L::kBytes);
-    auto vread = [&](int i) {
-      const int ch = i / (D / 32), d = i % (D / 32);
-      return *(const u32x4*)(Vt + (32 * d + l32) * L::vStride + 16 * ch + 8 * hi);
-    };
-    u32x4 va[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) va[i] = vread(i);
+  // V^T fragments of step t for O^T += V^T P^T: 16-key chunk ch, feature block d.
+  auto read_v = [&](int t, u32x4 (&vf)[NV]) {
+    const uint8_t* Vt = buf_of(t) + L::kBytes;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int ch = i / (D / 32), d = i % (D / 32);
-      o[d] = mfma_32x32x16<false>(va[i & 3], pf[ch], o[d]);
-      if (i + 4 < NV) va[i & 3] = vread(i + 4);
+      vf[i] = *(const u32x4*)(Vt + vt_off(32 * d + l32, 2 * ch + hi));
+    }
+  };
+  auto pv = [&](const u32x4 (&vf)[NV], const u32x4 (&pf)[4]) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int ch = i / (D / 32), d = i % (D / 32);
+      o[d] = mfma_32x32x16<false>(vf[i], pf[ch], o[d]);
     }
   };
 
@@ -312,42 +291,42 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
   auto step = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2], auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
     if (t + 2 < nkt) issue_loads(t + 2);
+    // every LDS fragment this step needs is requested up front, so their
+    // latency hides behind the score preparation below
+    u32x4 kf[2][KS], vf[NV];
+    if constexpr (FULL) read_k(t + 1, kf);
+    read_v(t, vf);
+    __builtin_amdgcn_sched_barrier(0);
     prepare(t, cur);
     u32x4 pf[4];
     float lsum = 0.f;
-    if constexpr (FULL) qk(t + 1, nxt);
+    if constexpr (FULL) qk(kf, nxt);
     probs(cur, pf, lsum);
     if constexpr (FULL) {
       // matrix pipe: 2*KS products of Q K^T; vector ALU: the exponentials in between
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
       for (int i = 0; i < 2 * KS; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-        if (i % 2 == 1 && i < 2 * KS - 4) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
     }
     l_run += lsum;
-    pv(t, pf);
-    if (t + 2 < nkt) {
-      __builtin_amdgcn_s_waitcnt(0);
-      store_v(t + 2);
-    }
+    pv(vf, pf);
+    if (t + 2 < nkt) __builtin_amdgcn_s_waitcnt(0);  // tile t+2 landed before anyone passes the barrier
     __syncthreads();
   };
 
   if (nkt > 0) {
     issue_loads(0);
+    if (nkt > 1) issue_loads(1);
     __builtin_amdgcn_s_waitcnt(0);
-    store_v(0);
-    if (nkt > 1) {
-      issue_loads(1);
-      __builtin_amdgcn_s_waitcnt(0);
-      store_v(1);
-    }
     __syncthreads();
     f32x16 sa[2], sb[2];
-    qk(0, sa);
+    {
+      u32x4 kf[2][KS];
+      read_k(0, kf);
+      qk(kf, sa);
+    }
     int t = 0;
     for (; t + 2 < nkt; t += 2) {
       step(t, sa, sb, std::true_type{});
@@ -391,6 +370,52 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
 #endif
 }
 
+// V pre-pass: the 64 keys of tile i of sequence b and key/value head g become
+// one V^T image [D][64] of IEEE halves at slot (seqstart_k[b] / 64 + b + i) *
+// Hkv + g of the workspace (the slots of consecutive sequences never overlap,
+// since a sequence of L keys has at most L / 64 + 1 tiles).  Keys past the
+// sequence's end are zero.  Thread (kq, cv) transposes 4 keys x 8 features in
+// registers.
+template <int D, bool BF16>
+__global__ __launch_bounds__(kThreads) void vt_images_kernel(FwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int BN = kPfBN;
+  const int g = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
+  const int sk0 = a.seqstart_k[b], Lk = a.seqstart_k[b + 1] - sk0;
+  if (i * BN >= Lk) return;
+  const int tid = threadIdx.x;
+  const int kq = tid % (BN / 4), cv = tid / (BN / 4);
+  if (cv >= D / 8) return;
+  const uint32_t rs_bytes = (uint32_t)a.Hkv * D * 2;
+  const __amdgpu_buffer_rsrc_t vrs =
+      rows_rsrc(a.v + ((size_t)sk0 * a.Hkv + g) * D, (uint32_t)(Lk - 1) * rs_bytes + D * 2);
+  u32x4 r[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    r[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                         vrs, (uint32_t)(i * BN + 4 * kq + k) * rs_bytes + cv * 16u, 0, 0));
+  if constexpr (BF16) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) r[k][w] = bf16x2_to_f16x2(r[k][w]);
+  }
+  uint8_t* img = reinterpret_cast<uint8_t*>(a.ws_vt + ((size_t)((sk0 / BN) + b + i) * a.Hkv + g) * (D * BN));
+  // word w of r[k] holds features 2w (low) and 2w+1 (high) of key 4kq + k
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    u32x2 even, odd;
+    even[0] = __builtin_amdgcn_perm(r[1][w], r[0][w], 0x05040100u);
+    even[1] = __builtin_amdgcn_perm(r[3][w], r[2][w], 0x05040100u);
+    odd[0] = __builtin_amdgcn_perm(r[1][w], r[0][w], 0x07060302u);
+    odd[1] = __builtin_amdgcn_perm(r[3][w], r[2][w], 0x07060302u);
+    const int row = 8 * cv + 2 * w;
+    *(u32x2*)(img + vt_off(row, kq / 2) + 8 * (kq % 2)) = even;
+    *(u32x2*)(img + vt_off(row + 1, kq / 2) + 8 * (kq % 2)) = odd;
+  }
+#endif
+}
+
 template <int D, bool BF16>
 static hipError_t launch_prefill_d(const FwdArgs& a, bool causal, bool alibi, dim3 grid,
                                    hipStream_t stream) {
@@ -406,7 +431,19 @@ static hipError_t launch_prefill_d(const FwdArgs& a, bool causal, bool alibi, di
 }
 
 hipError_t launch_prefill(const FwdArgs& a, int D, bool bf16, bool causal, bool alibi,
-                          int /*max_seqlen_q*/, hipStream_t stream) {
+                          int max_seqlen_k, hipStream_t stream) {
+  if (max_seqlen_k > 0) {
+    const dim3 vgrid(a.Hkv, (max_seqlen_k + kPfBN - 1) / kPfBN, a.num_seqs);
+    if (D == 64) {
+      if (bf16) hipLaunchKernelGGL((vt_images_kernel<64, true>), vgrid, dim3(kThreads), 0, stream, a);
+      else hipLaunchKernelGGL((vt_images_kernel<64, false>), vgrid, dim3(kThreads), 0, stream, a);
+    } else {
+      if (bf16) hipLaunchKernelGGL((vt_images_kernel<128, true>), vgrid, dim3(kThreads), 0, stream, a);
+      else hipLaunchKernelGGL((vt_images_kernel<128, false>), vgrid, dim3(kThreads), 0, stream, a);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const dim3 grid((unsigned)(((long long)a.pf_items + 7) / 8 * 8));
   if (D == 64) {
     return bf16 ? launch_prefill_d<64, true>(a, causal, alibi, grid, stream)

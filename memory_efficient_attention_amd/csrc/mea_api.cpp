@@ -51,9 +51,17 @@ size_t decode_ws_bytes(int32_t num_seqs, int32_t max_seqlen_k, int32_t Hq, int32
   return (size_t)num_seqs * nch * (size_t)Hq * (size_t)(D + 1) * sizeof(float);
 }
 
+// Prefill: one half-precision V^T image of D x 64 keys per key/value head and
+// key tile; sequence b's tiles start at slot seqstart_k[b] / 64 + b, so
+// total_k / 64 + num_seqs slots per head cover every sequence.
+size_t prefill_ws_bytes(int32_t num_seqs, int32_t total_k, int32_t Hkv, int32_t D) {
+  if (total_k == 0) return 0;
+  return ((size_t)total_k / mea::kPfBN + (size_t)num_seqs) * (size_t)Hkv * (size_t)D * mea::kPfBN * 2;
+}
+
 mea_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse,
                       const int32_t* seqstart_q, const int32_t* seqstart_k, int32_t num_seqs,
-                      int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq,
+                      int32_t total_q, int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq,
                       int32_t Hkv, int32_t D, mea_dtype_t dtype, int32_t causal,
                       const float* alibi_slopes, float scale, void* workspace,
                       size_t workspace_bytes, void* stream, int32_t chunk_keys, bool forced_split) {
@@ -62,9 +70,9 @@ mea_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, fl
     return fail(MEA_ERR_INVALID, "q, k, v and out must be non-NULL device pointers");
   if (seqstart_q == nullptr || seqstart_k == nullptr)
     return fail(MEA_ERR_INVALID, "seqstart_q and seqstart_k must be non-NULL device pointers");
-  if (num_seqs < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
-    return fail(MEA_ERR_INVALID, "negative size (num_seqs=%d total_q=%d max_seqlen_q=%d max_seqlen_k=%d)",
-                num_seqs, total_q, max_seqlen_q, max_seqlen_k);
+  if (num_seqs < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+    return fail(MEA_ERR_INVALID, "negative size (num_seqs=%d total_q=%d total_k=%d max_seqlen_q=%d max_seqlen_k=%d)",
+                num_seqs, total_q, total_k, max_seqlen_q, max_seqlen_k);
   if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
     return fail(MEA_ERR_INVALID, "need Hq > 0, Hkv > 0 and Hq %% Hkv == 0 (Hq=%d Hkv=%d)", Hq, Hkv);
   if (causal != 0 && causal != 1) return fail(MEA_ERR_INVALID, "causal must be 0 or 1 (got %d)", causal);
@@ -125,6 +133,13 @@ mea_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, fl
     if (a.max_chunks > 65535) return fail(MEA_ERR_UNSUPPORTED, "more than 65535 key chunks per sequence");
     err = mea::launch_decode(a, D, bf16, alibi, s);
   } else {
+    const size_t need = prefill_ws_bytes(num_seqs, total_k, Hkv, D);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+      return fail(MEA_ERR_INVALID, "workspace of %zu bytes is smaller than the %zu bytes required", workspace_bytes, need);
+    if (need > 0 && !aligned(workspace, 256)) return fail(MEA_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+    if ((long long)max_seqlen_k / mea::kPfBN + 1 > 65535)
+      return fail(MEA_ERR_UNSUPPORTED, "max_seqlen_k=%d needs more than 65535 key tiles", max_seqlen_k);
+    a.ws_vt = static_cast<uint16_t*>(workspace);
     a.heads_per_wg = gcd_int(a.group, mea::kPfWaves);
     a.head_slices = a.group / a.heads_per_wg;
     const int bt = 32 * (mea::kPfWaves / a.heads_per_wg);
@@ -134,7 +149,7 @@ mea_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, fl
       return fail(MEA_ERR_UNSUPPORTED, "%lld prefill work items exceed the grid limit", items);
     a.pf_max_tiles = (int32_t)tiles;
     a.pf_items = (int32_t)items;
-    err = mea::launch_prefill(a, D, bf16, causal != 0, alibi, max_seqlen_q, s);
+    err = mea::launch_prefill(a, D, bf16, causal != 0, alibi, max_seqlen_k, s);
   }
   if (err != hipSuccess) return fail(MEA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
   return MEA_OK;
@@ -146,33 +161,35 @@ extern "C" {
 
 mea_status_t mea_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                      const int32_t* seqstart_q, const int32_t* seqstart_k, int32_t num_seqs,
-                     int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq,
+                     int32_t total_q, int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq,
                      int32_t Hkv, int32_t D, mea_dtype_t dtype, int32_t causal,
                      const float* alibi_slopes, float scale, void* workspace,
                      size_t workspace_bytes, void* stream) {
-  return fwd_impl(q, k, v, out, lse, seqstart_q, seqstart_k, num_seqs, total_q, max_seqlen_q,
+  return fwd_impl(q, k, v, out, lse, seqstart_q, seqstart_k, num_seqs, total_q, total_k, max_seqlen_q,
                   max_seqlen_k, Hq, Hkv, D, dtype, causal, alibi_slopes, scale, workspace,
                   workspace_bytes, stream, 0, false);
 }
 
 mea_status_t mea_fwd_splitkv(const void* q, const void* k, const void* v, void* out, float* lse,
                              const int32_t* seqstart_q, const int32_t* seqstart_k,
-                             int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
+                             int32_t num_seqs, int32_t total_q, int32_t total_k, int32_t max_seqlen_q,
                              int32_t max_seqlen_k, int32_t Hq, int32_t Hkv, int32_t D,
                              mea_dtype_t dtype, int32_t causal, const float* alibi_slopes,
                              float scale, void* workspace, size_t workspace_bytes, void* stream,
                              int32_t chunk_keys) {
-  return fwd_impl(q, k, v, out, lse, seqstart_q, seqstart_k, num_seqs, total_q, max_seqlen_q,
+  return fwd_impl(q, k, v, out, lse, seqstart_q, seqstart_k, num_seqs, total_q, total_k, max_seqlen_q,
                   max_seqlen_k, Hq, Hkv, D, dtype, causal, alibi_slopes, scale, workspace,
                   workspace_bytes, stream, chunk_keys, true);
 }
 
-size_t mea_fwd_workspace_size(int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
+size_t mea_fwd_workspace_size(int32_t num_seqs, int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
                               int32_t Hq, int32_t Hkv, int32_t D, int32_t chunk_keys) {
-  if (max_seqlen_q != 1 || num_seqs <= 0 || max_seqlen_k <= 0 || Hq <= 0 || Hkv <= 0 ||
+  if (num_seqs <= 0 || total_k < 0 || max_seqlen_q <= 0 || max_seqlen_k < 0 || Hq <= 0 || Hkv <= 0 ||
       Hq % Hkv != 0 || (D != 64 && D != 128) || chunk_keys < 0 ||
       (chunk_keys > 0 && chunk_keys % mea::kDcBN != 0))
     return 0;
+  if (max_seqlen_q != 1) return prefill_ws_bytes(num_seqs, total_k, Hkv, D);
+  if (max_seqlen_k == 0) return 0;
   const int32_t chunk = chunk_keys > 0 ? chunk_keys : default_chunk(num_seqs, max_seqlen_k, Hkv);
   return decode_ws_bytes(num_seqs, max_seqlen_k, Hq, D, chunk);
 }

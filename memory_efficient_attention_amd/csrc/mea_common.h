@@ -30,6 +30,7 @@ struct FwdArgs {
   const float* slopes;       // [Hq] or nullptr
   float* ws_o;               // decode: [num_seqs, max_chunks, Hq, D] float32 partials
   float* ws_lse;             // decode: [num_seqs, max_chunks, Hq] float32 (log2 units)
+  uint16_t* ws_vt;           // prefill: transposed half-precision V tile images (see fwd_prefill.hip)
   float scale_log2;          // scale * log2(e)
   int32_t num_seqs;
   int32_t total_q;
@@ -74,10 +75,13 @@ __device__ __forceinline__ float halfwave_sum(float x) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Two float32 values to a packed pair of IEEE halves, round to nearest even.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Two float32 values to a packed pair of IEEE halves, round to nearest even
+// (one v_cvt_pk_f16_f32 on gfx950).
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
-  _Float16 a = (_Float16)lo, b = (_Float16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, f16x2));
 }
 
 // Two float32 values to the output dtype, packed, round to nearest even.

@@ -17,7 +17,7 @@ constexpr int kDcBN = 128;        // chunk granularity: 4 waves x 32-key blocks
 constexpr int kDcHeadsPerWg = 16;  // query heads of one group served per workgroup
 
 hipError_t launch_prefill(const FwdArgs& a, int D, bool bf16, bool causal, bool alibi,
-                          int max_seqlen_q, hipStream_t stream);
+                          int max_seqlen_k, hipStream_t stream);
 hipError_t launch_decode(const FwdArgs& a, int D, bool bf16, bool alibi, hipStream_t stream);
 
 }  // namespace mea

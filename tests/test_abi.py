@@ -60,7 +60,7 @@ P = 1 << 20
 
 def call(**kw):
     a = dict(q=P, k=P, v=P, out=P, lse=None, seqstart_q=P, seqstart_k=P, num_seqs=4, total_q=365,
-             max_seqlen_q=200, max_seqlen_k=200, Hq=8, Hkv=8, D=64, dtype=MEA_F16, causal=0,
+             total_k=365, max_seqlen_q=200, max_seqlen_k=200, Hq=8, Hkv=8, D=64, dtype=MEA_F16, causal=0,
              alibi_slopes=None, scale=0.125, workspace=None, workspace_bytes=0, stream=None)
     chunk = kw.pop("chunk_keys", None)
     a.update(kw)
@@ -92,6 +92,10 @@ def call(**kw):
     (dict(num_seqs=4, total_q=4, max_seqlen_q=1, max_seqlen_k=5000), MEA_ERR_INVALID, "workspace"),
     (dict(num_seqs=4, total_q=4, max_seqlen_q=1, max_seqlen_k=5000, workspace=P, workspace_bytes=100),
      MEA_ERR_INVALID, "workspace"),
+    # prefill needs the V^T images in the workspace
+    (dict(), MEA_ERR_INVALID, "workspace"),
+    (dict(workspace=P, workspace_bytes=1000), MEA_ERR_INVALID, "workspace"),
+    (dict(total_k=-1), MEA_ERR_INVALID, "negative"),
     # forced split entry point
     (dict(chunk_keys=100, total_q=4, max_seqlen_q=1), MEA_ERR_INVALID, "chunk_keys"),
     (dict(chunk_keys=0, total_q=4, max_seqlen_q=1), MEA_ERR_INVALID, "chunk_keys"),
@@ -109,13 +113,17 @@ def test_empty_problem_is_a_noop(kw):
 
 def test_workspace_size():
     ws = _native.mea_fwd_workspace_size
-    assert ws(4, 200, 200, 8, 8, 64, 0) == 0                       # prefill needs none
+    # prefill: one D x 64 half-precision V^T image per key/value head and tile slot
+    assert ws(4, 365, 200, 200, 8, 8, 64, 0) == (365 // 64 + 4) * 8 * 64 * 128
+    assert ws(64, 137663, 4085, 4085, 32, 8, 128, 0) == (137663 // 64 + 64) * 8 * 128 * 128
+    assert ws(4, 0, 200, 0, 8, 8, 64, 0) == 0
+    # decode: float32 partials per (sequence, chunk, query head)
     c = _native.mea_default_chunk_keys(64, 32680, 8)
     assert c == 2048
-    assert ws(64, 1, 32680, 64, 8, 128, 0) == 64 * 16 * 64 * 129 * 4
-    assert ws(64, 1, 32680, 64, 8, 128, 256) == 64 * 128 * 64 * 129 * 4
-    assert ws(64, 1, 32680, 64, 8, 128, 100) == 0                  # invalid chunk
-    assert ws(2, 1, 100, 6, 4, 128, 0) == 0                        # Hq % Hkv != 0
+    assert ws(64, 1101299, 1, 32680, 64, 8, 128, 0) == 64 * 16 * 64 * 129 * 4
+    assert ws(64, 1101299, 1, 32680, 64, 8, 128, 256) == 64 * 128 * 64 * 129 * 4
+    assert ws(64, 1101299, 1, 32680, 64, 8, 128, 100) == 0                  # invalid chunk
+    assert ws(2, 200, 1, 100, 6, 4, 128, 0) == 0                            # Hq % Hkv != 0
     assert _native.mea_default_chunk_keys(1, 32768, 8) == 128
     assert _native.mea_default_chunk_keys(1, 0, 8) == 128
     assert _native.mea_default_chunk_keys(0, 0, 0) == 128
