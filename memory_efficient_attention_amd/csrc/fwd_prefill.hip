@@ -10,12 +10,10 @@
 //   O^T += V^T P^T   32 features x 32 queries per product, P re-used from S^T's
 //                    registers without any data movement
 //
-// Software pipeline (one wave per SIMD, the whole register file per wave):
-// while the vector ALU turns tile t's scores into probabilities, the matrix
-// pipe already computes tile t+1's scores into a second score buffer; then
-// P V of tile t overlaps the staging of tile t+2.  K/V tiles rotate through
-// three LDS buffers, so every load has a full iteration to land and one
-// barrier per tile suffices.
+// Two waves per SIMD (two workgroups per CU): while one wave turns its scores
+// into probabilities on the vector ALU, the other keeps the matrix pipe busy.
+// K/V tiles are double-buffered in LDS: tile t+1 is fetched while tile t is
+// computed, with one barrier per tile.
 //
 // Key tiles run from the causal diagonal backwards, so the largest scores (and,
 // with ALiBi, the smallest distance penalties) come first and the running
@@ -45,7 +43,7 @@ namespace mea {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBufs = 3;                  // LDS ring of K/V tiles
+constexpr int kBufs = 2;                  // LDS double buffer of K/V tiles
 constexpr float kRescaleThreshold = 8.f;  // log2 units: p may reach 2^8 before O is rescaled
 
 template <int D>
@@ -79,7 +77,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base
 }  // namespace
 
 template <int D, bool BF16, bool CAUSAL, bool ALIBI>
-__global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void fwd_prefill_kernel(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the body uses buffer-resource types that exist only for the GPU target
   using L = PfLayout<D>;
   constexpr int BN = L::BN;
@@ -285,59 +283,37 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
     }
   };
 
-  // One pipeline step: scores of step t are in cur.  A full step also
-  // computes step t+1's scores into nxt while it finishes step t (the last
-  // step of a workgroup has no successor).
-  auto step = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2], auto full_tag) {
-    constexpr bool FULL = decltype(full_tag)::value;
-    if (t + 2 < nkt) issue_loads(t + 2);
-    // every LDS fragment this step needs is requested up front, so their
-    // latency hides behind the score preparation below
-    u32x4 kf[2][KS], vf[NV];
-    if constexpr (FULL) read_k(t + 1, kf);
-    read_v(t, vf);
-    __builtin_amdgcn_sched_barrier(0);
-    prepare(t, cur);
+  // One step: tile t+1 is requested (into the other LDS buffer), then tile t
+  // goes through S^T = K Q^T, the softmax update and O^T += V^T P^T.  The
+  // second wave on the SIMD (another workgroup) fills the matrix pipe while
+  // this one is in its softmax, and vice versa.
+  auto step = [&](int t) {
+    if (t + 1 < nkt) issue_loads(t + 1);
+    f32x16 s[2];
+    {
+      u32x4 kf[2][KS];
+      read_k(t, kf);
+      qk(kf, s);
+    }
+    prepare(t, s);
     u32x4 pf[4];
     float lsum = 0.f;
-    if constexpr (FULL) qk(kf, nxt);
-    probs(cur, pf, lsum);
-    if constexpr (FULL) {
-      // matrix pipe: 2*KS products of Q K^T; vector ALU: the exponentials in between
-#pragma unroll
-      for (int i = 0; i < 2 * KS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-      }
-    }
+    probs(s, pf, lsum);
     l_run += lsum;
-    pv(vf, pf);
-    if (t + 2 < nkt) __builtin_amdgcn_s_waitcnt(0);  // tile t+2 landed before anyone passes the barrier
+    {
+      u32x4 vf[NV];
+      read_v(t, vf);
+      pv(vf, pf);
+    }
+    if (t + 1 < nkt) __builtin_amdgcn_s_waitcnt(0);  // tile t+1 landed before anyone passes the barrier
     __syncthreads();
   };
 
   if (nkt > 0) {
     issue_loads(0);
-    if (nkt > 1) issue_loads(1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    f32x16 sa[2], sb[2];
-    {
-      u32x4 kf[2][KS];
-      read_k(0, kf);
-      qk(kf, sa);
-    }
-    int t = 0;
-    for (; t + 2 < nkt; t += 2) {
-      step(t, sa, sb, std::true_type{});
-      step(t + 1, sb, sa, std::true_type{});
-    }
-    if (nkt - t == 2) {
-      step(t, sa, sb, std::true_type{});
-      step(t + 1, sb, sa, std::false_type{});
-    } else {
-      step(t, sa, sb, std::false_type{});
-    }
+    for (int t = 0; t < nkt; ++t) step(t);
   }
 
   // ---- epilogue: normalise, round, stage the wave's 32 x D tile through LDS
