@@ -37,7 +37,7 @@ PEAK_HBM_GBS = 8000.0            # HBM3E
 PREFILL = "varlen_causal_gqa_64seq_h32kv8_d128_bf16"
 DECODE = "decode_splitkv_64req_h64kv8_d128_bf16"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-KERNEL_SOURCES = ["fwd_prefill.hip", "fwd_decode.hip", "mea_common.h", "mea_tiles.h", "mea_launch.h"]
+KERNEL_SOURCES = ["fwd_prefill.hip", "fwd_decode.hip", "mea_common.h", "mea_launch.h"]
 
 
 def unmasked_flops(inp) -> int:
