@@ -150,10 +150,34 @@ def cpu_baseline(pre_inp, gpu_out, gpu_lse, budget_s: float):
     }
 
 
+COPY_BYTES = 1 << 30   # calibration copy: 1 GiB read + 1 GiB written per launch
+
+
 def run_part(args, dev):
-    """Time one half of the step on its own (profiling aid); prints a short JSON line."""
+    """Time one half of the step on its own (profiling aid); prints a short JSON line.
+
+    ``--part copy`` runs a plain device-to-device copy of COPY_BYTES instead: the
+    known-size kernel that scales the FETCH_SIZE / WRITE_SIZE counters."""
     import torch
     from mea_workloads import generate
+    if args.part == "copy":
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).uniform_()
+        dst = torch.empty_like(src)
+        stream = torch.cuda.current_stream(dev)
+        for _ in range(args.warmup):
+            dst.copy_(src)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / max(args.steps, 1)
+        print(json.dumps({"part": "copy", "bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
+                          "ms": round(ms, 4), "gbs": round(2 * COPY_BYTES / (ms * 1e-3) / 1e9, 1)}),
+              flush=True)
+        return
     name = PREFILL if args.part == "prefill" else DECODE
     call = Call(generate(name, seed=args.seed), dev)
     stream = torch.cuda.current_stream(dev)
@@ -184,8 +208,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-alibi-variant", action="store_true")
-    ap.add_argument("--part", choices=["all", "prefill", "decode"], default="all",
-                    help="run only one half of the step (for profiling); the JSON line is for 'all'")
+    ap.add_argument("--part", choices=["all", "prefill", "decode", "copy"], default="all",
+                    help="run only one half of the step, or the calibration copy (for profiling); "
+                         "the JSON line is for 'all'")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
