@@ -310,7 +310,8 @@ def main():
         "roofline": {
             "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_BF16_TFLOPS, 4),
-            "traffic": traffic_pre, "kernel": "fwd_prefill_kernel<128,bf16,causal>",
+            "traffic": traffic_pre,
+            "kernel": "mea_fwd prefill call: vt_images_kernel + fwd_prefill_kernel<128,bf16,causal>",
             "launch_ms": round(pre_ms, 4),
         },
         "decode": {
