@@ -304,7 +304,7 @@ def main():
                         "unmasked_flops": pre_flops},
             "decode": {"requests": 64, "kv_tokens": dec.total_k, "Hq": 64, "Hkv": 8, "D": 128,
                        "algorithmic_bytes": dec_bytes,
-                       "chunk_keys": dec_call.native.mea_default_chunk_keys(64, dec.max_seqlen_k, 8)},
+                       "chunk_keys": dec_call.native.mea_default_chunk_keys(dec.total_k, 64, 8)},
             "seed": args.seed,
         },
         "roofline": {

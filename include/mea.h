@@ -26,9 +26,11 @@
  * The N x N score matrix is never written to memory: scores are produced
  * tile by tile on the matrix cores and folded into an online softmax.  A call
  * whose longest query sequence has one token (max_seqlen_q == 1, the decode
- * case) splits each sequence's keys into chunks processed in parallel and
- * merges the chunk results by their log-sum-exp (the split-K scheme named in
- * section 1 of "大模型推理加速终极指南：xformers如何让Transformer性能飙升300%"
+ * case) cuts the concatenated key axis [0, total_k) of all sequences into
+ * equal pieces processed in parallel, one partial result per (piece,
+ * sequence it touches), and merges each sequence's partials by their
+ * log-sum-exp (the split-K scheme named in section 1 of
+ * "大模型推理加速终极指南：xformers如何让Transformer性能飙升300%"
  * (zizhi168.cn)).
  *
  * Layouts (row-major, contiguous, element = 16-bit float of `dtype`):
@@ -66,7 +68,7 @@
 extern "C" {
 #endif
 
-#define MEA_ABI_VERSION 1
+#define MEA_ABI_VERSION 2
 
 #if defined(__GNUC__)
 #define MEA_EXPORT __attribute__((visibility("default")))
@@ -138,9 +140,10 @@ MEA_EXPORT mea_status_t mea_fwd(const void* q, const void* k, const void* v, voi
 
 /*
  * mea_fwd_splitkv -- mea_fwd for the decode case (max_seqlen_q must be 1)
- * with the key-chunk length forced to `chunk_keys` (a positive multiple of
- * 128) instead of the library's choice.  The result does not depend on the
- * chunk length beyond float32 rounding; this entry point exists to test that.
+ * with the piece length of the key axis forced to `chunk_keys` (a positive
+ * multiple of 32) instead of the library's choice.  The result does not
+ * depend on the piece length beyond float32 rounding; this entry point exists
+ * to test that.
  * Same arguments, ownership and errors as mea_fwd, plus MEA_ERR_INVALID for a
  * bad chunk_keys or max_seqlen_q != 1.
  */
@@ -156,8 +159,10 @@ MEA_EXPORT mea_status_t mea_fwd_splitkv(const void* q, const void* k, const void
  * mea_fwd_workspace_size -- bytes of workspace mea_fwd (chunk_keys == 0) or
  * mea_fwd_splitkv (chunk_keys > 0) needs for these sizes.  Pure host function;
  * returns 0 for arguments mea_fwd would reject.
- *   max_seqlen_q == 1 (decode): num_seqs * ceil(max_seqlen_k / chunk) * Hq *
- *     (D + 1) * 4 -- float32 partial outputs and log-sum-exps of the key chunks;
+ *   max_seqlen_q == 1 (decode): num_seqs * (ceil(max_seqlen_k / W) + 1) * Hq *
+ *     (D + 1) * 4, W = the piece length (chunk_keys, or the library's choice
+ *     mea_default_chunk_keys(total_k, Hq, Hkv)) -- float32 partial outputs
+ *     and log-sum-exps; 0 when total_k or max_seqlen_k is 0;
  *   max_seqlen_q > 1 (prefill): (total_k / 64 + num_seqs) * Hkv * D * 128 --
  *     one transposed half-precision copy of every 64-key tile of V (0 when
  *     total_k == 0).
@@ -166,8 +171,9 @@ MEA_EXPORT size_t mea_fwd_workspace_size(int32_t num_seqs, int32_t total_k, int3
                                          int32_t max_seqlen_k, int32_t Hq, int32_t Hkv, int32_t D,
                                          int32_t chunk_keys);
 
-/* Key-chunk length mea_fwd picks for a decode call of these sizes. Pure host function. */
-MEA_EXPORT int32_t mea_default_chunk_keys(int32_t num_seqs, int32_t max_seqlen_k, int32_t Hkv);
+/* Piece length of the key axis that mea_fwd picks for a decode call with
+ * these sizes (a multiple of 32, at least 128).  Pure host function. */
+MEA_EXPORT int32_t mea_default_chunk_keys(int32_t total_k, int32_t Hq, int32_t Hkv);
 
 /* Static text for a status code. */
 MEA_EXPORT const char* mea_status_string(mea_status_t status);

@@ -94,8 +94,8 @@ def mea_fwd_workspace_size(num_seqs, total_k, max_seqlen_q, max_seqlen_k, Hq, Hk
                                              Hkv, D, chunk_keys))
 
 
-def mea_default_chunk_keys(num_seqs, max_seqlen_k, Hkv) -> int:
-    return int(load().mea_default_chunk_keys(num_seqs, max_seqlen_k, Hkv))
+def mea_default_chunk_keys(total_k, Hq, Hkv) -> int:
+    return int(load().mea_default_chunk_keys(total_k, Hq, Hkv))
 
 
 def mea_status_string(status: int) -> str:

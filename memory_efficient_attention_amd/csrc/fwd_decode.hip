@@ -4,20 +4,31 @@
 // once, so the kernels are built to keep as many bytes in flight per CU as
 // possible and to spend little else.
 //
-// Partial kernel: a workgroup takes one sequence, one key/value head g (and up
-// to 16 of its query heads) and one chunk of the sequence's keys.  Its 4
-// waves stream interleaved 32-key blocks of the chunk independently (no
-// workgroup barrier until the end), each with its own online-softmax state:
+// Work split: the concatenated key axis [0, total_k) of all sequences is cut
+// into pieces of W keys, W chosen so that the launch is one round of
+// equal-sized workgroups on the chip (equal pieces leave no long tail, unlike
+// per-sequence chunks of unequal length).  A piece that spans the end of one
+// sequence and the start of the next produces one partial result per
+// sequence it touches.
+//
+// Partial kernel: a workgroup takes one piece and nh = gcd(Hkv, 4)
+// neighbouring key/value heads (with up to 16 query heads of each head's
+// group).  Wave w serves head w % nh and streams every (4/nh)-th 32-key block
+// of the piece's part of a sequence, starting at block w / nh, independently
+// (no workgroup barrier until the end of that part), with its own
+// online-softmax state.  The nh heads of a key are adjacent in memory, so a
+// workgroup reads runs of nh * D * 2 contiguous bytes per key rather than one
+// head's D * 2 bytes out of each token row.  Per block, a wave computes
 //   S^T = K Q^T   16x16x32 products; the query heads of the group are the 16
 //                 columns, so one K/V read serves every head of the group
 //                 (GQA's saving becomes fewer HBM bytes);
 //   O^T += V^T P^T  with V transposed through a per-wave LDS slot.
 // K goes from HBM straight into the product's operand registers; the loads of
-// block i+1 are in flight while block i is computed.  At the end the 4 waves
-// merge in LDS and write one normalised float32 partial output and its
-// log-sum-exp (log2 units) per head.
+// block i+1 are in flight while block i is computed.  At the end of each
+// sequence part the waves of a head merge in LDS and write one normalised
+// float32 partial output and its log-sum-exp (log2 units) per query head.
 //
-// Combine kernel: per (sequence, query head) the chunk partials are merged
+// Combine kernel: per (sequence, query head) the piece partials are merged
 // by their log-sum-exps: lse = log sum_c exp(lse_c), out = sum_c exp(lse_c -
 // lse) o_c, then rounded to the output dtype.
 #include "mea_common.h"
@@ -46,14 +57,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base
 // non-temporal policy for this access pattern).
 constexpr int kStreamPolicy = 0;
 
-constexpr int kWaves = 4;
+constexpr int kWaves = kDcWaves;
 constexpr int kBlk = 32;                  // keys per wave block
 constexpr int kVtStride = kBlk + 8;       // elements per V^T row in a wave's LDS slot
 
 }  // namespace
 
 template <int D, bool BF16, bool ALIBI>
-__global__ __launch_bounds__(256, 2) void fwd_decode_partial_kernel(FwdArgs a) {
+__global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void fwd_decode_partial_kernel(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the body uses buffer-resource types that exist only for the GPU target
   constexpr int KS = D / 32;              // k-steps of the 16x16x32 Q K^T product
   constexpr int DB = D / 16;              // 16-feature blocks of O^T
@@ -68,16 +79,40 @@ __global__ __launch_bounds__(256, 2) void fwd_decode_partial_kernel(FwdArgs a) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, q = lane & 15, g4 = lane >> 4;
-  // grid: x = key/value head slice (fastest, so the heads of one chunk are
-  // read together and share DRAM pages), y = chunk, z = sequence
-  const int g = blockIdx.x / a.head_slices, hs = blockIdx.x % a.head_slices;
-  const int chunk = blockIdx.y, b = blockIdx.z;
+  // grid: one workgroup per (piece, head group): x = piece * groups + group,
+  // so the head groups of one piece are read together and share DRAM pages.
+  // A head group is nh neighbouring key/value heads and one slice of 16
+  // query heads of each head's group.
+  const int nh = a.kv_per_wg, stripes = kWaves / nh;
+  const int hh = wave % nh, stripe = wave / nh;
+  const int groups = (a.Hkv / nh) * a.head_slices;
+  const int piece = blockIdx.x / groups, gi = blockIdx.x - piece * groups;
+  const int g = (gi / a.head_slices) * nh + hh, hs = gi % a.head_slices;
+  const int g0 = (gi / a.head_slices) * nh;  // first head of the group
 
+  // the piece: keys [k0, k1) of the concatenated key axis
+  const int W = a.chunk_keys;
+  const int k0 = piece * W, k1 = min(a.total_k, k0 + W);
+  // first sequence that owns a key >= k0: smallest b with seqstart_k[b + 1] > k0
+  int b = 0;
+  {
+    int hi = a.num_seqs - 1;
+    while (b < hi) {
+      const int mid = (b + hi) >> 1;
+      if (a.seqstart_k[mid + 1] > k0) hi = mid;
+      else b = mid + 1;
+    }
+  }
+  for (; b < a.num_seqs; ++b) {
+  const int sk0 = a.seqstart_k[b], sk1 = a.seqstart_k[b + 1];
+  if (sk0 >= k1) break;
+  const int Lk = sk1 - sk0;
   const int sq0 = a.seqstart_q[b], Lq = a.seqstart_q[b + 1] - sq0;
-  const int sk0 = a.seqstart_k[b], Lk = a.seqstart_k[b + 1] - sk0;
-  const int c0 = chunk * a.chunk_keys;
-  if (Lq == 0 || c0 >= Lk) return;
-  const int c1 = min(Lk, c0 + a.chunk_keys);
+  if (Lq == 0 || Lk == 0) continue;
+  // this segment: keys [c0, c1) of sequence b; its partial goes to slot
+  // `slot` of the sequence (slot 0 = the piece holding the sequence's first key)
+  const int c0 = max(k0, sk0) - sk0, c1 = min(k1, sk1) - sk0;
+  const int slot = piece - sk0 / W;
   const int qpos = Lk - 1;  // the single query is the sequence's last position
 
   const int hl = hs * 16 + q;  // query head within the group (= product column)
@@ -214,21 +249,21 @@ __global__ __launch_bounds__(256, 2) void fwd_decode_partial_kernel(FwdArgs a) {
     }
   };
 
-  // this wave's blocks: j = c0 + 32 * (wave + 4 * i)
+  // this wave's blocks: j = c0 + 32 * (stripe + stripes * i)
   const int nblk = (c1 - c0 + kBlk - 1) / kBlk;
   Regs ra, rb;
-  int i = wave;
+  int i = stripe;
   if (i < nblk) load(ra, c0 + kBlk * i);
-  for (; i < nblk; i += 2 * kWaves) {
-    const int inext = i + kWaves;
+  for (; i < nblk; i += 2 * stripes) {
+    const int inext = i + stripes;
     if (inext < nblk) load(rb, c0 + kBlk * inext);
     compute(ra, c0 + kBlk * i);
     if (inext >= nblk) break;
-    if (inext + kWaves < nblk) load(ra, c0 + kBlk * (inext + kWaves));
+    if (inext + stripes < nblk) load(ra, c0 + kBlk * (inext + stripes));
     compute(rb, c0 + kBlk * inext);
   }
 
-  // ---- merge the 4 waves' partial states in LDS
+  // ---- merge the partial states of the waves that share a head, in LDS
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
   __syncthreads();
@@ -245,31 +280,42 @@ __global__ __launch_bounds__(256, 2) void fwd_decode_partial_kernel(FwdArgs a) {
   }
   __syncthreads();
 
-  const int qc = tid >> 4, part = tid & 15;  // 16 columns x 16 parts of D/16 features
-  if (hs * 16 + qc >= a.group) return;
-  float M = kNegInf;
+  // thread (qc, part): query column qc, features part*FP..+FP-1, for each of
+  // the nh heads in turn; the waves of head h2 are h2, h2 + nh, ...
+  constexpr int kParts = 4 * kWaves, FP = D / kParts;
+  const int qc = tid / kParts, part = tid % kParts;
+  for (int h2 = 0; h2 < nh && hs * 16 + qc < a.group; ++h2) {
+    float M = kNegInf;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) M = __builtin_fmaxf(M, mred[w * 16 + qc]);
-  float wgt[kWaves], Ls = 0.f;
+    for (int s2 = 0; s2 < kWaves; ++s2)
+      if (s2 < stripes) M = __builtin_fmaxf(M, mred[(s2 * nh + h2) * 16 + qc]);
+    float wgt[kWaves], Ls = 0.f;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const float mw = mred[w * 16 + qc];
-    wgt[w] = (mw == kNegInf) ? 0.f : fast_exp2(mw - M);
-    Ls += wgt[w] * lred[w * 16 + qc];
+    for (int s2 = 0; s2 < kWaves; ++s2) {
+      wgt[s2] = 0.f;
+      if (s2 < stripes) {
+        const float mw = mred[(s2 * nh + h2) * 16 + qc];
+        wgt[s2] = (mw == kNegInf) ? 0.f : fast_exp2(mw - M);
+        Ls += wgt[s2] * lred[(s2 * nh + h2) * 16 + qc];
+      }
+    }
+    const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+    const int hq = (g0 + h2) * a.group + hs * 16 + qc;
+    const size_t prow = ((size_t)b * a.max_chunks + slot) * a.Hq + hq;
+    float* dst = a.ws_o + prow * D + part * FP;
+#pragma unroll
+    for (int e = 0; e < FP; ++e) {
+      const int d = part * FP + e;
+      float acc = 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < kWaves; ++s2)
+        if (s2 < stripes) acc += wgt[s2] * red[((s2 * nh + h2) * 16 + qc) * kRedStride + d];
+      dst[e] = acc * inv;
+    }
+    if (part == 0) a.ws_lse[prow] = Ls > 0.f ? M + fast_log2(Ls) : kNegInf;
   }
-  const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
-  const int hq = g * a.group + hs * 16 + qc;
-  const size_t prow = ((size_t)b * a.max_chunks + chunk) * a.Hq + hq;
-  float* dst = a.ws_o + prow * D + part * (D / 16);
-#pragma unroll
-  for (int e = 0; e < D / 16; ++e) {
-    const int d = part * (D / 16) + e;
-    float acc = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) acc += wgt[w] * red[(w * 16 + qc) * kRedStride + d];
-    dst[e] = acc * inv;
+  __syncthreads();  // the merge buffer is reused by the next segment
   }
-  if (part == 0) a.ws_lse[prow] = Ls > 0.f ? M + fast_log2(Ls) : kNegInf;
 #endif
 }
 
@@ -285,8 +331,9 @@ __global__ __launch_bounds__(256) void fwd_decode_combine_kernel(FwdArgs a) {
   if (h >= a.Hq) return;
   const int sq0 = a.seqstart_q[b], Lq = a.seqstart_q[b + 1] - sq0;
   if (Lq == 0) return;
-  const int Lk = a.seqstart_k[b + 1] - a.seqstart_k[b];
-  const int nch = (Lk + a.chunk_keys - 1) / a.chunk_keys;
+  const int sk0 = a.seqstart_k[b], sk1 = a.seqstart_k[b + 1];
+  // partial slots of sequence b: one per piece of the key axis its keys touch
+  const int nch = sk1 > sk0 ? (sk1 - 1) / a.chunk_keys - sk0 / a.chunk_keys + 1 : 0;
   const size_t row0 = (size_t)b * a.max_chunks * a.Hq + h;  // partial row of chunk 0
   const float* lse_p = a.ws_lse + row0;                        // chunk c at [c * Hq]
   float M = kNegInf;
@@ -341,10 +388,11 @@ __global__ __launch_bounds__(256) void fwd_decode_combine_kernel(FwdArgs a) {
 
 template <int D, bool BF16>
 static hipError_t launch_decode_d(const FwdArgs& a, bool alibi, hipStream_t stream) {
-  if (a.max_chunks > 0) {
-    const dim3 grid(a.Hkv * a.head_slices, a.max_chunks, a.num_seqs);
-    if (alibi) hipLaunchKernelGGL((fwd_decode_partial_kernel<D, BF16, true>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((fwd_decode_partial_kernel<D, BF16, false>), grid, dim3(256), 0, stream, a);
+  if (a.dc_pieces > 0) {
+    const dim3 grid((unsigned)a.dc_pieces * (unsigned)((a.Hkv / a.kv_per_wg) * a.head_slices));
+    const dim3 block(64 * kWaves);
+    if (alibi) hipLaunchKernelGGL((fwd_decode_partial_kernel<D, BF16, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((fwd_decode_partial_kernel<D, BF16, false>), grid, block, 0, stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -34,21 +34,36 @@ int gcd_int(int x, int y) {
   return x;
 }
 
-int32_t default_chunk(int32_t num_seqs, int32_t max_seqlen_k, int32_t Hkv) {
-  // Enough (sequence, chunk, kv-head) workgroups to fill 256 CUs several
-  // times over, but chunks long enough that the partials stay a small
-  // fraction of the K/V bytes.
-  const long long work = (long long)num_seqs * (long long)max_seqlen_k * (long long)Hkv;
-  long long c = (work + 2047) / 2048;
-  c = ((c + mea::kDcBN - 1) / mea::kDcBN) * mea::kDcBN;
-  if (c < mea::kDcBN) c = mea::kDcBN;
-  if (c > 2048) c = 2048;
-  return (int32_t)c;
+// Key/value heads that one decode workgroup serves together (one wave each).
+int32_t decode_kv_per_wg(int32_t Hkv) { return gcd_int(Hkv, mea::kDcWaves); }
+
+int32_t decode_head_groups(int32_t Hq, int32_t Hkv) {
+  const int32_t group = Hq / Hkv;
+  return (Hkv / decode_kv_per_wg(Hkv)) * ((group + mea::kDcHeadsPerWg - 1) / mea::kDcHeadsPerWg);
 }
 
-size_t decode_ws_bytes(int32_t num_seqs, int32_t max_seqlen_k, int32_t Hq, int32_t D, int32_t chunk) {
-  const size_t nch = (size_t)((max_seqlen_k + chunk - 1) / chunk);
-  return (size_t)num_seqs * nch * (size_t)Hq * (size_t)(D + 1) * sizeof(float);
+int32_t default_chunk(int32_t total_k, int32_t Hq, int32_t Hkv) {
+  // Piece length W of the concatenated key axis: about kDcTargetWgs
+  // equal-sized (piece, head group) workgroups in all, i.e. one full round of
+  // two workgroups per CU on 256 CUs: every workgroup starts at once and
+  // none is left over for a tail (measured: one round beats two or four,
+  // which pay each workgroup's start-up again).  Never below kDcMinPiece keys,
+  // so that partial results stay a small fraction of the K/V bytes.
+  const long long work = (long long)total_k * (long long)decode_head_groups(Hq, Hkv);
+  long long w = (work + mea::kDcTargetWgs - 1) / mea::kDcTargetWgs;
+  w = (w + mea::kDcPieceAlign - 1) / mea::kDcPieceAlign * mea::kDcPieceAlign;
+  if (w < mea::kDcMinPiece) w = mea::kDcMinPiece;
+  if (w > (1ll << 30)) w = 1ll << 30;
+  return (int32_t)w;
+}
+
+// Partial slots per sequence: the pieces a sequence of L keys touches are at
+// most ceil(L / W) + 1.
+int32_t decode_slots(int32_t max_seqlen_k, int32_t w) { return (int32_t)((max_seqlen_k + (long long)w - 1) / w) + 1; }
+
+size_t decode_ws_bytes(int32_t num_seqs, int32_t total_k, int32_t max_seqlen_k, int32_t Hq, int32_t D, int32_t w) {
+  if (total_k == 0 || max_seqlen_k == 0) return 0;
+  return (size_t)num_seqs * (size_t)decode_slots(max_seqlen_k, w) * (size_t)Hq * (size_t)(D + 1) * sizeof(float);
 }
 
 // Prefill: one half-precision V^T image of D x 64 keys per key/value head and
@@ -80,8 +95,8 @@ mea_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, fl
     return fail(MEA_ERR_INVALID, "total_q=%d > 0 but max_seqlen_q == 0", total_q);
   if (forced_split) {
     if (max_seqlen_q != 1) return fail(MEA_ERR_INVALID, "mea_fwd_splitkv needs max_seqlen_q == 1 (got %d)", max_seqlen_q);
-    if (chunk_keys <= 0 || chunk_keys % mea::kDcBN != 0)
-      return fail(MEA_ERR_INVALID, "chunk_keys must be a positive multiple of %d (got %d)", mea::kDcBN, chunk_keys);
+    if (chunk_keys <= 0 || chunk_keys % mea::kDcPieceAlign != 0)
+      return fail(MEA_ERR_INVALID, "chunk_keys must be a positive multiple of %d (got %d)", mea::kDcPieceAlign, chunk_keys);
   }
   if (D != 64 && D != 128) return fail(MEA_ERR_UNSUPPORTED, "head dimension D=%d is not 64 or 128", D);
   if (dtype != MEA_F16 && dtype != MEA_BF16) return fail(MEA_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
@@ -110,6 +125,7 @@ mea_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, fl
   a.scale_log2 = scale * mea::kLog2e;
   a.num_seqs = num_seqs;
   a.total_q = total_q;
+  a.total_k = total_k;
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.group = Hq / Hkv;
@@ -119,18 +135,21 @@ mea_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, fl
 
   hipError_t err;
   if (max_seqlen_q == 1) {
-    const int32_t chunk = forced_split ? chunk_keys : default_chunk(num_seqs, max_seqlen_k, Hkv);
-    const size_t need = decode_ws_bytes(num_seqs, max_seqlen_k, Hq, D, chunk);
+    const int32_t chunk = forced_split ? chunk_keys : default_chunk(total_k, Hq, Hkv);
+    const size_t need = decode_ws_bytes(num_seqs, total_k, max_seqlen_k, Hq, D, chunk);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need))
       return fail(MEA_ERR_INVALID, "workspace of %zu bytes is smaller than the %zu bytes required", workspace_bytes, need);
     if (need > 0 && !aligned(workspace, 256)) return fail(MEA_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
     a.chunk_keys = chunk;
-    a.max_chunks = (max_seqlen_k + chunk - 1) / chunk;
+    a.dc_pieces = need > 0 ? (int32_t)(((long long)total_k + chunk - 1) / chunk) : 0;
+    a.max_chunks = need > 0 ? decode_slots(max_seqlen_k, chunk) : 0;
     a.head_slices = (a.group + mea::kDcHeadsPerWg - 1) / mea::kDcHeadsPerWg;
     a.heads_per_wg = mea::kDcHeadsPerWg;
+    a.kv_per_wg = decode_kv_per_wg(Hkv);
     a.ws_o = static_cast<float*>(workspace);
     a.ws_lse = a.ws_o + (size_t)num_seqs * a.max_chunks * Hq * D;
-    if (a.max_chunks > 65535) return fail(MEA_ERR_UNSUPPORTED, "more than 65535 key chunks per sequence");
+    if ((long long)a.dc_pieces * decode_head_groups(Hq, Hkv) > 0x7fffffffll)
+      return fail(MEA_ERR_UNSUPPORTED, "too many decode workgroups (%d pieces of %d keys)", a.dc_pieces, chunk);
     err = mea::launch_decode(a, D, bf16, alibi, s);
   } else {
     const size_t need = prefill_ws_bytes(num_seqs, total_k, Hkv, D);
@@ -186,16 +205,16 @@ size_t mea_fwd_workspace_size(int32_t num_seqs, int32_t total_k, int32_t max_seq
                               int32_t Hq, int32_t Hkv, int32_t D, int32_t chunk_keys) {
   if (num_seqs <= 0 || total_k < 0 || max_seqlen_q <= 0 || max_seqlen_k < 0 || Hq <= 0 || Hkv <= 0 ||
       Hq % Hkv != 0 || (D != 64 && D != 128) || chunk_keys < 0 ||
-      (chunk_keys > 0 && chunk_keys % mea::kDcBN != 0))
+      (chunk_keys > 0 && chunk_keys % mea::kDcPieceAlign != 0))
     return 0;
   if (max_seqlen_q != 1) return prefill_ws_bytes(num_seqs, total_k, Hkv, D);
-  if (max_seqlen_k == 0) return 0;
-  const int32_t chunk = chunk_keys > 0 ? chunk_keys : default_chunk(num_seqs, max_seqlen_k, Hkv);
-  return decode_ws_bytes(num_seqs, max_seqlen_k, Hq, D, chunk);
+  const int32_t chunk = chunk_keys > 0 ? chunk_keys : default_chunk(total_k, Hq, Hkv);
+  return decode_ws_bytes(num_seqs, total_k, max_seqlen_k, Hq, D, chunk);
 }
 
-int32_t mea_default_chunk_keys(int32_t num_seqs, int32_t max_seqlen_k, int32_t Hkv) {
-  return default_chunk(num_seqs < 0 ? 0 : num_seqs, max_seqlen_k < 0 ? 0 : max_seqlen_k, Hkv < 1 ? 1 : Hkv);
+int32_t mea_default_chunk_keys(int32_t total_k, int32_t Hq, int32_t Hkv) {
+  if (Hkv < 1 || Hq < Hkv || Hq % Hkv != 0) return mea::kDcMinPiece;
+  return default_chunk(total_k < 0 ? 0 : total_k, Hq, Hkv);
 }
 
 const char* mea_status_string(mea_status_t status) {

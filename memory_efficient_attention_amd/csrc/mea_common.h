@@ -34,13 +34,16 @@ struct FwdArgs {
   float scale_log2;          // scale * log2(e)
   int32_t num_seqs;
   int32_t total_q;
+  int32_t total_k;
   int32_t Hq;
   int32_t Hkv;
   int32_t group;             // Hq / Hkv
   int32_t heads_per_wg;      // prefill: query heads of one group served per workgroup
   int32_t head_slices;       // prefill: group / heads_per_wg; decode: ceil(group / 16)
-  int32_t chunk_keys;        // decode: keys per chunk
-  int32_t max_chunks;        // decode: ceil(max_seqlen_k / chunk_keys)
+  int32_t kv_per_wg;         // decode: key/value heads per workgroup (one wave per head and key stripe)
+  int32_t chunk_keys;        // decode: keys per piece of the concatenated key axis
+  int32_t max_chunks;        // decode: partial slots per sequence, ceil(max_seqlen_k / chunk_keys) + 1
+  int32_t dc_pieces;         // decode: ceil(total_k / chunk_keys)
   int32_t pf_max_tiles;      // prefill: query tiles of the longest sequence
   int32_t pf_items;          // prefill: head slices * num_seqs * pf_max_tiles
 };

@@ -12,9 +12,14 @@ namespace mea {
 // query heads that share one key/value head.
 constexpr int kPfWaves = 4;
 constexpr int kPfBN = 64;          // keys per LDS tile
-// Decode: workgroups of 4 waves, each streaming its own 32-key blocks of a chunk.
-constexpr int kDcBN = 128;        // chunk granularity: 4 waves x 32-key blocks
-constexpr int kDcHeadsPerWg = 16;  // query heads of one group served per workgroup
+// Decode: workgroups of 4 waves; gcd(Hkv, 4) key/value heads per workgroup,
+// each wave streaming its own 32-key blocks of one head's part of a piece of
+// the concatenated key axis.
+constexpr int kDcWaves = 4;
+constexpr int kDcPieceAlign = 32;    // piece lengths are multiples of one wave block
+constexpr int kDcMinPiece = 128;     // shortest default piece
+constexpr int kDcTargetWgs = 512;    // default: one round of 2 workgroups per CU on 256 CUs
+constexpr int kDcHeadsPerWg = 16;    // query heads of one group served per workgroup
 
 hipError_t launch_prefill(const FwdArgs& a, int D, bool bf16, bool causal, bool alibi,
                           int max_seqlen_k, hipStream_t stream);

@@ -48,7 +48,7 @@ def test_every_kernel_stub_is_defined():
 
 
 def test_version_and_strings():
-    assert _native.mea_abi_version() == 1
+    assert _native.mea_abi_version() == 2
     for st in range(4):
         assert _native.mea_status_string(st).startswith("MEA_")
     assert "unknown" in _native.mea_status_string(99)
@@ -117,16 +117,23 @@ def test_workspace_size():
     assert ws(4, 365, 200, 200, 8, 8, 64, 0) == (365 // 64 + 4) * 8 * 64 * 128
     assert ws(64, 137663, 4085, 4085, 32, 8, 128, 0) == (137663 // 64 + 64) * 8 * 128 * 128
     assert ws(4, 0, 200, 0, 8, 8, 64, 0) == 0
-    # decode: float32 partials per (sequence, chunk, query head)
-    c = _native.mea_default_chunk_keys(64, 32680, 8)
-    assert c == 2048
-    assert ws(64, 1101299, 1, 32680, 64, 8, 128, 0) == 64 * 16 * 64 * 129 * 4
-    assert ws(64, 1101299, 1, 32680, 64, 8, 128, 256) == 64 * 128 * 64 * 129 * 4
-    assert ws(64, 1101299, 1, 32680, 64, 8, 128, 100) == 0                  # invalid chunk
+    # decode: float32 partials per (sequence, partial slot, query head); the
+    # key axis is cut into pieces of W keys, ~512 (piece, head group)
+    # workgroups in all; here 2 head groups (8 key/value heads, 4 per group)
+    W = _native.mea_default_chunk_keys(1101299, 64, 8)
+    assert W == 4320                                   # ceil(1101299 * 2 / 512) -> multiple of 32
+    slots = -(-32680 // W) + 1                         # a sequence touches at most ceil(L / W) + 1 pieces
+    assert ws(64, 1101299, 1, 32680, 64, 8, 128, 0) == 64 * slots * 64 * 129 * 4
+    assert ws(64, 1101299, 1, 32680, 64, 8, 128, 256) == 64 * (128 + 1) * 64 * 129 * 4
+    assert ws(64, 1101299, 1, 32680, 64, 8, 128, 100) == 0                  # not a multiple of 32
+    assert ws(64, 1101299, 1, 32680, 64, 8, 128, 96) == 64 * (341 + 1) * 64 * 129 * 4
     assert ws(2, 200, 1, 100, 6, 4, 128, 0) == 0                            # Hq % Hkv != 0
-    assert _native.mea_default_chunk_keys(1, 32768, 8) == 128
-    assert _native.mea_default_chunk_keys(1, 0, 8) == 128
+    assert ws(4, 0, 1, 0, 8, 8, 128, 0) == 0                                # no keys at all
+    assert _native.mea_default_chunk_keys(32768, 64, 8) == 128              # 2 x 32768 / 512 = 128
+    assert _native.mea_default_chunk_keys(8192, 64, 8) == 128               # floor of 128 keys
+    assert _native.mea_default_chunk_keys(0, 64, 8) == 128
     assert _native.mea_default_chunk_keys(0, 0, 0) == 128
-    for n, L, h in [(1, 1000, 1), (8, 4096, 8), (200, 32768, 8), (3, 77, 2)]:
-        c = _native.mea_default_chunk_keys(n, L, h)
-        assert c % 128 == 0 and 128 <= c <= 2048
+    assert _native.mea_default_chunk_keys(1 << 24, 32, 1) == (1 << 24) * 2 // 512   # 1 head x 2 slices
+    for T, Hq, h in [(1000, 1, 1), (8 * 4096, 64, 8), (200 * 32768, 64, 8), (3 * 77, 4, 2)]:
+        c = _native.mea_default_chunk_keys(T, Hq, h)
+        assert c % 32 == 0 and c >= 128

@@ -110,6 +110,22 @@ def test_decode_splitkv_subset_full_and_chunk_invariance():
         assert (o.double() - outs[0].double()).abs().max().item() <= 1e-2
 
 
+@pytest.mark.parametrize("piece", [None, 32, 96])
+def test_decode_pieces_spanning_many_sequences(piece):
+    """Short decode requests (some with no keys, some with no query): a piece
+    of the key axis covers parts of many sequences, each getting its own
+    partial result."""
+    import numpy as np
+    rng = np.random.default_rng(77)
+    lk = [int(x) for x in rng.integers(0, 90, size=150)]
+    lq = [0 if i % 37 == 5 else 1 for i in range(150)]
+    inp = random_case(4242, lq, lk, Hq=16, Hkv=4, D=128, dtype="bf16", causal=False, alibi=True)
+    _log(f"decode 150 short requests, sum Lk={inp.total_k}, piece={piece}")
+    out, lse = run_gpu(inp, chunk_keys=piece)
+    ref_out, ref_lse = oracle_full(inp)
+    _log(f"  {compare(out, lse, ref_out, ref_lse, 'bf16', f'decode short piece={piece}')}")
+
+
 # ----------------------------------------------------------------------------- edge cases
 EDGE = [
     # (seqlens_q, seqlens_k, Hq, Hkv, D, dtype, causal, alibi)
