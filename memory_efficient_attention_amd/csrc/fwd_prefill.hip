@@ -10,10 +10,13 @@
 //   O^T += V^T P^T   32 features x 32 queries per product, P re-used from S^T's
 //                    registers without any data movement
 //
-// Two waves per SIMD (two workgroups per CU): while one wave turns its scores
-// into probabilities on the vector ALU, the other keeps the matrix pipe busy.
-// K/V tiles are double-buffered in LDS: tile t+1 is fetched while tile t is
-// computed, with one barrier per tile.
+// Ping-pong: a workgroup is two groups of 4 waves (one workgroup per CU, two
+// waves per SIMD, the two waves of a SIMD in different groups).  Barriers cut
+// the work into phases, and the groups run one phase apart, so that on every
+// SIMD one wave issues matrix products (P V of the previous tile, then Q K of
+// this tile) while the other turns its scores into probabilities on the
+// vector ALU.  Both groups walk the same key tiles, so each staged K/V tile
+// serves 8 waves.
 //
 // Key tiles run from the causal diagonal backwards, so the largest scores (and,
 // with ALiBi, the smallest distance penalties) come first and the running
@@ -23,9 +26,12 @@
 // diagonal of the whole workgroup are never loaded.
 //
 // Staging: both tiles go HBM -> LDS directly (buffer loads with the LDS
-// destination, no registers, no vector ALU work).  K is read from the packed
-// input with a buffer resource bounded by the sequence's rows, so a tile that
-// runs past the sequence's end reads zeros instead of its neighbours.  V is
+// destination, no registers, no vector ALU work), into rings of 3 K and 3 V
+// buffers; each wave issues its share of a tile's requests during one of its
+// own vector phases, two phases before the tile is needed.  K is read from
+// the packed input with a buffer resource bounded by the sequence's rows, so a
+// tile that runs past the sequence's end reads zeros instead of its
+// neighbours.  V is
 // read from V^T tile images that a small pre-pass kernel writes into the
 // workspace: each (key/value head, 64-key tile of a sequence) becomes one
 // D x 64 image of IEEE halves (bfloat16 V is re-encoded), laid out exactly as
@@ -42,8 +48,9 @@ namespace mea {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kBufs = 2;                  // LDS double buffer of K/V tiles
+constexpr int kThreads = 64 * kPfWaves;  // main kernel: two groups of 4 waves
+constexpr int kVtThreads = 256;           // V pre-pass
+constexpr int kBufs = 3;                  // LDS buffers of K tiles and of V tiles (a ring of 3 each)
 constexpr float kRescaleThreshold = 8.f;  // log2 units: p may reach 2^8 before O is rescaled
 
 template <int D>
@@ -74,16 +81,34 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// Instruction order for a block of N LDS fragment reads feeding N matrix
+// products: three reads ahead, then one product and one read in turn, so a
+// product's operand has had three products' time to arrive and only a few
+// fragments are live at once.
+template <int N>
+__device__ __forceinline__ void interleave_reads_and_products() {
+  constexpr int kAhead = 3;
+  __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);  // DS reads
+#pragma unroll
+  for (int i = 0; i < N - kAhead; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
+}
+
 }  // namespace
 
 template <int D, bool BF16, bool CAUSAL, bool ALIBI>
-__global__ __launch_bounds__(kThreads, 2) void fwd_prefill_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the body uses buffer-resource types that exist only for the GPU target
   using L = PfLayout<D>;
   constexpr int BN = L::BN;
   constexpr int KS = D / 16;             // k-steps of the Q K^T product
   constexpr int NV = 4 * (D / 32);       // products of P V per tile
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kBufs * L::bufBytes];
+  constexpr int kStageBytes = kThreads / 64 * 32 * (D + 8) * 2;  // epilogue: a [32][D + 8] tile per wave
+  constexpr int kSmemBytes = kBufs * L::bufBytes > kStageBytes ? kBufs * L::bufBytes : kStageBytes;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmemBytes];
 
   // ---- work item: XCD-aware remap of the linear workgroup index
   const int per_xcd = (int)gridDim.x >> 3;
@@ -96,11 +121,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_prefill_kernel(FwdArgs a) {
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int grp = wave >> 2;                 // 0 leads, 1 trails by one phase
+  const int wq = wave & 3;                   // wave within its group
   const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int sq0 = a.seqstart_q[b], Lq = a.seqstart_q[b + 1] - sq0;
   const int sk0 = a.seqstart_k[b], Lk = a.seqstart_k[b + 1] - sk0;
-  const int tc = kPfWaves / a.heads_per_wg;   // 32-token chunks per workgroup
-  const int BT = 32 * tc;
+  const int tc = kPfGroupWaves / a.heads_per_wg;  // 32-token chunks per group
+  const int BT = kPfGroups * 32 * tc;             // tokens per workgroup
   const int ntiles = (Lq + BT - 1) / BT;
   if (t_rev >= ntiles) return;
   const int t0 = (ntiles - 1 - t_rev) * BT;    // longest causal tiles launch first
@@ -108,13 +135,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_prefill_kernel(FwdArgs a) {
 
   const int g = hslice / a.head_slices;
   const int hs = hslice % a.head_slices;
-  const int hw = wave % a.heads_per_wg, tw = wave / a.heads_per_wg;
+  const int hw = wq % a.heads_per_wg, tw = wq / a.heads_per_wg;
   const int head = g * a.group + hs * a.heads_per_wg + hw;
-  const int tok0 = t0 + 32 * tw;  // first query row of this wave
-  const int my_tok = tok0 + l32;  // this lane's query row
+  const int tok0 = t0 + 32 * (grp * tc + tw);  // first query row of this wave
+  const int my_tok = tok0 + l32;               // this lane's query row
   const bool row_valid = my_tok < Lq;
-  const int qpos = my_tok + off;  // key position of this query row
+  const int qpos = my_tok + off;               // key position of this query row
 
+  // key tiles of the whole workgroup (both groups walk the same tiles)
   int kv_end = Lk;
   if constexpr (CAUSAL) kv_end = min(Lk, min(t0 + BT, Lq) + off);
   const int nkt = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
@@ -139,11 +167,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_prefill_kernel(FwdArgs a) {
   const uint32_t seq_bytes = Lk > 0 ? (uint32_t)(Lk - 1) * rs_bytes + D * 2 : 0u;
   const size_t head_off = ((size_t)sk0 * a.Hkv + g) * D;
   const __amdgpu_buffer_rsrc_t krs = rows_rsrc(a.k + head_off, seq_bytes);
-  // K: direct loads, block q = i * 4 + wave of 1 KB (rowsPerKB rows) per instruction
+  // K: direct loads, 1 KB block q = i * 8 + wave (rowsPerKB rows) per instruction
   uint32_t k_voff[L::kLoads];
 #pragma unroll
   for (int i = 0; i < L::kLoads; ++i) {
-    const int q = i * 4 + wave;
+    const int q = i * kPfWaves + wave;
     const int r = q * L::rowsPerKB + lane / L::chunks;
     const int pos = lane % L::chunks;
     k_voff[i] = (uint32_t)r * rs_bytes + (uint32_t)k_pos<D>(r, pos) * 16u;
@@ -156,24 +184,27 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_prefill_kernel(FwdArgs a) {
       a.ws_vt + ((size_t)((sk0 / BN) + b) * a.Hkv + g) * (kImgBytes / 2),
       (uint32_t)ntk * a.Hkv * kImgBytes);
 
-  // tile index of pipeline step t (diagonal tile first) and its LDS buffer
+  // tile index of pipeline step t (diagonal tile first) and its LDS buffers
   auto tile_of = [&](int t) { return nkt - 1 - t; };
-  auto buf_of = [&](int t) { return smem + (t % kBufs) * L::bufBytes; };
+  auto kbuf = [&](int t) { return smem + (t % kBufs) * L::kBytes; };
+  auto vbuf = [&](int t) { return smem + kBufs * L::kBytes + (t % kBufs) * L::vBytes; };
 
-  auto issue_loads = [&](int t) {
-    const int ti = tile_of(t);
-    const int soff = ti * BN * (int)rs_bytes;
-    uint8_t* dst = buf_of(t);
+  auto issue_k = [&](int t) {
+    const int soff = tile_of(t) * BN * (int)rs_bytes;
+    uint8_t* dst = kbuf(t);
 #pragma unroll
     for (int i = 0; i < L::kLoads; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)(dst + (i * 4 + wave) * 1024),
-                                               16, k_voff[i], soff, 0, 0);
-    const int vsoff = ti * a.Hkv * kImgBytes;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          krs, (__attribute__((address_space(3))) void*)(dst + (i * kPfWaves + wave) * 1024), 16, k_voff[i], soff, 0, 0);
+  };
+  auto issue_v = [&](int t) {
+    const int vsoff = tile_of(t) * a.Hkv * kImgBytes;
+    uint8_t* dst = vbuf(t);
 #pragma unroll
     for (int i = 0; i < L::vLoads; ++i) {
-      const int blk = i * 4 + wave;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)(dst + L::kBytes + blk * 1024),
-                                               16, (uint32_t)(blk * 1024 + lane * 16), vsoff, 0, 0);
+      const int blk = i * kPfWaves + wave;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          vrs, (__attribute__((address_space(3))) void*)(dst + blk * 1024), 16, (uint32_t)(blk * 1024 + lane * 16), vsoff, 0, 0);
     }
   };
 
@@ -182,28 +213,26 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_prefill_kernel(FwdArgs a) {
   for (int d = 0; d < D / 32; ++d) o[d] = f32x16{};
   float m_run = kNegInf, l_run = 0.f;
 
-  // K fragments of step t for S^T = K Q^T: block kb, k-step ks.
-  auto read_k = [&](int t, u32x4 (&kf)[2][KS]) {
-    const uint8_t* Kb = buf_of(t);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int r = 32 * kb + key_of_row(l32);
-      const uint8_t* krow = Kb + r * (D * 2);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kf[kb][ks] = *(const u32x4*)(krow + k_pos<D>(r, 2 * ks + hi) * 16);
-    }
-  };
-  auto qk = [&](const u32x4 (&kf)[2][KS], f32x16 (&s)[2]) {
+  // S^T = K Q^T for tile t, K fragments straight from LDS
+  auto qk = [&](int t, f32x16 (&s)[2]) {
+    const uint8_t* Kb = kbuf(t);
     s[0] = f32x16{};
     s[1] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      s[0] = mfma_32x32x16<BF16>(kf[0][ks], qf[ks], s[0]);
-      s[1] = mfma_32x32x16<BF16>(kf[1][ks], qf[ks], s[1]);
+      u32x4 kf[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int r = 32 * kb + key_of_row(l32);
+        kf[kb] = *(const u32x4*)(Kb + r * (D * 2) + k_pos<D>(r, 2 * ks + hi) * 16);
+      }
+      s[0] = mfma_32x32x16<BF16>(kf[0], qf[ks], s[0]);
+      s[1] = mfma_32x32x16<BF16>(kf[1], qf[ks], s[1]);
     }
+    interleave_reads_and_products<2 * KS>();
   };
 
-  // Scores of step t -> log2 units with bias and masks, row maximum, and the
+  // Scores of tile t -> log2 units with bias and masks, row maximum, and the
   // (rare) rescale of O.
   auto prepare = [&](int t, f32x16 (&s)[2]) {
     const int j0 = tile_of(t) * BN;
@@ -266,54 +295,90 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_prefill_kernel(FwdArgs a) {
       }
   };
 
-  // V^T fragments of step t for O^T += V^T P^T: 16-key chunk ch, feature block d.
-  auto read_v = [&](int t, u32x4 (&vf)[NV]) {
-    const uint8_t* Vt = buf_of(t) + L::kBytes;
+  // O^T += V^T P^T for tile t: V^T fragment of 16-key chunk ch, feature block d
+  auto pv = [&](int t, const u32x4 (&pf)[4]) {
+    const uint8_t* Vt = vbuf(t);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int ch = i / (D / 32), d = i % (D / 32);
-      vf[i] = *(const u32x4*)(Vt + vt_off(32 * d + l32, 2 * ch + hi));
+      const u32x4 vf = *(const u32x4*)(Vt + vt_off(32 * d + l32, 2 * ch + hi));
+      o[d] = mfma_32x32x16<false>(vf, pf[ch], o[d]);
     }
-  };
-  auto pv = [&](const u32x4 (&vf)[NV], const u32x4 (&pf)[4]) {
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int ch = i / (D / 32), d = i % (D / 32);
-      o[d] = mfma_32x32x16<false>(vf[i], pf[ch], o[d]);
-    }
+    interleave_reads_and_products<NV>();
   };
 
-  // One step: tile t+1 is requested (into the other LDS buffer), then tile t
-  // goes through S^T = K Q^T, the softmax update and O^T += V^T P^T.  The
-  // second wave on the SIMD (another workgroup) fills the matrix pipe while
-  // this one is in its softmax, and vice versa.
-  auto step = [&](int t) {
-    if (t + 1 < nkt) issue_loads(t + 1);
-    f32x16 s[2];
-    {
-      u32x4 kf[2][KS];
-      read_k(t, kf);
-      qk(kf, s);
-    }
+  // ---- the ping-pong schedule.  The two waves on each SIMD belong to
+  // different groups (waves w and w + 4 share a SIMD).  Phase k is one step
+  // between two barriers; a group alternates
+  //   matrix phase   M(j): O += V(j-1) P(j-1), then S(j) = K(j) Q^T
+  //   vector phase   V(j): softmax update of S(j) -> P(j)
+  // and group 1 runs one phase behind group 0, so in every phase one wave of
+  // a SIMD feeds the matrix pipe while the other works on the vector ALU:
+  // group 0 runs M(j) in phase 2j and V(j) in phase 2j+1, group 1 runs M(j)
+  // in phase 2j+1 and V(j-1) in phase 2j.
+  //
+  // Staging: request R(j) = {K(j+1), V(j)} is split over all 8 waves; each
+  // wave issues its share during one of its own vector phases (group 0 in
+  // phase 2j-1, group 1 in phase 2j), so the issue cost never lengthens a
+  // matrix phase, and every wave waits for its share of R(j) at the end of
+  // phase 2j+1.  R(j) lands in the ring slots of K(j-2) and V(j-3), which the
+  // last reader (group 1) finished with in phase 2j-3.  Each group runs its
+  // own loop, so that within a loop the phase kinds are fixed and the scores
+  // and P are never both carried around it.  Both loops pass the same
+  // barriers: two per tile and two at the end.
+  auto softmax = [&](int t, f32x16 (&s)[2], u32x4 (&pf)[4]) {
     prepare(t, s);
-    u32x4 pf[4];
     float lsum = 0.f;
     probs(s, pf, lsum);
     l_run += lsum;
-    {
-      u32x4 vf[NV];
-      read_v(t, vf);
-      pv(vf, pf);
-    }
-    if (t + 1 < nkt) __builtin_amdgcn_s_waitcnt(0);  // tile t+1 landed before anyone passes the barrier
-    __syncthreads();
   };
-
+  auto request = [&](int j) {
+    if (j + 1 < nkt) issue_k(j + 1);
+    if (j < nkt) issue_v(j);
+  };
+  // s_waitcnt immediate: at most n vector-memory loads outstanding (other counters unchecked)
+  constexpr int kWaitNone = 0;
+  constexpr int kWaitV = 0xF70 | L::vLoads;
+  constexpr int kWaitKV = 0xF70 | (L::kLoads + L::vLoads);
+  static_assert(L::kLoads + L::vLoads < 16, "vmcnt immediate");
   if (nkt > 0) {
-    issue_loads(0);
+    issue_k(0);
+    if (grp == 0) request(0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int t = 0; t < nkt; ++t) step(t);
+    f32x16 s[2];
+    u32x4 pf[4];
+    if (grp == 0) {
+      for (int j = 0; j < nkt; ++j) {
+        if (j >= 1) pv(j - 1, pf);       // phase 2j: M(j)
+        qk(j, s);
+        __syncthreads();
+        request(j + 1);                  // phase 2j+1: V(j), and this wave's share of R(j+1)
+        softmax(j, s, pf);
+        // this wave's share of R(j) landed; R(j+1) may stay in flight
+        if (j + 2 < nkt) __builtin_amdgcn_s_waitcnt(kWaitKV);
+        else if (j + 1 < nkt) __builtin_amdgcn_s_waitcnt(kWaitV);
+        else __builtin_amdgcn_s_waitcnt(kWaitNone);
+        __syncthreads();
+      }
+      pv(nkt - 1, pf);                   // phase 2 nkt: M(nkt)
+      __syncthreads();
+      __syncthreads();                   // phase 2 nkt + 1
+    } else {
+      for (int j = 0; j < nkt; ++j) {
+        request(j);                      // phase 2j: V(j-1), and this wave's share of R(j)
+        if (j >= 1) softmax(j - 1, s, pf);
+        __syncthreads();
+        if (j >= 1) pv(j - 1, pf);       // phase 2j+1: M(j)
+        qk(j, s);
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's share of R(j) landed
+        __syncthreads();
+      }
+      softmax(nkt - 1, s, pf);           // phase 2 nkt: V(nkt-1)
+      __syncthreads();
+      pv(nkt - 1, pf);                   // phase 2 nkt + 1: M(nkt)
+      __syncthreads();
+    }
   }
 
   // ---- epilogue: normalise, round, stage the wave's 32 x D tile through LDS
@@ -353,7 +418,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_prefill_kernel(FwdArgs a) {
 // sequence's end are zero.  Thread (kq, cv) transposes 4 keys x 8 features in
 // registers.
 template <int D, bool BF16>
-__global__ __launch_bounds__(kThreads) void vt_images_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kVtThreads) void vt_images_kernel(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int BN = kPfBN;
   const int g = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
@@ -411,11 +476,11 @@ hipError_t launch_prefill(const FwdArgs& a, int D, bool bf16, bool causal, bool 
   if (max_seqlen_k > 0) {
     const dim3 vgrid(a.Hkv, (max_seqlen_k + kPfBN - 1) / kPfBN, a.num_seqs);
     if (D == 64) {
-      if (bf16) hipLaunchKernelGGL((vt_images_kernel<64, true>), vgrid, dim3(kThreads), 0, stream, a);
-      else hipLaunchKernelGGL((vt_images_kernel<64, false>), vgrid, dim3(kThreads), 0, stream, a);
+      if (bf16) hipLaunchKernelGGL((vt_images_kernel<64, true>), vgrid, dim3(kVtThreads), 0, stream, a);
+      else hipLaunchKernelGGL((vt_images_kernel<64, false>), vgrid, dim3(kVtThreads), 0, stream, a);
     } else {
-      if (bf16) hipLaunchKernelGGL((vt_images_kernel<128, true>), vgrid, dim3(kThreads), 0, stream, a);
-      else hipLaunchKernelGGL((vt_images_kernel<128, false>), vgrid, dim3(kThreads), 0, stream, a);
+      if (bf16) hipLaunchKernelGGL((vt_images_kernel<128, true>), vgrid, dim3(kVtThreads), 0, stream, a);
+      else hipLaunchKernelGGL((vt_images_kernel<128, false>), vgrid, dim3(kVtThreads), 0, stream, a);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -159,9 +159,9 @@ mea_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, fl
     if ((long long)max_seqlen_k / mea::kPfBN + 1 > 65535)
       return fail(MEA_ERR_UNSUPPORTED, "max_seqlen_k=%d needs more than 65535 key tiles", max_seqlen_k);
     a.ws_vt = static_cast<uint16_t*>(workspace);
-    a.heads_per_wg = gcd_int(a.group, mea::kPfWaves);
+    a.heads_per_wg = gcd_int(a.group, mea::kPfGroupWaves);
     a.head_slices = a.group / a.heads_per_wg;
-    const int bt = 32 * (mea::kPfWaves / a.heads_per_wg);
+    const int bt = mea::kPfGroups * 32 * (mea::kPfGroupWaves / a.heads_per_wg);
     const long long tiles = (max_seqlen_q + bt - 1) / bt;
     const long long items = (long long)Hkv * a.head_slices * num_seqs * tiles;
     if (items > (1ll << 31) - 8)

@@ -7,10 +7,13 @@
 
 namespace mea {
 
-// Prefill: workgroups of 4 waves; a wave owns 32 consecutive query rows of one
-// head, so a workgroup covers 32 * (4 / heads_per_wg) tokens of heads_per_wg
-// query heads that share one key/value head.
-constexpr int kPfWaves = 4;
+// Prefill: workgroups of two groups of 4 waves; a wave owns 32 consecutive
+// query rows of one head, so a group covers 32 * (4 / heads_per_wg) tokens of
+// heads_per_wg query heads that share one key/value head, and the second
+// group the next as many tokens.
+constexpr int kPfGroupWaves = 4;
+constexpr int kPfGroups = 2;
+constexpr int kPfWaves = kPfGroupWaves * kPfGroups;
 constexpr int kPfBN = 64;          // keys per LDS tile
 // Decode: workgroups of 4 waves; gcd(Hkv, 4) key/value heads per workgroup,
 // each wave streaming its own 32-key blocks of one head's part of a piece of
