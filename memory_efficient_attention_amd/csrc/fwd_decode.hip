@@ -53,9 +53,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Cache policy of the K/V stream loads (default: measured faster than the
-// non-temporal policy for this access pattern).
-constexpr int kStreamPolicy = 0;
+// Cache policy of the K/V stream loads: non-temporal (the nt bit).  Every K/V
+// byte is read once, and with each workgroup reading 1 KB runs of the token
+// rows the hint measured ~7% faster than the default policy.
+constexpr int kStreamPolicy = 2;
 
 constexpr int kWaves = kDcWaves;
 constexpr int kBlk = 32;                  // keys per wave block
