@@ -113,39 +113,32 @@ class Call:
 
 
 def cpu_baseline(pre_inp, gpu_out, gpu_lse, budget_s: float):
-    """Time the float64 CPU oracle on the first sequences of the prefill
-    workload (about budget_s seconds of work) and check the GPU rows there."""
+    """Time the float64 CPU oracle on the prefill workload's sequences, one at
+    a time in order, until about budget_s seconds have been spent (the budget
+    plus at most one sequence), and check the GPU rows of those sequences."""
     import torch
     import oracle
-    from mea_workloads import _lengths, get_workload, prefix, random_case
     # threads: torch's default (OMP_NUM_THREADS), i.e. the host share this process was given
-    lens, _ = _lengths(get_workload(PREFILL), 0)
-    per_seq = [4 * 128 * 32 * L * (L + 1) // 2 for L in lens]
-    # calibrate the oracle's rate on the first sequence, then take the longest
-    # prefix of sequences whose unmasked work fits the budget
-    probe = random_case(0, [1024], Hq=32, Hkv=8, D=128, dtype="bf16", causal=True)
-    t0 = time.perf_counter()
-    oracle.attention_forward(probe.q, probe.k, probe.v, probe.seqstart_q, probe.seqstart_k,
-                             causal=True, scale=probe.scale)
-    rate = unmasked_flops(probe) / max(time.perf_counter() - t0, 1e-6)   # FLOP/s
-    n, acc = 0, 0
-    while n < len(per_seq) and (acc + per_seq[n]) / rate <= budget_s:
-        acc += per_seq[n]
-        n += 1
-    n = max(n, 1)
-    sample = prefix(pre_inp, n)
-    t0 = time.perf_counter()
-    ref_out, ref_lse = oracle.attention_forward(sample.q, sample.k, sample.v, sample.seqstart_q,
-                                                sample.seqstart_k, causal=True, scale=sample.scale)
-    dt = time.perf_counter() - t0
-    T = sample.total_q
-    err = (gpu_out[:T].double() - ref_out).abs().max().item()
-    lerr = (gpu_lse[:, :T].double() - ref_lse).abs().max().item()
+    sq, sk = pre_inp.seqstart_q.tolist(), pre_inp.seqstart_k.tolist()
+    n_done, flops, dt, err, lerr = 0, 0, 0.0, 0.0, 0.0
+    for b in range(len(pre_inp.seqlens_q)):
+        if dt >= budget_s:
+            break
+        Lq, Lk = sq[b + 1] - sq[b], sk[b + 1] - sk[b]
+        t0 = time.perf_counter()
+        ref_out, ref_lse = oracle.attention_forward(
+            pre_inp.q[sq[b]:sq[b + 1]], pre_inp.k[sk[b]:sk[b + 1]], pre_inp.v[sk[b]:sk[b + 1]],
+            [0, Lq], [0, Lk], causal=True, scale=pre_inp.scale)
+        dt += time.perf_counter() - t0
+        flops += 4 * pre_inp.D * pre_inp.Hq * Lq * (Lq + 1) // 2
+        err = max(err, (gpu_out[sq[b]:sq[b + 1]].double() - ref_out).abs().max().item())
+        lerr = max(lerr, (gpu_lse[:, sq[b]:sq[b + 1]].double() - ref_lse).abs().max().item())
+        n_done += 1
     return {
-        "value": unmasked_flops(sample) / dt / 1e12, "unit": "TFLOP/s",
+        "value": flops / dt / 1e12, "unit": "TFLOP/s",
         "cores": torch.get_num_threads(), "kind": "oracle",
-        "sample": f"first {n} of 64 sequences of the prefill workload ({T} tokens, "
-                  f"{unmasked_flops(sample) / 1e9:.1f} unmasked GFLOP), float64, {dt:.1f} s",
+        "sample": f"first {n_done} of {len(pre_inp.seqlens_q)} sequences of the prefill workload "
+                  f"({sq[n_done]} tokens, {flops / 1e9:.1f} unmasked GFLOP), float64, {dt:.1f} s",
         "gpu_vs_oracle_on_sample": {"max_abs_out": err, "max_abs_lse": lerr},
     }
 
