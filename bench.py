@@ -17,7 +17,9 @@ figures (GB/s of algorithmic bytes Q + K + V + O + LSE) are in ``decode``.
 ``roofline`` describes the prefill kernel against the bf16 dense MFMA peak,
 ``decode.roofline`` the decode launches against HBM bandwidth, and
 ``cpu_baseline`` times the CPU float64 oracle on a bounded sample of the
-prefill workload.
+prefill workload.  Outside the step, ``prefill_alibi`` times the prefill
+workload with ALiBi and ``decode_paged`` the decode workload with K/V in a
+paged cache (pages of 64 keys in a shuffled order, through mea_fwd_paged).
 """
 from __future__ import annotations
 
@@ -112,6 +114,57 @@ class Call:
             raise RuntimeError(f"mea_fwd: {self.native.mea_status_string(st)}: {self.native.mea_last_error()}")
 
 
+PAGE_SIZE = 64   # keys per page of the paged decode variant
+
+
+class PagedCall:
+    """Pre-bound launch of one workload with K/V scattered into a paged cache
+    (pages in a seeded random order; see mea_workloads.to_paged)."""
+
+    def __init__(self, inp, dev, page_size):
+        import torch
+        from memory_efficient_attention_amd import _native
+        from mea_workloads import to_paged
+        pk = to_paged(inp, page_size, seed=1)
+        self.inp, self.page_size = inp, page_size
+        self.q = inp.q.to(dev)
+        self.kc, self.vc, self.bt = pk.k_cache.to(dev), pk.v_cache.to(dev), pk.block_table.to(dev)
+        self.ssq, self.ssk = inp.seqstart_q.to(dev), inp.seqstart_k.to(dev)
+        self.slopes = None if inp.alibi_slopes is None else inp.alibi_slopes.to(dev)
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty((inp.Hq, inp.total_q), dtype=torch.float32, device=dev)
+        self.ws_bytes = _native.mea_fwd_workspace_size(len(inp.seqlens_q), inp.total_k, inp.max_seqlen_q,
+                                                       inp.max_seqlen_k, inp.Hq, inp.Hkv, inp.D, 0)
+        self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=dev)
+        self.dtype = _native.MEA_BF16 if inp.dtype == "bf16" else _native.MEA_F16
+        self.native = _native
+
+    def __call__(self, stream):
+        inp = self.inp
+        st = self.native.mea_fwd_paged(
+            self.q.data_ptr(), self.kc.data_ptr(), self.vc.data_ptr(), self.out.data_ptr(),
+            self.lse.data_ptr(), self.ssq.data_ptr(), self.ssk.data_ptr(), self.bt.data_ptr(),
+            len(inp.seqlens_q), inp.total_q, inp.total_k, inp.max_seqlen_q, inp.max_seqlen_k,
+            self.page_size, self.kc.shape[0], self.bt.shape[1], inp.Hq, inp.Hkv, inp.D, self.dtype,
+            int(inp.causal), None if self.slopes is None else self.slopes.data_ptr(), inp.scale,
+            self.ws.data_ptr() if self.ws_bytes else None, self.ws_bytes, stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"mea_fwd_paged: {self.native.mea_status_string(st)}: {self.native.mea_last_error()}")
+
+
+def time_calls(call, stream, reps):
+    """Average ms of `reps` back-to-back calls, HIP events on the launch stream."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    call(stream)
+    e0.record(stream)
+    for _ in range(reps):
+        call(stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
 def cpu_baseline(pre_inp, gpu_out, gpu_lse, budget_s: float):
     """Time the float64 CPU oracle on the prefill workload's sequences, one at
     a time in order, until about budget_s seconds have been spent (the budget
@@ -172,7 +225,10 @@ def run_part(args, dev):
               flush=True)
         return
     name = PREFILL if args.part == "prefill" else DECODE
-    call = Call(generate(name, seed=args.seed), dev)
+    if args.part == "decode_paged":
+        call = PagedCall(generate(name, seed=args.seed), dev, PAGE_SIZE)
+    else:
+        call = Call(generate(name, seed=args.seed), dev)
     stream = torch.cuda.current_stream(dev)
     for _ in range(args.warmup):
         call(stream)
@@ -185,6 +241,8 @@ def run_part(args, dev):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / max(args.steps, 1)
     res = {"part": args.part, "workload": name, "ms": round(ms, 4)}
+    if args.part == "decode_paged":
+        res["page_size"] = PAGE_SIZE
     if args.part == "prefill":
         res["tflops"] = round(unmasked_flops(call.inp) / (ms * 1e-3) / 1e12, 2)
     else:
@@ -201,7 +259,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-alibi-variant", action="store_true")
-    ap.add_argument("--part", choices=["all", "prefill", "decode", "copy"], default="all",
+    ap.add_argument("--no-paged-variant", action="store_true")
+    ap.add_argument("--part", choices=["all", "prefill", "decode", "decode_paged", "copy"], default="all",
                     help="run only one half of the step, or the calibration copy (for profiling); "
                          "the JSON line is for 'all'")
     args = ap.parse_args()
@@ -229,6 +288,9 @@ def main():
     pre_alibi = None
     if not args.no_alibi_variant:
         pre_alibi = Call(generate(PREFILL, seed=args.seed, alibi=True), dev)
+    dec_paged = None
+    if not args.no_paged_variant:
+        dec_paged = PagedCall(dec, dev, PAGE_SIZE)
     torch.cuda.synchronize()
     print(f"[bench] inputs generated and resident in HBM in {time.perf_counter() - t_gen:.1f} s",
           file=sys.stderr, flush=True)
@@ -275,6 +337,13 @@ def main():
         alibi_res = {"ms": round(ams, 4), "tflops": round(atf, 2),
                      "frac": round(atf / PEAK_MFMA_BF16_TFLOPS, 4)}
 
+    paged_res = None
+    if dec_paged is not None:  # the decode workload with K/V in shuffled pages of PAGE_SIZE keys
+        pms = time_calls(dec_paged, stream, max(5, K // 2))
+        pgb = dec_bytes / (pms * 1e-3) / 1e9
+        paged_res = {"page_size": PAGE_SIZE, "ms": round(pms, 4), "value": round(pgb, 1), "unit": "GB/s",
+                     "frac": round(pgb / PEAK_HBM_GBS, 4)}
+
     traffic_pre = measured_traffic("fwd_prefill")
     traffic_dec = measured_traffic("fwd_decode")
     line = {
@@ -315,6 +384,7 @@ def main():
                          "kernel": "fwd_decode_partial_kernel + fwd_decode_combine_kernel"},
         },
         "prefill_alibi": alibi_res,
+        "decode_paged": paged_res,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

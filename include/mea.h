@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define MEA_ABI_VERSION 2
+#define MEA_ABI_VERSION 3
 
 #if defined(__GNUC__)
 #define MEA_EXPORT __attribute__((visibility("default")))
@@ -154,6 +154,37 @@ MEA_EXPORT mea_status_t mea_fwd_splitkv(const void* q, const void* k, const void
                              mea_dtype_t dtype, int32_t causal, const float* alibi_slopes,
                              float scale, void* workspace, size_t workspace_bytes, void* stream,
                              int32_t chunk_keys);
+
+/*
+ * mea_fwd_paged -- mea_fwd with K and V held in a paged cache.  Section 4 of
+ * the 7minutos.es tutorial names vLLM-style batching of requests of
+ * different lengths as the use of packed sequences; engines of that kind keep
+ * K and V in pages addressed through a block table.  Computes exactly what
+ * mea_fwd computes on the sequences' keys gathered into the packed layout.
+ *   k_cache, v_cache  [num_pages, page_size, Hkv, D], 16-bit float of dtype
+ *   block_table       int32 [num_seqs, max_blocks] device array: entry
+ *                     [b, i] is the page holding keys i*page_size ..
+ *                     (i+1)*page_size - 1 of sequence b
+ *   seqstart_k        as for mea_fwd: the logical key offsets (sequence b
+ *                     has seqstart_k[b+1] - seqstart_k[b] keys; total_k is
+ *                     their sum), used for the work split only
+ * page_size must be a positive multiple of 64.  Rows of a sequence's last
+ * page past its length are never read.  Preconditions, not checked (device
+ * memory): every block_table entry a sequence uses is in [0, num_pages).
+ * Workspace: mea_fwd_workspace_size with the same sizes.  Same ownership and
+ * errors as mea_fwd, plus MEA_ERR_INVALID for a NULL block_table, a
+ * non-positive page_size, num_pages or max_blocks, or max_blocks *
+ * page_size < max_seqlen_k, and MEA_ERR_UNSUPPORTED for a page_size that is
+ * not a multiple of 64 or a page of 2 GiB or more.
+ */
+MEA_EXPORT mea_status_t mea_fwd_paged(const void* q, const void* k_cache, const void* v_cache, void* out,
+                           float* lse, const int32_t* seqstart_q, const int32_t* seqstart_k,
+                           const int32_t* block_table, int32_t num_seqs, int32_t total_q,
+                           int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                           int32_t page_size, int32_t num_pages, int32_t max_blocks, int32_t Hq,
+                           int32_t Hkv, int32_t D, mea_dtype_t dtype, int32_t causal,
+                           const float* alibi_slopes, float scale, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /*
  * mea_fwd_workspace_size -- bytes of workspace mea_fwd (chunk_keys == 0) or

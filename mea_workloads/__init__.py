@@ -32,7 +32,7 @@ import torch
 
 __all__ = [
     "Workload", "Inputs", "WORKLOADS", "get_workload", "generate", "random_case",
-    "alibi_slopes", "seqstart_from_lengths", "sample_rows", "prefix",
+    "alibi_slopes", "seqstart_from_lengths", "sample_rows", "prefix", "PagedKV", "to_paged",
 ]
 
 _DTYPES = {"fp16": torch.float16, "bf16": torch.bfloat16}
@@ -238,6 +238,44 @@ def prefix(inp: Inputs, n: int) -> Inputs:
         inp, q=inp.q[:sq[n]], k=inp.k[:sk[n]], v=inp.v[:sk[n]],
         seqstart_q=inp.seqstart_q[:n + 1].clone(), seqstart_k=inp.seqstart_k[:n + 1].clone(),
         seqlens_q=inp.seqlens_q[:n], seqlens_k=inp.seqlens_k[:n], bmghk=None)
+
+
+@dataclasses.dataclass
+class PagedKV:
+    """K/V of a packed input scattered into a paged cache."""
+    k_cache: torch.Tensor      # [num_pages, page_size, Hkv, D]
+    v_cache: torch.Tensor      # [num_pages, page_size, Hkv, D]
+    block_table: torch.Tensor  # int32 [num_seqs, max_blocks]
+    page_size: int
+
+
+def to_paged(inp: Inputs, page_size: int, seed: int = 0, spare_pages: int = 3,
+             filler: float = float("nan")) -> PagedKV:
+    """Scatter the keys and values of ``inp`` into pages of ``page_size`` keys
+    in a seeded random page order, with ``spare_pages`` unused pages.  Every
+    slot that holds no key of a sequence (the tail of a sequence's last page,
+    the spare pages) is set to ``filler``, so a read of such a slot shows up in
+    the result.  Unused block-table entries point at page 0."""
+    lens = list(inp.seqlens_k)
+    blocks = [-(-L // page_size) for L in lens]
+    num_pages = sum(blocks) + spare_pages
+    max_blocks = max([1] + blocks)
+    perm = np.random.default_rng(seed + 777).permutation(num_pages)
+    shape = (num_pages, page_size, inp.Hkv, inp.D)
+    k_cache = torch.full(shape, filler, dtype=inp.k.dtype)
+    v_cache = torch.full(shape, filler, dtype=inp.v.dtype)
+    table = torch.zeros((len(lens), max_blocks), dtype=torch.int32)
+    sk = inp.seqstart_k.tolist()
+    nxt = 0
+    for b, L in enumerate(lens):
+        for i in range(blocks[b]):
+            page = int(perm[nxt])
+            nxt += 1
+            table[b, i] = page
+            j0, j1 = i * page_size, min(L, (i + 1) * page_size)
+            k_cache[page, :j1 - j0] = inp.k[sk[b] + j0:sk[b] + j1]
+            v_cache[page, :j1 - j0] = inp.v[sk[b] + j0:sk[b] + j1]
+    return PagedKV(k_cache, v_cache, table, page_size)
 
 
 def sample_rows(inp: Inputs, count: int, seed: int = 0) -> List[Tuple[int, int]]:

@@ -13,7 +13,7 @@ import threading
 
 __all__ = [
     "MEA_OK", "MEA_ERR_INVALID", "MEA_ERR_UNSUPPORTED", "MEA_ERR_HIP", "MEA_F16", "MEA_BF16",
-    "EXPORTED_SYMBOLS", "library_path", "load", "mea_fwd", "mea_fwd_splitkv",
+    "EXPORTED_SYMBOLS", "library_path", "load", "mea_fwd", "mea_fwd_splitkv", "mea_fwd_paged",
     "mea_fwd_workspace_size", "mea_default_chunk_keys", "mea_status_string", "mea_last_error",
     "mea_abi_version",
 ]
@@ -22,7 +22,7 @@ MEA_OK, MEA_ERR_INVALID, MEA_ERR_UNSUPPORTED, MEA_ERR_HIP = 0, 1, 2, 3
 MEA_F16, MEA_BF16 = 0, 1
 
 EXPORTED_SYMBOLS = (
-    "mea_fwd", "mea_fwd_splitkv", "mea_fwd_workspace_size", "mea_default_chunk_keys",
+    "mea_fwd", "mea_fwd_splitkv", "mea_fwd_paged", "mea_fwd_workspace_size", "mea_default_chunk_keys",
     "mea_status_string", "mea_last_error", "mea_abi_version",
 )
 
@@ -35,6 +35,14 @@ _FWD_ARGS = [_vp, _vp, _vp, _vp, _vp,                # q k v out lse
              _vp, _vp, _i32, _i32, _i32, _i32, _i32,  # seqstart_q seqstart_k num_seqs total_q total_k max_q max_k
              _i32, _i32, _i32, _i32, _i32,      # Hq Hkv D dtype causal
              _vp, _f32, _vp, _sz, _vp]          # slopes scale workspace workspace_bytes stream
+
+
+_PAGED_ARGS = [_vp, _vp, _vp, _vp, _vp,                # q k_cache v_cache out lse
+               _vp, _vp, _vp,                          # seqstart_q seqstart_k block_table
+               _i32, _i32, _i32, _i32, _i32,           # num_seqs total_q total_k max_q max_k
+               _i32, _i32, _i32,                       # page_size num_pages max_blocks
+               _i32, _i32, _i32, _i32, _i32,           # Hq Hkv D dtype causal
+               _vp, _f32, _vp, _sz, _vp]               # slopes scale workspace workspace_bytes stream
 
 
 def library_path() -> str:
@@ -57,6 +65,8 @@ def load() -> ctypes.CDLL:
         lib.mea_fwd.restype = ctypes.c_int
         lib.mea_fwd_splitkv.argtypes = _FWD_ARGS + [_i32]
         lib.mea_fwd_splitkv.restype = ctypes.c_int
+        lib.mea_fwd_paged.argtypes = _PAGED_ARGS
+        lib.mea_fwd_paged.restype = ctypes.c_int
         lib.mea_fwd_workspace_size.argtypes = [_i32] * 8
         lib.mea_fwd_workspace_size.restype = _sz
         lib.mea_default_chunk_keys.argtypes = [_i32] * 3
@@ -86,6 +96,15 @@ def mea_fwd_splitkv(q, k, v, out, lse, seqstart_q, seqstart_k, num_seqs, total_q
                                   total_k, max_seqlen_q, max_seqlen_k, Hq, Hkv, D, dtype, causal,
                                   alibi_slopes, scale, workspace, workspace_bytes, stream,
                                   chunk_keys)
+
+
+def mea_fwd_paged(q, k_cache, v_cache, out, lse, seqstart_q, seqstart_k, block_table, num_seqs,
+                  total_q, total_k, max_seqlen_q, max_seqlen_k, page_size, num_pages, max_blocks, Hq,
+                  Hkv, D, dtype, causal, alibi_slopes, scale, workspace, workspace_bytes, stream) -> int:
+    return load().mea_fwd_paged(q, k_cache, v_cache, out, lse, seqstart_q, seqstart_k, block_table,
+                                num_seqs, total_q, total_k, max_seqlen_q, max_seqlen_k, page_size,
+                                num_pages, max_blocks, Hq, Hkv, D, dtype, causal, alibi_slopes, scale,
+                                workspace, workspace_bytes, stream)
 
 
 def mea_fwd_workspace_size(num_seqs, total_k, max_seqlen_q, max_seqlen_k, Hq, Hkv, D,

@@ -23,7 +23,7 @@ from . import _native
 
 __all__ = [
     "BlockDiagonalMask", "BlockDiagonalCausalMask", "memory_efficient_attention",
-    "attention_packed", "MeaError",
+    "attention_packed", "attention_paged", "MeaError",
 ]
 
 
@@ -188,6 +188,71 @@ def attention_packed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             st = _native.mea_fwd(*args)
         else:
             st = _native.mea_fwd_splitkv(*args, int(chunk_keys))
+    if st != _native.MEA_OK:
+        raise MeaError(st, _native.mea_last_error())
+    return (out, lse) if return_lse else out
+
+
+def attention_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                    block_table: torch.Tensor, seqstart_q: torch.Tensor, seqstart_k: torch.Tensor,
+                    max_seqlen_q: int, max_seqlen_k: int, *, causal: bool = False,
+                    alibi_slopes: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                    return_lse: bool = False, out: Optional[torch.Tensor] = None,
+                    lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                    total_k: Optional[int] = None, stream: Optional[torch.cuda.Stream] = None):
+    """Packed queries over a paged K/V cache: q ``[Tq, Hq, D]``, k/v cache
+    ``[num_pages, page_size, Hkv, D]``, int32 device ``block_table``
+    ``[n, max_blocks]`` (page of each page_size-key block of a sequence) and
+    int32 device ``seqstart_q/k`` ``[n + 1]`` (logical key offsets).
+    ``total_k`` is the total number of keys (read from ``seqstart_k``, with a
+    device synchronisation, when not given).  Returns ``out`` or
+    ``(out, lse)`` as :func:`attention_packed` does."""
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.dim() != 4:
+        raise ValueError("q must be [tokens, heads, D] and the caches [pages, page_size, heads, D]")
+    Tq, Hq, D = q.shape
+    num_pages, page_size, Hkv, Dk = k_cache.shape
+    if Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k_cache {tuple(k_cache.shape)} "
+                         f"v_cache {tuple(v_cache.shape)}")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("q and the caches must share a dtype")
+    dev = q.device
+    if dev.type != "cuda" or k_cache.device != dev or v_cache.device != dev or block_table.device != dev:
+        raise ValueError("q, the caches and block_table must be on the same GPU")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2:
+        raise TypeError("block_table must be an int32 [num_seqs, max_blocks] tensor")
+    q, k_cache, v_cache = q.contiguous(), k_cache.contiguous(), v_cache.contiguous()
+    block_table = block_table.contiguous()
+    if seqstart_q.dtype != torch.int32 or seqstart_k.dtype != torch.int32:
+        raise TypeError("seqstart tensors must be int32")
+    num_seqs = seqstart_q.numel() - 1
+    if seqstart_k.numel() != num_seqs + 1 or block_table.shape[0] != num_seqs:
+        raise ValueError("seqstart_q, seqstart_k and block_table disagree on the number of sequences")
+    Tk = int(total_k) if total_k is not None else (int(seqstart_k[-1].item()) if num_seqs > 0 else 0)
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((Hq, Tq), dtype=torch.float32, device=dev)
+    slopes = None
+    if alibi_slopes is not None:
+        slopes = alibi_slopes.to(device=dev, dtype=torch.float32).contiguous()
+        if slopes.numel() != Hq:
+            raise ValueError(f"alibi_slopes needs {Hq} values (one per query head)")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    scale = float(np.float32(scale))
+    ws_bytes = _native.mea_fwd_workspace_size(num_seqs, Tk, max_seqlen_q, max_seqlen_k, Hq, Hkv, D, 0)
+    if ws_bytes > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        st = _native.mea_fwd_paged(
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), _ptr(seqstart_q),
+            _ptr(seqstart_k), _ptr(block_table), num_seqs, Tq, Tk, int(max_seqlen_q), int(max_seqlen_k),
+            page_size, num_pages, block_table.shape[1], Hq, Hkv, D, _dtype_code(q.dtype),
+            int(bool(causal)), _ptr(slopes), scale, _ptr(workspace) if ws_bytes > 0 else None,
+            ws_bytes, stream.cuda_stream)
     if st != _native.MEA_OK:
         raise MeaError(st, _native.mea_last_error())
     return (out, lse) if return_lse else out

@@ -64,7 +64,7 @@ constexpr int kVtStride = kBlk + 8;       // elements per V^T row in a wave's LD
 
 }  // namespace
 
-template <int D, bool BF16, bool ALIBI>
+template <int D, bool BF16, bool ALIBI, bool PAGED>
 __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void fwd_decode_partial_kernel(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the body uses buffer-resource types that exist only for the GPU target
   constexpr int KS = D / 32;              // k-steps of the 16x16x32 Q K^T product
@@ -137,7 +137,8 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void fwd_decode_partial_ke
   float slope2 = 0.f;
   if constexpr (ALIBI) slope2 = col_valid ? a.slopes[head] * kLog2e : 0.f;
 
-  // K/V rows of this sequence and head, bounded: rows past the end read zeros
+  // K/V rows of this sequence and head, bounded: rows past the end read zeros.
+  // With a block table the rows live in pages instead (see load below).
   const uint32_t rs_bytes = (uint32_t)a.Hkv * D * 2;
   const uint32_t seq_bytes = (uint32_t)(Lk - 1) * rs_bytes + D * 2;
   const size_t head_off = ((size_t)sk0 * a.Hkv + g) * D;
@@ -158,18 +159,32 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void fwd_decode_partial_ke
     u32x4 k[2][KS];
     u32x4 v[VCH][4];
   };
+  // Block j0 (a multiple of 32) of the sequence.  Paged: the block lies in
+  // one page (page_size is a multiple of 64); its resource is bounded by the
+  // rows of that page the sequence uses, so rows past the sequence's end read
+  // zeros whatever the page holds there.
   auto load = [&](Regs& R, int j0) {
-    const int soff = j0 * (int)rs_bytes;
+    int soff = j0 * (int)rs_bytes;
+    __amdgpu_buffer_rsrc_t kr = krs, vr = vrs;
+    if constexpr (PAGED) {
+      const int pb = j0 / a.page_size;
+      const int page = a.block_table[(size_t)b * a.max_blocks + pb];
+      const uint32_t rows = (uint32_t)min(a.page_size, Lk - pb * a.page_size);
+      const size_t off = ((size_t)page * a.page_size * a.Hkv + g) * D;
+      kr = rows_rsrc(a.k + off, (rows - 1) * rs_bytes + D * 2);
+      vr = rows_rsrc(a.v + off, (rows - 1) * rs_bytes + D * 2);
+      soff = (j0 - pb * a.page_size) * (int)rs_bytes;
+    }
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        R.k[bb][ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, k_off[bb] + 64 * ks, soff, kStreamPolicy));
+        R.k[bb][ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, k_off[bb] + 64 * ks, soff, kStreamPolicy));
 #pragma unroll
     for (int x = 0; x < VCH; ++x)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        R.v[x][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, v_off + i * rs_bytes + x * 128, soff, kStreamPolicy));
+        R.v[x][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, v_off + i * rs_bytes + x * 128, soff, kStreamPolicy));
   };
 
   f32x4 o[DB];
@@ -220,7 +235,7 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void fwd_decode_partial_ke
       float v;
       if constexpr (ALIBI) v = __builtin_fmaf(sc, c, slope2 * (float)(jlane + e - qpos));
       else v = sc * c;
-      if (jlane + e >= c1) v = kNegInf;
+      if (jlane + e >= c1 || (PAGED && jlane + e < c0)) v = kNegInf;
       x[e] = v;
       mx = __builtin_fmaxf(mx, v);
     }
@@ -250,18 +265,21 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void fwd_decode_partial_ke
     }
   };
 
-  // this wave's blocks: j = c0 + 32 * (stripe + stripes * i)
-  const int nblk = (c1 - c0 + kBlk - 1) / kBlk;
+  // this wave's blocks: j = cb + 32 * (stripe + stripes * i).  Paged, the
+  // blocks sit on the sequence's 32-key grid so none crosses a page (keys
+  // before c0 are masked in the first block); packed, they start at c0.
+  const int cb = PAGED ? (c0 & ~(kBlk - 1)) : c0;
+  const int nblk = (c1 - cb + kBlk - 1) / kBlk;
   Regs ra, rb;
   int i = stripe;
-  if (i < nblk) load(ra, c0 + kBlk * i);
+  if (i < nblk) load(ra, cb + kBlk * i);
   for (; i < nblk; i += 2 * stripes) {
     const int inext = i + stripes;
-    if (inext < nblk) load(rb, c0 + kBlk * inext);
-    compute(ra, c0 + kBlk * i);
+    if (inext < nblk) load(rb, cb + kBlk * inext);
+    compute(ra, cb + kBlk * i);
     if (inext >= nblk) break;
-    if (inext + stripes < nblk) load(ra, c0 + kBlk * (inext + stripes));
-    compute(rb, c0 + kBlk * inext);
+    if (inext + stripes < nblk) load(ra, cb + kBlk * (inext + stripes));
+    compute(rb, cb + kBlk * inext);
   }
 
   // ---- merge the partial states of the waves that share a head, in LDS
@@ -392,8 +410,13 @@ static hipError_t launch_decode_d(const FwdArgs& a, bool alibi, hipStream_t stre
   if (a.dc_pieces > 0) {
     const dim3 grid((unsigned)a.dc_pieces * (unsigned)((a.Hkv / a.kv_per_wg) * a.head_slices));
     const dim3 block(64 * kWaves);
-    if (alibi) hipLaunchKernelGGL((fwd_decode_partial_kernel<D, BF16, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((fwd_decode_partial_kernel<D, BF16, false>), grid, block, 0, stream, a);
+    if (a.block_table != nullptr) {
+      if (alibi) hipLaunchKernelGGL((fwd_decode_partial_kernel<D, BF16, true, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((fwd_decode_partial_kernel<D, BF16, false, true>), grid, block, 0, stream, a);
+    } else {
+      if (alibi) hipLaunchKernelGGL((fwd_decode_partial_kernel<D, BF16, true, false>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((fwd_decode_partial_kernel<D, BF16, false, false>), grid, block, 0, stream, a);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

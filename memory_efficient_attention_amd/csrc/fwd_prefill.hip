@@ -189,13 +189,25 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
   auto kbuf = [&](int t) { return smem + (t % kBufs) * L::kBytes; };
   auto vbuf = [&](int t) { return smem + kBufs * L::kBytes + (t % kBufs) * L::vBytes; };
 
+  // K tile of step t.  Paged: the 64-key tile lies in one page (page_size
+  // is a multiple of 64); its resource is bounded by the rows of that page
+  // the sequence uses, so rows past the sequence's end read zeros.
   auto issue_k = [&](int t) {
-    const int soff = tile_of(t) * BN * (int)rs_bytes;
+    const int kt = tile_of(t) * BN;
+    int soff = kt * (int)rs_bytes;
+    __amdgpu_buffer_rsrc_t kr = krs;
+    if (a.block_table != nullptr) {
+      const int pb = kt / a.page_size;
+      const int page = a.block_table[(size_t)b * a.max_blocks + pb];
+      const uint32_t rows = (uint32_t)min(a.page_size, Lk - pb * a.page_size);
+      kr = rows_rsrc(a.k + ((size_t)page * a.page_size * a.Hkv + g) * D, (rows - 1) * rs_bytes + D * 2);
+      soff = (kt - pb * a.page_size) * (int)rs_bytes;
+    }
     uint8_t* dst = kbuf(t);
 #pragma unroll
     for (int i = 0; i < L::kLoads; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          krs, (__attribute__((address_space(3))) void*)(dst + (i * kPfWaves + wave) * 1024), 16, k_voff[i], soff, 0, 0);
+          kr, (__attribute__((address_space(3))) void*)(dst + (i * kPfWaves + wave) * 1024), 16, k_voff[i], soff, 0, 0);
   };
   auto issue_v = [&](int t) {
     const int vsoff = tile_of(t) * a.Hkv * kImgBytes;
@@ -428,13 +440,25 @@ __global__ __launch_bounds__(kVtThreads) void vt_images_kernel(FwdArgs a) {
   const int kq = tid % (BN / 4), cv = tid / (BN / 4);
   if (cv >= D / 8) return;
   const uint32_t rs_bytes = (uint32_t)a.Hkv * D * 2;
-  const __amdgpu_buffer_rsrc_t vrs =
-      rows_rsrc(a.v + ((size_t)sk0 * a.Hkv + g) * D, (uint32_t)(Lk - 1) * rs_bytes + D * 2);
+  // the tile's rows, bounded so that rows past the sequence's end read zeros
+  // (paged: the tile lies in one page, bounded by the rows the sequence uses)
+  __amdgpu_buffer_rsrc_t vrs;
+  uint32_t row0;
+  if (a.block_table != nullptr) {
+    const int pb = (i * BN) / a.page_size;
+    const int page = a.block_table[(size_t)b * a.max_blocks + pb];
+    const uint32_t rows = (uint32_t)min(a.page_size, Lk - pb * a.page_size);
+    vrs = rows_rsrc(a.v + ((size_t)page * a.page_size * a.Hkv + g) * D, (rows - 1) * rs_bytes + D * 2);
+    row0 = (uint32_t)(i * BN - pb * a.page_size);
+  } else {
+    vrs = rows_rsrc(a.v + ((size_t)sk0 * a.Hkv + g) * D, (uint32_t)(Lk - 1) * rs_bytes + D * 2);
+    row0 = (uint32_t)(i * BN);
+  }
   u32x4 r[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k)
     r[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                         vrs, (uint32_t)(i * BN + 4 * kq + k) * rs_bytes + cv * 16u, 0, 0));
+                                         vrs, (row0 + 4 * kq + k) * rs_bytes + cv * 16u, 0, 0));
   if constexpr (BF16) {
 #pragma unroll
     for (int k = 0; k < 4; ++k)

@@ -74,12 +74,20 @@ size_t prefill_ws_bytes(int32_t num_seqs, int32_t total_k, int32_t Hkv, int32_t 
   return ((size_t)total_k / mea::kPfBN + (size_t)num_seqs) * (size_t)Hkv * (size_t)D * mea::kPfBN * 2;
 }
 
+// Paged K/V cache: block_table[b * max_blocks + i] is the page holding keys
+// [i * page_size, (i + 1) * page_size) of sequence b.
+struct PagedKv {
+  const int32_t* block_table;
+  int32_t page_size, num_pages, max_blocks;
+};
+
 mea_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse,
                       const int32_t* seqstart_q, const int32_t* seqstart_k, int32_t num_seqs,
                       int32_t total_q, int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq,
                       int32_t Hkv, int32_t D, mea_dtype_t dtype, int32_t causal,
                       const float* alibi_slopes, float scale, void* workspace,
-                      size_t workspace_bytes, void* stream, int32_t chunk_keys, bool forced_split) {
+                      size_t workspace_bytes, void* stream, int32_t chunk_keys, bool forced_split,
+                      const PagedKv* paged = nullptr) {
   g_last_error[0] = '\0';
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
     return fail(MEA_ERR_INVALID, "q, k, v and out must be non-NULL device pointers");
@@ -108,6 +116,20 @@ mea_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, fl
       !aligned(seqstart_q, 4) || !aligned(seqstart_k, 4))
     return fail(MEA_ERR_UNSUPPORTED, "lse, alibi_slopes and seqstart arrays must be 4-byte aligned");
   if (num_seqs > 65535) return fail(MEA_ERR_UNSUPPORTED, "num_seqs=%d exceeds 65535", num_seqs);
+  if (paged != nullptr) {
+    if (paged->block_table == nullptr) return fail(MEA_ERR_INVALID, "block_table must be a non-NULL device pointer");
+    if (!aligned(paged->block_table, 4)) return fail(MEA_ERR_UNSUPPORTED, "block_table must be 4-byte aligned");
+    if (paged->page_size <= 0 || paged->num_pages <= 0 || paged->max_blocks <= 0)
+      return fail(MEA_ERR_INVALID, "need page_size > 0, num_pages > 0 and max_blocks > 0 (got %d, %d, %d)",
+                  paged->page_size, paged->num_pages, paged->max_blocks);
+    if (paged->page_size % 64 != 0)
+      return fail(MEA_ERR_UNSUPPORTED, "page_size=%d is not a multiple of 64", paged->page_size);
+    if ((long long)paged->max_blocks * paged->page_size < max_seqlen_k)
+      return fail(MEA_ERR_INVALID, "max_blocks * page_size = %lld keys < max_seqlen_k = %d",
+                  (long long)paged->max_blocks * paged->page_size, max_seqlen_k);
+    if ((long long)paged->page_size * Hkv * D * 2 >= (1ll << 31))
+      return fail(MEA_ERR_UNSUPPORTED, "page_size * Hkv * D * 2 bytes must stay below 2^31");
+  }
   // key/value rows of one sequence are addressed with 32-bit byte offsets
   if ((long long)max_seqlen_k * Hkv * D * 2 >= (1ll << 31))
     return fail(MEA_ERR_UNSUPPORTED, "max_seqlen_k * Hkv * D * 2 bytes must stay below 2^31");
@@ -129,6 +151,11 @@ mea_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, fl
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.group = Hq / Hkv;
+  if (paged != nullptr) {
+    a.block_table = paged->block_table;
+    a.page_size = paged->page_size;
+    a.max_blocks = paged->max_blocks;
+  }
   const bool bf16 = dtype == MEA_BF16;
   const bool alibi = alibi_slopes != nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -199,6 +226,19 @@ mea_status_t mea_fwd_splitkv(const void* q, const void* k, const void* v, void* 
   return fwd_impl(q, k, v, out, lse, seqstart_q, seqstart_k, num_seqs, total_q, total_k, max_seqlen_q,
                   max_seqlen_k, Hq, Hkv, D, dtype, causal, alibi_slopes, scale, workspace,
                   workspace_bytes, stream, chunk_keys, true);
+}
+
+mea_status_t mea_fwd_paged(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
+                           const int32_t* seqstart_q, const int32_t* seqstart_k, const int32_t* block_table,
+                           int32_t num_seqs, int32_t total_q, int32_t total_k, int32_t max_seqlen_q,
+                           int32_t max_seqlen_k, int32_t page_size, int32_t num_pages, int32_t max_blocks,
+                           int32_t Hq, int32_t Hkv, int32_t D, mea_dtype_t dtype, int32_t causal,
+                           const float* alibi_slopes, float scale, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  const PagedKv paged{block_table, page_size, num_pages, max_blocks};
+  return fwd_impl(q, k_cache, v_cache, out, lse, seqstart_q, seqstart_k, num_seqs, total_q, total_k,
+                  max_seqlen_q, max_seqlen_k, Hq, Hkv, D, dtype, causal, alibi_slopes, scale, workspace,
+                  workspace_bytes, stream, 0, false, &paged);
 }
 
 size_t mea_fwd_workspace_size(int32_t num_seqs, int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k,

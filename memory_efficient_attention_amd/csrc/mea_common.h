@@ -31,6 +31,9 @@ struct FwdArgs {
   float* ws_o;               // decode: [num_seqs, max_chunks, Hq, D] float32 partials
   float* ws_lse;             // decode: [num_seqs, max_chunks, Hq] float32 (log2 units)
   uint16_t* ws_vt;           // prefill: transposed half-precision V tile images (see fwd_prefill.hip)
+  const int32_t* block_table;  // paged K/V: [num_seqs, max_blocks] page of each page_size-key block, or nullptr
+  int32_t page_size;         // paged K/V: keys per page (a multiple of 64)
+  int32_t max_blocks;        // paged K/V: row length of block_table
   float scale_log2;          // scale * log2(e)
   int32_t num_seqs;
   int32_t total_q;

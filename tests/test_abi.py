@@ -48,7 +48,7 @@ def test_every_kernel_stub_is_defined():
 
 
 def test_version_and_strings():
-    assert _native.mea_abi_version() == 2
+    assert _native.mea_abi_version() == 3
     for st in range(4):
         assert _native.mea_status_string(st).startswith("MEA_")
     assert "unknown" in _native.mea_status_string(99)
@@ -104,6 +104,38 @@ def call(**kw):
 def test_rejected_before_launch(kw, status, needle):
     assert call(**kw) == status
     assert needle in _native.mea_last_error()
+
+
+def call_paged(**kw):
+    a = dict(q=P, k_cache=P, v_cache=P, out=P, lse=None, seqstart_q=P, seqstart_k=P, block_table=P,
+             num_seqs=4, total_q=4, total_k=365, max_seqlen_q=1, max_seqlen_k=200, page_size=64,
+             num_pages=10, max_blocks=4, Hq=8, Hkv=8, D=64, dtype=MEA_F16, causal=0, alibi_slopes=None,
+             scale=0.125, workspace=P, workspace_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return _native.mea_fwd_paged(**a)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(block_table=None), MEA_ERR_INVALID, "block_table"),
+    (dict(block_table=P + 2), MEA_ERR_UNSUPPORTED, "block_table"),
+    (dict(page_size=0), MEA_ERR_INVALID, "page_size > 0"),
+    (dict(num_pages=0), MEA_ERR_INVALID, "num_pages > 0"),
+    (dict(max_blocks=0), MEA_ERR_INVALID, "max_blocks > 0"),
+    (dict(page_size=16), MEA_ERR_UNSUPPORTED, "multiple of 64"),
+    (dict(page_size=96), MEA_ERR_UNSUPPORTED, "multiple of 64"),
+    (dict(max_blocks=3), MEA_ERR_INVALID, "max_seqlen_k"),
+    (dict(page_size=1 << 20, D=128, max_blocks=1), MEA_ERR_UNSUPPORTED, "2^31"),
+    (dict(k_cache=None), MEA_ERR_INVALID, "non-NULL"),
+    (dict(D=96), MEA_ERR_UNSUPPORTED, "D=96"),
+    (dict(workspace=None, workspace_bytes=0), MEA_ERR_INVALID, "workspace"),
+])
+def test_paged_rejected_before_launch(kw, status, needle):
+    assert call_paged(**kw) == status
+    assert needle in _native.mea_last_error()
+
+
+def test_paged_empty_problem_is_a_noop():
+    assert call_paged(num_seqs=0, total_q=0) == MEA_OK
 
 
 @pytest.mark.parametrize("kw", [dict(num_seqs=0, total_q=0), dict(total_q=0, max_seqlen_q=0)])

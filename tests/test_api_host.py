@@ -47,3 +47,28 @@ def test_bmghk_kv_head_axis():
     assert kf.shape == (B, M, G * Hg, K) and torch.equal(kf[:, :, 5], full[:, :, 1, 1])
     with pytest.raises(ValueError):
         _kv_heads_bmghk(torch.randn(B, M, G, 3, K), Hg)
+
+
+def test_to_paged_round_trip():
+    """The paging helper used by the paged parity tests: gathering every
+    sequence's pages back in block-table order reproduces its keys and values,
+    and every other slot holds the filler."""
+    import math as _m
+    from mea_workloads import random_case, to_paged
+    inp = random_case(5, [1, 1, 1, 1], [0, 64, 65, 300], Hq=4, Hkv=2, D=64, dtype="fp16")
+    pk = to_paged(inp, 64, seed=3, spare_pages=2)
+    sk = inp.seqstart_k.tolist()
+    used = set()
+    for b, L in enumerate(inp.seqlens_k):
+        nb = -(-L // 64)
+        pages = pk.block_table[b, :nb].tolist()
+        used.update(pages)
+        k = torch.cat([pk.k_cache[p] for p in pages])[:L] if nb else pk.k_cache[:0, 0]
+        v = torch.cat([pk.v_cache[p] for p in pages])[:L] if nb else pk.v_cache[:0, 0]
+        assert torch.equal(k, inp.k[sk[b]:sk[b + 1]]) and torch.equal(v, inp.v[sk[b]:sk[b + 1]])
+        if nb and L % 64:
+            assert torch.isnan(pk.k_cache[pages[-1], L % 64:].float()).all()
+    assert len(used) == sum(-(-L // 64) for L in inp.seqlens_k)
+    spare = [p for p in range(pk.k_cache.shape[0]) if p not in used]
+    assert len(spare) == 2 and all(torch.isnan(pk.v_cache[p].float()).all() for p in spare)
+    assert not _m.isnan(float(pk.block_table.sum()))
