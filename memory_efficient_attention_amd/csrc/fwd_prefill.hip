@@ -99,7 +99,7 @@ __device__ __forceinline__ void interleave_reads_and_products() {
 
 }  // namespace
 
-template <int D, bool BF16, bool CAUSAL, bool ALIBI>
+template <int D, bool BF16, bool CAUSAL, bool ALIBI, bool PAGED>
 __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the body uses buffer-resource types that exist only for the GPU target
   using L = PfLayout<D>;
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
     const int kt = tile_of(t) * BN;
     int soff = kt * (int)rs_bytes;
     __amdgpu_buffer_rsrc_t kr = krs;
-    if (a.block_table != nullptr) {
+    if constexpr (PAGED) {
       const int pb = kt / a.page_size;
       const int page = a.block_table[(size_t)b * a.max_blocks + pb];
       const uint32_t rows = (uint32_t)min(a.page_size, Lk - pb * a.page_size);
@@ -429,7 +429,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
 // since a sequence of L keys has at most L / 64 + 1 tiles).  Keys past the
 // sequence's end are zero.  Thread (kq, cv) transposes 4 keys x 8 features in
 // registers.
-template <int D, bool BF16>
+template <int D, bool BF16, bool PAGED>
 __global__ __launch_bounds__(kVtThreads) void vt_images_kernel(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int BN = kPfBN;
@@ -444,7 +444,7 @@ __global__ __launch_bounds__(kVtThreads) void vt_images_kernel(FwdArgs a) {
   // (paged: the tile lies in one page, bounded by the rows the sequence uses)
   __amdgpu_buffer_rsrc_t vrs;
   uint32_t row0;
-  if (a.block_table != nullptr) {
+  if constexpr (PAGED) {
     const int pb = (i * BN) / a.page_size;
     const int page = a.block_table[(size_t)b * a.max_blocks + pb];
     const uint32_t rows = (uint32_t)min(a.page_size, Lk - pb * a.page_size);
@@ -481,41 +481,48 @@ __global__ __launch_bounds__(kVtThreads) void vt_images_kernel(FwdArgs a) {
 #endif
 }
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool PAGED>
 static hipError_t launch_prefill_d(const FwdArgs& a, bool causal, bool alibi, dim3 grid,
                                    hipStream_t stream) {
   const dim3 block(kThreads);
   if (causal) {
-    if (alibi) hipLaunchKernelGGL((fwd_prefill_kernel<D, BF16, true, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((fwd_prefill_kernel<D, BF16, true, false>), grid, block, 0, stream, a);
+    if (alibi) hipLaunchKernelGGL((fwd_prefill_kernel<D, BF16, true, true, PAGED>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((fwd_prefill_kernel<D, BF16, true, false, PAGED>), grid, block, 0, stream, a);
   } else {
-    if (alibi) hipLaunchKernelGGL((fwd_prefill_kernel<D, BF16, false, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((fwd_prefill_kernel<D, BF16, false, false>), grid, block, 0, stream, a);
+    if (alibi) hipLaunchKernelGGL((fwd_prefill_kernel<D, BF16, false, true, PAGED>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((fwd_prefill_kernel<D, BF16, false, false, PAGED>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_prefill(const FwdArgs& a, int D, bool bf16, bool causal, bool alibi,
-                          int max_seqlen_k, hipStream_t stream) {
+template <int D, bool BF16, bool PAGED>
+static hipError_t launch_prefill_dp(const FwdArgs& a, bool causal, bool alibi, int max_seqlen_k,
+                                    hipStream_t stream) {
   if (max_seqlen_k > 0) {
     const dim3 vgrid(a.Hkv, (max_seqlen_k + kPfBN - 1) / kPfBN, a.num_seqs);
-    if (D == 64) {
-      if (bf16) hipLaunchKernelGGL((vt_images_kernel<64, true>), vgrid, dim3(kVtThreads), 0, stream, a);
-      else hipLaunchKernelGGL((vt_images_kernel<64, false>), vgrid, dim3(kVtThreads), 0, stream, a);
-    } else {
-      if (bf16) hipLaunchKernelGGL((vt_images_kernel<128, true>), vgrid, dim3(kVtThreads), 0, stream, a);
-      else hipLaunchKernelGGL((vt_images_kernel<128, false>), vgrid, dim3(kVtThreads), 0, stream, a);
-    }
+    hipLaunchKernelGGL((vt_images_kernel<D, BF16, PAGED>), vgrid, dim3(kVtThreads), 0, stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const dim3 grid((unsigned)(((long long)a.pf_items + 7) / 8 * 8));
+  return launch_prefill_d<D, BF16, PAGED>(a, causal, alibi, grid, stream);
+}
+
+template <int D, bool BF16>
+static hipError_t launch_prefill_db(const FwdArgs& a, bool causal, bool alibi, int max_seqlen_k,
+                                    hipStream_t stream) {
+  return a.block_table != nullptr ? launch_prefill_dp<D, BF16, true>(a, causal, alibi, max_seqlen_k, stream)
+                                  : launch_prefill_dp<D, BF16, false>(a, causal, alibi, max_seqlen_k, stream);
+}
+
+hipError_t launch_prefill(const FwdArgs& a, int D, bool bf16, bool causal, bool alibi,
+                          int max_seqlen_k, hipStream_t stream) {
   if (D == 64) {
-    return bf16 ? launch_prefill_d<64, true>(a, causal, alibi, grid, stream)
-                : launch_prefill_d<64, false>(a, causal, alibi, grid, stream);
+    return bf16 ? launch_prefill_db<64, true>(a, causal, alibi, max_seqlen_k, stream)
+                : launch_prefill_db<64, false>(a, causal, alibi, max_seqlen_k, stream);
   }
-  return bf16 ? launch_prefill_d<128, true>(a, causal, alibi, grid, stream)
-              : launch_prefill_d<128, false>(a, causal, alibi, grid, stream);
+  return bf16 ? launch_prefill_db<128, true>(a, causal, alibi, max_seqlen_k, stream)
+              : launch_prefill_db<128, false>(a, causal, alibi, max_seqlen_k, stream);
 }
 
 }  // namespace mea
