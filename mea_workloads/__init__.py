@@ -33,6 +33,7 @@ import torch
 __all__ = [
     "Workload", "Inputs", "WORKLOADS", "get_workload", "generate", "random_case",
     "alibi_slopes", "seqstart_from_lengths", "sample_rows", "prefix", "PagedKV", "to_paged",
+    "random_dout",
 ]
 
 _DTYPES = {"fp16": torch.float16, "bf16": torch.bfloat16}
@@ -228,6 +229,12 @@ def random_case(seed: int, seqlens_q: Sequence[int], seqlens_k: Optional[Sequenc
         alibi_slopes=slopes if alibi else None,
         scale=default_scale(D) if scale is None else float(np.float32(scale)),
         dtype=dtype if isinstance(dtype, str) else {v_: k_ for k_, v_ in _DTYPES.items()}[dt])
+
+
+def random_dout(seed: int, inp: Inputs, std: float = 1.0) -> torch.Tensor:
+    """A seeded upstream gradient dO for ``inp``: N(0, std^2) of q's shape and dtype."""
+    g = torch.Generator("cpu").manual_seed(seed + 7919)
+    return (torch.randn(tuple(inp.q.shape), generator=g) * std).to(inp.q.dtype)
 
 
 def prefix(inp: Inputs, n: int) -> Inputs:

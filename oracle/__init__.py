@@ -7,12 +7,12 @@ Python binding (the seeded input generators in ``mea_workloads`` are the only
 code both sides use, and they hold none of the attention arithmetic).
 
 What it computes is the plain definition of attention over packed
-variable-length sequences; see ``oracle.attention`` for the definition and the
+variable-length sequences, and its gradients; see ``oracle.attention`` for the definition and the
 passages of the pages it follows.  Every function here is pinned by
 ``tests/test_oracle.py`` (brute force, closed forms, invariants and a library
 routine) except the readings listed as "parity unpinned" in
 ``oracle.attention``'s module docstring.
 """
-from .attention import attention_forward, attention_rows
+from .attention import attention_backward, attention_forward, attention_rows
 
-__all__ = ["attention_forward", "attention_rows"]
+__all__ = ["attention_forward", "attention_rows", "attention_backward"]

@@ -51,7 +51,7 @@ from typing import List, Optional, Sequence, Tuple
 
 import torch
 
-__all__ = ["attention_forward", "attention_rows"]
+__all__ = ["attention_forward", "attention_rows", "attention_backward"]
 
 
 def _f64(x: torch.Tensor) -> torch.Tensor:
@@ -63,11 +63,10 @@ def _starts(seqstart) -> List[int]:
     return [int(s) for s in (seqstart.tolist() if torch.is_tensor(seqstart) else seqstart)]
 
 
-def _one_row_block(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, qpos: torch.Tensor,
-                   causal: bool, slope: Optional[float], scale: float
-                   ) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Attention of query rows Q [R, D] (at key positions qpos [R]) over one
-    sequence's keys K, V [L_k, D].  Returns out [R, D] and lse [R]."""
+def _softmax_block(Q: torch.Tensor, K: torch.Tensor, qpos: torch.Tensor, causal: bool,
+                   slope: Optional[float], scale: float) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Softmax weights P [R, L_k] and lse [R] of query rows Q [R, D] (at key
+    positions qpos [R]) over one sequence's keys K [L_k, D]."""
     L_k = K.shape[0]
     kpos = torch.arange(L_k, dtype=torch.float64)
     S = scale * (Q @ K.transpose(0, 1))                       # [P3]: scaled scores
@@ -82,6 +81,15 @@ def _one_row_block(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, qpos: torc
     empty = torch.isneginf(lse)
     P = torch.exp(S - torch.where(empty, 0.0, lse)[:, None])  # softmax weights
     P = torch.where(empty[:, None], 0.0, P)
+    return P, lse
+
+
+def _one_row_block(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, qpos: torch.Tensor,
+                   causal: bool, slope: Optional[float], scale: float
+                   ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Attention of query rows Q [R, D] (at key positions qpos [R]) over one
+    sequence's keys K, V [L_k, D].  Returns out [R, D] and lse [R]."""
+    P, lse = _softmax_block(Q, K, qpos, causal, slope, scale)
     out = P @ V
     return out, lse
 
@@ -150,3 +158,59 @@ def attention_rows(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seqstart_q
         outs[n] = o[0]
         lses[n] = l[0]
     return outs, lses
+
+
+def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor,
+                       seqstart_q, seqstart_k, *, causal: bool = False,
+                       alibi_slopes: Optional[torch.Tensor] = None,
+                       scale: Optional[float] = None
+                       ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Gradients of sum(out * dout) with respect to q, k and v, for the
+    forward that ``attention_forward`` computes.
+
+    The pages time the backward pass of the same attention and train with it
+    ([P2]: forward and backward timing; the training loop of [P1]); they give
+    no formulas, so this is the derivative of the definition written out by
+    the chain rule, per sequence b and query head h with g = h // (Hq / Hkv):
+      P   = softmax weights of the forward (zero rows where no key is allowed)
+      dV_g += P^T dO_h                          (out = P V)
+      dP  = dO_h V_g^T
+      dS  = P * (dP - rowsum(P * dP))           (Jacobian of a row softmax)
+      dQ_h  = scale * dS K_g
+      dK_g += scale * dS^T Q_h                  (S = scale Q K^T + bias)
+    The sums over the query heads of one group give the K/V gradients of the
+    shared head [P5].  The ALiBi slopes, the causal mask and the block-diagonal
+    mask are constants: no gradient flows to them.
+    Returns dq float64 [Tq, Hq, D], dk and dv float64 [Tk, Hkv, D].
+    """
+    Q64, K64, V64, dO64 = _f64(q), _f64(k), _f64(v), _f64(dout)
+    Tq, Hq, D = Q64.shape
+    Tk, Hkv, _ = K64.shape
+    assert tuple(dO64.shape) == (Tq, Hq, D) and Hq % Hkv == 0
+    if scale is None:
+        scale = D ** -0.5
+    slopes = None if alibi_slopes is None else [float(s) for s in _f64(alibi_slopes)]
+    sq, sk = _starts(seqstart_q), _starts(seqstart_k)
+    per_group = Hq // Hkv
+    dq = torch.zeros((Tq, Hq, D), dtype=torch.float64)
+    dk = torch.zeros((Tk, Hkv, D), dtype=torch.float64)
+    dv = torch.zeros((Tk, Hkv, D), dtype=torch.float64)
+    for b in range(len(sq) - 1):
+        L_q, L_k = sq[b + 1] - sq[b], sk[b + 1] - sk[b]
+        if L_q == 0 or L_k == 0:
+            continue
+        qpos = torch.arange(L_q, dtype=torch.float64) + (L_k - L_q)
+        for h in range(Hq):
+            g = h // per_group
+            Qh = Q64[sq[b]:sq[b + 1], h, :]
+            Kg = K64[sk[b]:sk[b + 1], g, :]
+            Vg = V64[sk[b]:sk[b + 1], g, :]
+            dOh = dO64[sq[b]:sq[b + 1], h, :]
+            P, _ = _softmax_block(Qh, Kg, qpos, causal, None if slopes is None else slopes[h],
+                                  float(scale))
+            dv[sk[b]:sk[b + 1], g, :] += P.transpose(0, 1) @ dOh
+            dP = dOh @ Vg.transpose(0, 1)
+            dS = P * (dP - (P * dP).sum(dim=1, keepdim=True))
+            dq[sq[b]:sq[b + 1], h, :] = scale * (dS @ Kg)
+            dk[sk[b]:sk[b + 1], g, :] += scale * (dS.transpose(0, 1) @ Qh)
+    return dq, dk, dv
