@@ -1,6 +1,6 @@
 /*
- * mea.h -- C ABI of the fused memory-efficient attention forward for AMD
- * Instinct MI355X (gfx950).
+ * mea.h -- C ABI of the fused memory-efficient attention forward and backward
+ * for AMD Instinct MI355X (gfx950).
  *
  * What is computed (for every packed sequence b and query head h):
  *
@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define MEA_ABI_VERSION 3
+#define MEA_ABI_VERSION 4
 
 #if defined(__GNUC__)
 #define MEA_EXPORT __attribute__((visibility("default")))
@@ -201,6 +201,71 @@ MEA_EXPORT mea_status_t mea_fwd_paged(const void* q, const void* k_cache, const 
 MEA_EXPORT size_t mea_fwd_workspace_size(int32_t num_seqs, int32_t total_k, int32_t max_seqlen_q,
                                          int32_t max_seqlen_k, int32_t Hq, int32_t Hkv, int32_t D,
                                          int32_t chunk_keys);
+
+/*
+ * mea_bwd -- gradients of the attention of mea_fwd: given dout = dL/dout for
+ * some scalar L, writes dq = dL/dq, dk = dL/dk and dv = dL/dv.  The
+ * yifor-blog page's performance comparison (xFormers vs standard attention)
+ * times the backward pass of this attention beside the forward, and the
+ * tutorial trains a GPT-style model with it; the pages give no formulas, so
+ * this is the chain rule applied to the
+ * definition above, per sequence b and query head h (g = g(h), P the softmax
+ * weights, zero in rows with no allowed key):
+ *   dv[g] += P^T dout[h]
+ *   dP     = dout[h] v[g]^T
+ *   dS     = P * (dP - rowsum(dout[h] * out[h]))     (rowsum(P * dP))
+ *   dq[h]  = scale * dS k[g]
+ *   dk[g] += scale * dS^T q[h]
+ * summed over the query heads of g's group.  ALiBi slopes and masks are
+ * constants; lse receives no gradient.
+ *
+ *   q, k, v, seqstart_q/k, sizes, Hq, Hkv, D, dtype, causal, alibi_slopes,
+ *                  scale: exactly as passed to the mea_fwd call that produced
+ *                  out and lse (same preconditions).
+ *   out            device [total_q, Hq, D], the forward's output.
+ *   lse            device [Hq, total_q] float32, the forward's log-sum-exp
+ *                  (required: it is how P is recomputed without the score
+ *                  matrix).
+ *   dout           device [total_q, Hq, D], the upstream gradient.
+ *   dq             device output [total_q, Hq, D]; every row is written.
+ *   dk, dv         device outputs [total_k, Hkv, D]; every row is written
+ *                  (zero for keys no query row sees).
+ *   workspace      device scratch of at least mea_bwd_workspace_size(...)
+ *                  bytes, 256-byte aligned; clobbered.
+ * dtype applies to q, k, v, out, dout, dq, dk and dv; all 16-byte aligned.
+ * Ownership and execution as for mea_fwd (outputs must not alias inputs).
+ * Returns MEA_ERR_INVALID for a NULL pointer among q, k, v, out, lse, dout,
+ * dq, dk, dv, seqstart_q/k; negative sizes; bad heads; causal not 0/1;
+ * total_q > 0 with max_seqlen_q == 0 or total_k > 0 with max_seqlen_k == 0;
+ * a workspace smaller than required.  MEA_ERR_UNSUPPORTED for D not 64/128,
+ * an unknown dtype, a non-finite or non-positive scale, misalignment,
+ * num_seqs > 65535, (max_seqlen + 64) * heads * D * 2 >= 2^31 for q or k,
+ * or more than 65535 tiles of 64 rows in one sequence.  num_seqs == 0, or
+ * total_q == total_k == 0, is a no-op returning MEA_OK.
+ *
+ * Numerics: S = q k^T and dP = dout v^T run on the matrix cores in the input
+ * dtype with float32 accumulation; P and dS are float32 and are rounded to the
+ * input dtype as operands of the second products (dv, dk, dq), which
+ * accumulate in float32; rowsum(dout * out) is float32; outputs are rounded
+ * to nearest even.
+ */
+MEA_EXPORT mea_status_t mea_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                                const void* dout, void* dq, void* dk, void* dv, const int32_t* seqstart_q,
+                                const int32_t* seqstart_k, int32_t num_seqs, int32_t total_q, int32_t total_k,
+                                int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq, int32_t Hkv, int32_t D,
+                                mea_dtype_t dtype, int32_t causal, const float* alibi_slopes, float scale,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mea_bwd_workspace_size -- bytes of workspace mea_bwd needs (0 for arguments
+ * it would reject).  Pure host function.  Four parts, each rounded up to a
+ * multiple of 256 bytes: 2 x Hq * total_q * 4 (float32 row terms) when
+ * total_q > 0; 2 x (total_q / 64 + num_seqs) * Hq * D * 128 (transposed
+ * tiles of q and dout) when total_q > 0; (total_k / 64 + num_seqs) * Hkv * D
+ * * 128 (transposed tiles of k) when total_k > 0.
+ */
+MEA_EXPORT size_t mea_bwd_workspace_size(int32_t num_seqs, int32_t total_q, int32_t total_k, int32_t Hq,
+                                         int32_t Hkv, int32_t D);
 
 /* Piece length of the key axis that mea_fwd picks for a decode call with
  * these sizes (a multiple of 32, at least 128).  Pure host function. */

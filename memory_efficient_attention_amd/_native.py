@@ -14,8 +14,8 @@ import threading
 __all__ = [
     "MEA_OK", "MEA_ERR_INVALID", "MEA_ERR_UNSUPPORTED", "MEA_ERR_HIP", "MEA_F16", "MEA_BF16",
     "EXPORTED_SYMBOLS", "library_path", "load", "mea_fwd", "mea_fwd_splitkv", "mea_fwd_paged",
-    "mea_fwd_workspace_size", "mea_default_chunk_keys", "mea_status_string", "mea_last_error",
-    "mea_abi_version",
+    "mea_fwd_workspace_size", "mea_default_chunk_keys", "mea_bwd", "mea_bwd_workspace_size",
+    "mea_status_string", "mea_last_error", "mea_abi_version",
 ]
 
 MEA_OK, MEA_ERR_INVALID, MEA_ERR_UNSUPPORTED, MEA_ERR_HIP = 0, 1, 2, 3
@@ -23,7 +23,7 @@ MEA_F16, MEA_BF16 = 0, 1
 
 EXPORTED_SYMBOLS = (
     "mea_fwd", "mea_fwd_splitkv", "mea_fwd_paged", "mea_fwd_workspace_size", "mea_default_chunk_keys",
-    "mea_status_string", "mea_last_error", "mea_abi_version",
+    "mea_bwd", "mea_bwd_workspace_size", "mea_status_string", "mea_last_error", "mea_abi_version",
 )
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -43,6 +43,13 @@ _PAGED_ARGS = [_vp, _vp, _vp, _vp, _vp,                # q k_cache v_cache out l
                _i32, _i32, _i32,                       # page_size num_pages max_blocks
                _i32, _i32, _i32, _i32, _i32,           # Hq Hkv D dtype causal
                _vp, _f32, _vp, _sz, _vp]               # slopes scale workspace workspace_bytes stream
+
+
+_BWD_ARGS = [_vp, _vp, _vp, _vp, _vp, _vp,            # q k v out lse dout
+             _vp, _vp, _vp,                          # dq dk dv
+             _vp, _vp, _i32, _i32, _i32, _i32, _i32,  # seqstart_q seqstart_k num_seqs total_q total_k max_q max_k
+             _i32, _i32, _i32, _i32, _i32,           # Hq Hkv D dtype causal
+             _vp, _f32, _vp, _sz, _vp]               # slopes scale workspace workspace_bytes stream
 
 
 def library_path() -> str:
@@ -71,6 +78,10 @@ def load() -> ctypes.CDLL:
         lib.mea_fwd_workspace_size.restype = _sz
         lib.mea_default_chunk_keys.argtypes = [_i32] * 3
         lib.mea_default_chunk_keys.restype = _i32
+        lib.mea_bwd.argtypes = _BWD_ARGS
+        lib.mea_bwd.restype = ctypes.c_int
+        lib.mea_bwd_workspace_size.argtypes = [_i32] * 6
+        lib.mea_bwd_workspace_size.restype = _sz
         lib.mea_status_string.argtypes = [ctypes.c_int]
         lib.mea_status_string.restype = ctypes.c_char_p
         lib.mea_last_error.argtypes = []
@@ -115,6 +126,18 @@ def mea_fwd_workspace_size(num_seqs, total_k, max_seqlen_q, max_seqlen_k, Hq, Hk
 
 def mea_default_chunk_keys(total_k, Hq, Hkv) -> int:
     return int(load().mea_default_chunk_keys(total_k, Hq, Hkv))
+
+
+def mea_bwd(q, k, v, out, lse, dout, dq, dk, dv, seqstart_q, seqstart_k, num_seqs, total_q, total_k,
+            max_seqlen_q, max_seqlen_k, Hq, Hkv, D, dtype, causal, alibi_slopes, scale, workspace,
+            workspace_bytes, stream) -> int:
+    return load().mea_bwd(q, k, v, out, lse, dout, dq, dk, dv, seqstart_q, seqstart_k, num_seqs,
+                          total_q, total_k, max_seqlen_q, max_seqlen_k, Hq, Hkv, D, dtype, causal,
+                          alibi_slopes, scale, workspace, workspace_bytes, stream)
+
+
+def mea_bwd_workspace_size(num_seqs, total_q, total_k, Hq, Hkv, D) -> int:
+    return int(load().mea_bwd_workspace_size(num_seqs, total_q, total_k, Hq, Hkv, D))
 
 
 def mea_status_string(status: int) -> str:

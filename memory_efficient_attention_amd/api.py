@@ -23,7 +23,7 @@ from . import _native
 
 __all__ = [
     "BlockDiagonalMask", "BlockDiagonalCausalMask", "memory_efficient_attention",
-    "attention_packed", "attention_paged", "MeaError",
+    "attention_packed", "attention_paged", "attention_backward_packed", "MeaError",
 ]
 
 
@@ -258,6 +258,89 @@ def attention_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
     return (out, lse) if return_lse else out
 
 
+def attention_backward_packed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                              lse: torch.Tensor, dout: torch.Tensor, seqstart_q: torch.Tensor,
+                              seqstart_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int, *,
+                              causal: bool = False, alibi_slopes: Optional[torch.Tensor] = None,
+                              scale: Optional[float] = None, dq: Optional[torch.Tensor] = None,
+                              dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
+                              workspace: Optional[torch.Tensor] = None,
+                              stream: Optional[torch.cuda.Stream] = None):
+    """Gradients of the packed attention: the arguments of the forward call
+    (q, k, v, offsets, masks, slopes, scale), its ``out`` and ``lse``, and the
+    upstream gradient ``dout`` (shaped like ``out``).  Returns ``(dq, dk, dv)``
+    shaped like q, k and v."""
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("packed q, k, v must be [tokens, heads, D]")
+    Tq, Hq, D = q.shape
+    Tk, Hkv, Dk = k.shape
+    if Dk != D or tuple(v.shape) != (Tk, Hkv, D):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    if tuple(out.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape):
+        raise ValueError("out and dout must be shaped like q")
+    if tuple(lse.shape) != (Hq, Tq) or lse.dtype != torch.float32:
+        raise ValueError(f"lse must be float32 [{Hq}, {Tq}]")
+    if not (q.dtype == k.dtype == v.dtype == out.dtype == dout.dtype):
+        raise TypeError("q, k, v, out and dout must share a dtype")
+    dev = q.device
+    if dev.type != "cuda" or any(t.device != dev for t in (k, v, out, lse, dout, seqstart_q, seqstart_k)):
+        raise ValueError("all tensors must be on the same GPU")
+    q, k, v, out, lse, dout = (t.contiguous() for t in (q, k, v, out, lse, dout))
+    if seqstart_q.dtype != torch.int32 or seqstart_k.dtype != torch.int32:
+        raise TypeError("seqstart tensors must be int32")
+    num_seqs = seqstart_q.numel() - 1
+    if seqstart_k.numel() != num_seqs + 1:
+        raise ValueError("seqstart_q and seqstart_k differ in length")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    slopes = None
+    if alibi_slopes is not None:
+        slopes = alibi_slopes.to(device=dev, dtype=torch.float32).contiguous()
+        if slopes.numel() != Hq:
+            raise ValueError(f"alibi_slopes needs {Hq} values (one per query head)")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    scale = float(np.float32(scale))
+    ws_bytes = _native.mea_bwd_workspace_size(num_seqs, Tq, Tk, Hq, Hkv, D)
+    if ws_bytes > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        st = _native.mea_bwd(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+            _ptr(seqstart_q), _ptr(seqstart_k), num_seqs, Tq, Tk, int(max_seqlen_q), int(max_seqlen_k),
+            Hq, Hkv, D, _dtype_code(q.dtype), int(bool(causal)), _ptr(slopes), scale,
+            _ptr(workspace) if ws_bytes > 0 else None, ws_bytes, stream.cuda_stream)
+    if st != _native.MEA_OK:
+        raise MeaError(st, _native.mea_last_error())
+    return dq, dk, dv
+
+
+class _PackedAttention(torch.autograd.Function):
+    """Autograd node of the packed attention: forward through ``mea_fwd``
+    (keeping out and lse), backward through ``mea_bwd``."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, seqstart_q, seqstart_k, max_seqlen_q, max_seqlen_k, causal, slopes, scale):
+        out, lse = attention_packed(q, k, v, seqstart_q, seqstart_k, max_seqlen_q, max_seqlen_k,
+                                    causal=causal, alibi_slopes=slopes, scale=scale, return_lse=True)
+        ctx.save_for_backward(q, k, v, out, lse, seqstart_q, seqstart_k)
+        ctx.meta = (max_seqlen_q, max_seqlen_k, causal, slopes, scale)
+        ctx.mark_non_differentiable(lse)
+        return out, lse
+
+    @staticmethod
+    def backward(ctx, dout, _dlse):
+        q, k, v, out, lse, seqstart_q, seqstart_k = ctx.saved_tensors
+        max_seqlen_q, max_seqlen_k, causal, slopes, scale = ctx.meta
+        dq, dk, dv = attention_backward_packed(q, k, v, out, lse, dout.contiguous(), seqstart_q, seqstart_k,
+                                               max_seqlen_q, max_seqlen_k, causal=causal,
+                                               alibi_slopes=slopes, scale=scale)
+        return dq, dk, dv, None, None, None, None, None, None, None
+
+
 def _kv_heads_bmghk(k: torch.Tensor, hq: int) -> torch.Tensor:
     """[B, M, G, Hk, K] key/value tensor with Hk == 1 (or broadcast along that
     axis) -> [B, M, G, K]; Hk == hq (one K/V head per query head) -> [B, M, G*hq, K]."""
@@ -284,7 +367,9 @@ def memory_efficient_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
     and the token axis is the packed sequences.  ``alibi_slopes`` (one per
     query head, in the flattened head order) adds -slope * |i - j| with
     sequence-local positions.  Returns a tensor shaped like ``q`` (and the
-    log-sum-exp ``[Hq_total, B*M]`` float32 if ``return_lse``).
+    log-sum-exp ``[Hq_total, B*M]`` float32 if ``return_lse``).  Differentiable
+    in q, k and v: when any of them requires grad, the backward runs the HIP
+    backward kernels (``mea_bwd``).
     """
     if q.dim() == 5:
         B, M, G, Hg, K = q.shape
@@ -316,6 +401,11 @@ def memory_efficient_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
                              f"tensors have {M} / {Mk}")
         mask = attn_bias
     ssq, ssk = mask.seqstart_tensors(q.device)
+    if torch.is_grad_enabled() and (q.requires_grad or k.requires_grad or v.requires_grad):
+        out, lse = _PackedAttention.apply(qp.contiguous(), kp.contiguous(), vp.contiguous(), ssq, ssk,
+                                          mask.max_seqlen_q, mask.max_seqlen_kv, mask.causal,
+                                          alibi_slopes, scale)
+        return (out.view(q.shape), lse) if return_lse else out.view(q.shape)
     res = attention_packed(qp, kp, vp, ssq, ssk, mask.max_seqlen_q, mask.max_seqlen_kv,
                            causal=mask.causal, alibi_slopes=alibi_slopes, scale=scale,
                            return_lse=return_lse)

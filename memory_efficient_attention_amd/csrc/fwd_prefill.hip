@@ -43,6 +43,7 @@
 // one sequence's K/V at the same time share one XCD's L2.
 #include "mea_common.h"
 #include "mea_launch.h"
+#include "mea_tiles.h"
 
 namespace mea {
 
@@ -64,38 +65,6 @@ struct PfLayout {
   static constexpr int kLoads = kBytes / (kThreads * 16);
   static constexpr int vLoads = vBytes / (kThreads * 16);
 };
-
-// Position of 16-byte chunk c of K row r inside the row: rows that 16 lanes
-// read together land on 16 different bank groups.
-template <int D>
-__device__ __forceinline__ int k_pos(int r, int c) {
-  if constexpr (D == 128) return c ^ (r & 15);
-  else return c ^ ((r >> 1) & 7);
-}
-
-// Byte offset of keys 8c..8c+7 of feature row r in a V^T image / LDS tile
-// (rows of 64 keys = 128 bytes; two rows share a 256-byte bank line).
-__device__ __forceinline__ int vt_off(int r, int c) { return r * 128 + 16 * (c ^ ((r >> 1) & 7)); }
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-// Instruction order for a block of N LDS fragment reads feeding N matrix
-// products: three reads ahead, then one product and one read in turn, so a
-// product's operand has had three products' time to arrive and only a few
-// fragments are live at once.
-template <int N>
-__device__ __forceinline__ void interleave_reads_and_products() {
-  constexpr int kAhead = 3;
-  __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);  // DS reads
-#pragma unroll
-  for (int i = 0; i < N - kAhead; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
-}
 
 }  // namespace
 
@@ -454,30 +423,8 @@ __global__ __launch_bounds__(kVtThreads) void vt_images_kernel(FwdArgs a) {
     vrs = rows_rsrc(a.v + ((size_t)sk0 * a.Hkv + g) * D, (uint32_t)(Lk - 1) * rs_bytes + D * 2);
     row0 = (uint32_t)(i * BN);
   }
-  u32x4 r[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k)
-    r[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                         vrs, (row0 + 4 * kq + k) * rs_bytes + cv * 16u, 0, 0));
-  if constexpr (BF16) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) r[k][w] = bf16x2_to_f16x2(r[k][w]);
-  }
   uint8_t* img = reinterpret_cast<uint8_t*>(a.ws_vt + ((size_t)((sk0 / BN) + b + i) * a.Hkv + g) * (D * BN));
-  // word w of r[k] holds features 2w (low) and 2w+1 (high) of key 4kq + k
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    u32x2 even, odd;
-    even[0] = __builtin_amdgcn_perm(r[1][w], r[0][w], 0x05040100u);
-    even[1] = __builtin_amdgcn_perm(r[3][w], r[2][w], 0x05040100u);
-    odd[0] = __builtin_amdgcn_perm(r[1][w], r[0][w], 0x07060302u);
-    odd[1] = __builtin_amdgcn_perm(r[3][w], r[2][w], 0x07060302u);
-    const int row = 8 * cv + 2 * w;
-    *(u32x2*)(img + vt_off(row, kq / 2) + 8 * (kq % 2)) = even;
-    *(u32x2*)(img + vt_off(row + 1, kq / 2) + 8 * (kq % 2)) = odd;
-  }
+  write_tile_image<D, BF16>(vrs, row0, rs_bytes, img, kq, cv);
 #endif
 }
 

@@ -1,4 +1,4 @@
-// C ABI of the attention forward: argument validation, path choice, launch.
+// C ABI of the attention forward and backward: argument validation, path choice, launch.
 // The contract (layouts, ownership, errors) is documented in include/mea.h.
 #include "mea.h"
 
@@ -201,6 +201,129 @@ mea_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, fl
   return MEA_OK;
 }
 
+// Backward workspace, each part 256-byte aligned: lse2 and Dsum [Hq, total_q]
+// float32; Q^T and dO^T images (total_q / 64 + num_seqs slots per query head,
+// as for the forward's V^T images); K^T images (total_k / 64 + num_seqs slots
+// per key/value head).
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+struct BwdWs {
+  size_t lse2, dsum, qt, dot, kt, total;
+};
+
+BwdWs bwd_ws_layout(int32_t num_seqs, int32_t total_q, int32_t total_k, int32_t Hq, int32_t Hkv, int32_t D) {
+  BwdWs w{};
+  const size_t rows = total_q > 0 ? align256((size_t)Hq * (size_t)total_q * sizeof(float)) : 0;
+  const size_t qimg = total_q > 0 ? align256(((size_t)total_q / mea::kBwImg + (size_t)num_seqs) * (size_t)Hq *
+                                             (size_t)D * mea::kBwImg * 2)
+                                  : 0;
+  const size_t kimg = total_k > 0 ? align256(((size_t)total_k / mea::kBwImg + (size_t)num_seqs) * (size_t)Hkv *
+                                             (size_t)D * mea::kBwImg * 2)
+                                  : 0;
+  w.lse2 = 0;
+  w.dsum = rows;
+  w.qt = 2 * rows;
+  w.dot = 2 * rows + qimg;
+  w.kt = 2 * rows + 2 * qimg;
+  w.total = 2 * rows + 2 * qimg + kimg;
+  return w;
+}
+
+mea_status_t bwd_impl(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                      const void* dout, void* dq, void* dk, void* dv, const int32_t* seqstart_q,
+                      const int32_t* seqstart_k, int32_t num_seqs, int32_t total_q, int32_t total_k,
+                      int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq, int32_t Hkv, int32_t D,
+                      mea_dtype_t dtype, int32_t causal, const float* alibi_slopes, float scale,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || lse == nullptr || dout == nullptr)
+    return fail(MEA_ERR_INVALID, "q, k, v, out, lse and dout must be non-NULL device pointers");
+  if (dq == nullptr || dk == nullptr || dv == nullptr)
+    return fail(MEA_ERR_INVALID, "dq, dk and dv must be non-NULL device pointers");
+  if (seqstart_q == nullptr || seqstart_k == nullptr)
+    return fail(MEA_ERR_INVALID, "seqstart_q and seqstart_k must be non-NULL device pointers");
+  if (num_seqs < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+    return fail(MEA_ERR_INVALID, "negative size (num_seqs=%d total_q=%d total_k=%d max_seqlen_q=%d max_seqlen_k=%d)",
+                num_seqs, total_q, total_k, max_seqlen_q, max_seqlen_k);
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
+    return fail(MEA_ERR_INVALID, "need Hq > 0, Hkv > 0 and Hq %% Hkv == 0 (Hq=%d Hkv=%d)", Hq, Hkv);
+  if (causal != 0 && causal != 1) return fail(MEA_ERR_INVALID, "causal must be 0 or 1 (got %d)", causal);
+  if (total_q > 0 && max_seqlen_q == 0)
+    return fail(MEA_ERR_INVALID, "total_q=%d > 0 but max_seqlen_q == 0", total_q);
+  if (total_k > 0 && max_seqlen_k == 0)
+    return fail(MEA_ERR_INVALID, "total_k=%d > 0 but max_seqlen_k == 0", total_k);
+  if (D != 64 && D != 128) return fail(MEA_ERR_UNSUPPORTED, "head dimension D=%d is not 64 or 128", D);
+  if (dtype != MEA_F16 && dtype != MEA_BF16) return fail(MEA_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(MEA_ERR_UNSUPPORTED, "scale must be finite and > 0 (got %g)", (double)scale);
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(dout, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+    return fail(MEA_ERR_UNSUPPORTED, "q, k, v, out, dout, dq, dk and dv must be 16-byte aligned");
+  if (!aligned(lse, 4) || (alibi_slopes != nullptr && !aligned(alibi_slopes, 4)) || !aligned(seqstart_q, 4) ||
+      !aligned(seqstart_k, 4))
+    return fail(MEA_ERR_UNSUPPORTED, "lse, alibi_slopes and seqstart arrays must be 4-byte aligned");
+  if (num_seqs > 65535) return fail(MEA_ERR_UNSUPPORTED, "num_seqs=%d exceeds 65535", num_seqs);
+  // one sequence's rows (and tile images) are addressed with 32-bit byte offsets
+  if (((long long)max_seqlen_k + mea::kBwImg) * Hkv * D * 2 >= (1ll << 31))
+    return fail(MEA_ERR_UNSUPPORTED, "(max_seqlen_k + 64) * Hkv * D * 2 bytes must stay below 2^31");
+  if (((long long)max_seqlen_q + mea::kBwImg) * Hq * D * 2 >= (1ll << 31))
+    return fail(MEA_ERR_UNSUPPORTED, "(max_seqlen_q + 64) * Hq * D * 2 bytes must stay below 2^31");
+  if ((long long)max_seqlen_q / mea::kBwImg + 1 > 65535 || (long long)max_seqlen_k / mea::kBwImg + 1 > 65535)
+    return fail(MEA_ERR_UNSUPPORTED, "a sequence needs more than 65535 tiles of 64 rows");
+  if (num_seqs == 0 || (total_q == 0 && total_k == 0)) return MEA_OK;
+
+  const BwdWs lay = bwd_ws_layout(num_seqs, total_q, total_k, Hq, Hkv, D);
+  if (lay.total > 0 && (workspace == nullptr || workspace_bytes < lay.total))
+    return fail(MEA_ERR_INVALID, "workspace of %zu bytes is smaller than the %zu bytes required", workspace_bytes,
+                lay.total);
+  if (lay.total > 0 && !aligned(workspace, 256)) return fail(MEA_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+
+  mea::BwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.out = static_cast<const uint16_t*>(out);
+  a.lse = lse;
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.dq = static_cast<uint16_t*>(dq);
+  a.dk = static_cast<uint16_t*>(dk);
+  a.dv = static_cast<uint16_t*>(dv);
+  a.seqstart_q = seqstart_q;
+  a.seqstart_k = seqstart_k;
+  a.slopes = alibi_slopes;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  a.ws_lse2 = reinterpret_cast<float*>(ws + lay.lse2);
+  a.ws_dsum = reinterpret_cast<float*>(ws + lay.dsum);
+  a.ws_qt = reinterpret_cast<uint16_t*>(ws + lay.qt);
+  a.ws_dot = reinterpret_cast<uint16_t*>(ws + lay.dot);
+  a.ws_kt = reinterpret_cast<uint16_t*>(ws + lay.kt);
+  a.scale = scale;
+  a.scale_log2 = scale * mea::kLog2e;
+  a.num_seqs = num_seqs;
+  a.total_q = total_q;
+  a.total_k = total_k;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.group = Hq / Hkv;
+  const long long kv_tiles = ((long long)max_seqlen_k + mea::kBwKeys - 1) / mea::kBwKeys;
+  const long long kv_items = (long long)Hkv * num_seqs * kv_tiles;
+  a.heads_per_wg = gcd_int(a.group, mea::kBwWaves);
+  a.head_slices = a.group / a.heads_per_wg;
+  const int bt = 32 * (mea::kBwWaves / a.heads_per_wg);
+  const long long q_tiles = ((long long)max_seqlen_q + bt - 1) / bt;
+  const long long q_items = (long long)Hkv * a.head_slices * num_seqs * q_tiles;
+  if (kv_items > (1ll << 31) - 8 || q_items > (1ll << 31) - 8)
+    return fail(MEA_ERR_UNSUPPORTED, "backward work items exceed the grid limit");
+  a.kv_tiles = (int32_t)kv_tiles;
+  a.kv_items = (int32_t)kv_items;
+  a.q_tiles = (int32_t)q_tiles;
+  a.q_items = (int32_t)q_items;
+  const hipError_t err = mea::launch_backward(a, D, dtype == MEA_BF16, causal != 0, alibi_slopes != nullptr,
+                                              max_seqlen_q, max_seqlen_k, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(MEA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+  return MEA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -239,6 +362,25 @@ mea_status_t mea_fwd_paged(const void* q, const void* k_cache, const void* v_cac
   return fwd_impl(q, k_cache, v_cache, out, lse, seqstart_q, seqstart_k, num_seqs, total_q, total_k,
                   max_seqlen_q, max_seqlen_k, Hq, Hkv, D, dtype, causal, alibi_slopes, scale, workspace,
                   workspace_bytes, stream, 0, false, &paged);
+}
+
+mea_status_t mea_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv, const int32_t* seqstart_q,
+                     const int32_t* seqstart_k, int32_t num_seqs, int32_t total_q, int32_t total_k,
+                     int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq, int32_t Hkv, int32_t D,
+                     mea_dtype_t dtype, int32_t causal, const float* alibi_slopes, float scale, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  return bwd_impl(q, k, v, out, lse, dout, dq, dk, dv, seqstart_q, seqstart_k, num_seqs, total_q, total_k,
+                  max_seqlen_q, max_seqlen_k, Hq, Hkv, D, dtype, causal, alibi_slopes, scale, workspace,
+                  workspace_bytes, stream);
+}
+
+size_t mea_bwd_workspace_size(int32_t num_seqs, int32_t total_q, int32_t total_k, int32_t Hq, int32_t Hkv,
+                              int32_t D) {
+  if (num_seqs <= 0 || total_q < 0 || total_k < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 ||
+      (D != 64 && D != 128))
+    return 0;
+  return bwd_ws_layout(num_seqs, total_q, total_k, Hq, Hkv, D).total;
 }
 
 size_t mea_fwd_workspace_size(int32_t num_seqs, int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k,

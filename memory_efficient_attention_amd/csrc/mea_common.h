@@ -51,6 +51,41 @@ struct FwdArgs {
   int32_t pf_items;          // prefill: head slices * num_seqs * pf_max_tiles
 };
 
+// Everything a backward launch needs; passed by value as the kernel argument.
+struct BwdArgs {
+  const uint16_t* q;         // [total_q, Hq, D]
+  const uint16_t* k;         // [total_k, Hkv, D]
+  const uint16_t* v;         // [total_k, Hkv, D]
+  const uint16_t* out;       // [total_q, Hq, D] forward output
+  const float* lse;          // [Hq, total_q] forward log-sum-exp (natural log)
+  const uint16_t* dout;      // [total_q, Hq, D] gradient of the output
+  uint16_t* dq;              // [total_q, Hq, D]
+  uint16_t* dk;              // [total_k, Hkv, D]
+  uint16_t* dv;              // [total_k, Hkv, D]
+  const int32_t* seqstart_q; // [num_seqs + 1]
+  const int32_t* seqstart_k; // [num_seqs + 1]
+  const float* slopes;       // [Hq] or nullptr
+  float* ws_lse2;            // [Hq, total_q] lse * log2(e); +inf for a row with no key
+  float* ws_dsum;            // [Hq, total_q] rowsum(dO * O)
+  uint16_t* ws_qt;           // Q^T tile images, one [D][64] per (64-row tile of a sequence, query head)
+  uint16_t* ws_dot;          // dO^T tile images, same slots
+  uint16_t* ws_kt;           // K^T tile images, one [D][64] per (64-key tile of a sequence, key/value head)
+  float scale;
+  float scale_log2;          // scale * log2(e)
+  int32_t num_seqs;
+  int32_t total_q;
+  int32_t total_k;
+  int32_t Hq;
+  int32_t Hkv;
+  int32_t group;             // Hq / Hkv
+  int32_t kv_tiles;          // dK/dV: key tiles of the longest sequence
+  int32_t kv_items;          // dK/dV: Hkv * num_seqs * kv_tiles
+  int32_t heads_per_wg;      // dQ: query heads of one group served per workgroup
+  int32_t head_slices;       // dQ: group / heads_per_wg
+  int32_t q_tiles;           // dQ: query tiles of the longest sequence
+  int32_t q_items;           // dQ: Hkv * head_slices * num_seqs * q_tiles
+};
+
 // 32x32x16 matrix-core products, float32 accumulate.  Lane l holds row (or
 // column) l % 32 of a 32 x 16 operand and the 8 consecutive k-values 8*(l/32)..+7;
 // the accumulator register r of lane l is element (8*(r/4) + 4*(l/32) + r%4, l%32).

@@ -1,0 +1,96 @@
+// LDS tile layouts and staging helpers shared by the prefill forward and the
+// backward kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include "mea_common.h"
+
+namespace mea {
+
+// Position of 16-byte chunk c of row r inside a row-major [rows][D] LDS tile
+// (rows of D half-precision values): the rows that 16 lanes read together
+// land on 16 different bank groups.  An involution in c for every r, so the
+// same function maps a position to its chunk and a chunk to its position.
+template <int D>
+__device__ __forceinline__ int k_pos(int r, int c) {
+  if constexpr (D == 128) return c ^ (r & 15);
+  else return c ^ ((r >> 1) & 7);
+}
+
+// Byte offset of columns 8c..8c+7 of row r in a transposed [D][64] tile image
+// (rows of 64 half-precision values = 128 bytes; two rows share a 256-byte
+// bank line).  The same layout is used in HBM and in LDS.
+__device__ __forceinline__ int vt_off(int r, int c) { return r * 128 + 16 * (c ^ ((r >> 1) & 7)); }
+
+// A raw buffer resource over `bytes` bytes from `base`: loads past the end
+// return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base, uint32_t bytes) {
+  return buf_rsrc(base, bytes);
+}
+
+// Direct HBM -> LDS loads: lane l's 16 (or 4) bytes land at lds + l * 16 (or 4).
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, void* lds, uint32_t voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void load_lds4(__amdgpu_buffer_rsrc_t rs, void* lds, uint32_t voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 4, voff, soff, 0, 0);
+}
+
+// s_waitcnt immediate: at most n vector-memory loads outstanding, the other
+// counters unchecked (vmcnt is split over bits 3:0 and 15:14).
+__device__ __forceinline__ constexpr int vmcnt_at_most(int n) {
+  return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14);
+}
+
+// Instruction order for a block of N LDS fragment reads feeding N matrix
+// products: three reads ahead, then one product and one read in turn, so a
+// product's operand has had three products' time to arrive and only a few
+// fragments are live at once.
+template <int N>
+__device__ __forceinline__ void interleave_reads_and_products() {
+  constexpr int kAhead = 3;
+  __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);  // DS reads
+#pragma unroll
+  for (int i = 0; i < N - kAhead; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
+}
+
+// One thread's share of writing a transposed tile image: rows row0 + 4kq ..
+// row0 + 4kq + 3 (kq < 16) and columns 8cv .. 8cv + 7 (cv < D / 8) of a
+// 64-row tile, read through `rs` (row stride rs_bytes; rows past the
+// resource's end read zeros), land in the [D][64] image at `img` (vt_off
+// layout).  TO_F16: the values are bfloat16 and are re-encoded as IEEE halves.
+template <int D, bool TO_F16>
+__device__ __forceinline__ void write_tile_image(__amdgpu_buffer_rsrc_t rs, uint32_t row0, uint32_t rs_bytes,
+                                                 uint8_t* img, int kq, int cv) {
+  u32x4 r[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    r[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                         rs, (row0 + 4 * kq + k) * rs_bytes + cv * 16u, 0, 0));
+  if constexpr (TO_F16) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) r[k][w] = bf16x2_to_f16x2(r[k][w]);
+  }
+  // word w of r[k] holds columns 2w (low) and 2w+1 (high) of row 4kq + k
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    u32x2 even, odd;
+    even[0] = __builtin_amdgcn_perm(r[1][w], r[0][w], 0x05040100u);
+    even[1] = __builtin_amdgcn_perm(r[3][w], r[2][w], 0x05040100u);
+    odd[0] = __builtin_amdgcn_perm(r[1][w], r[0][w], 0x07060302u);
+    odd[1] = __builtin_amdgcn_perm(r[3][w], r[2][w], 0x07060302u);
+    const int row = 8 * cv + 2 * w;
+    *(u32x2*)(img + vt_off(row, kq / 2) + 8 * (kq % 2)) = even;
+    *(u32x2*)(img + vt_off(row + 1, kq / 2) + 8 * (kq % 2)) = odd;
+  }
+}
+
+}  // namespace mea

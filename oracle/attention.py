@@ -168,10 +168,11 @@ def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: 
     """Gradients of sum(out * dout) with respect to q, k and v, for the
     forward that ``attention_forward`` computes.
 
-    The pages time the backward pass of the same attention and train with it
-    ([P2]: forward and backward timing; the training loop of [P1]); they give
-    no formulas, so this is the derivative of the definition written out by
-    the chain rule, per sequence b and query head h with g = h // (Hq / Hkv):
+    The pages time the backward pass of the same attention beside the
+    forward ([P2], the performance comparison of xFormers against standard
+    attention) and train a GPT-style model with it; they give no formulas, so
+    this is the derivative of the definition written out by the chain rule,
+    per sequence b and query head h with g = h // (Hq / Hkv):
       P   = softmax weights of the forward (zero rows where no key is allowed)
       dV_g += P^T dO_h                          (out = P V)
       dP  = dO_h V_g^T

@@ -78,3 +78,51 @@ def compare_rows(out_gpu: torch.Tensor, lse_gpu: torch.Tensor, inp: Inputs,
     go = torch.stack([out_gpu[t, h] for t, h in rows])
     gl = torch.stack([lse_gpu[h, t] for t, h in rows])
     return compare(go, gl, ro, rl, inp.dtype, what)
+
+
+# Backward tolerance.  Q K^T and dO V^T run in the input precision with
+# float32 accumulation; P and dS are rounded to the input precision (unit
+# roundoff u: 2^-11 for fp16, 2^-8 for bf16) before the second products, and
+# dq, dk, dv are rounded once more on output, so each element carries a few u
+# of relative error on its largest terms.  The bound is 4 u of the largest
+# reference magnitude of that gradient, plus 1e-6 absolute for all-zero ones.
+GRAD_TOL_REL = {"fp16": 4 * 2.0 ** -11, "bf16": 4 * 2.0 ** -8}
+
+
+def run_gpu_backward(inp: Inputs, dout: torch.Tensor, dev: Optional[dict] = None):
+    """Forward (out, lse) then backward through the HIP library; dq, dk, dv
+    are pre-filled with NaN so that any row the kernels fail to write shows up."""
+    from memory_efficient_attention_amd import attention_backward_packed, attention_packed
+    d = dev or to_device(inp)
+    out, lse = attention_packed(d["q"], d["k"], d["v"], d["seqstart_q"], d["seqstart_k"],
+                                inp.max_seqlen_q, inp.max_seqlen_k, causal=inp.causal,
+                                alibi_slopes=d["slopes"], scale=inp.scale, return_lse=True)
+    nan = float("nan")
+    dq = torch.full_like(d["q"], nan)
+    dk = torch.full_like(d["k"], nan)
+    dv = torch.full_like(d["v"], nan)
+    attention_backward_packed(d["q"], d["k"], d["v"], out, lse, dout.to(d["q"].device), d["seqstart_q"],
+                              d["seqstart_k"], inp.max_seqlen_q, inp.max_seqlen_k, causal=inp.causal,
+                              alibi_slopes=d["slopes"], scale=inp.scale, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    return dq.cpu(), dk.cpu(), dv.cpu()
+
+
+def oracle_backward(inp: Inputs, dout: torch.Tensor):
+    return oracle.attention_backward(inp.q, inp.k, inp.v, dout, inp.seqstart_q, inp.seqstart_k,
+                                     causal=inp.causal, alibi_slopes=inp.alibi_slopes, scale=inp.scale)
+
+
+def compare_grads(got, ref, dtype: str, what: str = "") -> dict:
+    """Assert parity of (dq, dk, dv) with the oracle's; returns error figures."""
+    res = {}
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        assert g.shape == r.shape, (what, name, g.shape, r.shape)
+        gd = g.double()
+        assert not torch.isnan(gd).any(), f"{what}: NaN in {name} (unwritten or invalid rows)"
+        scale = r.abs().max().item() if r.numel() else 0.0
+        tol = GRAD_TOL_REL[dtype] * scale + 1e-6
+        err = (gd - r).abs().max().item() if r.numel() else 0.0
+        res[name] = (err, scale)
+        assert err <= tol, f"{what}: {name} error {err:.3e} > {tol:.3e} (max |ref| {scale:.3e})"
+    return res

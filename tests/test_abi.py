@@ -48,7 +48,7 @@ def test_every_kernel_stub_is_defined():
 
 
 def test_version_and_strings():
-    assert _native.mea_abi_version() == 3
+    assert _native.mea_abi_version() == 4
     for st in range(4):
         assert _native.mea_status_string(st).startswith("MEA_")
     assert "unknown" in _native.mea_status_string(99)
@@ -169,3 +169,65 @@ def test_workspace_size():
     for T, Hq, h in [(1000, 1, 1), (8 * 4096, 64, 8), (200 * 32768, 64, 8), (3 * 77, 4, 2)]:
         c = _native.mea_default_chunk_keys(T, Hq, h)
         assert c % 32 == 0 and c >= 128
+
+
+def call_bwd(**kw):
+    a = dict(q=P, k=P, v=P, out=P, lse=P, dout=P, dq=P, dk=P, dv=P, seqstart_q=P, seqstart_k=P,
+             num_seqs=4, total_q=365, total_k=365, max_seqlen_q=200, max_seqlen_k=200, Hq=8, Hkv=2, D=64,
+             dtype=MEA_BF16, causal=1, alibi_slopes=None, scale=0.125, workspace=P,
+             workspace_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return _native.mea_bwd(**a)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(lse=None), MEA_ERR_INVALID, "non-NULL"),
+    (dict(dout=None), MEA_ERR_INVALID, "non-NULL"),
+    (dict(out=None), MEA_ERR_INVALID, "non-NULL"),
+    (dict(dk=None), MEA_ERR_INVALID, "dq, dk and dv"),
+    (dict(seqstart_q=None), MEA_ERR_INVALID, "seqstart"),
+    (dict(total_q=-1), MEA_ERR_INVALID, "negative"),
+    (dict(Hq=8, Hkv=3), MEA_ERR_INVALID, "Hq % Hkv"),
+    (dict(causal=3), MEA_ERR_INVALID, "causal"),
+    (dict(max_seqlen_q=0), MEA_ERR_INVALID, "max_seqlen_q == 0"),
+    (dict(max_seqlen_k=0), MEA_ERR_INVALID, "max_seqlen_k == 0"),
+    (dict(D=32), MEA_ERR_UNSUPPORTED, "D=32"),
+    (dict(dtype=5), MEA_ERR_UNSUPPORTED, "dtype"),
+    (dict(scale=0.0), MEA_ERR_UNSUPPORTED, "scale"),
+    (dict(dv=P + 4), MEA_ERR_UNSUPPORTED, "16-byte"),
+    (dict(dout=P + 2), MEA_ERR_UNSUPPORTED, "16-byte"),
+    (dict(lse=P + 1), MEA_ERR_UNSUPPORTED, "4-byte"),
+    (dict(num_seqs=70000), MEA_ERR_UNSUPPORTED, "65535"),
+    (dict(max_seqlen_q=1 << 20, Hq=8, D=128), MEA_ERR_UNSUPPORTED, "2^31"),
+    (dict(max_seqlen_k=1 << 22, Hkv=2, D=128), MEA_ERR_UNSUPPORTED, "2^31"),
+    (dict(workspace=None, workspace_bytes=0), MEA_ERR_INVALID, "workspace"),
+    (dict(workspace_bytes=1000), MEA_ERR_INVALID, "workspace"),
+    (dict(workspace=P + 16), MEA_ERR_UNSUPPORTED, "256-byte"),
+])
+def test_bwd_rejected_before_launch(kw, status, needle):
+    assert call_bwd(**kw) == status
+    assert needle in _native.mea_last_error()
+
+
+@pytest.mark.parametrize("kw", [dict(num_seqs=0), dict(total_q=0, total_k=0, max_seqlen_q=0, max_seqlen_k=0)])
+def test_bwd_empty_problem_is_a_noop(kw):
+    assert call_bwd(**kw) == MEA_OK
+
+
+def test_bwd_workspace_size():
+    ws = _native.mea_bwd_workspace_size
+
+    def al(x):
+        return -(-x // 256) * 256
+
+    # row terms (2 x float32 [Hq, total_q]), Q^T and dO^T images, K^T images
+    assert ws(4, 365, 365, 8, 2, 64) == (2 * al(8 * 365 * 4) + 2 * al((365 // 64 + 4) * 8 * 64 * 128)
+                                         + al((365 // 64 + 4) * 2 * 64 * 128))
+    assert ws(64, 137663, 137663, 32, 8, 128) == (2 * al(32 * 137663 * 4)
+                                                  + 2 * (137663 // 64 + 64) * 32 * 128 * 128
+                                                  + (137663 // 64 + 64) * 8 * 128 * 128)
+    assert ws(4, 0, 365, 8, 2, 64) == al((365 // 64 + 4) * 2 * 64 * 128)   # keys only: K^T images
+    assert ws(4, 365, 0, 8, 2, 64) == 2 * al(8 * 365 * 4) + 2 * al((365 // 64 + 4) * 8 * 64 * 128)
+    assert ws(0, 10, 10, 8, 2, 64) == 0
+    assert ws(4, 365, 365, 8, 3, 64) == 0
+    assert ws(4, 365, 365, 8, 2, 96) == 0
