@@ -1,5 +1,5 @@
 #!/usr/bin/env python3
-"""Benchmark of the attention forward hot path on one MI355X.
+"""Benchmark of the attention hot path on one MI355X.
 
 One step = one pass of the whole path over one batch of synthetic inputs:
   1. packed causal GQA prefill: 64 sequences with lengths U[128, 4096] from
@@ -18,8 +18,10 @@ figures (GB/s of algorithmic bytes Q + K + V + O + LSE) are in ``decode``.
 ``decode.roofline`` the decode launches against HBM bandwidth, and
 ``cpu_baseline`` times the CPU float64 oracle on a bounded sample of the
 prefill workload.  Outside the step, ``prefill_alibi`` times the prefill
-workload with ALiBi and ``decode_paged`` the decode workload with K/V in a
-paged cache (pages of 64 keys in a shuffled order, through mea_fwd_paged).
+workload with ALiBi, ``decode_paged`` the decode workload with K/V in a
+paged cache (pages of 64 keys in a shuffled order, through mea_fwd_paged),
+and ``backward`` the prefill workload's gradients (mea_bwd, dq/dk/dv from a
+seeded dO) at 2.5x the forward's unmasked FLOPs (five products against two).
 """
 from __future__ import annotations
 
@@ -152,6 +154,40 @@ class PagedCall:
             raise RuntimeError(f"mea_fwd_paged: {self.native.mea_status_string(st)}: {self.native.mea_last_error()}")
 
 
+class BwdCall:
+    """Pre-bound backward launch (mea_bwd) of one workload: out and lse come
+    from one forward call at set-up, dO is seeded N(0, 1)."""
+
+    def __init__(self, fwd_call, dev, seed):
+        import torch
+        from mea_workloads import random_dout
+        inp = fwd_call.inp
+        fwd_call(torch.cuda.current_stream(dev))
+        self.f = fwd_call
+        self.inp = inp
+        self.dout = random_dout(seed, inp).to(dev)
+        self.dq, self.dk, self.dv = (torch.empty_like(x) for x in (self.f.q, self.f.k, self.f.v))
+        self.native = fwd_call.native
+        self.ws_bytes = self.native.mea_bwd_workspace_size(len(inp.seqlens_q), inp.total_q, inp.total_k, inp.Hq,
+                                                           inp.Hkv, inp.D)
+        self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    def __call__(self, stream):
+        inp, f = self.inp, self.f
+        st = self.native.mea_bwd(
+            f.q.data_ptr(), f.k.data_ptr(), f.v.data_ptr(), f.out.data_ptr(), f.lse.data_ptr(),
+            self.dout.data_ptr(), self.dq.data_ptr(), self.dk.data_ptr(), self.dv.data_ptr(),
+            f.ssq.data_ptr(), f.ssk.data_ptr(), len(inp.seqlens_q), inp.total_q, inp.total_k,
+            inp.max_seqlen_q, inp.max_seqlen_k, inp.Hq, inp.Hkv, inp.D, f.dtype, int(inp.causal),
+            None if f.slopes is None else f.slopes.data_ptr(), inp.scale,
+            self.ws.data_ptr() if self.ws_bytes else None, self.ws_bytes, stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"mea_bwd: {self.native.mea_status_string(st)}: {self.native.mea_last_error()}")
+
+
+BWD_GEMMS = 2.5   # backward algorithmic FLOPs / forward's: Q K^T, dO V^T, P^T dO, dS K, dS^T Q vs Q K^T, P V
+
+
 def time_calls(call, stream, reps):
     """Average ms of `reps` back-to-back calls, HIP events on the launch stream."""
     import torch
@@ -224,9 +260,11 @@ def run_part(args, dev):
                           "ms": round(ms, 4), "gbs": round(2 * COPY_BYTES / (ms * 1e-3) / 1e9, 1)}),
               flush=True)
         return
-    name = PREFILL if args.part == "prefill" else DECODE
+    name = PREFILL if args.part in ("prefill", "backward") else DECODE
     if args.part == "decode_paged":
         call = PagedCall(generate(name, seed=args.seed), dev, PAGE_SIZE)
+    elif args.part == "backward":
+        call = BwdCall(Call(generate(name, seed=args.seed), dev), dev, args.seed)
     else:
         call = Call(generate(name, seed=args.seed), dev)
     stream = torch.cuda.current_stream(dev)
@@ -245,6 +283,8 @@ def run_part(args, dev):
         res["page_size"] = PAGE_SIZE
     if args.part == "prefill":
         res["tflops"] = round(unmasked_flops(call.inp) / (ms * 1e-3) / 1e12, 2)
+    elif args.part == "backward":
+        res["tflops"] = round(BWD_GEMMS * unmasked_flops(call.inp) / (ms * 1e-3) / 1e12, 2)
     else:
         res["gbs"] = round(algorithmic_bytes(call.inp) / (ms * 1e-3) / 1e9, 1)
     print(json.dumps(res), flush=True)
@@ -260,7 +300,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-alibi-variant", action="store_true")
     ap.add_argument("--no-paged-variant", action="store_true")
-    ap.add_argument("--part", choices=["all", "prefill", "decode", "decode_paged", "copy"], default="all",
+    ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--part", choices=["all", "prefill", "decode", "decode_paged", "backward", "copy"],
+                    default="all",
                     help="run only one half of the step, or the calibration copy (for profiling); "
                          "the JSON line is for 'all'")
     args = ap.parse_args()
@@ -291,6 +333,9 @@ def main():
     dec_paged = None
     if not args.no_paged_variant:
         dec_paged = PagedCall(dec, dev, PAGE_SIZE)
+    bwd_call = None
+    if not args.no_backward:
+        bwd_call = BwdCall(Call(pre, dev), dev, args.seed)
     torch.cuda.synchronize()
     print(f"[bench] inputs generated and resident in HBM in {time.perf_counter() - t_gen:.1f} s",
           file=sys.stderr, flush=True)
@@ -344,6 +389,18 @@ def main():
         paged_res = {"page_size": PAGE_SIZE, "ms": round(pms, 4), "value": round(pgb, 1), "unit": "GB/s",
                      "frac": round(pgb / PEAK_HBM_GBS, 4)}
 
+    bwd_res = None
+    if bwd_call is not None:  # the prefill workload's gradients (dq, dk, dv) from a seeded dO
+        bms = time_calls(bwd_call, stream, max(3, K // 3))
+        btf = BWD_GEMMS * pre_flops / (bms * 1e-3) / 1e12
+        bwd_res = {"ms": round(bms, 4), "value": round(btf, 2), "unit": "TFLOP/s",
+                   "roofline": {"bound": "mfma", "achieved": round(btf, 2), "peak": PEAK_MFMA_BF16_TFLOPS,
+                                "unit": "TFLOP/s", "frac": round(btf / PEAK_MFMA_BF16_TFLOPS, 4),
+                                "traffic": None,
+                                "kernel": "mea_bwd call: prep + images + bwd_dkdv_kernel + bwd_dq_kernel "
+                                          "<128,bf16,causal>"},
+                   "algorithmic_flops": int(BWD_GEMMS * pre_flops)}
+
     traffic_pre = measured_traffic("fwd_prefill")
     traffic_dec = measured_traffic("fwd_decode")
     line = {
@@ -384,6 +441,7 @@ def main():
                          "kernel": "fwd_decode_partial_kernel + fwd_decode_combine_kernel"},
         },
         "prefill_alibi": alibi_res,
+        "backward": bwd_res,
         "decode_paged": paged_res,
         "cpu_baseline": None,
     }

@@ -239,9 +239,8 @@ MEA_EXPORT size_t mea_fwd_workspace_size(int32_t num_seqs, int32_t total_k, int3
  * total_q > 0 with max_seqlen_q == 0 or total_k > 0 with max_seqlen_k == 0;
  * a workspace smaller than required.  MEA_ERR_UNSUPPORTED for D not 64/128,
  * an unknown dtype, a non-finite or non-positive scale, misalignment,
- * num_seqs > 65535, (max_seqlen + 64) * heads * D * 2 >= 2^31 for q or k,
- * or more than 65535 tiles of 64 rows in one sequence.  num_seqs == 0, or
- * total_q == total_k == 0, is a no-op returning MEA_OK.
+ * num_seqs > 65535, or max_seqlen * heads * D * 2 >= 2^31 for q or k.
+ * num_seqs == 0, or total_q == total_k == 0, is a no-op returning MEA_OK.
  *
  * Numerics: S = q k^T and dP = dout v^T run on the matrix cores in the input
  * dtype with float32 accumulation; P and dS are float32 and are rounded to the
@@ -258,11 +257,9 @@ MEA_EXPORT mea_status_t mea_bwd(const void* q, const void* k, const void* v, con
 
 /*
  * mea_bwd_workspace_size -- bytes of workspace mea_bwd needs (0 for arguments
- * it would reject).  Pure host function.  Four parts, each rounded up to a
- * multiple of 256 bytes: 2 x Hq * total_q * 4 (float32 row terms) when
- * total_q > 0; 2 x (total_q / 64 + num_seqs) * Hq * D * 128 (transposed
- * tiles of q and dout) when total_q > 0; (total_k / 64 + num_seqs) * Hkv * D
- * * 128 (transposed tiles of k) when total_k > 0.
+ * it would reject).  Pure host function: 2 x Hq * total_q * 4, each half
+ * rounded up to a multiple of 256 bytes (float32 per-row terms: the
+ * log-sum-exp in log2 units and rowsum(dout * out)); 0 when total_q == 0.
  */
 MEA_EXPORT size_t mea_bwd_workspace_size(int32_t num_seqs, int32_t total_q, int32_t total_k, int32_t Hq,
                                          int32_t Hkv, int32_t D);

@@ -15,27 +15,27 @@
 //   prep     per (query row, head): Dsum from O and dO in float32, and the
 //            log-sum-exp in log2 units (+inf for a row with no allowed key,
 //            so that its weights come out as 0);
-//   images   transposed [D][64] tile images of Q, dO (per 64-row tile of a
-//            sequence and query head) and of K (per 64-key tile and
-//            key/value head), in the LDS layout, so that operands that enter
-//            a product along their row axis load as 16-byte rows;
-//   dK/dV    a workgroup owns 128 keys of one key/value head (32 per wave,
-//            with their dK^T and dV^T accumulators and the K and V operands in
-//            registers) and walks the 64-row query tiles of every query head
-//            of the group that can see them (causal: rows from the key tile's
-//            diagonal on).  Per tile, with Q and dO rows and their images
-//            staged in LDS:
+//   dK/dV    a workgroup of 8 waves owns 128 keys of one key/value head: K
+//            and V rows sit in LDS for the whole walk, each wave accumulates
+//            dK^T and dV^T of 32 keys in registers, and the two groups of 4
+//            waves take the two 32-row halves of every 64-row query tile of
+//            every query head of the group that can see the keys (causal:
+//            rows from the key tile's diagonal on).  Per tile, with the Q and
+//            dO rows staged in LDS:
 //              S = Q K^T, dP = dO V^T        query rows fed in key_of_row
 //                                            order, so a lane's registers hold
 //                                            two runs of 8 consecutive rows
 //              P, dS                         float32, per element
 //              dV^T += dO^T P, dK^T += Q^T dS  P and dS taken straight from
-//                                            the registers as the k-operand;
-//            no atomics: the group's query heads are summed in registers;
-//   dQ       a workgroup owns 32-row chunks of one or more query heads of a
-//            group (as in the forward), Q and dO in registers, and walks
-//            64-key tiles staged in LDS (K rows, V rows, K^T image):
-//              S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T.
+//                                            the registers as the k-operand,
+//                                            dO^T and Q^T read from the same
+//                                            row tiles by LDS transpose loads;
+//            the two groups' partial sums meet in LDS at the end; no atomics;
+//   dQ       a workgroup of 8 waves owns 32-row chunks of one or more query
+//            heads of a group (as in the forward), Q and dO in registers, and
+//            walks 64-key tiles of K and V rows staged in LDS:
+//              S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T
+//            with K^T read from the K rows by transpose loads.
 // Products run in the input precision (P and dS are rounded to it) with
 // float32 accumulation.
 #include "mea_common.h"
@@ -47,31 +47,32 @@ namespace mea {
 namespace {
 
 constexpr int kThreads = 64 * kBwWaves;
-constexpr int kAuxThreads = 256;  // prep and image kernels
+constexpr int kAuxThreads = 256;  // prep kernel
 
 template <int D>
 struct DkvLayout {
+  static constexpr int kvBytes = kBwKeys * D * 2;           // K or V rows [128][D], k_pos swizzle
   static constexpr int rowBytes = kBwRows * D * 2;          // Q or dO rows [64][D], k_pos swizzle
-  static constexpr int imgBytes = D * kBwImg * 2;           // Q^T or dO^T image [D][64]
-  static constexpr int offQ = 0;
+  static constexpr int offK = 0;
+  static constexpr int offV = kvBytes;
+  static constexpr int offStage = 2 * kvBytes;
+  static constexpr int offQ = 0;                            // within a stage buffer
   static constexpr int offDO = rowBytes;
-  static constexpr int offQT = 2 * rowBytes;
-  static constexpr int offDOT = 2 * rowBytes + imgBytes;
-  static constexpr int offL = 2 * rowBytes + 2 * imgBytes;  // lse2[64], then Dsum[64] (float32)
-  static constexpr int bufBytes = offL + 2 * kBwRows * 4;
+  static constexpr int offL = 2 * rowBytes;                 // lse2[64], then Dsum[64] (float32)
+  static constexpr int stageBytes = offL + 2 * kBwRows * 4;
+  static constexpr int bytes = offStage + 2 * stageBytes;
   static constexpr int chunks = D / 8;                      // 16-byte chunks per row
   static constexpr int rowsPerKB = 1024 / (D * 2);          // rows per 1 KB direct-load block
-  static constexpr int loads = rowBytes / (kThreads * 16);  // 1 KB blocks per wave for each tile
+  static constexpr int kvLoads = kvBytes / (kThreads * 16); // 1 KB blocks per wave for K (and for V)
+  static constexpr int loads = rowBytes / (kThreads * 16);  // 1 KB blocks per wave for Q (and for dO)
 };
 
 template <int D>
 struct DqLayout {
   static constexpr int rowBytes = kBwKeyTile * D * 2;       // K or V rows [64][D], k_pos swizzle
-  static constexpr int imgBytes = D * kBwImg * 2;           // K^T image [D][64]
   static constexpr int offK = 0;
   static constexpr int offV = rowBytes;
-  static constexpr int offKT = 2 * rowBytes;
-  static constexpr int bufBytes = 2 * rowBytes + imgBytes;
+  static constexpr int bufBytes = 2 * rowBytes;
   static constexpr int chunks = D / 8;
   static constexpr int rowsPerKB = 1024 / (D * 2);
   static constexpr int loads = rowBytes / (kThreads * 16);
@@ -151,37 +152,17 @@ __global__ __launch_bounds__(kAuxThreads) void bwd_prep_kernel(BwdArgs a) {
   }
 }
 
-// ---------------------------------------------------------------------------- images
-// Rows 64 i .. 64 i + 63 of sequence b, head h of src [T, H, D] become the
-// [D][64] image at slot (seqstart[b] / 64 + b + i) * H + h of dst (rows past
-// the sequence's end are zero).
-template <int D>
-__global__ __launch_bounds__(kAuxThreads) void bwd_images_kernel(const uint16_t* src, uint16_t* dst,
-                                                                 const int32_t* seqstart, int H) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  const int h = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
-  const int s0 = seqstart[b], L = seqstart[b + 1] - s0;
-  if (i * kBwImg >= L) return;
-  const int tid = threadIdx.x;
-  const int kq = tid % (kBwImg / 4), cv = tid / (kBwImg / 4);
-  if (cv >= D / 8) return;
-  const uint32_t rs_bytes = (uint32_t)H * D * 2;
-  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(src + ((size_t)s0 * H + h) * D, (uint32_t)(L - 1) * rs_bytes + D * 2);
-  uint8_t* img = reinterpret_cast<uint8_t*>(dst + ((size_t)(s0 / kBwImg + b + i) * H + h) * (D * kBwImg));
-  write_tile_image<D, false>(rs, (uint32_t)(i * kBwImg), rs_bytes, img, kq, cv);
-#endif
-}
-
 // ---------------------------------------------------------------------------- dK, dV
 template <int D, bool BF16, bool CAUSAL, bool ALIBI>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using L = DkvLayout<D>;
   constexpr int KS = D / 16;  // k-steps of S = Q K^T
   constexpr int ND = D / 32;  // 32-feature blocks of dK^T, dV^T
-  constexpr int kStageBytes = kBwWaves * 2 * 32 * (D + 8) * 2;
-  constexpr int kSmemBytes = 2 * L::bufBytes > kStageBytes ? 2 * L::bufBytes : kStageBytes;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmemBytes];
+  constexpr int kPartBytes = kBwWaves * 32 * D * 4;      // one fp32 accumulator set per wave
+  constexpr int kStageOut = kBwWaves * 32 * (D + 8) * 2;  // one [32][D + 8] output tile per wave
+  static_assert(kPartBytes <= L::bytes && kStageOut <= L::bytes, "LDS reuse");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[L::bytes];
 
   // ---- work item (XCD-aware remap): key tile kt of sequence b, key/value head g
   const int per_xcd = (int)gridDim.x >> 3;
@@ -199,27 +180,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave / kBwGroupWaves;  // which 32-row half of each query tile
+  const int wk = wave % kBwGroupWaves;   // which 32-key block
   const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-  const int wkey0 = kt0 + 32 * wave;  // first key of this wave
+  const int wkey0 = kt0 + 32 * wk;  // first key of this wave
   const int my_key = wkey0 + l32;
 
-  // K and V as the k-operands of S = Q K^T and dP = dO V^T: lane holds key
-  // my_key, features 16 s + 8 hi .. + 7 (zero past the sequence's end)
-  u32x4 kf[KS], vf[KS];
-  {
-    const bool valid = my_key < Lk;
-    const size_t base = ((size_t)(sk0 + my_key) * a.Hkv + g) * D + 8 * hi;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-      if (valid) {
-        x = *(const u32x4*)(a.k + base + 16 * s);
-        y = *(const u32x4*)(a.v + base + 16 * s);
-      }
-      kf[s] = x;
-      vf[s] = y;
-    }
-  }
   f32x16 dk[ND], dv[ND];
 #pragma unroll
   for (int d = 0; d < ND; ++d) {
@@ -233,110 +199,113 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int nqt = Lq > q_first ? (Lq + kBwRows - 1) / kBwRows - qb0 : 0;
   const int nst = nqt * a.group;  // stages: (query tile, query head of the group)
 
-  // ---- staging: Q, dO rows of the sequence (all heads; rows past the end read
-  // zeros) and the images of the sequence's tiles
+  // ---- staging: K and V rows of the 128 keys once; Q and dO rows of the
+  // sequence (all heads) per stage; rows past a sequence's end read zeros
+  const uint32_t rs_k = (uint32_t)a.Hkv * D * 2;
+  const uint32_t kv_bytes = (uint32_t)(Lk - kt0 - 1) * rs_k + D * 2;
+  const size_t kv_first = ((size_t)(sk0 + kt0) * a.Hkv + g) * D;
+  const __amdgpu_buffer_rsrc_t krs = buf_rsrc(a.k + kv_first, kv_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = buf_rsrc(a.v + kv_first, kv_bytes);
   const uint32_t rs_q = (uint32_t)a.Hq * D * 2;
   const __amdgpu_buffer_rsrc_t qrs = buf_rsrc(a.q + (size_t)sq0 * a.Hq * D, (uint32_t)Lq * rs_q);
   const __amdgpu_buffer_rsrc_t dors = buf_rsrc(a.dout + (size_t)sq0 * a.Hq * D, (uint32_t)Lq * rs_q);
-  const int ntq = (Lq + kBwImg - 1) / kBwImg;
-  const size_t img0 = ((size_t)(sq0 / kBwImg) + b) * a.Hq * (D * kBwImg);
-  const uint32_t img_bytes = (uint32_t)ntq * a.Hq * L::imgBytes;
-  const __amdgpu_buffer_rsrc_t qtrs = buf_rsrc(a.ws_qt + img0, img_bytes);
-  const __amdgpu_buffer_rsrc_t dotrs = buf_rsrc(a.ws_dot + img0, img_bytes);
-  uint32_t row_voff[L::loads];
-#pragma unroll
-  for (int i = 0; i < L::loads; ++i) {
-    const int blk = i * kBwWaves + wave;
+  auto row_voff = [&](int blk, uint32_t rs) {
     const int r = blk * L::rowsPerKB + lane / L::chunks;
-    row_voff[i] = (uint32_t)r * rs_q + (uint32_t)k_pos<D>(r, lane % L::chunks) * 16u;
+    return (uint32_t)r * rs + (uint32_t)k_pos<D>(r, lane % L::chunks) * 16u;
+  };
+  if (nst > 0) {
+#pragma unroll
+    for (int i = 0; i < L::kvLoads; ++i) {
+      const int blk = i * kBwWaves + wave;
+      load_lds16(krs, smem + L::offK + blk * 1024, row_voff(blk, rs_k), 0);
+      load_lds16(vrs, smem + L::offV + blk * 1024, row_voff(blk, rs_k), 0);
+    }
   }
 
   auto issue = [&](int st) {
     const int hh = st % a.group, qb = qb0 + st / a.group;
     const int h = g * a.group + hh;
-    uint8_t* buf = smem + (st & 1) * L::bufBytes;
+    uint8_t* buf = smem + L::offStage + (st & 1) * L::stageBytes;
     if (wave < 2) {  // issued first: the count-based wait below may only over-wait for it
       const float* src = (wave == 0 ? a.ws_lse2 : a.ws_dsum) + (size_t)h * a.total_q + sq0;
       load_lds4(buf_rsrc(src, (uint32_t)Lq * 4), buf + L::offL + wave * (kBwRows * 4), (uint32_t)lane * 4,
                 qb * kBwRows * 4);
     }
     const int rsoff = qb * kBwRows * (int)rs_q + h * D * 2;
-    const int isoff = (qb * a.Hq + h) * L::imgBytes;
 #pragma unroll
     for (int i = 0; i < L::loads; ++i) {
       const int blk = i * kBwWaves + wave;
-      load_lds16(qrs, buf + L::offQ + blk * 1024, row_voff[i], rsoff);
-      load_lds16(dors, buf + L::offDO + blk * 1024, row_voff[i], rsoff);
-      load_lds16(qtrs, buf + L::offQT + blk * 1024, (uint32_t)(blk * 1024 + lane * 16), isoff);
-      load_lds16(dotrs, buf + L::offDOT + blk * 1024, (uint32_t)(blk * 1024 + lane * 16), isoff);
+      load_lds16(qrs, buf + L::offQ + blk * 1024, row_voff(blk, rs_q), rsoff);
+      load_lds16(dors, buf + L::offDO + blk * 1024, row_voff(blk, rs_q), rsoff);
     }
   };
 
   const float c = a.scale_log2;
+  const int sb = grp;  // this wave's 32-row half of every stage
   auto compute = [&](int st) {
     const int hh = st % a.group, qb = qb0 + st / a.group;
     const int h = g * a.group + hh;
-    const uint8_t* buf = smem + (st & 1) * L::bufBytes;
+    const uint8_t* buf = smem + L::offStage + (st & 1) * L::stageBytes;
     float slope2 = 0.f;
     if constexpr (ALIBI) slope2 = a.slopes[h] * kLog2e;
     const int kd0 = my_key - (qb * kBwRows + off);  // key position minus the stage's first query position
-    const bool need_mask = CAUSAL && (wkey0 + 31 > qb * kBwRows + off);
+    const bool need_mask = CAUSAL && (wkey0 + 31 > qb * kBwRows + 32 * sb + off);
+    f32x16 s = f32x16{}, dp = f32x16{};
+    const int rr = 32 * sb + key_of_row(l32);  // query row fed to A-row l32
+    const int kr = 32 * wk + l32;              // key row of this lane's K and V operands
 #pragma unroll
-    for (int sb = 0; sb < kBwRows / 32; ++sb) {
-      f32x16 s = f32x16{}, dp = f32x16{};
-      const int rr = 32 * sb + key_of_row(l32);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int at = rr * (D * 2) + k_pos<D>(rr, 2 * ks + hi) * 16;
-        const u32x4 qa = *(const u32x4*)(buf + L::offQ + at);
-        const u32x4 da = *(const u32x4*)(buf + L::offDO + at);
-        s = mfma_32x32x16<BF16>(qa, kf[ks], s);
-        dp = mfma_32x32x16<BF16>(da, vf[ks], dp);
-      }
-      // register r holds stage row 32 sb + key_of_reg(r, hi)
-      const float* lrow = reinterpret_cast<const float*>(buf + L::offL) + 32 * sb + 8 * hi;
-      const float* drow = lrow + kBwRows;
-      u32x4 pf[2], dsf[2];
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float p[2], ds[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int ro = 16 * ((r + e) / 8) + (r + e) % 8;  // key_of_reg(r + e, hi) - 8 hi
-          const int dist = kd0 - (32 * sb + 8 * hi + ro);     // key position - query position
-          float x = __builtin_fmaf(s[r + e], c, -lrow[ro]);
-          if constexpr (ALIBI) x = __builtin_fmaf(-slope2, __builtin_fabsf((float)dist), x);
-          float pe = fast_exp2(x);
-          if constexpr (CAUSAL) {
-            if (need_mask && dist > 0) pe = 0.f;
-          }
-          p[e] = pe;
-          ds[e] = pe * (dp[r + e] - drow[ro]);
-        }
-        pf[r / 8][(r % 8) / 2] = pack_out_x2<BF16>(p[0], p[1]);
-        dsf[r / 8][(r % 8) / 2] = pack_out_x2<BF16>(ds[0], ds[1]);
-      }
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int d = 0; d < ND; ++d) {
-          const int at = vt_off(32 * d + l32, 4 * sb + 2 * kk + hi);
-          const u32x4 oa = *(const u32x4*)(buf + L::offDOT + at);
-          const u32x4 qa = *(const u32x4*)(buf + L::offQT + at);
-          dv[d] = mfma_32x32x16<BF16>(oa, pf[kk], dv[d]);
-          dk[d] = mfma_32x32x16<BF16>(qa, dsf[kk], dk[d]);
-        }
+    for (int ks = 0; ks < KS; ++ks) {
+      const int at = rr * (D * 2) + k_pos<D>(rr, 2 * ks + hi) * 16;
+      const int kat = kr * (D * 2) + k_pos<D>(kr, 2 * ks + hi) * 16;
+      const u32x4 qa = *(const u32x4*)(buf + L::offQ + at);
+      const u32x4 kb = *(const u32x4*)(smem + L::offK + kat);
+      const u32x4 da = *(const u32x4*)(buf + L::offDO + at);
+      const u32x4 vb = *(const u32x4*)(smem + L::offV + kat);
+      s = mfma_32x32x16<BF16>(qa, kb, s);
+      dp = mfma_32x32x16<BF16>(da, vb, dp);
     }
+    // register r holds stage row 32 sb + key_of_reg(r, hi)
+    const float* lrow = reinterpret_cast<const float*>(buf + L::offL) + 32 * sb + 8 * hi;
+    const float* drow = lrow + kBwRows;
+    u32x4 pf[2], dsf[2];
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      float p[2], ds[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int ro = 16 * ((r + e) / 8) + (r + e) % 8;  // key_of_reg(r + e, hi) - 8 hi
+        const int dist = kd0 - (32 * sb + 8 * hi + ro);     // key position - query position
+        float x = __builtin_fmaf(s[r + e], c, -lrow[ro]);
+        if constexpr (ALIBI) x = __builtin_fmaf(-slope2, __builtin_fabsf((float)dist), x);
+        float pe = fast_exp2(x);
+        if constexpr (CAUSAL) {
+          if (need_mask && dist > 0) pe = 0.f;
+        }
+        p[e] = pe;
+        ds[e] = pe * (dp[r + e] - drow[ro]);
+      }
+      pf[r / 8][(r % 8) / 2] = pack_out_x2<BF16>(p[0], p[1]);
+      dsf[r / 8][(r % 8) / 2] = pack_out_x2<BF16>(ds[0], ds[1]);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        const u32x4 oa = read_rows_transposed<D>(buf + L::offDO, 32 * sb + 16 * kk, 32 * d, lane);
+        const u32x4 qa = read_rows_transposed<D>(buf + L::offQ, 32 * sb + 16 * kk, 32 * d, lane);
+        dv[d] = mfma_32x32x16<BF16>(oa, pf[kk], dv[d]);
+        dk[d] = mfma_32x32x16<BF16>(qa, dsf[kk], dk[d]);
+      }
   };
 
   // ---- double-buffered stages: tile st + 1 loads while tile st is computed
-  constexpr int kWaitNext = vmcnt_at_most(4 * L::loads);
+  constexpr int kWaitNext = vmcnt_at_most(2 * L::loads);
   if (nst > 0) {
     issue(0);
     for (int st = 0; st < nst; ++st) {
       if (st + 1 < nst) {
         issue(st + 1);
-        __builtin_amdgcn_s_waitcnt(kWaitNext);  // this wave's share of tile st landed
+        __builtin_amdgcn_s_waitcnt(kWaitNext);  // this wave's share of tile st (and of K, V) landed
       } else {
         __builtin_amdgcn_s_waitcnt(0);
       }
@@ -346,23 +315,41 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     }
   }
 
-  // ---- epilogue: dK = scale dS^T Q and dV, staged through LDS as rows
-  uint16_t* tk = reinterpret_cast<uint16_t*>(smem) + wave * 2 * 32 * (D + 8);
-  uint16_t* tv = tk + 32 * (D + 8);
-  stage_rows<D, BF16>(tk, dk, a.scale, l32, hi);
-  stage_rows<D, BF16>(tv, dv, 1.f, l32, hi);
+  // ---- epilogue: the two groups' partial sums meet in LDS.  Group 0 hands
+  // its dV^T to group 1 and finishes dK; group 1 hands its dK^T to group 0 and
+  // finishes dV.  Partials are laid out [wave][block d][register r][lane].
+  float* part = reinterpret_cast<float*>(smem);
+  {
+    const f32x16* mine = grp == 0 ? dv : dk;
+    float* dst = part + (size_t)(grp * kBwGroupWaves + wk) * (ND * 16 * 64);
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dst[(d * 16 + r) * 64 + lane] = mine[d][r];
+  }
+  __syncthreads();
+  {
+    f32x16* acc = grp == 0 ? dk : dv;
+    const float* src = part + (size_t)((1 - grp) * kBwGroupWaves + wk) * (ND * 16 * 64);
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[d][r] += src[(d * 16 + r) * 64 + lane];
+  }
+  __syncthreads();
+  uint16_t* tile = reinterpret_cast<uint16_t*>(smem) + wave * 32 * (D + 8);
+  if (grp == 0) stage_rows<D, BF16>(tile, dk, a.scale, l32, hi);
+  else stage_rows<D, BF16>(tile, dv, 1.f, l32, hi);
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_wave_barrier();
   const size_t first = ((size_t)(sk0 + wkey0) * a.Hkv + g) * D;
-  const size_t stride = (size_t)a.Hkv * D;
-  store_rows<D>(tk, a.dk + first, stride, Lk - wkey0, lane);
-  store_rows<D>(tv, a.dv + first, stride, Lk - wkey0, lane);
+  store_rows<D>(tile, (grp == 0 ? a.dk : a.dv) + first, (size_t)a.Hkv * D, Lk - wkey0, lane);
 #endif
 }
 
 // ---------------------------------------------------------------------------- dQ
 template <int D, bool BF16, bool CAUSAL, bool ALIBI>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using L = DqLayout<D>;
   constexpr int KS = D / 16;
@@ -429,15 +416,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   if constexpr (CAUSAL) kv_end = min(Lk, min(t0 + BT, Lq) + off);
   const int nkt = kv_end > 0 ? (kv_end + kBwKeyTile - 1) / kBwKeyTile : 0;
 
-  // ---- staging: K and V rows of head g (rows past the end read zeros), K^T images
+  // ---- staging: K and V rows of head g (rows past the end read zeros)
   const uint32_t rs_k = (uint32_t)a.Hkv * D * 2;
   const uint32_t seq_bytes = Lk > 0 ? (uint32_t)(Lk - 1) * rs_k + D * 2 : 0u;
   const size_t head_off = ((size_t)sk0 * a.Hkv + g) * D;
   const __amdgpu_buffer_rsrc_t krs = rows_rsrc(a.k + head_off, seq_bytes);
   const __amdgpu_buffer_rsrc_t vrs = rows_rsrc(a.v + head_off, seq_bytes);
-  const int ntk = (Lk + kBwImg - 1) / kBwImg;
-  const __amdgpu_buffer_rsrc_t ktrs =
-      buf_rsrc(a.ws_kt + ((size_t)(sk0 / kBwImg) + b) * a.Hkv * (D * kBwImg), (uint32_t)ntk * a.Hkv * L::imgBytes);
   uint32_t row_voff[L::loads];
 #pragma unroll
   for (int i = 0; i < L::loads; ++i) {
@@ -449,13 +433,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   auto issue = [&](int t) {
     uint8_t* buf = smem + (t & 1) * L::bufBytes;
     const int rsoff = t * kBwKeyTile * (int)rs_k;
-    const int isoff = (t * a.Hkv + g) * L::imgBytes;
 #pragma unroll
     for (int i = 0; i < L::loads; ++i) {
       const int blk = i * kBwWaves + wave;
       load_lds16(krs, buf + L::offK + blk * 1024, row_voff[i], rsoff);
       load_lds16(vrs, buf + L::offV + blk * 1024, row_voff[i], rsoff);
-      load_lds16(ktrs, buf + L::offKT + blk * 1024, (uint32_t)(blk * 1024 + lane * 16), isoff);
     }
   };
 
@@ -468,50 +450,45 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs a) {
     const int j0 = t * kBwKeyTile;
     const int jlane = j0 + 8 * hi;  // key of register 0 in block 0
     const bool need_mask = (j0 + kBwKeyTile > Lk) || (CAUSAL && j0 + kBwKeyTile - 1 > tok0 + off);
-    f32x16 s[2], dp[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      dp[kb] = f32x16{};
-    }
+      f32x16 s = f32x16{}, dp = f32x16{};
+      const int rr = 32 * kb + key_of_row(l32);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int rr = 32 * kb + key_of_row(l32);
+      for (int ks = 0; ks < KS; ++ks) {
         const int at = rr * (D * 2) + k_pos<D>(rr, 2 * ks + hi) * 16;
         const u32x4 ka = *(const u32x4*)(buf + L::offK + at);
         const u32x4 va = *(const u32x4*)(buf + L::offV + at);
-        s[kb] = mfma_32x32x16<BF16>(ka, qf[ks], s[kb]);
-        dp[kb] = mfma_32x32x16<BF16>(va, of[ks], dp[kb]);
+        s = mfma_32x32x16<BF16>(ka, qf[ks], s);
+        dp = mfma_32x32x16<BF16>(va, of[ks], dp);
       }
-    u32x4 dsf[4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      u32x4 dsf[2];
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         float ds[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int j = jlane + 32 * kb + key_of_reg(r + e, 0);
-          float x = __builtin_fmaf(s[kb][r + e], c, -lse2);
+          float x = __builtin_fmaf(s[r + e], c, -lse2);
           if constexpr (ALIBI) x = __builtin_fmaf(-slope2, __builtin_fabsf((float)(qpos - j)), x);
           float pe = fast_exp2(x);
           if (need_mask && (j >= Lk || (CAUSAL && j > qpos))) pe = 0.f;
-          ds[e] = pe * (dp[kb][r + e] - dsum);
+          ds[e] = pe * (dp[r + e] - dsum);
         }
-        dsf[2 * kb + r / 8][(r % 8) / 2] = pack_out_x2<BF16>(ds[0], ds[1]);
+        dsf[r / 8][(r % 8) / 2] = pack_out_x2<BF16>(ds[0], ds[1]);
       }
+      // dQ^T += K^T dS^T over this block's 32 keys (two k-steps of 16)
 #pragma unroll
-    for (int ch = 0; ch < 4; ++ch)
+      for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int d = 0; d < ND; ++d) {
-        const u32x4 ka = *(const u32x4*)(buf + L::offKT + vt_off(32 * d + l32, 2 * ch + hi));
-        dq[d] = mfma_32x32x16<BF16>(ka, dsf[ch], dq[d]);
-      }
+        for (int d = 0; d < ND; ++d) {
+          const u32x4 ka = read_rows_transposed<D>(buf + L::offK, 32 * kb + 16 * kk, 32 * d, lane);
+          dq[d] = mfma_32x32x16<BF16>(ka, dsf[kk], dq[d]);
+        }
+    }
   };
 
-  constexpr int kWaitNext = vmcnt_at_most(3 * L::loads);
+  constexpr int kWaitNext = vmcnt_at_most(2 * L::loads);
   if (nkt > 0) {
     issue(0);
     for (int t = 0; t < nkt; ++t) {
@@ -555,25 +532,12 @@ hipError_t launch_main(const BwdArgs& a, hipStream_t stream) {
 }
 
 template <int D, bool BF16>
-hipError_t launch_backward_d(const BwdArgs& a, bool causal, bool alibi, int max_seqlen_q, int max_seqlen_k,
-                             hipStream_t stream) {
+hipError_t launch_backward_d(const BwdArgs& a, bool causal, bool alibi, hipStream_t stream) {
   if (a.total_q > 0) {
     constexpr int rows_per_block = kAuxThreads / (D / 8);
     const long long rows = (long long)a.total_q * a.Hq;
     hipLaunchKernelGGL((bwd_prep_kernel<D, BF16>), dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)),
                        dim3(kAuxThreads), 0, stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const dim3 qgrid(a.Hq, (max_seqlen_q + kBwImg - 1) / kBwImg, a.num_seqs);
-    hipLaunchKernelGGL((bwd_images_kernel<D>), qgrid, dim3(kAuxThreads), 0, stream, a.q, a.ws_qt, a.seqstart_q, a.Hq);
-    hipLaunchKernelGGL((bwd_images_kernel<D>), qgrid, dim3(kAuxThreads), 0, stream, a.dout, a.ws_dot, a.seqstart_q,
-                       a.Hq);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (a.total_k > 0 && max_seqlen_k > 0 && a.q_items > 0) {
-    const dim3 kgrid(a.Hkv, (max_seqlen_k + kBwImg - 1) / kBwImg, a.num_seqs);
-    hipLaunchKernelGGL((bwd_images_kernel<D>), kgrid, dim3(kAuxThreads), 0, stream, a.k, a.ws_kt, a.seqstart_k, a.Hkv);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -585,14 +549,13 @@ hipError_t launch_backward_d(const BwdArgs& a, bool causal, bool alibi, int max_
 
 }  // namespace
 
-hipError_t launch_backward(const BwdArgs& a, int D, bool bf16, bool causal, bool alibi, int max_seqlen_q,
-                           int max_seqlen_k, hipStream_t stream) {
+hipError_t launch_backward(const BwdArgs& a, int D, bool bf16, bool causal, bool alibi, hipStream_t stream) {
   if (D == 64) {
-    return bf16 ? launch_backward_d<64, true>(a, causal, alibi, max_seqlen_q, max_seqlen_k, stream)
-                : launch_backward_d<64, false>(a, causal, alibi, max_seqlen_q, max_seqlen_k, stream);
+    return bf16 ? launch_backward_d<64, true>(a, causal, alibi, stream)
+                : launch_backward_d<64, false>(a, causal, alibi, stream);
   }
-  return bf16 ? launch_backward_d<128, true>(a, causal, alibi, max_seqlen_q, max_seqlen_k, stream)
-              : launch_backward_d<128, false>(a, causal, alibi, max_seqlen_q, max_seqlen_k, stream);
+  return bf16 ? launch_backward_d<128, true>(a, causal, alibi, stream)
+              : launch_backward_d<128, false>(a, causal, alibi, stream);
 }
 
 }  // namespace mea

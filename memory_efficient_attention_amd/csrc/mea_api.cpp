@@ -201,31 +201,20 @@ mea_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, fl
   return MEA_OK;
 }
 
-// Backward workspace, each part 256-byte aligned: lse2 and Dsum [Hq, total_q]
-// float32; Q^T and dO^T images (total_q / 64 + num_seqs slots per query head,
-// as for the forward's V^T images); K^T images (total_k / 64 + num_seqs slots
-// per key/value head).
+// Backward workspace: lse2 and Dsum [Hq, total_q] float32, each part
+// 256-byte aligned.
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct BwdWs {
-  size_t lse2, dsum, qt, dot, kt, total;
+  size_t lse2, dsum, total;
 };
 
-BwdWs bwd_ws_layout(int32_t num_seqs, int32_t total_q, int32_t total_k, int32_t Hq, int32_t Hkv, int32_t D) {
+BwdWs bwd_ws_layout(int32_t total_q, int32_t Hq) {
   BwdWs w{};
   const size_t rows = total_q > 0 ? align256((size_t)Hq * (size_t)total_q * sizeof(float)) : 0;
-  const size_t qimg = total_q > 0 ? align256(((size_t)total_q / mea::kBwImg + (size_t)num_seqs) * (size_t)Hq *
-                                             (size_t)D * mea::kBwImg * 2)
-                                  : 0;
-  const size_t kimg = total_k > 0 ? align256(((size_t)total_k / mea::kBwImg + (size_t)num_seqs) * (size_t)Hkv *
-                                             (size_t)D * mea::kBwImg * 2)
-                                  : 0;
   w.lse2 = 0;
   w.dsum = rows;
-  w.qt = 2 * rows;
-  w.dot = 2 * rows + qimg;
-  w.kt = 2 * rows + 2 * qimg;
-  w.total = 2 * rows + 2 * qimg + kimg;
+  w.total = 2 * rows;
   return w;
 }
 
@@ -263,16 +252,14 @@ mea_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o
       !aligned(seqstart_k, 4))
     return fail(MEA_ERR_UNSUPPORTED, "lse, alibi_slopes and seqstart arrays must be 4-byte aligned");
   if (num_seqs > 65535) return fail(MEA_ERR_UNSUPPORTED, "num_seqs=%d exceeds 65535", num_seqs);
-  // one sequence's rows (and tile images) are addressed with 32-bit byte offsets
-  if (((long long)max_seqlen_k + mea::kBwImg) * Hkv * D * 2 >= (1ll << 31))
-    return fail(MEA_ERR_UNSUPPORTED, "(max_seqlen_k + 64) * Hkv * D * 2 bytes must stay below 2^31");
-  if (((long long)max_seqlen_q + mea::kBwImg) * Hq * D * 2 >= (1ll << 31))
-    return fail(MEA_ERR_UNSUPPORTED, "(max_seqlen_q + 64) * Hq * D * 2 bytes must stay below 2^31");
-  if ((long long)max_seqlen_q / mea::kBwImg + 1 > 65535 || (long long)max_seqlen_k / mea::kBwImg + 1 > 65535)
-    return fail(MEA_ERR_UNSUPPORTED, "a sequence needs more than 65535 tiles of 64 rows");
+  // one sequence's rows are addressed with 32-bit byte offsets
+  if ((long long)max_seqlen_k * Hkv * D * 2 >= (1ll << 31))
+    return fail(MEA_ERR_UNSUPPORTED, "max_seqlen_k * Hkv * D * 2 bytes must stay below 2^31");
+  if ((long long)max_seqlen_q * Hq * D * 2 >= (1ll << 31))
+    return fail(MEA_ERR_UNSUPPORTED, "max_seqlen_q * Hq * D * 2 bytes must stay below 2^31");
   if (num_seqs == 0 || (total_q == 0 && total_k == 0)) return MEA_OK;
 
-  const BwdWs lay = bwd_ws_layout(num_seqs, total_q, total_k, Hq, Hkv, D);
+  const BwdWs lay = bwd_ws_layout(total_q, Hq);
   if (lay.total > 0 && (workspace == nullptr || workspace_bytes < lay.total))
     return fail(MEA_ERR_INVALID, "workspace of %zu bytes is smaller than the %zu bytes required", workspace_bytes,
                 lay.total);
@@ -294,9 +281,6 @@ mea_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   a.ws_lse2 = reinterpret_cast<float*>(ws + lay.lse2);
   a.ws_dsum = reinterpret_cast<float*>(ws + lay.dsum);
-  a.ws_qt = reinterpret_cast<uint16_t*>(ws + lay.qt);
-  a.ws_dot = reinterpret_cast<uint16_t*>(ws + lay.dot);
-  a.ws_kt = reinterpret_cast<uint16_t*>(ws + lay.kt);
   a.scale = scale;
   a.scale_log2 = scale * mea::kLog2e;
   a.num_seqs = num_seqs;
@@ -319,7 +303,7 @@ mea_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o
   a.q_tiles = (int32_t)q_tiles;
   a.q_items = (int32_t)q_items;
   const hipError_t err = mea::launch_backward(a, D, dtype == MEA_BF16, causal != 0, alibi_slopes != nullptr,
-                                              max_seqlen_q, max_seqlen_k, static_cast<hipStream_t>(stream));
+                                              static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return fail(MEA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
   return MEA_OK;
 }
@@ -380,7 +364,7 @@ size_t mea_bwd_workspace_size(int32_t num_seqs, int32_t total_q, int32_t total_k
   if (num_seqs <= 0 || total_q < 0 || total_k < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 ||
       (D != 64 && D != 128))
     return 0;
-  return bwd_ws_layout(num_seqs, total_q, total_k, Hq, Hkv, D).total;
+  return bwd_ws_layout(total_q, Hq).total;
 }
 
 size_t mea_fwd_workspace_size(int32_t num_seqs, int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k,

@@ -67,9 +67,6 @@ struct BwdArgs {
   const float* slopes;       // [Hq] or nullptr
   float* ws_lse2;            // [Hq, total_q] lse * log2(e); +inf for a row with no key
   float* ws_dsum;            // [Hq, total_q] rowsum(dO * O)
-  uint16_t* ws_qt;           // Q^T tile images, one [D][64] per (64-row tile of a sequence, query head)
-  uint16_t* ws_dot;          // dO^T tile images, same slots
-  uint16_t* ws_kt;           // K^T tile images, one [D][64] per (64-key tile of a sequence, key/value head)
   float scale;
   float scale_log2;          // scale * log2(e)
   int32_t num_seqs;

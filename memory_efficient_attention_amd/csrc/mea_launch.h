@@ -24,20 +24,19 @@ constexpr int kDcMinPiece = 128;     // shortest default piece
 constexpr int kDcTargetWgs = 512;    // default: one round of 2 workgroups per CU on 256 CUs
 constexpr int kDcHeadsPerWg = 16;    // query heads of one group served per workgroup
 
-// Backward: workgroups of 4 waves.  dK/dV: a wave owns 32 keys of one
-// key/value head (128 keys per workgroup) and walks 64-row query tiles of
-// every query head of the group; dQ: a wave owns 32 query rows of one head
-// and walks 64-key tiles.
-constexpr int kBwWaves = 4;
-constexpr int kBwKeys = 32 * kBwWaves;   // keys per dK/dV workgroup
-constexpr int kBwRows = 64;              // query rows per dK/dV stage
-constexpr int kBwKeyTile = 64;           // keys per dQ stage
-constexpr int kBwImg = 64;               // rows per transposed tile image
+// Backward: workgroups of 8 waves (two groups of 4).  dK/dV: a wave owns 32
+// keys of one key/value head (128 keys per workgroup, each owned by one wave
+// of each group) and its group takes one 32-row half of every 64-row query
+// tile; dQ: a wave owns 32 query rows of one head and walks 64-key tiles.
+constexpr int kBwWaves = 8;
+constexpr int kBwGroupWaves = 4;
+constexpr int kBwKeys = 32 * kBwGroupWaves;  // keys per dK/dV workgroup
+constexpr int kBwRows = 64;                  // query rows per dK/dV stage
+constexpr int kBwKeyTile = 64;               // keys per dQ stage
 
 hipError_t launch_prefill(const FwdArgs& a, int D, bool bf16, bool causal, bool alibi,
                           int max_seqlen_k, hipStream_t stream);
 hipError_t launch_decode(const FwdArgs& a, int D, bool bf16, bool alibi, hipStream_t stream);
-hipError_t launch_backward(const BwdArgs& a, int D, bool bf16, bool causal, bool alibi, int max_seqlen_q,
-                           int max_seqlen_k, hipStream_t stream);
+hipError_t launch_backward(const BwdArgs& a, int D, bool bf16, bool causal, bool alibi, hipStream_t stream);
 
 }  // namespace mea

@@ -60,6 +60,35 @@ __device__ __forceinline__ void interleave_reads_and_products() {
   __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// The k-operand of a product whose k axis runs along the rows of a row-major
+// [rows][D] LDS tile (k_pos layout), read transposed by the gfx950 LDS
+// transpose loads: lane l receives column f0 + l % 32 of rows
+// r0 + 8 (l / 32) .. + 7 (f0 a multiple of 32, r0 a multiple of 16).
+// ds_read_b64_tr_b16 works on groups of 16 lanes: lane j of a group reads 4
+// consecutive 16-bit values, and lane i of the group receives value i % 4 of
+// lanes 4c + i / 4 for c = 0..3.  Lane j here reads columns
+// f + 4 (j % 4) .. + 3 of row r + j / 4, so lane i receives column f + i of
+// rows r .. r + 3; two such reads give the 8 rows.
+template <int D>
+__device__ __forceinline__ u32x4 read_rows_transposed(const uint8_t* tile, int r0, int f0, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int f = f0 + 16 * (g & 1) + 4 * (j & 3);
+  u32x4 res;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = r0 + 8 * (g >> 1) + 4 * h + (j >> 2);
+    const int at = r * (D * 2) + k_pos<D>(r, f >> 3) * 16 + (f & 7) * 2;
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(tile + at));
+    const u32x2 w = __builtin_bit_cast(u32x2, v);
+    res[2 * h] = w[0];
+    res[2 * h + 1] = w[1];
+  }
+  return res;
+}
+
 // One thread's share of writing a transposed tile image: rows row0 + 4kq ..
 // row0 + 4kq + 3 (kq < 16) and columns 8cv .. 8cv + 7 (cv < D / 8) of a
 // 64-row tile, read through `rs` (row stride rs_bytes; rows past the
