@@ -51,8 +51,8 @@ constexpr int kAuxThreads = 256;  // prep kernel
 
 template <int D>
 struct DkvLayout {
-  static constexpr int kvBytes = kBwKeys * D * 2;           // K or V rows [128][D], k_pos swizzle
-  static constexpr int rowBytes = kBwRows * D * 2;          // Q or dO rows [64][D], k_pos swizzle
+  static constexpr int kvBytes = kBwKeys * D * 2;           // K or V rows [128][D], kt_pos swizzle
+  static constexpr int rowBytes = kBwRows * D * 2;          // Q or dO rows [64][D], kt_pos swizzle
   static constexpr int offK = 0;
   static constexpr int offV = kvBytes;
   static constexpr int offStage = 2 * kvBytes;
@@ -60,7 +60,8 @@ struct DkvLayout {
   static constexpr int offDO = rowBytes;
   static constexpr int offL = 2 * rowBytes;                 // lse2[64], then Dsum[64] (float32)
   static constexpr int stageBytes = offL + 2 * kBwRows * 4;
-  static constexpr int bytes = offStage + 2 * stageBytes;
+  static constexpr int slots = 2;                           // stage buffers
+  static constexpr int bytes = offStage + slots * stageBytes;
   static constexpr int chunks = D / 8;                      // 16-byte chunks per row
   static constexpr int rowsPerKB = 1024 / (D * 2);          // rows per 1 KB direct-load block
   static constexpr int kvLoads = kvBytes / (kThreads * 16); // 1 KB blocks per wave for K (and for V)
@@ -69,10 +70,11 @@ struct DkvLayout {
 
 template <int D>
 struct DqLayout {
-  static constexpr int rowBytes = kBwKeyTile * D * 2;       // K or V rows [64][D], k_pos swizzle
+  static constexpr int rowBytes = kBwKeyTile * D * 2;       // K or V rows [64][D], kt_pos swizzle
   static constexpr int offK = 0;
   static constexpr int offV = rowBytes;
   static constexpr int bufBytes = 2 * rowBytes;
+  static constexpr int slots = 3;                           // ring of stage buffers
   static constexpr int chunks = D / 8;
   static constexpr int rowsPerKB = 1024 / (D * 2);
   static constexpr int loads = rowBytes / (kThreads * 16);
@@ -211,7 +213,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
   const __amdgpu_buffer_rsrc_t dors = buf_rsrc(a.dout + (size_t)sq0 * a.Hq * D, (uint32_t)Lq * rs_q);
   auto row_voff = [&](int blk, uint32_t rs) {
     const int r = blk * L::rowsPerKB + lane / L::chunks;
-    return (uint32_t)r * rs + (uint32_t)k_pos<D>(r, lane % L::chunks) * 16u;
+    return (uint32_t)r * rs + (uint32_t)kt_pos<D>(r, lane % L::chunks) * 16u;
   };
   if (nst > 0) {
 #pragma unroll
@@ -225,8 +227,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
   auto issue = [&](int st) {
     const int hh = st % a.group, qb = qb0 + st / a.group;
     const int h = g * a.group + hh;
-    uint8_t* buf = smem + L::offStage + (st & 1) * L::stageBytes;
-    if (wave < 2) {  // issued first: the count-based wait below may only over-wait for it
+    uint8_t* buf = smem + L::offStage + (st % L::slots) * L::stageBytes;
+    if (wave < 2) {
       const float* src = (wave == 0 ? a.ws_lse2 : a.ws_dsum) + (size_t)h * a.total_q + sq0;
       load_lds4(buf_rsrc(src, (uint32_t)Lq * 4), buf + L::offL + wave * (kBwRows * 4), (uint32_t)lane * 4,
                 qb * kBwRows * 4);
@@ -245,7 +247,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
   auto compute = [&](int st) {
     const int hh = st % a.group, qb = qb0 + st / a.group;
     const int h = g * a.group + hh;
-    const uint8_t* buf = smem + L::offStage + (st & 1) * L::stageBytes;
+    const uint8_t* buf = smem + L::offStage + (st % L::slots) * L::stageBytes;
     float slope2 = 0.f;
     if constexpr (ALIBI) slope2 = a.slopes[h] * kLog2e;
     const int kd0 = my_key - (qb * kBwRows + off);  // key position minus the stage's first query position
@@ -255,8 +257,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
     const int kr = 32 * wk + l32;              // key row of this lane's K and V operands
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int at = rr * (D * 2) + k_pos<D>(rr, 2 * ks + hi) * 16;
-      const int kat = kr * (D * 2) + k_pos<D>(kr, 2 * ks + hi) * 16;
+      const int at = rr * (D * 2) + kt_pos<D>(rr, 2 * ks + hi) * 16;
+      const int kat = kr * (D * 2) + kt_pos<D>(kr, 2 * ks + hi) * 16;
       const u32x4 qa = *(const u32x4*)(buf + L::offQ + at);
       const u32x4 kb = *(const u32x4*)(smem + L::offK + kat);
       const u32x4 da = *(const u32x4*)(buf + L::offDO + at);
@@ -264,7 +266,15 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
       s = mfma_32x32x16<BF16>(qa, kb, s);
       dp = mfma_32x32x16<BF16>(da, vb, dp);
     }
-    // register r holds stage row 32 sb + key_of_reg(r, hi)
+    // register r holds stage row 32 sb + key_of_reg(r, hi); key position minus
+    // query position of register r: kd0 - 32 sb - 8 hi - ro(r)
+    if constexpr (CAUSAL) {
+      if (need_mask) {  // scores of keys after the query row -> -inf, so their weights are 0
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kd0 - (32 * sb + 8 * hi + 16 * (r / 8) + r % 8) > 0) s[r] = kNegInf;
+      }
+    }
     const float* lrow = reinterpret_cast<const float*>(buf + L::offL) + 32 * sb + 8 * hi;
     const float* drow = lrow + kBwRows;
     u32x4 pf[2], dsf[2];
@@ -274,13 +284,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int ro = 16 * ((r + e) / 8) + (r + e) % 8;  // key_of_reg(r + e, hi) - 8 hi
-        const int dist = kd0 - (32 * sb + 8 * hi + ro);     // key position - query position
         float x = __builtin_fmaf(s[r + e], c, -lrow[ro]);
-        if constexpr (ALIBI) x = __builtin_fmaf(-slope2, __builtin_fabsf((float)dist), x);
-        float pe = fast_exp2(x);
-        if constexpr (CAUSAL) {
-          if (need_mask && dist > 0) pe = 0.f;
-        }
+        if constexpr (ALIBI) x = __builtin_fmaf(-slope2, __builtin_fabsf((float)(kd0 - (32 * sb + 8 * hi + ro))), x);
+        const float pe = fast_exp2(x);
         p[e] = pe;
         ds[e] = pe * (dp[r + e] - drow[ro]);
       }
@@ -298,21 +304,19 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
       }
   };
 
-  // ---- double-buffered stages: tile st + 1 loads while tile st is computed
-  constexpr int kWaitNext = vmcnt_at_most(2 * L::loads);
+  // ---- two stage buffers, one barrier per stage.  In iteration st: wait for
+  // this wave's share of tile st, barrier (every wave has its share of tile
+  // st and is done with tile st - 1, whose buffer tile st + 1 takes), request
+  // tile st + 1, compute st.
   if (nst > 0) {
     issue(0);
     for (int st = 0; st < nst; ++st) {
-      if (st + 1 < nst) {
-        issue(st + 1);
-        __builtin_amdgcn_s_waitcnt(kWaitNext);  // this wave's share of tile st (and of K, V) landed
-      } else {
-        __builtin_amdgcn_s_waitcnt(0);
-      }
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
+      if (st + 1 < nst) issue(st + 1);
       compute(st);
-      __syncthreads();  // everyone is done with buffer st & 1 before tile st + 2 refills it
     }
+    __syncthreads();  // every wave is done with the buffers before the epilogue reuses LDS
   }
 
   // ---- epilogue: the two groups' partial sums meet in LDS.  Group 0 hands
@@ -355,7 +359,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
   constexpr int KS = D / 16;
   constexpr int ND = D / 32;
   constexpr int kStageBytes = kBwWaves * 32 * (D + 8) * 2;
-  constexpr int kSmemBytes = 2 * L::bufBytes > kStageBytes ? 2 * L::bufBytes : kStageBytes;
+  constexpr int kSmemBytes = L::slots * L::bufBytes > kStageBytes ? L::slots * L::bufBytes : kStageBytes;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmemBytes];
 
   // ---- work item (XCD-aware remap): query tile of sequence b, head slice
@@ -427,11 +431,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
   for (int i = 0; i < L::loads; ++i) {
     const int blk = i * kBwWaves + wave;
     const int r = blk * L::rowsPerKB + lane / L::chunks;
-    row_voff[i] = (uint32_t)r * rs_k + (uint32_t)k_pos<D>(r, lane % L::chunks) * 16u;
+    row_voff[i] = (uint32_t)r * rs_k + (uint32_t)kt_pos<D>(r, lane % L::chunks) * 16u;
   }
 
   auto issue = [&](int t) {
-    uint8_t* buf = smem + (t & 1) * L::bufBytes;
+    uint8_t* buf = smem + (t % L::slots) * L::bufBytes;
     const int rsoff = t * kBwKeyTile * (int)rs_k;
 #pragma unroll
     for (int i = 0; i < L::loads; ++i) {
@@ -446,7 +450,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
   for (int d = 0; d < ND; ++d) dq[d] = f32x16{};
 
   auto compute = [&](int t) {
-    const uint8_t* buf = smem + (t & 1) * L::bufBytes;
+    const uint8_t* buf = smem + (t % L::slots) * L::bufBytes;
     const int j0 = t * kBwKeyTile;
     const int jlane = j0 + 8 * hi;  // key of register 0 in block 0
     const bool need_mask = (j0 + kBwKeyTile > Lk) || (CAUSAL && j0 + kBwKeyTile - 1 > tok0 + off);
@@ -456,11 +460,18 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
       const int rr = 32 * kb + key_of_row(l32);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int at = rr * (D * 2) + k_pos<D>(rr, 2 * ks + hi) * 16;
+        const int at = rr * (D * 2) + kt_pos<D>(rr, 2 * ks + hi) * 16;
         const u32x4 ka = *(const u32x4*)(buf + L::offK + at);
         const u32x4 va = *(const u32x4*)(buf + L::offV + at);
         s = mfma_32x32x16<BF16>(ka, qf[ks], s);
         dp = mfma_32x32x16<BF16>(va, of[ks], dp);
+      }
+      if (need_mask) {  // keys past the end, or after the query row -> -inf, so their weights are 0
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = jlane + 32 * kb + key_of_reg(r, 0);
+          if (j >= Lk || (CAUSAL && j > qpos)) s[r] = kNegInf;
+        }
       }
       u32x4 dsf[2];
 #pragma unroll
@@ -468,11 +479,12 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
         float ds[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          const int j = jlane + 32 * kb + key_of_reg(r + e, 0);
           float x = __builtin_fmaf(s[r + e], c, -lse2);
-          if constexpr (ALIBI) x = __builtin_fmaf(-slope2, __builtin_fabsf((float)(qpos - j)), x);
-          float pe = fast_exp2(x);
-          if (need_mask && (j >= Lk || (CAUSAL && j > qpos))) pe = 0.f;
+          if constexpr (ALIBI) {
+            const int j = jlane + 32 * kb + key_of_reg(r + e, 0);
+            x = __builtin_fmaf(-slope2, __builtin_fabsf((float)(qpos - j)), x);
+          }
+          const float pe = fast_exp2(x);
           ds[e] = pe * (dp[r + e] - dsum);
         }
         dsf[r / 8][(r % 8) / 2] = pack_out_x2<BF16>(ds[0], ds[1]);
@@ -488,20 +500,20 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
     }
   };
 
+  // ---- a ring of 3 tile buffers, tiles requested two ahead, one barrier per
+  // tile (as in the dK/dV kernel)
   constexpr int kWaitNext = vmcnt_at_most(2 * L::loads);
   if (nkt > 0) {
     issue(0);
+    if (nkt > 1) issue(1);
     for (int t = 0; t < nkt; ++t) {
-      if (t + 1 < nkt) {
-        issue(t + 1);
-        __builtin_amdgcn_s_waitcnt(kWaitNext);
-      } else {
-        __builtin_amdgcn_s_waitcnt(0);
-      }
+      if (t + 1 < nkt) __builtin_amdgcn_s_waitcnt(kWaitNext);
+      else __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
+      if (t + 2 < nkt) issue(t + 2);
       compute(t);
-      __syncthreads();
     }
+    __syncthreads();  // every wave is done with the ring before the epilogue reuses LDS
   }
 
   // ---- epilogue: dQ = scale dS K, staged through LDS as rows

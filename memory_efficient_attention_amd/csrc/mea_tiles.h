@@ -16,6 +16,20 @@ __device__ __forceinline__ int k_pos(int r, int c) {
   else return c ^ ((r >> 1) & 7);
 }
 
+// Position of 16-byte chunk c of row r in a row-major [rows][D] LDS tile that
+// is read both by rows (16 lanes: 16 consecutive rows, one chunk) and by the
+// transpose loads below (32 lanes: 4 consecutive rows x 4 consecutive chunks).
+// The chunk is XORed with a bit permutation of the row that is a bijection on
+// any 16 consecutive rows (rows) and puts the row's low two bits (D = 128: 16
+// chunks per 256-byte bank line) or bit 1 (D = 64: two rows per line) on chunk
+// bit 2 and up (transpose loads), so both patterns touch every bank once.
+// An involution in c for every r.
+template <int D>
+__device__ __forceinline__ int kt_pos(int r, int c) {
+  if constexpr (D == 128) return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
+  else return c ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
 // Byte offset of columns 8c..8c+7 of row r in a transposed [D][64] tile image
 // (rows of 64 half-precision values = 128 bytes; two rows share a 256-byte
 // bank line).  The same layout is used in HBM and in LDS.
@@ -63,7 +77,7 @@ __device__ __forceinline__ void interleave_reads_and_products() {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // The k-operand of a product whose k axis runs along the rows of a row-major
-// [rows][D] LDS tile (k_pos layout), read transposed by the gfx950 LDS
+// [rows][D] LDS tile (kt_pos layout), read transposed by the gfx950 LDS
 // transpose loads: lane l receives column f0 + l % 32 of rows
 // r0 + 8 (l / 32) .. + 7 (f0 a multiple of 32, r0 a multiple of 16).
 // ds_read_b64_tr_b16 works on groups of 16 lanes: lane j of a group reads 4
@@ -79,7 +93,7 @@ __device__ __forceinline__ u32x4 read_rows_transposed(const uint8_t* tile, int r
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int r = r0 + 8 * (g >> 1) + 4 * h + (j >> 2);
-    const int at = r * (D * 2) + k_pos<D>(r, f >> 3) * 16 + (f & 7) * 2;
+    const int at = r * (D * 2) + kt_pos<D>(r, f >> 3) * 16 + (f & 7) * 2;
     const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) s16x4*)(tile + at));
     const u32x2 w = __builtin_bit_cast(u32x2, v);
