@@ -123,12 +123,14 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, f16x2));
 }
 
-// Two float32 values to the output dtype, packed, round to nearest even.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two float32 values to the output dtype, packed, round to nearest even (one
+// v_cvt_pk_bf16_f32 or v_cvt_pk_f16_f32).
 template <bool BF16>
 __device__ __forceinline__ uint32_t pack_out_x2(float lo, float hi) {
   if constexpr (BF16) {
-    __bf16 a = (__bf16)lo, b = (__bf16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
   } else {
     return pack_f16x2(lo, hi);
   }
