@@ -41,7 +41,7 @@ PEAK_HBM_GBS = 8000.0            # HBM3E
 PREFILL = "varlen_causal_gqa_64seq_h32kv8_d128_bf16"
 DECODE = "decode_splitkv_64req_h64kv8_d128_bf16"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-KERNEL_SOURCES = ["fwd_prefill.hip", "fwd_decode.hip", "mea_common.h", "mea_launch.h"]
+KERNEL_SOURCES = ["fwd_prefill.hip", "fwd_decode.hip", "bwd.hip", "mea_common.h", "mea_launch.h", "mea_tiles.h"]
 
 
 def unmasked_flops(inp) -> int:
@@ -396,8 +396,8 @@ def main():
         bwd_res = {"ms": round(bms, 4), "value": round(btf, 2), "unit": "TFLOP/s",
                    "roofline": {"bound": "mfma", "achieved": round(btf, 2), "peak": PEAK_MFMA_BF16_TFLOPS,
                                 "unit": "TFLOP/s", "frac": round(btf / PEAK_MFMA_BF16_TFLOPS, 4),
-                                "traffic": None,
-                                "kernel": "mea_bwd call: prep + images + bwd_dkdv_kernel + bwd_dq_kernel "
+                                "traffic": measured_traffic("bwd"),
+                                "kernel": "mea_bwd call: bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel "
                                           "<128,bf16,causal>"},
                    "algorithmic_flops": int(BWD_GEMMS * pre_flops)}
 

@@ -200,6 +200,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
   const int qb0 = q_first / kBwRows;
   const int nqt = Lq > q_first ? (Lq + kBwRows - 1) / kBwRows - qb0 : 0;
   const int nst = nqt * a.group;  // stages: (query tile, query head of the group)
+  // Query tiles run from the sequence's last down to the key tile's diagonal,
+  // so that the workgroups of one sequence (consecutive work items, one XCD)
+  // start on the same tile and read the same Q and dO rows at about the same
+  // time: one fetch from HBM serves them all from the XCD's L2.
+  const int qb_last = qb0 + nqt - 1;
 
   // ---- staging: K and V rows of the 128 keys once; Q and dO rows of the
   // sequence (all heads) per stage; rows past a sequence's end read zeros
@@ -225,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
   }
 
   auto issue = [&](int st) {
-    const int hh = st % a.group, qb = qb0 + st / a.group;
+    const int hh = st % a.group, qb = qb_last - st / a.group;
     const int h = g * a.group + hh;
     uint8_t* buf = smem + L::offStage + (st % L::slots) * L::stageBytes;
     if (wave < 2) {
@@ -245,7 +250,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
   const float c = a.scale_log2;
   const int sb = grp;  // this wave's 32-row half of every stage
   auto compute = [&](int st) {
-    const int hh = st % a.group, qb = qb0 + st / a.group;
+    const int hh = st % a.group, qb = qb_last - st / a.group;
     const int h = g * a.group + hh;
     const uint8_t* buf = smem + L::offStage + (st % L::slots) * L::stageBytes;
     float slope2 = 0.f;
