@@ -33,7 +33,7 @@ import torch
 __all__ = [
     "Workload", "Inputs", "WORKLOADS", "get_workload", "generate", "random_case",
     "alibi_slopes", "seqstart_from_lengths", "sample_rows", "prefix", "PagedKV", "to_paged",
-    "random_dout",
+    "random_dout", "Fp8Inputs", "to_fp8",
 ]
 
 _DTYPES = {"fp16": torch.float16, "bf16": torch.bfloat16}
@@ -245,6 +245,37 @@ def prefix(inp: Inputs, n: int) -> Inputs:
         inp, q=inp.q[:sq[n]], k=inp.k[:sk[n]], v=inp.v[:sk[n]],
         seqstart_q=inp.seqstart_q[:n + 1].clone(), seqstart_k=inp.seqstart_k[:n + 1].clone(),
         seqlens_q=inp.seqlens_q[:n], seqlens_k=inp.seqlens_k[:n], bmghk=None)
+
+
+FP8_MAX = 448.0   # largest finite OCP e4m3 value
+
+
+@dataclasses.dataclass
+class Fp8Inputs:
+    """q, k, v of an input quantised to OCP e4m3 with one float32 scale per
+    tensor: the values meant are scale * tensor."""
+    q8: torch.Tensor           # float8_e4m3fn [Tq, Hq, D]
+    k8: torch.Tensor           # float8_e4m3fn [Tk, Hkv, D]
+    v8: torch.Tensor           # float8_e4m3fn [Tk, Hkv, D]
+    q_scale: float
+    k_scale: float
+    v_scale: float
+
+
+def _quantise(x: torch.Tensor) -> Tuple[torch.Tensor, float]:
+    """Per-tensor scale max|x| / 448 (float32), values x / scale rounded to e4m3."""
+    amax = float(x.float().abs().max()) if x.numel() else 0.0
+    scale = float(np.float32(amax / FP8_MAX)) if amax > 0 else 1.0
+    return (x.float() / scale).to(torch.float8_e4m3fn), scale
+
+
+def to_fp8(inp: Inputs) -> Fp8Inputs:
+    """The q, k, v of ``inp`` quantised to e4m3 with per-tensor scales (the
+    rest of ``inp`` -- lengths, masks, slopes, score scale -- applies as is)."""
+    q8, qs = _quantise(inp.q)
+    k8, ks = _quantise(inp.k)
+    v8, vs = _quantise(inp.v)
+    return Fp8Inputs(q8=q8, k8=k8, v8=v8, q_scale=qs, k_scale=ks, v_scale=vs)
 
 
 @dataclasses.dataclass

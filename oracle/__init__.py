@@ -13,6 +13,6 @@ passages of the pages it follows.  Every function here is pinned by
 routine) except the readings listed as "parity unpinned" in
 ``oracle.attention``'s module docstring.
 """
-from .attention import attention_backward, attention_forward, attention_rows
+from .attention import attention_backward, attention_forward, attention_forward_fp8, attention_rows
 
-__all__ = ["attention_forward", "attention_rows", "attention_backward"]
+__all__ = ["attention_forward", "attention_rows", "attention_backward", "attention_forward_fp8"]

@@ -16,6 +16,8 @@ Sources (web pages; section names as printed on them):
        5 (causal attention: implicit lower-triangular mask).
   [P3] "multi query attention代码" (cidian.kuaisou.com) -- the self-attention
        snippet: scores = Q K^T / sqrt(d_k), softmax, weighted sum of V.
+  [P4] "大模型推理加速终极指南：xformers如何让Transformer性能飙升300%"
+       (zizhi168.cn) -- section 3, mixed-precision pipeline (FP16/BF16/FP8).
   [P5] "group query attention gqa" (cidian.kuaisou.com) -- GQA-G definition
        (G groups, each sharing one K/V head; GQA-1 = MQA, GQA-H = MHA) and the
        check that SDPA with enable_gqa equals SDPA after repeat_interleave of
@@ -51,7 +53,7 @@ from typing import List, Optional, Sequence, Tuple
 
 import torch
 
-__all__ = ["attention_forward", "attention_rows", "attention_backward"]
+__all__ = ["attention_forward", "attention_rows", "attention_backward", "attention_forward_fp8"]
 
 
 def _f64(x: torch.Tensor) -> torch.Tensor:
@@ -215,3 +217,23 @@ def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: 
             dq[sq[b]:sq[b + 1], h, :] = scale * (dS @ Kg)
             dk[sk[b]:sk[b + 1], g, :] += scale * (dS.transpose(0, 1) @ Qh)
     return dq, dk, dv
+
+
+def attention_forward_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, q_scale: float,
+                          k_scale: float, v_scale: float, seqstart_q, seqstart_k, *,
+                          causal: bool = False, alibi_slopes: Optional[torch.Tensor] = None,
+                          scale: Optional[float] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The forward on 8-bit inputs with per-tensor scales.
+
+    [P4] section 3 lists FP8 among the formats of the mixed-precision attention
+    pipeline.  The tensors hold OCP e4m3 codes (torch.float8_e4m3fn; the
+    decoding is pinned against the format's definition in the tests) and the
+    values meant are scale * code: q = q_scale * q8, k = k_scale * k8,
+    v = v_scale * v8, each formed exactly in float64, then the same definition
+    as ``attention_forward``.
+    """
+    q = _f64(q8) * float(q_scale)
+    k = _f64(k8) * float(k_scale)
+    v = _f64(v8) * float(v_scale)
+    return attention_forward(q, k, v, seqstart_q, seqstart_k, causal=causal,
+                             alibi_slopes=alibi_slopes, scale=scale)
