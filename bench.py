@@ -20,8 +20,10 @@ figures (GB/s of algorithmic bytes Q + K + V + O + LSE) are in ``decode``.
 prefill workload.  Outside the step, ``prefill_alibi`` times the prefill
 workload with ALiBi, ``decode_paged`` the decode workload with K/V in a
 paged cache (pages of 64 keys in a shuffled order, through mea_fwd_paged),
-and ``backward`` the prefill workload's gradients (mea_bwd, dq/dk/dv from a
-seeded dO) at 2.5x the forward's unmasked FLOPs (five products against two).
+``backward`` the prefill workload's gradients (mea_bwd, dq/dk/dv from a
+seeded dO) at 2.5x the forward's unmasked FLOPs (five products against two),
+and ``prefill_fp8`` the prefill workload with q, k, v quantised to OCP e4m3
+(mea_fwd_fp8, per-tensor scales, bf16 output).
 """
 from __future__ import annotations
 
@@ -185,6 +187,43 @@ class BwdCall:
             raise RuntimeError(f"mea_bwd: {self.native.mea_status_string(st)}: {self.native.mea_last_error()}")
 
 
+class Fp8Call:
+    """Pre-bound launch of the fp8 forward (mea_fwd_fp8) on a workload whose
+    q, k, v are quantised to OCP e4m3 with per-tensor scales; bf16 output."""
+
+    def __init__(self, inp, dev):
+        import torch
+        from memory_efficient_attention_amd import _native
+        from mea_workloads import to_fp8
+        f = to_fp8(inp)
+        self.inp, self.f = inp, f
+        self.q, self.k, self.v = f.q8.to(dev), f.k8.to(dev), f.v8.to(dev)
+        self.ssq, self.ssk = inp.seqstart_q.to(dev), inp.seqstart_k.to(dev)
+        self.slopes = None if inp.alibi_slopes is None else inp.alibi_slopes.to(dev)
+        self.out = torch.empty((inp.total_q, inp.Hq, inp.D), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((inp.Hq, inp.total_q), dtype=torch.float32, device=dev)
+        self.ws_bytes = _native.mea_fwd_fp8_workspace_size(len(inp.seqlens_q), inp.total_k, inp.Hkv, inp.D)
+        self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=dev)
+        self.native = _native
+
+    def __call__(self, stream):
+        inp, f = self.inp, self.f
+        st = self.native.mea_fwd_fp8(
+            self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), f.q_scale, f.k_scale, f.v_scale,
+            self.out.data_ptr(), self.lse.data_ptr(), self.ssq.data_ptr(), self.ssk.data_ptr(),
+            len(inp.seqlens_q), inp.total_q, inp.total_k, inp.max_seqlen_q, inp.max_seqlen_k, inp.Hq, inp.Hkv,
+            inp.D, self.native.MEA_BF16, int(inp.causal), None if self.slopes is None else self.slopes.data_ptr(),
+            inp.scale, self.ws.data_ptr() if self.ws_bytes else None, self.ws_bytes, stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"mea_fwd_fp8: {self.native.mea_status_string(st)}: {self.native.mea_last_error()}")
+
+
+PEAK_MFMA_FP8_TFLOPS = 5033.2    # dense fp8 MFMA: twice the bf16 rate
+# fp8 forward: Q K^T on fp8 matrix cores, P V on half precision ones; its
+# roofline peak is the rate at which the two halves of the FLOPs could run
+# back to back: 1 / (0.5 / fp8 peak + 0.5 / bf16 peak)
+PEAK_FP8_FWD_TFLOPS = 1.0 / (0.5 / PEAK_MFMA_FP8_TFLOPS + 0.5 / PEAK_MFMA_BF16_TFLOPS)
+
 BWD_GEMMS = 2.5   # backward algorithmic FLOPs / forward's: Q K^T, dO V^T, P^T dO, dS K, dS^T Q vs Q K^T, P V
 
 
@@ -260,8 +299,10 @@ def run_part(args, dev):
                           "ms": round(ms, 4), "gbs": round(2 * COPY_BYTES / (ms * 1e-3) / 1e9, 1)}),
               flush=True)
         return
-    name = PREFILL if args.part in ("prefill", "backward") else DECODE
-    if args.part == "decode_paged":
+    name = PREFILL if args.part in ("prefill", "backward", "prefill_fp8") else DECODE
+    if args.part == "prefill_fp8":
+        call = Fp8Call(generate(name, seed=args.seed), dev)
+    elif args.part == "decode_paged":
         call = PagedCall(generate(name, seed=args.seed), dev, PAGE_SIZE)
     elif args.part == "backward":
         call = BwdCall(Call(generate(name, seed=args.seed), dev), dev, args.seed)
@@ -281,7 +322,7 @@ def run_part(args, dev):
     res = {"part": args.part, "workload": name, "ms": round(ms, 4)}
     if args.part == "decode_paged":
         res["page_size"] = PAGE_SIZE
-    if args.part == "prefill":
+    if args.part in ("prefill", "prefill_fp8"):
         res["tflops"] = round(unmasked_flops(call.inp) / (ms * 1e-3) / 1e12, 2)
     elif args.part == "backward":
         res["tflops"] = round(BWD_GEMMS * unmasked_flops(call.inp) / (ms * 1e-3) / 1e12, 2)
@@ -301,7 +342,9 @@ def main():
     ap.add_argument("--no-alibi-variant", action="store_true")
     ap.add_argument("--no-paged-variant", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
-    ap.add_argument("--part", choices=["all", "prefill", "decode", "decode_paged", "backward", "copy"],
+    ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--part", choices=["all", "prefill", "decode", "decode_paged", "backward", "prefill_fp8",
+                                       "copy"],
                     default="all",
                     help="run only one half of the step, or the calibration copy (for profiling); "
                          "the JSON line is for 'all'")
@@ -336,6 +379,9 @@ def main():
     bwd_call = None
     if not args.no_backward:
         bwd_call = BwdCall(Call(pre, dev), dev, args.seed)
+    fp8_call = None
+    if not args.no_fp8:
+        fp8_call = Fp8Call(pre, dev)
     torch.cuda.synchronize()
     print(f"[bench] inputs generated and resident in HBM in {time.perf_counter() - t_gen:.1f} s",
           file=sys.stderr, flush=True)
@@ -401,6 +447,17 @@ def main():
                                           "<128,bf16,causal>"},
                    "algorithmic_flops": int(BWD_GEMMS * pre_flops)}
 
+    fp8_res = None
+    if fp8_call is not None:  # the prefill workload with q, k, v in e4m3 and per-tensor scales
+        fms = time_calls(fp8_call, stream, max(5, K // 2))
+        ftf = pre_flops / (fms * 1e-3) / 1e12
+        fp8_res = {"ms": round(fms, 4), "value": round(ftf, 2), "unit": "TFLOP/s",
+                   "roofline": {"bound": "mfma", "achieved": round(ftf, 2), "peak": round(PEAK_FP8_FWD_TFLOPS, 1),
+                                "unit": "TFLOP/s", "frac": round(ftf / PEAK_FP8_FWD_TFLOPS, 4),
+                                "traffic": measured_traffic("fwd_prefill_fp8"),
+                                "kernel": "mea_fwd_fp8 call: vt_images_kernel<fp8> + fwd_prefill_kernel<128,bf16 out,"
+                                          "causal,fp8>"}}
+
     traffic_pre = measured_traffic("fwd_prefill")
     traffic_dec = measured_traffic("fwd_decode")
     line = {
@@ -442,6 +499,7 @@ def main():
         },
         "prefill_alibi": alibi_res,
         "backward": bwd_res,
+        "prefill_fp8": fp8_res,
         "decode_paged": paged_res,
         "cpu_baseline": None,
     }

@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define MEA_ABI_VERSION 4
+#define MEA_ABI_VERSION 5
 
 #if defined(__GNUC__)
 #define MEA_EXPORT __attribute__((visibility("default")))
@@ -201,6 +201,44 @@ MEA_EXPORT mea_status_t mea_fwd_paged(const void* q, const void* k_cache, const 
 MEA_EXPORT size_t mea_fwd_workspace_size(int32_t num_seqs, int32_t total_k, int32_t max_seqlen_q,
                                          int32_t max_seqlen_k, int32_t Hq, int32_t Hkv, int32_t D,
                                          int32_t chunk_keys);
+
+/*
+ * mea_fwd_fp8 -- mea_fwd with q, k and v in 8-bit floating point (OCP FP8
+ * E4M3: 1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no infinities,
+ * S.1111.111 = NaN) and one scale per tensor.  Section 3 of
+ * "大模型推理加速终极指南：xformers如何让Transformer性能飙升300%"
+ * (zizhi168.cn) names FP8 among the supported formats of the attention's
+ * mixed-precision pipeline and asks for the key steps in high precision.
+ * Computes exactly what mea_fwd computes on the values
+ *   q = q_scale * q8,  k = k_scale * k8,  v = v_scale * v8
+ * (same masks, ALiBi, GQA and lse; scale multiplies q k^T as usual).
+ * Precision: q8 k8^T runs on the fp8 matrix cores (each product exact, fp32
+ * accumulation), scaled by scale * q_scale * k_scale in fp32; the softmax is
+ * fp32; the weights enter P V as IEEE halves with v8 widened to halves
+ * (exact), fp32 accumulation; v_scale and the 1/rowsum are applied in fp32
+ * before the output is rounded to out_dtype (MEA_F16 or MEA_BF16).
+ *   q, k, v        device, bytes, layouts as for mea_fwd ([T, H, D], one byte
+ *                  per element), 16-byte aligned.
+ *   q/k/v_scale    host floats, finite and > 0.
+ *   out            device [total_q, Hq, D] of out_dtype.
+ *   D              128 only (MEA_ERR_UNSUPPORTED otherwise).
+ *   workspace      mea_fwd_fp8_workspace_size(num_seqs, total_k, Hkv, D) bytes
+ *                  (half-precision V^T tile images), 256-byte aligned.
+ * Every call, decode-shaped (max_seqlen_q == 1) ones included, runs the
+ * prefill kernel.  No paged variant.  Same ownership and errors as mea_fwd,
+ * plus MEA_ERR_UNSUPPORTED for a non-finite or non-positive scale.
+ */
+MEA_EXPORT mea_status_t mea_fwd_fp8(const void* q, const void* k, const void* v, float q_scale, float k_scale,
+                                    float v_scale, void* out, float* lse, const int32_t* seqstart_q,
+                                    const int32_t* seqstart_k, int32_t num_seqs, int32_t total_q, int32_t total_k,
+                                    int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq, int32_t Hkv, int32_t D,
+                                    mea_dtype_t out_dtype, int32_t causal, const float* alibi_slopes, float scale,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of mea_fwd_fp8: (total_k / 64 + num_seqs) * Hkv * D * 128
+ * (0 when total_k == 0 or for arguments mea_fwd_fp8 rejects).  Pure host
+ * function. */
+MEA_EXPORT size_t mea_fwd_fp8_workspace_size(int32_t num_seqs, int32_t total_k, int32_t Hkv, int32_t D);
 
 /*
  * mea_bwd -- gradients of the attention of mea_fwd: given dout = dL/dout for

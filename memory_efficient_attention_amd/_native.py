@@ -15,7 +15,7 @@ __all__ = [
     "MEA_OK", "MEA_ERR_INVALID", "MEA_ERR_UNSUPPORTED", "MEA_ERR_HIP", "MEA_F16", "MEA_BF16",
     "EXPORTED_SYMBOLS", "library_path", "load", "mea_fwd", "mea_fwd_splitkv", "mea_fwd_paged",
     "mea_fwd_workspace_size", "mea_default_chunk_keys", "mea_bwd", "mea_bwd_workspace_size",
-    "mea_status_string", "mea_last_error", "mea_abi_version",
+    "mea_fwd_fp8", "mea_fwd_fp8_workspace_size", "mea_status_string", "mea_last_error", "mea_abi_version",
 ]
 
 MEA_OK, MEA_ERR_INVALID, MEA_ERR_UNSUPPORTED, MEA_ERR_HIP = 0, 1, 2, 3
@@ -23,7 +23,8 @@ MEA_F16, MEA_BF16 = 0, 1
 
 EXPORTED_SYMBOLS = (
     "mea_fwd", "mea_fwd_splitkv", "mea_fwd_paged", "mea_fwd_workspace_size", "mea_default_chunk_keys",
-    "mea_bwd", "mea_bwd_workspace_size", "mea_status_string", "mea_last_error", "mea_abi_version",
+    "mea_bwd", "mea_bwd_workspace_size", "mea_fwd_fp8", "mea_fwd_fp8_workspace_size", "mea_status_string",
+    "mea_last_error", "mea_abi_version",
 )
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -50,6 +51,12 @@ _BWD_ARGS = [_vp, _vp, _vp, _vp, _vp, _vp,            # q k v out lse dout
              _vp, _vp, _i32, _i32, _i32, _i32, _i32,  # seqstart_q seqstart_k num_seqs total_q total_k max_q max_k
              _i32, _i32, _i32, _i32, _i32,           # Hq Hkv D dtype causal
              _vp, _f32, _vp, _sz, _vp]               # slopes scale workspace workspace_bytes stream
+
+
+_FP8_ARGS = [_vp, _vp, _vp, _f32, _f32, _f32, _vp, _vp,   # q k v q_scale k_scale v_scale out lse
+             _vp, _vp, _i32, _i32, _i32, _i32, _i32,      # seqstart_q seqstart_k num_seqs total_q total_k max_q max_k
+             _i32, _i32, _i32, _i32, _i32,                # Hq Hkv D out_dtype causal
+             _vp, _f32, _vp, _sz, _vp]                    # slopes scale workspace workspace_bytes stream
 
 
 def library_path() -> str:
@@ -82,6 +89,10 @@ def load() -> ctypes.CDLL:
         lib.mea_bwd.restype = ctypes.c_int
         lib.mea_bwd_workspace_size.argtypes = [_i32] * 6
         lib.mea_bwd_workspace_size.restype = _sz
+        lib.mea_fwd_fp8.argtypes = _FP8_ARGS
+        lib.mea_fwd_fp8.restype = ctypes.c_int
+        lib.mea_fwd_fp8_workspace_size.argtypes = [_i32] * 4
+        lib.mea_fwd_fp8_workspace_size.restype = _sz
         lib.mea_status_string.argtypes = [ctypes.c_int]
         lib.mea_status_string.restype = ctypes.c_char_p
         lib.mea_last_error.argtypes = []
@@ -138,6 +149,18 @@ def mea_bwd(q, k, v, out, lse, dout, dq, dk, dv, seqstart_q, seqstart_k, num_seq
 
 def mea_bwd_workspace_size(num_seqs, total_q, total_k, Hq, Hkv, D) -> int:
     return int(load().mea_bwd_workspace_size(num_seqs, total_q, total_k, Hq, Hkv, D))
+
+
+def mea_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, out, lse, seqstart_q, seqstart_k, num_seqs, total_q,
+                total_k, max_seqlen_q, max_seqlen_k, Hq, Hkv, D, out_dtype, causal, alibi_slopes, scale,
+                workspace, workspace_bytes, stream) -> int:
+    return load().mea_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, out, lse, seqstart_q, seqstart_k, num_seqs,
+                              total_q, total_k, max_seqlen_q, max_seqlen_k, Hq, Hkv, D, out_dtype, causal,
+                              alibi_slopes, scale, workspace, workspace_bytes, stream)
+
+
+def mea_fwd_fp8_workspace_size(num_seqs, total_k, Hkv, D) -> int:
+    return int(load().mea_fwd_fp8_workspace_size(num_seqs, total_k, Hkv, D))
 
 
 def mea_status_string(status: int) -> str:

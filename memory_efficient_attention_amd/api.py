@@ -23,7 +23,7 @@ from . import _native
 
 __all__ = [
     "BlockDiagonalMask", "BlockDiagonalCausalMask", "memory_efficient_attention",
-    "attention_packed", "attention_paged", "attention_backward_packed", "MeaError",
+    "attention_packed", "attention_paged", "attention_backward_packed", "attention_packed_fp8", "MeaError",
 ]
 
 
@@ -339,6 +339,64 @@ class _PackedAttention(torch.autograd.Function):
                                                max_seqlen_q, max_seqlen_k, causal=causal,
                                                alibi_slopes=slopes, scale=scale)
         return dq, dk, dv, None, None, None, None, None, None, None
+
+
+def attention_packed_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, q_scale: float,
+                         k_scale: float, v_scale: float, seqstart_q: torch.Tensor, seqstart_k: torch.Tensor,
+                         max_seqlen_q: int, max_seqlen_k: int, *, causal: bool = False,
+                         alibi_slopes: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                         out_dtype: torch.dtype = torch.bfloat16, return_lse: bool = False,
+                         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None,
+                         stream: Optional[torch.cuda.Stream] = None):
+    """Packed call on 8-bit inputs: ``q8 [Tq, Hq, 128]``, ``k8``/``v8``
+    ``[Tk, Hkv, 128]`` of ``torch.float8_e4m3fn`` with one scale per tensor
+    (the values are scale * tensor).  Returns ``out`` of ``out_dtype`` (or
+    ``(out, lse)``), as :func:`attention_packed` does on the dequantised
+    values."""
+    if q8.dim() != 3 or k8.dim() != 3 or v8.dim() != 3:
+        raise ValueError("packed q8, k8, v8 must be [tokens, heads, D]")
+    Tq, Hq, D = q8.shape
+    Tk, Hkv, Dk = k8.shape
+    if Dk != D or tuple(v8.shape) != (Tk, Hkv, D):
+        raise ValueError(f"shape mismatch: q8 {tuple(q8.shape)} k8 {tuple(k8.shape)} v8 {tuple(v8.shape)}")
+    if not (q8.dtype == k8.dtype == v8.dtype == torch.float8_e4m3fn):
+        raise TypeError("q8, k8 and v8 must be torch.float8_e4m3fn")
+    dev = q8.device
+    if dev.type != "cuda" or k8.device != dev or v8.device != dev:
+        raise ValueError("q8, k8 and v8 must be on the same GPU")
+    q8, k8, v8 = q8.contiguous(), k8.contiguous(), v8.contiguous()
+    if seqstart_q.dtype != torch.int32 or seqstart_k.dtype != torch.int32:
+        raise TypeError("seqstart tensors must be int32")
+    num_seqs = seqstart_q.numel() - 1
+    if seqstart_k.numel() != num_seqs + 1:
+        raise ValueError("seqstart_q and seqstart_k differ in length")
+    if out is None:
+        out = torch.empty((Tq, Hq, D), dtype=out_dtype, device=dev)
+    if return_lse and lse is None:
+        lse = torch.empty((Hq, Tq), dtype=torch.float32, device=dev)
+    slopes = None
+    if alibi_slopes is not None:
+        slopes = alibi_slopes.to(device=dev, dtype=torch.float32).contiguous()
+        if slopes.numel() != Hq:
+            raise ValueError(f"alibi_slopes needs {Hq} values (one per query head)")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    scale = float(np.float32(scale))
+    ws_bytes = _native.mea_fwd_fp8_workspace_size(num_seqs, Tk, Hkv, D)
+    if ws_bytes > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        st = _native.mea_fwd_fp8(
+            _ptr(q8), _ptr(k8), _ptr(v8), float(q_scale), float(k_scale), float(v_scale), _ptr(out), _ptr(lse),
+            _ptr(seqstart_q), _ptr(seqstart_k), num_seqs, Tq, Tk, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv,
+            D, _dtype_code(out.dtype), int(bool(causal)), _ptr(slopes), scale,
+            _ptr(workspace) if ws_bytes > 0 else None, ws_bytes, stream.cuda_stream)
+    if st != _native.MEA_OK:
+        raise MeaError(st, _native.mea_last_error())
+    return (out, lse) if return_lse else out
 
 
 def _kv_heads_bmghk(k: torch.Tensor, hq: int) -> torch.Tensor:

@@ -54,24 +54,28 @@ constexpr int kVtThreads = 256;           // V pre-pass
 constexpr int kBufs = 3;                  // LDS buffers of K tiles and of V tiles (a ring of 3 each)
 constexpr float kRescaleThreshold = 8.f;  // log2 units: p may reach 2^8 before O is rescaled
 
-template <int D>
+template <int D, int ESZ = 2>
 struct PfLayout {
   static constexpr int BN = kPfBN;                    // keys per tile
-  static constexpr int kBytes = BN * D * 2;           // K rows [BN][D], 16-byte chunks XOR-swizzled
-  static constexpr int vBytes = D * BN * 2;           // V^T rows [D][BN], 16-byte chunks XOR-swizzled
+  static constexpr int kBytes = BN * D * ESZ;         // K rows [BN][D] of ESZ-byte values, 16-byte chunks XOR-swizzled
+  static constexpr int vBytes = D * BN * 2;           // V^T rows [D][BN] of halves, 16-byte chunks XOR-swizzled
   static constexpr int bufBytes = kBytes + vBytes;
-  static constexpr int chunks = D / 8;                // 16-byte chunks per K row
-  static constexpr int rowsPerKB = 1024 / (D * 2);    // K rows per 1 KB direct-load block
+  static constexpr int chunks = D * ESZ / 16;         // 16-byte chunks per K row
+  static constexpr int rowsPerKB = 1024 / (D * ESZ);  // K rows per 1 KB direct-load block
   static constexpr int kLoads = kBytes / (kThreads * 16);
   static constexpr int vLoads = vBytes / (kThreads * 16);
 };
 
 }  // namespace
 
-template <int D, bool BF16, bool CAUSAL, bool ALIBI, bool PAGED>
+// FP8: q, k and v hold OCP e4m3 values (one byte each) and BF16 names the
+// output dtype; Q K^T runs on the fp8 matrix cores, V enters P V as halves
+// (the pre-pass widens it exactly), and the output is scaled by out_scale.
+template <int D, bool BF16, bool CAUSAL, bool ALIBI, bool PAGED, bool FP8 = false>
 __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the body uses buffer-resource types that exist only for the GPU target
-  using L = PfLayout<D>;
+  constexpr int ESZ = FP8 ? 1 : 2;        // bytes per q/k element
+  using L = PfLayout<D, ESZ>;
   constexpr int BN = L::BN;
   constexpr int KS = D / 16;             // k-steps of the Q K^T product
   constexpr int NV = 4 * (D / 32);       // products of P V per tile
@@ -117,8 +121,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
   const int nkt = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
 
   // ---- Q^T operand: lane holds features 16*s + 8*hi .. +7 of its row
-  u32x4 qf[KS];
-  {
+  // (fp8: chunk s holds features 64 (s / 2) + 32 hi + 16 (s % 2) .. + 15)
+  constexpr int QC = FP8 ? D / 32 : KS;  // 16-byte chunks of Q per lane
+  u32x4 qf[QC];
+  if constexpr (FP8) {
+    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) + ((size_t)(sq0 + my_tok) * a.Hq + head) * D + 32 * hi;
+#pragma unroll
+    for (int s = 0; s < QC; ++s) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (row_valid) x = *(const u32x4*)(qrow + 64 * (s / 2) + 16 * (s % 2));
+      qf[s] = x;
+    }
+  } else {
     const uint16_t* qrow = a.q + ((size_t)(sq0 + my_tok) * a.Hq + head) * D + 8 * hi;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -132,10 +146,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
   if constexpr (ALIBI) slope2 = a.slopes[head] * kLog2e;
 
   // ---- staging setup: buffer resources over this sequence's rows of head g
-  const uint32_t rs_bytes = (uint32_t)a.Hkv * D * 2;   // bytes between key rows
-  const uint32_t seq_bytes = Lk > 0 ? (uint32_t)(Lk - 1) * rs_bytes + D * 2 : 0u;
+  const uint32_t rs_bytes = (uint32_t)a.Hkv * D * ESZ;   // bytes between key rows
+  const uint32_t seq_bytes = Lk > 0 ? (uint32_t)(Lk - 1) * rs_bytes + D * ESZ : 0u;
   const size_t head_off = ((size_t)sk0 * a.Hkv + g) * D;
-  const __amdgpu_buffer_rsrc_t krs = rows_rsrc(a.k + head_off, seq_bytes);
+  const __amdgpu_buffer_rsrc_t krs =
+      buf_rsrc(reinterpret_cast<const uint8_t*>(a.k) + head_off * ESZ, seq_bytes);
   // K: direct loads, 1 KB block q = i * 8 + wave (rowsPerKB rows) per instruction
   uint32_t k_voff[L::kLoads];
 #pragma unroll
@@ -143,7 +158,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
     const int q = i * kPfWaves + wave;
     const int r = q * L::rowsPerKB + lane / L::chunks;
     const int pos = lane % L::chunks;
-    k_voff[i] = (uint32_t)r * rs_bytes + (uint32_t)k_pos<D>(r, pos) * 16u;
+    k_voff[i] = (uint32_t)r * rs_bytes + (uint32_t)k_pos<D * ESZ / 2>(r, pos) * 16u;
   }
   // V: V^T images of this sequence and head in the workspace (tile ti at
   // ti * Hkv images from the first), loaded 1 KB per instruction per wave
@@ -199,18 +214,31 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
     const uint8_t* Kb = kbuf(t);
     s[0] = f32x16{};
     s[1] = f32x16{};
+    if constexpr (FP8) {
+      // K fragment of k-step ks: row r, bytes 64 ks + 32 hi .. + 31 (chunks 4 ks + 2 hi, + 1)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4 kf[2];
+      for (int ks = 0; ks < D / 64; ++ks)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int r = 32 * kb + key_of_row(l32);
-        kf[kb] = *(const u32x4*)(Kb + r * (D * 2) + k_pos<D>(r, 2 * ks + hi) * 16);
+        for (int kb = 0; kb < 2; ++kb) {
+          const int r = 32 * kb + key_of_row(l32);
+          const u32x4 k0 = *(const u32x4*)(Kb + r * D + k_pos<D / 2>(r, 4 * ks + 2 * hi) * 16);
+          const u32x4 k1 = *(const u32x4*)(Kb + r * D + k_pos<D / 2>(r, 4 * ks + 2 * hi + 1) * 16);
+          s[kb] = mfma_32x32x64_fp8(k0, k1, qf[2 * ks], qf[2 * ks + 1], s[kb]);
+        }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4 kf[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int r = 32 * kb + key_of_row(l32);
+          kf[kb] = *(const u32x4*)(Kb + r * (D * 2) + k_pos<D>(r, 2 * ks + hi) * 16);
+        }
+        s[0] = mfma_32x32x16<BF16>(kf[0], qf[ks], s[0]);
+        s[1] = mfma_32x32x16<BF16>(kf[1], qf[ks], s[1]);
       }
-      s[0] = mfma_32x32x16<BF16>(kf[0], qf[ks], s[0]);
-      s[1] = mfma_32x32x16<BF16>(kf[1], qf[ks], s[1]);
+      interleave_reads_and_products<2 * KS>();
     }
-    interleave_reads_and_products<2 * KS>();
   };
 
   // Scores of tile t -> log2 units with bias and masks, row maximum, and the
@@ -365,7 +393,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
   // ---- epilogue: normalise, round, stage the wave's 32 x D tile through LDS
   // so that every global store writes whole 16-byte runs of a row.
   const float l_tot = halfwave_sum(l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if constexpr (FP8) inv *= a.out_scale;
   uint16_t* ot = reinterpret_cast<uint16_t*>(smem) + wave * 32 * (D + 8);  // [32][D + 8]
 #pragma unroll
   for (int d = 0; d < D / 32; ++d)
@@ -380,10 +409,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
     a.lse[(size_t)head * a.total_q + sq0 + my_tok] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_wave_barrier();
-  constexpr int RPI = 64 / L::chunks;  // rows per store instruction
+  constexpr int kOutChunks = D / 8;     // 16-byte chunks per output row (16-bit values)
+  constexpr int RPI = 64 / kOutChunks;  // rows per store instruction
 #pragma unroll
   for (int i = 0; i < 32 / RPI; ++i) {
-    const int row = i * RPI + lane / L::chunks, ch = lane % L::chunks;
+    const int row = i * RPI + lane / kOutChunks, ch = lane % kOutChunks;
     if (tok0 + row < Lq) {
       const u32x4 val = *(const u32x4*)(ot + row * (D + 8) + ch * 8);
       *(u32x4*)(a.out + ((size_t)(sq0 + tok0 + row) * a.Hq + head) * D + ch * 8) = val;
@@ -398,7 +428,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
 // since a sequence of L keys has at most L / 64 + 1 tiles).  Keys past the
 // sequence's end are zero.  Thread (kq, cv) transposes 4 keys x 8 features in
 // registers.
-template <int D, bool BF16, bool PAGED>
+template <int D, bool BF16, bool PAGED, bool FP8 = false>
 __global__ __launch_bounds__(kVtThreads) void vt_images_kernel(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int BN = kPfBN;
@@ -424,35 +454,42 @@ __global__ __launch_bounds__(kVtThreads) void vt_images_kernel(FwdArgs a) {
     row0 = (uint32_t)(i * BN);
   }
   uint8_t* img = reinterpret_cast<uint8_t*>(a.ws_vt + ((size_t)((sk0 / BN) + b + i) * a.Hkv + g) * (D * BN));
-  write_tile_image<D, BF16>(vrs, row0, rs_bytes, img, kq, cv);
+  if constexpr (FP8) {
+    const uint32_t rs8 = (uint32_t)a.Hkv * D;  // one byte per value
+    const __amdgpu_buffer_rsrc_t v8 =
+        buf_rsrc(reinterpret_cast<const uint8_t*>(a.v) + ((size_t)sk0 * a.Hkv + g) * D, (uint32_t)(Lk - 1) * rs8 + D);
+    write_tile_image_fp8(v8, (uint32_t)(i * BN), rs8, img, kq, cv);
+  } else {
+    write_tile_image<D, BF16>(vrs, row0, rs_bytes, img, kq, cv);
+  }
 #endif
 }
 
-template <int D, bool BF16, bool PAGED>
+template <int D, bool BF16, bool PAGED, bool FP8>
 static hipError_t launch_prefill_d(const FwdArgs& a, bool causal, bool alibi, dim3 grid,
                                    hipStream_t stream) {
   const dim3 block(kThreads);
   if (causal) {
-    if (alibi) hipLaunchKernelGGL((fwd_prefill_kernel<D, BF16, true, true, PAGED>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((fwd_prefill_kernel<D, BF16, true, false, PAGED>), grid, block, 0, stream, a);
+    if (alibi) hipLaunchKernelGGL((fwd_prefill_kernel<D, BF16, true, true, PAGED, FP8>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((fwd_prefill_kernel<D, BF16, true, false, PAGED, FP8>), grid, block, 0, stream, a);
   } else {
-    if (alibi) hipLaunchKernelGGL((fwd_prefill_kernel<D, BF16, false, true, PAGED>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((fwd_prefill_kernel<D, BF16, false, false, PAGED>), grid, block, 0, stream, a);
+    if (alibi) hipLaunchKernelGGL((fwd_prefill_kernel<D, BF16, false, true, PAGED, FP8>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((fwd_prefill_kernel<D, BF16, false, false, PAGED, FP8>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }
 
-template <int D, bool BF16, bool PAGED>
+template <int D, bool BF16, bool PAGED, bool FP8 = false>
 static hipError_t launch_prefill_dp(const FwdArgs& a, bool causal, bool alibi, int max_seqlen_k,
                                     hipStream_t stream) {
   if (max_seqlen_k > 0) {
     const dim3 vgrid(a.Hkv, (max_seqlen_k + kPfBN - 1) / kPfBN, a.num_seqs);
-    hipLaunchKernelGGL((vt_images_kernel<D, BF16, PAGED>), vgrid, dim3(kVtThreads), 0, stream, a);
+    hipLaunchKernelGGL((vt_images_kernel<D, BF16, PAGED, FP8>), vgrid, dim3(kVtThreads), 0, stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const dim3 grid((unsigned)(((long long)a.pf_items + 7) / 8 * 8));
-  return launch_prefill_d<D, BF16, PAGED>(a, causal, alibi, grid, stream);
+  return launch_prefill_d<D, BF16, PAGED, FP8>(a, causal, alibi, grid, stream);
 }
 
 template <int D, bool BF16>
@@ -470,6 +507,13 @@ hipError_t launch_prefill(const FwdArgs& a, int D, bool bf16, bool causal, bool 
   }
   return bf16 ? launch_prefill_db<128, true>(a, causal, alibi, max_seqlen_k, stream)
               : launch_prefill_db<128, false>(a, causal, alibi, max_seqlen_k, stream);
+}
+
+// fp8 (OCP e4m3) q, k, v; D = 128; out_bf16 picks the output dtype.
+hipError_t launch_prefill_fp8(const FwdArgs& a, bool out_bf16, bool causal, bool alibi, int max_seqlen_k,
+                              hipStream_t stream) {
+  return out_bf16 ? launch_prefill_dp<128, true, false, true>(a, causal, alibi, max_seqlen_k, stream)
+                  : launch_prefill_dp<128, false, false, true>(a, causal, alibi, max_seqlen_k, stream);
 }
 
 }  // namespace mea

@@ -81,13 +81,19 @@ struct PagedKv {
   int32_t page_size, num_pages, max_blocks;
 };
 
+// fp8 (OCP e4m3) q, k, v with per-tensor scales: the values are q_scale * q8
+// etc.  q_scale * k_scale folds into the score scale, v_scale into the output.
+struct Fp8Scales {
+  float q, k, v;
+};
+
 mea_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse,
                       const int32_t* seqstart_q, const int32_t* seqstart_k, int32_t num_seqs,
                       int32_t total_q, int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq,
                       int32_t Hkv, int32_t D, mea_dtype_t dtype, int32_t causal,
                       const float* alibi_slopes, float scale, void* workspace,
                       size_t workspace_bytes, void* stream, int32_t chunk_keys, bool forced_split,
-                      const PagedKv* paged = nullptr) {
+                      const PagedKv* paged = nullptr, const Fp8Scales* fp8 = nullptr) {
   g_last_error[0] = '\0';
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
     return fail(MEA_ERR_INVALID, "q, k, v and out must be non-NULL device pointers");
@@ -107,6 +113,13 @@ mea_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, fl
       return fail(MEA_ERR_INVALID, "chunk_keys must be a positive multiple of %d (got %d)", mea::kDcPieceAlign, chunk_keys);
   }
   if (D != 64 && D != 128) return fail(MEA_ERR_UNSUPPORTED, "head dimension D=%d is not 64 or 128", D);
+  if (fp8 != nullptr) {
+    if (D != 128) return fail(MEA_ERR_UNSUPPORTED, "fp8 inputs need D=128 (got %d)", D);
+    if (!std::isfinite(fp8->q) || !(fp8->q > 0.f) || !std::isfinite(fp8->k) || !(fp8->k > 0.f) ||
+        !std::isfinite(fp8->v) || !(fp8->v > 0.f))
+      return fail(MEA_ERR_UNSUPPORTED, "fp8 scales must be finite and > 0 (got %g, %g, %g)", (double)fp8->q,
+                  (double)fp8->k, (double)fp8->v);
+  }
   if (dtype != MEA_F16 && dtype != MEA_BF16) return fail(MEA_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
   if (!std::isfinite(scale) || !(scale > 0.f))
     return fail(MEA_ERR_UNSUPPORTED, "scale must be finite and > 0 (got %g)", (double)scale);
@@ -145,6 +158,11 @@ mea_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, fl
   a.seqstart_k = seqstart_k;
   a.slopes = alibi_slopes;
   a.scale_log2 = scale * mea::kLog2e;
+  a.out_scale = 1.f;
+  if (fp8 != nullptr) {
+    a.scale_log2 = (float)((double)scale * fp8->q * fp8->k * (double)mea::kLog2e);
+    a.out_scale = fp8->v;
+  }
   a.num_seqs = num_seqs;
   a.total_q = total_q;
   a.total_k = total_k;
@@ -161,7 +179,7 @@ mea_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, fl
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   hipError_t err;
-  if (max_seqlen_q == 1) {
+  if (max_seqlen_q == 1 && fp8 == nullptr) {
     const int32_t chunk = forced_split ? chunk_keys : default_chunk(total_k, Hq, Hkv);
     const size_t need = decode_ws_bytes(num_seqs, total_k, max_seqlen_k, Hq, D, chunk);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need))
@@ -195,7 +213,8 @@ mea_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, fl
       return fail(MEA_ERR_UNSUPPORTED, "%lld prefill work items exceed the grid limit", items);
     a.pf_max_tiles = (int32_t)tiles;
     a.pf_items = (int32_t)items;
-    err = mea::launch_prefill(a, D, bf16, causal != 0, alibi, max_seqlen_k, s);
+    err = fp8 != nullptr ? mea::launch_prefill_fp8(a, bf16, causal != 0, alibi, max_seqlen_k, s)
+                         : mea::launch_prefill(a, D, bf16, causal != 0, alibi, max_seqlen_k, s);
   }
   if (err != hipSuccess) return fail(MEA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
   return MEA_OK;
@@ -365,6 +384,23 @@ size_t mea_bwd_workspace_size(int32_t num_seqs, int32_t total_q, int32_t total_k
       (D != 64 && D != 128))
     return 0;
   return bwd_ws_layout(total_q, Hq).total;
+}
+
+mea_status_t mea_fwd_fp8(const void* q, const void* k, const void* v, float q_scale, float k_scale, float v_scale,
+                         void* out, float* lse, const int32_t* seqstart_q, const int32_t* seqstart_k,
+                         int32_t num_seqs, int32_t total_q, int32_t total_k, int32_t max_seqlen_q,
+                         int32_t max_seqlen_k, int32_t Hq, int32_t Hkv, int32_t D, mea_dtype_t out_dtype,
+                         int32_t causal, const float* alibi_slopes, float scale, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  const Fp8Scales sc{q_scale, k_scale, v_scale};
+  return fwd_impl(q, k, v, out, lse, seqstart_q, seqstart_k, num_seqs, total_q, total_k, max_seqlen_q,
+                  max_seqlen_k, Hq, Hkv, D, out_dtype, causal, alibi_slopes, scale, workspace, workspace_bytes,
+                  stream, 0, false, nullptr, &sc);
+}
+
+size_t mea_fwd_fp8_workspace_size(int32_t num_seqs, int32_t total_k, int32_t Hkv, int32_t D) {
+  if (num_seqs <= 0 || total_k < 0 || Hkv <= 0 || D != 128) return 0;
+  return prefill_ws_bytes(num_seqs, total_k, Hkv, D);
 }
 
 size_t mea_fwd_workspace_size(int32_t num_seqs, int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k,

@@ -50,6 +50,7 @@ struct FwdArgs {
   int32_t dc_pieces;         // decode: ceil(total_k / chunk_keys)
   int32_t pf_max_tiles;      // prefill: query tiles of the longest sequence
   int32_t pf_items;          // prefill: head slices * num_seqs * pf_max_tiles
+  float out_scale;           // fp8 inputs: the V scale, applied to the output (else 1)
 };
 
 // Everything a backward launch needs; passed by value as the kernel argument.
@@ -96,6 +97,20 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
+}
+
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// 32x32x64 products of OCP e4m3 (fp8) operands, float32 accumulate.  Lane l
+// holds row (or column) l % 32 and 32 k-values, 16 bytes in each of lo and hi;
+// the output layout is that of mfma_32x32x16.  Any assignment of k-values to
+// lanes and bytes gives the same product as long as both operands share it.
+__device__ __forceinline__ f32x16 mfma_32x32x64_fp8(u32x4 alo, u32x4 ahi, u32x4 blo, u32x4 bhi, f32x16 c) {
+  const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(alo, ahi, 0, 1, 2, 3, 4, 5, 6, 7));
+  const i32x8 b = __builtin_bit_cast(i32x8, __builtin_shufflevector(blo, bhi, 0, 1, 2, 3, 4, 5, 6, 7));
+  // format 0 (e4m3) for both operands; no block scales
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
 // The other half-wave's value of x (lane l <-> lane l ^ 32), combined.

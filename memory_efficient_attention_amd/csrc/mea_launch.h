@@ -36,6 +36,8 @@ constexpr int kBwKeyTile = 64;               // keys per dQ stage
 
 hipError_t launch_prefill(const FwdArgs& a, int D, bool bf16, bool causal, bool alibi,
                           int max_seqlen_k, hipStream_t stream);
+hipError_t launch_prefill_fp8(const FwdArgs& a, bool out_bf16, bool causal, bool alibi, int max_seqlen_k,
+                              hipStream_t stream);
 hipError_t launch_decode(const FwdArgs& a, int D, bool bf16, bool alibi, hipStream_t stream);
 hipError_t launch_backward(const BwdArgs& a, int D, bool bf16, bool causal, bool alibi, hipStream_t stream);
 

@@ -103,11 +103,28 @@ __device__ __forceinline__ u32x4 read_rows_transposed(const uint8_t* tile, int r
   return res;
 }
 
-// One thread's share of writing a transposed tile image: rows row0 + 4kq ..
-// row0 + 4kq + 3 (kq < 16) and columns 8cv .. 8cv + 7 (cv < D / 8) of a
-// 64-row tile, read through `rs` (row stride rs_bytes; rows past the
-// resource's end read zeros), land in the [D][64] image at `img` (vt_off
-// layout).  TO_F16: the values are bfloat16 and are re-encoded as IEEE halves.
+// One thread's share of writing a transposed tile image: r[k] holds columns
+// 8cv .. 8cv + 7 of row 4kq + k (kq < 16) of a 64-row tile as packed 16-bit
+// values (word w: columns 2w low, 2w + 1 high); they land in the [D][64] image
+// at `img` (vt_off layout).
+__device__ __forceinline__ void store_tile_image(const u32x4 (&r)[4], uint8_t* img, int kq, int cv) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    u32x2 even, odd;
+    even[0] = __builtin_amdgcn_perm(r[1][w], r[0][w], 0x05040100u);
+    even[1] = __builtin_amdgcn_perm(r[3][w], r[2][w], 0x05040100u);
+    odd[0] = __builtin_amdgcn_perm(r[1][w], r[0][w], 0x07060302u);
+    odd[1] = __builtin_amdgcn_perm(r[3][w], r[2][w], 0x07060302u);
+    const int row = 8 * cv + 2 * w;
+    *(u32x2*)(img + vt_off(row, kq / 2) + 8 * (kq % 2)) = even;
+    *(u32x2*)(img + vt_off(row + 1, kq / 2) + 8 * (kq % 2)) = odd;
+  }
+}
+
+// Rows row0 + 4kq .. + 3 and columns 8cv .. 8cv + 7 of a 64-row tile of 16-bit
+// values, read through `rs` (row stride rs_bytes; rows past the resource's end
+// read zeros), into the [D][64] image.  TO_F16: the values are bfloat16 and
+// are re-encoded as IEEE halves.
 template <int D, bool TO_F16>
 __device__ __forceinline__ void write_tile_image(__amdgpu_buffer_rsrc_t rs, uint32_t row0, uint32_t rs_bytes,
                                                  uint8_t* img, int kq, int cv) {
@@ -122,18 +139,28 @@ __device__ __forceinline__ void write_tile_image(__amdgpu_buffer_rsrc_t rs, uint
 #pragma unroll
       for (int w = 0; w < 4; ++w) r[k][w] = bf16x2_to_f16x2(r[k][w]);
   }
-  // word w of r[k] holds columns 2w (low) and 2w+1 (high) of row 4kq + k
+  store_tile_image(r, img, kq, cv);
+}
+
+// The same for a tile of OCP e4m3 (fp8) values, re-encoded as IEEE halves
+// (exact: every e4m3 value is a half).
+__device__ __forceinline__ void write_tile_image_fp8(__amdgpu_buffer_rsrc_t rs, uint32_t row0, uint32_t rs_bytes,
+                                                     uint8_t* img, int kq, int cv) {
+  u32x4 r[4];
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    u32x2 even, odd;
-    even[0] = __builtin_amdgcn_perm(r[1][w], r[0][w], 0x05040100u);
-    even[1] = __builtin_amdgcn_perm(r[3][w], r[2][w], 0x05040100u);
-    odd[0] = __builtin_amdgcn_perm(r[1][w], r[0][w], 0x07060302u);
-    odd[1] = __builtin_amdgcn_perm(r[3][w], r[2][w], 0x07060302u);
-    const int row = 8 * cv + 2 * w;
-    *(u32x2*)(img + vt_off(row, kq / 2) + 8 * (kq % 2)) = even;
-    *(u32x2*)(img + vt_off(row + 1, kq / 2) + 8 * (kq % 2)) = odd;
+  for (int k = 0; k < 4; ++k) {
+    const u32x2 b = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                  rs, (row0 + 4 * kq + k) * rs_bytes + cv * 8u, 0, 0));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t word = b[h];
+      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
+      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true);
+      r[k][2 * h] = pack_f16x2(lo[0], lo[1]);
+      r[k][2 * h + 1] = pack_f16x2(hi[0], hi[1]);
+    }
   }
+  store_tile_image(r, img, kq, cv);
 }
 
 }  // namespace mea

@@ -48,7 +48,7 @@ def test_every_kernel_stub_is_defined():
 
 
 def test_version_and_strings():
-    assert _native.mea_abi_version() == 4
+    assert _native.mea_abi_version() == 5
     for st in range(4):
         assert _native.mea_status_string(st).startswith("MEA_")
     assert "unknown" in _native.mea_status_string(99)
@@ -228,3 +228,36 @@ def test_bwd_workspace_size():
     assert ws(0, 10, 10, 8, 2, 64) == 0
     assert ws(4, 365, 365, 8, 3, 64) == 0
     assert ws(4, 365, 365, 8, 2, 96) == 0
+
+
+def call_fp8(**kw):
+    a = dict(q=P, k=P, v=P, q_scale=0.01, k_scale=0.02, v_scale=0.03, out=P, lse=None, seqstart_q=P,
+             seqstart_k=P, num_seqs=4, total_q=365, total_k=365, max_seqlen_q=200, max_seqlen_k=200, Hq=8, Hkv=2,
+             D=128, out_dtype=MEA_BF16, causal=1, alibi_slopes=None, scale=0.088, workspace=P,
+             workspace_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return _native.mea_fwd_fp8(**a)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(D=64), MEA_ERR_UNSUPPORTED, "D=128"),
+    (dict(q_scale=0.0), MEA_ERR_UNSUPPORTED, "fp8 scales"),
+    (dict(v_scale=float("inf")), MEA_ERR_UNSUPPORTED, "fp8 scales"),
+    (dict(k_scale=-1.0), MEA_ERR_UNSUPPORTED, "fp8 scales"),
+    (dict(q=None), MEA_ERR_INVALID, "non-NULL"),
+    (dict(out_dtype=9), MEA_ERR_UNSUPPORTED, "dtype"),
+    (dict(workspace=None, workspace_bytes=0), MEA_ERR_INVALID, "workspace"),
+    # decode-shaped calls still take the prefill kernel and its workspace
+    (dict(total_q=4, max_seqlen_q=1, workspace=None, workspace_bytes=0), MEA_ERR_INVALID, "workspace"),
+])
+def test_fp8_rejected_before_launch(kw, status, needle):
+    assert call_fp8(**kw) == status
+    assert needle in _native.mea_last_error()
+
+
+def test_fp8_workspace_size():
+    ws = _native.mea_fwd_fp8_workspace_size
+    assert ws(64, 137663, 8, 128) == (137663 // 64 + 64) * 8 * 128 * 128
+    assert ws(4, 365, 2, 64) == 0
+    assert ws(0, 365, 2, 128) == 0
+    assert ws(4, 0, 2, 128) == 0

@@ -1,0 +1,88 @@
+"""GPU parity of the fp8 forward (``mea_fwd_fp8``): q, k, v quantised to OCP
+e4m3 with per-tensor scales; the HIP result is compared with the float64
+oracle on the same codes and scales (``attention_forward_fp8``), with the
+output gates of the 16-bit path for the output dtype."""
+import sys
+
+import pytest
+import torch
+
+import oracle
+from mea_workloads import generate, random_case, sample_rows, to_fp8
+from parity import compare
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def _run(inp, f, out_dtype):
+    from memory_efficient_attention_amd import attention_packed_fp8
+    dev = "cuda"
+    out = torch.full((inp.total_q, inp.Hq, inp.D), float("nan"), dtype=out_dtype, device=dev)
+    res = attention_packed_fp8(f.q8.to(dev), f.k8.to(dev), f.v8.to(dev), f.q_scale, f.k_scale, f.v_scale,
+                               inp.seqstart_q.to(dev), inp.seqstart_k.to(dev), inp.max_seqlen_q, inp.max_seqlen_k,
+                               causal=inp.causal,
+                               alibi_slopes=None if inp.alibi_slopes is None else inp.alibi_slopes.to(dev),
+                               scale=inp.scale, out_dtype=out_dtype, return_lse=True, out=out)
+    torch.cuda.synchronize()
+    return res[0].cpu(), res[1].cpu()
+
+
+def _ref(inp, f):
+    return oracle.attention_forward_fp8(f.q8, f.k8, f.v8, f.q_scale, f.k_scale, f.v_scale, inp.seqstart_q,
+                                        inp.seqstart_k, causal=inp.causal, alibi_slopes=inp.alibi_slopes,
+                                        scale=inp.scale)
+
+
+CASES = [
+    # (name, seqlens_q, seqlens_k, Hq, Hkv, causal, alibi, out dtype)
+    ("varlen_causal_bf16", [37, 120, 8, 200], None, 8, 8, True, False, torch.bfloat16),
+    ("varlen_alibi_fp16", [37, 120, 8, 200], None, 8, 8, False, True, torch.float16),
+    ("gqa_causal_alibi", [130, 1, 77, 300], None, 8, 2, True, True, torch.bfloat16),
+    ("mqa", [256, 129], None, 8, 1, False, False, torch.float16),
+    ("lq_gt_lk_causal", [3, 5, 70, 150], [7, 2, 200, 64], 4, 2, True, False, torch.bfloat16),
+    ("lq_lt_lk_causal_alibi", [65, 17, 200], [300, 17, 333], 4, 4, True, True, torch.bfloat16),
+    ("empty_sides", [0, 65, 10, 0, 33], [5, 0, 10, 0, 129], 4, 2, True, False, torch.bfloat16),
+    ("decode_shaped", [1, 1, 1, 1], [300, 1, 64, 1000], 8, 2, True, True, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(CASES)))
+def test_fp8_parity(ci):
+    name, lq, lk, Hq, Hkv, causal, alibi, odt = CASES[ci]
+    inp = random_case(700 + ci, lq, lk, Hq=Hq, Hkv=Hkv, D=128, dtype="bf16", causal=causal, alibi=alibi)
+    f = to_fp8(inp)
+    _log(f"fp8 {name}")
+    out, lse = _run(inp, f, odt)
+    ref_out, ref_lse = _ref(inp, f)
+    _log(f"  {compare(out, lse, ref_out, ref_lse, 'bf16' if odt == torch.bfloat16 else 'fp16', name)}")
+
+
+def test_fp8_causal_alibi_gqa_4x2048():
+    inp = generate("causal_alibi_gqa_4x2048_h32kv8_d128_bf16")
+    f = to_fp8(inp)
+    _log("fp8 4x2048")
+    out, lse = _run(inp, f, torch.bfloat16)
+    ref_out, ref_lse = _ref(inp, f)
+    _log(f"  {compare(out, lse, ref_out, ref_lse, 'bf16', 'fp8 4x2048')}")
+
+
+def test_fp8_full_size_sampled():
+    """The 64-sequence prefill workload (137,663 tokens) in fp8; sampled rows."""
+    inp = generate("varlen_causal_gqa_64seq_h32kv8_d128_bf16")
+    f = to_fp8(inp)
+    _log("fp8 full size")
+    out, lse = _run(inp, f, torch.bfloat16)
+    assert not torch.isnan(out).any()
+    rows = sample_rows(inp, 160, seed=5)
+    q = f.q8.to(torch.float64) * f.q_scale
+    k = f.k8.to(torch.float64) * f.k_scale
+    v = f.v8.to(torch.float64) * f.v_scale
+    ro, rl = oracle.attention_rows(q, k, v, inp.seqstart_q, inp.seqstart_k, rows, causal=True,
+                                   scale=inp.scale)
+    go = torch.stack([out[t, h] for t, h in rows])
+    gl = torch.stack([lse[h, t] for t, h in rows])
+    _log(f"  {compare(go, gl, ro, rl, 'bf16', 'fp8 full size sampled')}")
