@@ -33,7 +33,7 @@ import torch
 __all__ = [
     "Workload", "Inputs", "WORKLOADS", "get_workload", "generate", "random_case",
     "alibi_slopes", "seqstart_from_lengths", "sample_rows", "prefix", "PagedKV", "to_paged",
-    "random_dout", "Fp8Inputs", "to_fp8",
+    "random_dout", "Fp8Inputs", "to_fp8", "FfnInputs", "swiglu_case", "FFN_WORKLOAD",
 ]
 
 _DTYPES = {"fp16": torch.float16, "bf16": torch.bfloat16}
@@ -276,6 +276,33 @@ def to_fp8(inp: Inputs) -> Fp8Inputs:
     k8, ks = _quantise(inp.k)
     v8, vs = _quantise(inp.v)
     return Fp8Inputs(q8=q8, k8=k8, v8=v8, q_scale=qs, k_scale=ks, v_scale=vs)
+
+
+@dataclasses.dataclass
+class FfnInputs:
+    """Inputs of one SwiGLU feed-forward call (host tensors)."""
+    x: torch.Tensor        # [tokens, d_model]
+    w_gate: torch.Tensor   # [d_ff, d_model]
+    w_up: torch.Tensor     # [d_ff, d_model]
+    w_down: torch.Tensor   # [d_model, d_ff]
+    dtype: str
+
+
+# The feed-forward layer of the prefill workload's transformer block: its
+# 137,663 packed tokens, d_model = 32 heads x 128, d_ff = 11008 (the LLaMA-7B
+# feed-forward width; the zizhi168.cn page uses LLaMA-7B as its example model).
+FFN_WORKLOAD = dict(tokens=137663, d_model=4096, d_ff=11008, dtype="bf16")
+
+
+def swiglu_case(seed: int, tokens: int, d_model: int, d_ff: int, dtype: str = "bf16") -> FfnInputs:
+    """x ~ N(0, 1); weights ~ N(0, 1 / fan_in), so that activations stay O(1)."""
+    dt = _DTYPES[dtype]
+    g = torch.Generator("cpu").manual_seed(seed + 11)
+    x = torch.randn((tokens, d_model), generator=g).to(dt)
+    w_gate = (torch.randn((d_ff, d_model), generator=g) * d_model ** -0.5).to(dt)
+    w_up = (torch.randn((d_ff, d_model), generator=g) * d_model ** -0.5).to(dt)
+    w_down = (torch.randn((d_model, d_ff), generator=g) * d_ff ** -0.5).to(dt)
+    return FfnInputs(x=x, w_gate=w_gate, w_up=w_up, w_down=w_down, dtype=dtype)
 
 
 @dataclasses.dataclass

@@ -7,12 +7,15 @@ Python binding (the seeded input generators in ``mea_workloads`` are the only
 code both sides use, and they hold none of the attention arithmetic).
 
 What it computes is the plain definition of attention over packed
-variable-length sequences, and its gradients; see ``oracle.attention`` for the definition and the
+variable-length sequences, its gradients, its fp8-input form, and the SwiGLU
+feed-forward layer of the same transformer block (``oracle.ffn``); see ``oracle.attention`` for the definition and the
 passages of the pages it follows.  Every function here is pinned by
 ``tests/test_oracle.py`` (brute force, closed forms, invariants and a library
 routine) except the readings listed as "parity unpinned" in
 ``oracle.attention``'s module docstring.
 """
 from .attention import attention_backward, attention_forward, attention_forward_fp8, attention_rows
+from .ffn import silu, swiglu_ffn, swiglu_ffn_rows
 
-__all__ = ["attention_forward", "attention_rows", "attention_backward", "attention_forward_fp8"]
+__all__ = ["attention_forward", "attention_rows", "attention_backward", "attention_forward_fp8", "silu",
+           "swiglu_ffn", "swiglu_ffn_rows"]

@@ -1,0 +1,138 @@
+"""Pins for the SwiGLU feed-forward oracle (``oracle.ffn``).
+
+  * brute force: scalar loops with math.fsum and math.exp on tiny inputs;
+  * a library routine: torch.nn.functional.silu and linear in float64;
+  * closed forms: SiLU(0) = 0, SiLU(z) -> z for large z and -> 0 for very
+    negative z, SiLU(1) = 1 / (1 + 1/e); a zero gate or a zero up projection
+    gives a zero output; with w_gate scaled so the gate is large, the layer
+    reduces to the bilinear (x Wg^T) * (x Wu^T) W_down^T;
+  * mutation tests: planted mistakes in a copy of the oracle must each fail.
+"""
+import math
+import os
+import types
+
+import pytest
+import torch
+
+import oracle
+from oracle.ffn import silu, swiglu_ffn
+from mea_workloads import swiglu_case
+
+FFN_SRC = os.path.join(os.path.dirname(oracle.__file__), "ffn.py")
+
+
+def brute(x, wg, wu, wd):
+    X, G, U, Dn = (t.double().tolist() for t in (x, wg, wu, wd))
+    T, dm, df = len(X), len(X[0]), len(G)
+    hid = [[0.0] * df for _ in range(T)]
+    out = [[0.0] * dm for _ in range(T)]
+    for t in range(T):
+        for f in range(df):
+            g = math.fsum(X[t][i] * G[f][i] for i in range(dm))
+            u = math.fsum(X[t][i] * U[f][i] for i in range(dm))
+            hid[t][f] = g / (1.0 + math.exp(-g)) * u
+        for j in range(dm):
+            out[t][j] = math.fsum(hid[t][f] * Dn[j][f] for f in range(df))
+    return torch.tensor(hid, dtype=torch.float64), torch.tensor(out, dtype=torch.float64)
+
+
+CASES = [(3, 4, 6), (5, 8, 3), (1, 16, 16), (7, 5, 9)]
+
+
+def _brute_ok(fn, ci):
+    T, dm, df = CASES[ci]
+    f = swiglu_case(100 + ci, T, dm, df, dtype="bf16")
+    h, o, _ = fn(f.x, f.w_gate, f.w_up, f.w_down)
+    bh, bo = brute(f.x, f.w_gate, f.w_up, f.w_down)
+    return (h - bh).abs().max().item() < 1e-12 and (o - bo).abs().max().item() < 1e-12
+
+
+def _library_ok(fn, seed=5):
+    F = torch.nn.functional
+    f = swiglu_case(seed, 33, 64, 96, dtype="fp16")
+    h, o, _ = fn(f.x, f.w_gate, f.w_up, f.w_down)
+    X, Wg, Wu, Wd = (t.double() for t in (f.x, f.w_gate, f.w_up, f.w_down))
+    ref_h = F.silu(F.linear(X, Wg)) * F.linear(X, Wu)
+    ref_o = F.linear(ref_h, Wd)
+    return (h - ref_h).abs().max().item() < 1e-12 and (o - ref_o).abs().max().item() < 1e-12
+
+
+def _special_ok(fn):
+    f = swiglu_case(9, 6, 8, 10, dtype="bf16")
+    zero = torch.zeros_like(f.w_gate)
+    _, o1, _ = fn(f.x, zero, f.w_up, f.w_down)      # SiLU(0) = 0
+    _, o2, _ = fn(f.x, f.w_gate, zero, f.w_down)    # up = 0
+    # large positive gate: SiLU(z) = z (to 1e-30 relative); make the gate x Wg^T >= 100 by a ramp input
+    x = torch.ones((2, 8), dtype=torch.float64)
+    wg = torch.full((10, 8), 20.0, dtype=torch.float64)
+    wu = f.w_up.double()
+    wd = f.w_down.double()
+    h3, o3, _ = fn(x, wg, wu, wd)
+    g = x @ wg.T
+    ok3 = (h3 - g * (x @ wu.T)).abs().max().item() < 1e-9
+    return o1.abs().max().item() == 0 and o2.abs().max().item() == 0 and ok3
+
+
+def test_silu_closed_forms():
+    z = torch.tensor([0.0, 1.0, -1.0, 50.0, -800.0], dtype=torch.float64)
+    s = silu(z)
+    assert s[0].item() == 0.0
+    assert abs(s[1].item() - 1.0 / (1.0 + math.exp(-1.0))) < 1e-15
+    assert abs(s[2].item() - (-1.0 / (1.0 + math.e))) < 1e-15
+    assert abs(s[3].item() - 50.0) < 1e-15
+    assert s[4].item() == 0.0 or abs(s[4].item()) < 1e-300
+
+
+@pytest.mark.parametrize("ci", range(len(CASES)))
+def test_brute_force(ci):
+    assert _brute_ok(swiglu_ffn, ci)
+
+
+def test_library_routine():
+    assert _library_ok(swiglu_ffn)
+
+
+def test_special_cases():
+    assert _special_ok(swiglu_ffn)
+
+
+def test_out_abs_bounds_out():
+    f = swiglu_case(3, 9, 16, 24)
+    _, o, a = swiglu_ffn(f.x, f.w_gate, f.w_up, f.w_down)
+    assert bool((o.abs() <= a + 1e-12).all())
+
+
+MUTATIONS = [
+    ("return z / (1.0 + torch.exp(-z))", "return 1.0 / (1.0 + torch.exp(-z))"),   # sigmoid for SiLU
+    ("return z / (1.0 + torch.exp(-z))", "return z / (1.0 + torch.exp(z))"),       # sign in the exponent
+    ("hidden = silu(gate) * up", "hidden = silu(up) * gate"),                      # gate and up swapped
+    ("hidden = silu(gate) * up", "hidden = gate * up"),                            # gate not activated
+    ("out = hidden @ Wd.transpose(0, 1)", "out = hidden @ Wd.transpose(0, 1) + hidden.sum() * 0 + 1e-9"),
+    ("gate = X @ Wg.transpose(0, 1)", "gate = X @ Wu.transpose(0, 1)"),            # wrong weight
+]
+
+
+def _mutant(old, new):
+    src = open(FFN_SRC).read()
+    assert src.count(old) == 1, old
+    mod = types.ModuleType("ffn_mutant")
+    mod.__dict__["math"] = math
+    exec(compile(src.replace(old, new), "ffn_mutant", "exec"), mod.__dict__)
+    return mod.swiglu_ffn
+
+
+def _pins_pass(fn):
+    try:
+        return all(_brute_ok(fn, ci) for ci in range(len(CASES))) and _library_ok(fn) and _special_ok(fn)
+    except Exception:
+        return False
+
+
+def test_unmutated_ffn_oracle_passes_pins():
+    assert _pins_pass(swiglu_ffn)
+
+
+@pytest.mark.parametrize("mi", range(len(MUTATIONS)))
+def test_planted_ffn_mistake_fails_pins(mi):
+    assert not _pins_pass(_mutant(*MUTATIONS[mi]))
