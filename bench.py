@@ -22,8 +22,10 @@ workload with ALiBi, ``decode_paged`` the decode workload with K/V in a
 paged cache (pages of 64 keys in a shuffled order, through mea_fwd_paged),
 ``backward`` the prefill workload's gradients (mea_bwd, dq/dk/dv from a
 seeded dO) at 2.5x the forward's unmasked FLOPs (five products against two),
-and ``prefill_fp8`` the prefill workload with q, k, v quantised to OCP e4m3
-(mea_fwd_fp8, per-tensor scales, bf16 output).
+``prefill_fp8`` the prefill workload with q, k, v quantised to OCP e4m3
+(mea_fwd_fp8, per-tensor scales, bf16 output), and ``swiglu_ffn`` the SwiGLU
+feed-forward layer of the same block on the same 137,663 tokens (d_model
+4096, d_ff 11008, bf16; 6 * T * d_model * d_ff FLOPs).
 """
 from __future__ import annotations
 
@@ -43,7 +45,8 @@ PEAK_HBM_GBS = 8000.0            # HBM3E
 PREFILL = "varlen_causal_gqa_64seq_h32kv8_d128_bf16"
 DECODE = "decode_splitkv_64req_h64kv8_d128_bf16"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-KERNEL_SOURCES = ["fwd_prefill.hip", "fwd_decode.hip", "bwd.hip", "mea_common.h", "mea_launch.h", "mea_tiles.h"]
+KERNEL_SOURCES = ["fwd_prefill.hip", "fwd_decode.hip", "bwd.hip", "ffn.hip", "mea_common.h", "mea_launch.h",
+                  "mea_tiles.h"]
 
 
 def unmasked_flops(inp) -> int:
@@ -224,6 +227,35 @@ PEAK_MFMA_FP8_TFLOPS = 5033.2    # dense fp8 MFMA: twice the bf16 rate
 # back to back: 1 / (0.5 / fp8 peak + 0.5 / bf16 peak)
 PEAK_FP8_FWD_TFLOPS = 1.0 / (0.5 / PEAK_MFMA_FP8_TFLOPS + 0.5 / PEAK_MFMA_BF16_TFLOPS)
 
+class FfnCall:
+    """Pre-bound SwiGLU feed-forward launch (mea_swiglu_ffn) on the prefill
+    workload's tokens: d_model 4096, d_ff 11008, bf16, seeded weights."""
+
+    def __init__(self, dev, seed):
+        import torch
+        from memory_efficient_attention_amd import _native
+        from mea_workloads import FFN_WORKLOAD, swiglu_case
+        w = FFN_WORKLOAD
+        f = swiglu_case(seed, w["tokens"], w["d_model"], w["d_ff"], dtype=w["dtype"])
+        self.shape = (w["tokens"], w["d_model"], w["d_ff"])
+        self.x, self.wg, self.wu, self.wd = (t.to(dev) for t in (f.x, f.w_gate, f.w_up, f.w_down))
+        self.hidden = torch.empty((w["tokens"], w["d_ff"]), dtype=self.x.dtype, device=dev)
+        self.out = torch.empty_like(self.x)
+        self.native = _native
+
+    def flops(self) -> int:
+        T, d, F = self.shape
+        return 6 * T * d * F   # gate, up (2 T d F each) and down (2 T F d)
+
+    def __call__(self, stream):
+        T, d, F = self.shape
+        st = self.native.mea_swiglu_ffn(self.x.data_ptr(), self.wg.data_ptr(), self.wu.data_ptr(), self.wd.data_ptr(),
+                                        self.hidden.data_ptr(), self.out.data_ptr(), T, d, F, self.native.MEA_BF16,
+                                        stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"mea_swiglu_ffn: {self.native.mea_status_string(st)}: {self.native.mea_last_error()}")
+
+
 BWD_GEMMS = 2.5   # backward algorithmic FLOPs / forward's: Q K^T, dO V^T, P^T dO, dS K, dS^T Q vs Q K^T, P V
 
 
@@ -300,7 +332,9 @@ def run_part(args, dev):
               flush=True)
         return
     name = PREFILL if args.part in ("prefill", "backward", "prefill_fp8") else DECODE
-    if args.part == "prefill_fp8":
+    if args.part == "ffn":
+        call = FfnCall(dev, args.seed)
+    elif args.part == "prefill_fp8":
         call = Fp8Call(generate(name, seed=args.seed), dev)
     elif args.part == "decode_paged":
         call = PagedCall(generate(name, seed=args.seed), dev, PAGE_SIZE)
@@ -319,13 +353,15 @@ def run_part(args, dev):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / max(args.steps, 1)
-    res = {"part": args.part, "workload": name, "ms": round(ms, 4)}
+    res = {"part": args.part, "workload": "swiglu_ffn" if args.part == "ffn" else name, "ms": round(ms, 4)}
     if args.part == "decode_paged":
         res["page_size"] = PAGE_SIZE
     if args.part in ("prefill", "prefill_fp8"):
         res["tflops"] = round(unmasked_flops(call.inp) / (ms * 1e-3) / 1e12, 2)
     elif args.part == "backward":
         res["tflops"] = round(BWD_GEMMS * unmasked_flops(call.inp) / (ms * 1e-3) / 1e12, 2)
+    elif args.part == "ffn":
+        res["tflops"] = round(call.flops() / (ms * 1e-3) / 1e12, 2)
     else:
         res["gbs"] = round(algorithmic_bytes(call.inp) / (ms * 1e-3) / 1e9, 1)
     print(json.dumps(res), flush=True)
@@ -343,8 +379,9 @@ def main():
     ap.add_argument("--no-paged-variant", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--no-ffn", action="store_true")
     ap.add_argument("--part", choices=["all", "prefill", "decode", "decode_paged", "backward", "prefill_fp8",
-                                       "copy"],
+                                       "ffn", "copy"],
                     default="all",
                     help="run only one half of the step, or the calibration copy (for profiling); "
                          "the JSON line is for 'all'")
@@ -382,6 +419,9 @@ def main():
     fp8_call = None
     if not args.no_fp8:
         fp8_call = Fp8Call(pre, dev)
+    ffn_call = None
+    if not args.no_ffn:
+        ffn_call = FfnCall(dev, args.seed)
     torch.cuda.synchronize()
     print(f"[bench] inputs generated and resident in HBM in {time.perf_counter() - t_gen:.1f} s",
           file=sys.stderr, flush=True)
@@ -458,6 +498,18 @@ def main():
                                 "kernel": "mea_fwd_fp8 call: vt_images_kernel<fp8> + fwd_prefill_kernel<128,bf16 out,"
                                           "causal,fp8>"}}
 
+    ffn_res = None
+    if ffn_call is not None:  # the SwiGLU feed-forward layer on the prefill workload's tokens
+        nms = time_calls(ffn_call, stream, max(3, K // 6))
+        ntf = ffn_call.flops() / (nms * 1e-3) / 1e12
+        T, d, F = ffn_call.shape
+        ffn_res = {"ms": round(nms, 4), "value": round(ntf, 2), "unit": "TFLOP/s",
+                   "config": {"tokens": T, "d_model": d, "d_ff": F, "dtype": "bf16", "flops": ffn_call.flops()},
+                   "roofline": {"bound": "mfma", "achieved": round(ntf, 2), "peak": PEAK_MFMA_BF16_TFLOPS,
+                                "unit": "TFLOP/s", "frac": round(ntf / PEAK_MFMA_BF16_TFLOPS, 4),
+                                "traffic": measured_traffic("ffn"),
+                                "kernel": "mea_swiglu_ffn call: ffn_gemm_kernel<bf16,gated> + ffn_gemm_kernel<bf16>"}}
+
     traffic_pre = measured_traffic("fwd_prefill")
     traffic_dec = measured_traffic("fwd_decode")
     line = {
@@ -500,6 +552,7 @@ def main():
         "prefill_alibi": alibi_res,
         "backward": bwd_res,
         "prefill_fp8": fp8_res,
+        "swiglu_ffn": ffn_res,
         "decode_paged": paged_res,
         "cpu_baseline": None,
     }

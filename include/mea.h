@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define MEA_ABI_VERSION 5
+#define MEA_ABI_VERSION 6
 
 #if defined(__GNUC__)
 #define MEA_EXPORT __attribute__((visibility("default")))
@@ -301,6 +301,31 @@ MEA_EXPORT mea_status_t mea_bwd(const void* q, const void* k, const void* v, con
  */
 MEA_EXPORT size_t mea_bwd_workspace_size(int32_t num_seqs, int32_t total_q, int32_t total_k, int32_t Hq,
                                          int32_t Hkv, int32_t D);
+
+/*
+ * mea_swiglu_ffn -- the SwiGLU feed-forward layer of the transformer block the
+ * tutorials build around this attention: section 4 of the yifor-blog page's
+ * optimisations replaces the ReLU/GELU feed-forward with a SwiGLU one (the
+ * 7minutos.es title names it too).  The pages give no formula; this is the
+ * gated form with the SiLU (swish) gate:
+ *   hidden = SiLU(x w_gate^T) * (x w_up^T)       SiLU(z) = z / (1 + exp(-z))
+ *   out    = hidden w_down^T
+ *   x       [tokens, d_model]      w_gate, w_up [d_ff, d_model]
+ *   hidden  [tokens, d_ff]         w_down       [d_model, d_ff]
+ *   out     [tokens, d_model]
+ * (weights in the out_features x in_features layout of a linear layer).  All
+ * arrays are device memory of `dtype` (MEA_F16 or MEA_BF16), row-major and
+ * 16-byte aligned; hidden is written (rounded to dtype) and is the input of
+ * the second product.  Products run on the matrix cores in dtype with float32
+ * accumulation; SiLU and the gate product are float32.
+ * Returns MEA_ERR_INVALID for a NULL pointer, tokens < 0, d_model or d_ff <= 0;
+ * MEA_ERR_UNSUPPORTED for another dtype, misalignment, d_model not a multiple
+ * of 256 or d_ff not a multiple of 128 (or either above 65536).  tokens == 0
+ * is a no-op.  Ownership and execution as for mea_fwd.
+ */
+MEA_EXPORT mea_status_t mea_swiglu_ffn(const void* x, const void* w_gate, const void* w_up, const void* w_down,
+                                       void* hidden, void* out, int32_t tokens, int32_t d_model, int32_t d_ff,
+                                       mea_dtype_t dtype, void* stream);
 
 /* Piece length of the key axis that mea_fwd picks for a decode call with
  * these sizes (a multiple of 32, at least 128).  Pure host function. */

@@ -15,7 +15,8 @@ __all__ = [
     "MEA_OK", "MEA_ERR_INVALID", "MEA_ERR_UNSUPPORTED", "MEA_ERR_HIP", "MEA_F16", "MEA_BF16",
     "EXPORTED_SYMBOLS", "library_path", "load", "mea_fwd", "mea_fwd_splitkv", "mea_fwd_paged",
     "mea_fwd_workspace_size", "mea_default_chunk_keys", "mea_bwd", "mea_bwd_workspace_size",
-    "mea_fwd_fp8", "mea_fwd_fp8_workspace_size", "mea_status_string", "mea_last_error", "mea_abi_version",
+    "mea_fwd_fp8", "mea_fwd_fp8_workspace_size", "mea_swiglu_ffn", "mea_status_string", "mea_last_error",
+    "mea_abi_version",
 ]
 
 MEA_OK, MEA_ERR_INVALID, MEA_ERR_UNSUPPORTED, MEA_ERR_HIP = 0, 1, 2, 3
@@ -23,8 +24,8 @@ MEA_F16, MEA_BF16 = 0, 1
 
 EXPORTED_SYMBOLS = (
     "mea_fwd", "mea_fwd_splitkv", "mea_fwd_paged", "mea_fwd_workspace_size", "mea_default_chunk_keys",
-    "mea_bwd", "mea_bwd_workspace_size", "mea_fwd_fp8", "mea_fwd_fp8_workspace_size", "mea_status_string",
-    "mea_last_error", "mea_abi_version",
+    "mea_bwd", "mea_bwd_workspace_size", "mea_fwd_fp8", "mea_fwd_fp8_workspace_size", "mea_swiglu_ffn",
+    "mea_status_string", "mea_last_error", "mea_abi_version",
 )
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -93,6 +94,8 @@ def load() -> ctypes.CDLL:
         lib.mea_fwd_fp8.restype = ctypes.c_int
         lib.mea_fwd_fp8_workspace_size.argtypes = [_i32] * 4
         lib.mea_fwd_fp8_workspace_size.restype = _sz
+        lib.mea_swiglu_ffn.argtypes = [_vp] * 6 + [_i32, _i32, _i32, _i32, _vp]
+        lib.mea_swiglu_ffn.restype = ctypes.c_int
         lib.mea_status_string.argtypes = [ctypes.c_int]
         lib.mea_status_string.restype = ctypes.c_char_p
         lib.mea_last_error.argtypes = []
@@ -161,6 +164,10 @@ def mea_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, out, lse, seqstart_q, seqsta
 
 def mea_fwd_fp8_workspace_size(num_seqs, total_k, Hkv, D) -> int:
     return int(load().mea_fwd_fp8_workspace_size(num_seqs, total_k, Hkv, D))
+
+
+def mea_swiglu_ffn(x, w_gate, w_up, w_down, hidden, out, tokens, d_model, d_ff, dtype, stream) -> int:
+    return load().mea_swiglu_ffn(x, w_gate, w_up, w_down, hidden, out, tokens, d_model, d_ff, dtype, stream)
 
 
 def mea_status_string(status: int) -> str:

@@ -23,7 +23,8 @@ from . import _native
 
 __all__ = [
     "BlockDiagonalMask", "BlockDiagonalCausalMask", "memory_efficient_attention",
-    "attention_packed", "attention_paged", "attention_backward_packed", "attention_packed_fp8", "MeaError",
+    "attention_packed", "attention_paged", "attention_backward_packed", "attention_packed_fp8", "swiglu_ffn",
+    "MeaError",
 ]
 
 
@@ -397,6 +398,41 @@ def attention_packed_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, q
     if st != _native.MEA_OK:
         raise MeaError(st, _native.mea_last_error())
     return (out, lse) if return_lse else out
+
+
+def swiglu_ffn(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor, *,
+               hidden: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+               return_hidden: bool = False, stream: Optional[torch.cuda.Stream] = None):
+    """SwiGLU feed-forward: ``(SiLU(x w_gate^T) * (x w_up^T)) w_down^T`` for
+    ``x [tokens, d_model]``, ``w_gate``/``w_up [d_ff, d_model]``,
+    ``w_down [d_model, d_ff]`` (torch Linear weight layout).  Returns ``out``
+    (and the hidden activations if ``return_hidden``)."""
+    if x.dim() != 2:
+        raise ValueError("x must be [tokens, d_model]")
+    T, d_model = x.shape
+    d_ff = w_gate.shape[0]
+    if tuple(w_gate.shape) != (d_ff, d_model) or tuple(w_up.shape) != (d_ff, d_model) \
+            or tuple(w_down.shape) != (d_model, d_ff):
+        raise ValueError(f"weight shapes {tuple(w_gate.shape)}, {tuple(w_up.shape)}, {tuple(w_down.shape)} "
+                         f"do not match x {tuple(x.shape)}")
+    if not (x.dtype == w_gate.dtype == w_up.dtype == w_down.dtype):
+        raise TypeError("x and the weights must share a dtype")
+    dev = x.device
+    if dev.type != "cuda" or any(t.device != dev for t in (w_gate, w_up, w_down)):
+        raise ValueError("x and the weights must be on the same GPU")
+    x, w_gate, w_up, w_down = (t.contiguous() for t in (x, w_gate, w_up, w_down))
+    if hidden is None:
+        hidden = torch.empty((T, d_ff), dtype=x.dtype, device=dev)
+    if out is None:
+        out = torch.empty((T, d_model), dtype=x.dtype, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        st = _native.mea_swiglu_ffn(_ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(hidden), _ptr(out), T,
+                                    d_model, d_ff, _dtype_code(x.dtype), stream.cuda_stream)
+    if st != _native.MEA_OK:
+        raise MeaError(st, _native.mea_last_error())
+    return (out, hidden) if return_hidden else out
 
 
 def _kv_heads_bmghk(k: torch.Tensor, hq: int) -> torch.Tensor:

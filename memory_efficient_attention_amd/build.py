@@ -15,7 +15,7 @@ REPO_DIR = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(REPO_DIR, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libmea.so")
-SOURCES = ["fwd_prefill.hip", "fwd_decode.hip", "bwd.hip", "mea_api.cpp"]
+SOURCES = ["fwd_prefill.hip", "fwd_decode.hip", "bwd.hip", "ffn.hip", "mea_api.cpp"]
 ARCH = "gfx950"
 
 

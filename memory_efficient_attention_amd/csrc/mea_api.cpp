@@ -403,6 +403,29 @@ size_t mea_fwd_fp8_workspace_size(int32_t num_seqs, int32_t total_k, int32_t Hkv
   return prefill_ws_bytes(num_seqs, total_k, Hkv, D);
 }
 
+mea_status_t mea_swiglu_ffn(const void* x, const void* w_gate, const void* w_up, const void* w_down, void* hidden,
+                            void* out, int32_t tokens, int32_t d_model, int32_t d_ff, mea_dtype_t dtype,
+                            void* stream) {
+  g_last_error[0] = '\0';
+  if (x == nullptr || w_gate == nullptr || w_up == nullptr || w_down == nullptr || hidden == nullptr ||
+      out == nullptr)
+    return fail(MEA_ERR_INVALID, "x, w_gate, w_up, w_down, hidden and out must be non-NULL device pointers");
+  if (tokens < 0) return fail(MEA_ERR_INVALID, "negative tokens (%d)", tokens);
+  if (d_model <= 0 || d_ff <= 0) return fail(MEA_ERR_INVALID, "need d_model > 0 and d_ff > 0 (got %d, %d)", d_model, d_ff);
+  if (dtype != MEA_F16 && dtype != MEA_BF16) return fail(MEA_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+  if (d_model % 256 != 0 || d_ff % 128 != 0 || d_model > 65536 || d_ff > 65536)
+    return fail(MEA_ERR_UNSUPPORTED, "need d_model a multiple of 256 and d_ff a multiple of 128, both <= 65536 "
+                "(got %d, %d)", d_model, d_ff);
+  if (!aligned(x, 16) || !aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(w_down, 16) || !aligned(hidden, 16) ||
+      !aligned(out, 16))
+    return fail(MEA_ERR_UNSUPPORTED, "all pointers must be 16-byte aligned");
+  if (tokens == 0) return MEA_OK;
+  const hipError_t err = mea::launch_swiglu_ffn(x, w_gate, w_up, w_down, hidden, out, tokens, d_model, d_ff,
+                                                dtype == MEA_BF16, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(MEA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+  return MEA_OK;
+}
+
 size_t mea_fwd_workspace_size(int32_t num_seqs, int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
                               int32_t Hq, int32_t Hkv, int32_t D, int32_t chunk_keys) {
   if (num_seqs <= 0 || total_k < 0 || max_seqlen_q <= 0 || max_seqlen_k < 0 || Hq <= 0 || Hkv <= 0 ||

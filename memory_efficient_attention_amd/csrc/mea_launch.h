@@ -40,5 +40,7 @@ hipError_t launch_prefill_fp8(const FwdArgs& a, bool out_bf16, bool causal, bool
                               hipStream_t stream);
 hipError_t launch_decode(const FwdArgs& a, int D, bool bf16, bool alibi, hipStream_t stream);
 hipError_t launch_backward(const BwdArgs& a, int D, bool bf16, bool causal, bool alibi, hipStream_t stream);
+hipError_t launch_swiglu_ffn(const void* x, const void* w_gate, const void* w_up, const void* w_down, void* hidden,
+                             void* out, int tokens, int d_model, int d_ff, bool bf16, hipStream_t stream);
 
 }  // namespace mea

@@ -48,7 +48,7 @@ def test_every_kernel_stub_is_defined():
 
 
 def test_version_and_strings():
-    assert _native.mea_abi_version() == 5
+    assert _native.mea_abi_version() == 6
     for st in range(4):
         assert _native.mea_status_string(st).startswith("MEA_")
     assert "unknown" in _native.mea_status_string(99)
@@ -261,3 +261,30 @@ def test_fp8_workspace_size():
     assert ws(4, 365, 2, 64) == 0
     assert ws(0, 365, 2, 128) == 0
     assert ws(4, 0, 2, 128) == 0
+
+
+def call_ffn(**kw):
+    a = dict(x=P, w_gate=P, w_up=P, w_down=P, hidden=P, out=P, tokens=100, d_model=4096, d_ff=11008,
+             dtype=MEA_BF16, stream=None)
+    a.update(kw)
+    return _native.mea_swiglu_ffn(**a)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(x=None), MEA_ERR_INVALID, "non-NULL"),
+    (dict(hidden=None), MEA_ERR_INVALID, "non-NULL"),
+    (dict(tokens=-1), MEA_ERR_INVALID, "negative"),
+    (dict(d_ff=0), MEA_ERR_INVALID, "d_ff > 0"),
+    (dict(d_model=4000), MEA_ERR_UNSUPPORTED, "multiple of 256"),
+    (dict(d_ff=11000), MEA_ERR_UNSUPPORTED, "multiple of 128"),
+    (dict(d_model=1 << 17), MEA_ERR_UNSUPPORTED, "65536"),
+    (dict(dtype=3), MEA_ERR_UNSUPPORTED, "dtype"),
+    (dict(w_down=P + 8), MEA_ERR_UNSUPPORTED, "16-byte"),
+])
+def test_ffn_rejected_before_launch(kw, status, needle):
+    assert call_ffn(**kw) == status
+    assert needle in _native.mea_last_error()
+
+
+def test_ffn_empty_is_a_noop():
+    assert call_ffn(tokens=0) == MEA_OK
