@@ -124,27 +124,45 @@ __global__ __launch_bounds__(kFfThreads) void ffn_gemm_kernel(FfnArgs p) {
 #pragma unroll
     for (int j = 0; j < 2 * NB / (GATED ? 1 : 2); ++j) acc[i][j] = f32x16{};
 
+  // Fragments of sub-step kk are read one sub-step ahead into the other half
+  // of a register double buffer, so each read has 8 products' time to land.
+  constexpr int NJ = 2 * NB / (GATED ? 1 : 2);  // B fragments per sub-step
+  auto read_frags = [&](const uint8_t* A, const uint8_t* B, int kk, u32x4 (&af)[2], u32x4 (&bf)[NJ]) {
+    const int c = 2 * kk + hi;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int r = 64 * wm + 32 * mb + l32;
+      af[mb] = *(const u32x4*)(A + r * kRowBytes + ff_pos(r, c) * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      // GATED: j < 2 gate columns 64 wn + 32 j, j >= 2 up columns 128 + 64 wn + 32 (j - 2)
+      const int r = GATED ? (j < 2 ? 64 * wn + 32 * j : 128 + 64 * wn + 32 * (j - 2)) + l32
+                          : 128 * wn + 32 * j + l32;
+      bf[j] = *(const u32x4*)(B + r * kRowBytes + ff_pos(r, c) * 16);
+    }
+  };
   auto compute = [&](int ks) {
     const uint8_t* A = smem + (ks & 1) * kStageBytes;
     const uint8_t* B = A + kTileBytes;
+    u32x4 af[2][2], bf[2][NJ];
+    read_frags(A, B, 0, af[0], bf[0]);
 #pragma unroll
     for (int kk = 0; kk < kBK / 16; ++kk) {
-      const int c = 2 * kk + hi;
-      u32x4 af[2];
+      if (kk + 1 < kBK / 16) read_frags(A, B, kk + 1, af[(kk + 1) & 1], bf[(kk + 1) & 1]);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const int r = 64 * wm + 32 * mb + l32;
-        af[mb] = *(const u32x4*)(A + r * kRowBytes + ff_pos(r, c) * 16);
-      }
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int j = 0; j < 2 * NB / (GATED ? 1 : 2); ++j) {
-        // GATED: j < 2 gate columns 64 wn + 32 j, j >= 2 up columns 128 + 64 wn + 32 (j - 2)
-        const int r = GATED ? (j < 2 ? 64 * wn + 32 * j : 128 + 64 * wn + 32 * (j - 2)) + l32
-                            : 128 * wn + 32 * j + l32;
-        const u32x4 bf = *(const u32x4*)(B + r * kRowBytes + ff_pos(r, c) * 16);
+        for (int mb = 0; mb < 2; ++mb) acc[mb][j] = mfma_32x32x16<BF16>(af[kk & 1][mb], bf[kk & 1][j], acc[mb][j]);
+    }
+    // order: reads of sub-steps 0 and 1, then (products of kk, reads of kk + 2),
+    // so every read is issued a full sub-step of products before its use
+    constexpr int NR = 2 + NJ;  // reads per sub-step
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * NR, 0);
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) acc[mb][j] = mfma_32x32x16<BF16>(af[mb], bf, acc[mb][j]);
-      }
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NJ, 0);
+      if (kk + 2 < kBK / 16) __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
     }
   };
 
