@@ -70,6 +70,14 @@ def algorithmic_bytes(inp, with_lse=True) -> int:
     return b
 
 
+def algorithmic_bytes_fp8(inp, with_lse=True) -> int:
+    """The fp8 call's Q + K + V (one byte each) + O (bf16) (+ LSE)."""
+    b = inp.q.numel() * (1 + 2) + inp.k.numel() + inp.v.numel()
+    if with_lse:
+        b += inp.Hq * inp.total_q * 4
+    return b
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
@@ -205,7 +213,8 @@ class Fp8Call:
         self.slopes = None if inp.alibi_slopes is None else inp.alibi_slopes.to(dev)
         self.out = torch.empty((inp.total_q, inp.Hq, inp.D), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((inp.Hq, inp.total_q), dtype=torch.float32, device=dev)
-        self.ws_bytes = _native.mea_fwd_fp8_workspace_size(len(inp.seqlens_q), inp.total_k, inp.Hkv, inp.D)
+        self.ws_bytes = _native.mea_fwd_fp8_workspace_size(len(inp.seqlens_q), inp.total_k, inp.max_seqlen_q,
+                                                            inp.max_seqlen_k, inp.Hq, inp.Hkv, inp.D)
         self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=dev)
         self.native = _native
 
@@ -334,7 +343,7 @@ def run_part(args, dev):
     name = PREFILL if args.part in ("prefill", "backward", "prefill_fp8") else DECODE
     if args.part == "ffn":
         call = FfnCall(dev, args.seed)
-    elif args.part == "prefill_fp8":
+    elif args.part in ("prefill_fp8", "decode_fp8"):
         call = Fp8Call(generate(name, seed=args.seed), dev)
     elif args.part == "decode_paged":
         call = PagedCall(generate(name, seed=args.seed), dev, PAGE_SIZE)
@@ -362,6 +371,8 @@ def run_part(args, dev):
         res["tflops"] = round(BWD_GEMMS * unmasked_flops(call.inp) / (ms * 1e-3) / 1e12, 2)
     elif args.part == "ffn":
         res["tflops"] = round(call.flops() / (ms * 1e-3) / 1e12, 2)
+    elif args.part == "decode_fp8":
+        res["gbs"] = round(algorithmic_bytes_fp8(call.inp) / (ms * 1e-3) / 1e9, 1)
     else:
         res["gbs"] = round(algorithmic_bytes(call.inp) / (ms * 1e-3) / 1e9, 1)
     print(json.dumps(res), flush=True)
@@ -381,7 +392,7 @@ def main():
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-ffn", action="store_true")
     ap.add_argument("--part", choices=["all", "prefill", "decode", "decode_paged", "backward", "prefill_fp8",
-                                       "ffn", "copy"],
+                                       "decode_fp8", "ffn", "copy"],
                     default="all",
                     help="run only one half of the step, or the calibration copy (for profiling); "
                          "the JSON line is for 'all'")
@@ -416,9 +427,10 @@ def main():
     bwd_call = None
     if not args.no_backward:
         bwd_call = BwdCall(Call(pre, dev), dev, args.seed)
-    fp8_call = None
+    fp8_call = fp8_dec_call = None
     if not args.no_fp8:
         fp8_call = Fp8Call(pre, dev)
+        fp8_dec_call = Fp8Call(dec, dev)
     ffn_call = None
     if not args.no_ffn:
         ffn_call = FfnCall(dev, args.seed)
@@ -498,6 +510,19 @@ def main():
                                 "kernel": "mea_fwd_fp8 call: vt_images_kernel<fp8> + fwd_prefill_kernel<128,bf16 out,"
                                           "causal,fp8>"}}
 
+    fp8_dec_res = None
+    if fp8_dec_call is not None:  # the decode workload with q, k, v in e4m3: half the K/V bytes
+        dfms = time_calls(fp8_dec_call, stream, max(5, K // 2))
+        dfb = algorithmic_bytes_fp8(dec)
+        dfgb = dfb / (dfms * 1e-3) / 1e9
+        fp8_dec_res = {"ms": round(dfms, 4), "value": round(dfgb, 1), "unit": "GB/s",
+                       "speedup_vs_bf16_decode": round(dec_ms / dfms, 3), "algorithmic_bytes": dfb,
+                       "roofline": {"bound": "hbm", "achieved": round(dfgb, 1), "peak": PEAK_HBM_GBS,
+                                    "unit": "GB/s", "frac": round(dfgb / PEAK_HBM_GBS, 4),
+                                    "traffic": measured_traffic("fwd_decode_fp8"),
+                                    "kernel": "mea_fwd_fp8 decode call: fwd_decode_partial_kernel<128,bf16 out,"
+                                              "fp8> + fwd_decode_combine_kernel"}}
+
     ffn_res = None
     if ffn_call is not None:  # the SwiGLU feed-forward layer on the prefill workload's tokens
         nms = time_calls(ffn_call, stream, max(3, K // 6))
@@ -552,6 +577,7 @@ def main():
         "prefill_alibi": alibi_res,
         "backward": bwd_res,
         "prefill_fp8": fp8_res,
+        "decode_fp8": fp8_dec_res,
         "swiglu_ffn": ffn_res,
         "decode_paged": paged_res,
         "cpu_baseline": None,

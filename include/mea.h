@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define MEA_ABI_VERSION 6
+#define MEA_ABI_VERSION 7
 
 #if defined(__GNUC__)
 #define MEA_EXPORT __attribute__((visibility("default")))
@@ -222,11 +222,14 @@ MEA_EXPORT size_t mea_fwd_workspace_size(int32_t num_seqs, int32_t total_k, int3
  *   q/k/v_scale    host floats, finite and > 0.
  *   out            device [total_q, Hq, D] of out_dtype.
  *   D              128 only (MEA_ERR_UNSUPPORTED otherwise).
- *   workspace      mea_fwd_fp8_workspace_size(num_seqs, total_k, Hkv, D) bytes
- *                  (half-precision V^T tile images), 256-byte aligned.
- * Every call, decode-shaped (max_seqlen_q == 1) ones included, runs the
- * prefill kernel.  No paged variant.  Same ownership and errors as mea_fwd,
- * plus MEA_ERR_UNSUPPORTED for a non-finite or non-positive scale.
+ *   workspace      mea_fwd_fp8_workspace_size(num_seqs, total_k, max_seqlen_q,
+ *                  max_seqlen_k, Hq, Hkv, D) bytes, 256-byte aligned.
+ * Path choice as in mea_fwd: max_seqlen_q == 1 runs the split-KV decode
+ * kernels (pieces of mea_default_chunk_keys(total_k, Hq, Hkv) keys, float32
+ * partials in the workspace), anything else the prefill kernel (half-precision
+ * V^T tile images in the workspace).  No paged variant.  Same ownership and
+ * errors as mea_fwd, plus MEA_ERR_UNSUPPORTED for a non-finite or
+ * non-positive scale.
  */
 MEA_EXPORT mea_status_t mea_fwd_fp8(const void* q, const void* k, const void* v, float q_scale, float k_scale,
                                     float v_scale, void* out, float* lse, const int32_t* seqstart_q,
@@ -235,10 +238,11 @@ MEA_EXPORT mea_status_t mea_fwd_fp8(const void* q, const void* k, const void* v,
                                     mea_dtype_t out_dtype, int32_t causal, const float* alibi_slopes, float scale,
                                     void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes of mea_fwd_fp8: (total_k / 64 + num_seqs) * Hkv * D * 128
- * (0 when total_k == 0 or for arguments mea_fwd_fp8 rejects).  Pure host
+/* Workspace bytes of mea_fwd_fp8: mea_fwd_workspace_size(num_seqs, total_k,
+ * max_seqlen_q, max_seqlen_k, Hq, Hkv, D, 0) for D == 128, else 0.  Pure host
  * function. */
-MEA_EXPORT size_t mea_fwd_fp8_workspace_size(int32_t num_seqs, int32_t total_k, int32_t Hkv, int32_t D);
+MEA_EXPORT size_t mea_fwd_fp8_workspace_size(int32_t num_seqs, int32_t total_k, int32_t max_seqlen_q,
+                                             int32_t max_seqlen_k, int32_t Hq, int32_t Hkv, int32_t D);
 
 /*
  * mea_bwd -- gradients of the attention of mea_fwd: given dout = dL/dout for

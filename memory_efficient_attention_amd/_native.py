@@ -92,7 +92,7 @@ def load() -> ctypes.CDLL:
         lib.mea_bwd_workspace_size.restype = _sz
         lib.mea_fwd_fp8.argtypes = _FP8_ARGS
         lib.mea_fwd_fp8.restype = ctypes.c_int
-        lib.mea_fwd_fp8_workspace_size.argtypes = [_i32] * 4
+        lib.mea_fwd_fp8_workspace_size.argtypes = [_i32] * 7
         lib.mea_fwd_fp8_workspace_size.restype = _sz
         lib.mea_swiglu_ffn.argtypes = [_vp] * 6 + [_i32, _i32, _i32, _i32, _vp]
         lib.mea_swiglu_ffn.restype = ctypes.c_int
@@ -162,8 +162,8 @@ def mea_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, out, lse, seqstart_q, seqsta
                               alibi_slopes, scale, workspace, workspace_bytes, stream)
 
 
-def mea_fwd_fp8_workspace_size(num_seqs, total_k, Hkv, D) -> int:
-    return int(load().mea_fwd_fp8_workspace_size(num_seqs, total_k, Hkv, D))
+def mea_fwd_fp8_workspace_size(num_seqs, total_k, max_seqlen_q, max_seqlen_k, Hq, Hkv, D) -> int:
+    return int(load().mea_fwd_fp8_workspace_size(num_seqs, total_k, max_seqlen_q, max_seqlen_k, Hq, Hkv, D))
 
 
 def mea_swiglu_ffn(x, w_gate, w_up, w_down, hidden, out, tokens, d_model, d_ff, dtype, stream) -> int:

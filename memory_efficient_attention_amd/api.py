@@ -384,7 +384,7 @@ def attention_packed_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, q
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     scale = float(np.float32(scale))
-    ws_bytes = _native.mea_fwd_fp8_workspace_size(num_seqs, Tk, Hkv, D)
+    ws_bytes = _native.mea_fwd_fp8_workspace_size(num_seqs, Tk, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, D)
     if ws_bytes > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     if stream is None:

@@ -11,22 +11,25 @@
 // sequence and the start of the next produces one partial result per
 // sequence it touches.
 //
-// Partial kernel: a workgroup takes one piece and nh = gcd(Hkv, 4)
-// neighbouring key/value heads (with up to 16 query heads of each head's
-// group).  Wave w serves head w % nh and streams every (4/nh)-th 32-key block
-// of the piece's part of a sequence, starting at block w / nh, independently
-// (no workgroup barrier until the end of that part), with its own
-// online-softmax state.  The nh heads of a key are adjacent in memory, so a
+// Partial kernel: a workgroup of 8 waves (one per CU) takes one piece and
+// nh = gcd(Hkv, 4) neighbouring key/value heads (with up to 16 query heads of
+// each head's group).  The nh heads of a key are adjacent in memory, so a
 // workgroup reads runs of nh * D * 2 contiguous bytes per key rather than one
-// head's D * 2 bytes out of each token row.  Per block, a wave computes
+// head's D * 2 bytes out of each token row.  Wave w serves head w % nh; the
+// 8 / nh waves of a head claim the 32-key blocks of the piece's part of a
+// sequence one at a time from a counter in LDS (the two waves of a SIMD do
+// not issue at the same rate, and a fixed split would leave the workgroup
+// waiting for the slower one), each with its own online-softmax state.  Per
+// block, a wave computes
 //   S^T = K Q^T   16x16x32 products; the query heads of the group are the 16
 //                 columns, so one K/V read serves every head of the group
 //                 (GQA's saving becomes fewer HBM bytes);
 //   O^T += V^T P^T  with V transposed through a per-wave LDS slot.
 // K goes from HBM straight into the product's operand registers; the loads of
-// block i+1 are in flight while block i is computed.  At the end of each
-// sequence part the waves of a head merge in LDS and write one normalised
-// float32 partial output and its log-sum-exp (log2 units) per query head.
+// the next claimed block are in flight while a block is computed.  At the end
+// of each sequence part the waves of a head merge in LDS and write one
+// normalised float32 partial output and its log-sum-exp (log2 units) per
+// query head.
 //
 // Combine kernel: per (sequence, query head) the piece partials are merged
 // by their log-sum-exps: lse = log sum_c exp(lse_c), out = sum_c exp(lse_c -
@@ -38,8 +41,6 @@ namespace mea {
 
 namespace {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
 template <bool BF16>
 __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   if constexpr (BF16) {
@@ -49,8 +50,8 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   }
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, (int)bytes, 0x00020000);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
 // Cache policy of the K/V stream loads: non-temporal (the nt bit).  Every K/V
@@ -64,12 +65,23 @@ constexpr int kVtStride = kBlk + 8;       // elements per V^T row in a wave's LD
 
 }  // namespace
 
-template <int D, bool BF16, bool ALIBI, bool PAGED>
+// FP8: q, k and v hold OCP e4m3 values (one byte each) and BF16 names the
+// output dtype.  Q K^T runs on the 16x16x128 fp8 products; V is widened to
+// IEEE halves (exactly) on its way into the LDS transpose, so P V is the
+// 16-bit path's product.  A wave block is then two 32-key sub-blocks, which
+// keeps the bytes in flight per wave those of the 16-bit kernel.
+template <int D, bool BF16, bool ALIBI, bool PAGED, bool FP8 = false>
 __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void fwd_decode_partial_kernel(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the body uses buffer-resource types that exist only for the GPU target
+  constexpr int ESZ = FP8 ? 1 : 2;        // bytes per q/k/v element
   constexpr int KS = D / 32;              // k-steps of the 16x16x32 Q K^T product
+  constexpr int KR = FP8 ? D / 64 : KS;   // 16-byte K chunks per lane and 16-key half of a sub-block
+  constexpr int QR = FP8 ? D / 64 : KS;   // 16-byte Q chunks per lane
+  constexpr int NSB = FP8 ? 2 : 1;        // 32-key sub-blocks per wave block
+  constexpr int NBUF = 2;                 // register buffers: NBUF - 1 blocks in flight
+  constexpr int kBlkKeys = kBlk * NSB;    // keys per wave block
   constexpr int DB = D / 16;              // 16-feature blocks of O^T
-  constexpr int VCH = D / 64;             // 16-byte V chunks per lane per key
+  constexpr int VCH = D * ESZ / 128;      // 16-byte V chunks per lane per key
   constexpr int kSlotElems = D * kVtStride;
   constexpr int kRedStride = D + 1;       // floats per query column in the merge buffer
   constexpr int kSmemBytes = kWaves * kSlotElems * 2 > kWaves * 16 * kRedStride * 4 + 2 * kWaves * 16 * 4
@@ -85,11 +97,16 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void fwd_decode_partial_ke
   // A head group is nh neighbouring key/value heads and one slice of 16
   // query heads of each head's group.
   const int nh = a.kv_per_wg, stripes = kWaves / nh;
-  const int hh = wave % nh, stripe = wave / nh;
+  const int hh = wave % nh;
   const int groups = (a.Hkv / nh) * a.head_slices;
   const int piece = blockIdx.x / groups, gi = blockIdx.x - piece * groups;
   const int g = (gi / a.head_slices) * nh + hh, hs = gi % a.head_slices;
   const int g0 = (gi / a.head_slices) * nh;  // first head of the group
+
+  // next unclaimed block of the current segment, per head of the group
+  __shared__ int next_blk[kDcKvPerWgMax];
+  if (tid < kDcKvPerWgMax) next_blk[tid] = 0;
+  __syncthreads();
 
   // the piece: keys [k0, k1) of the concatenated key axis
   const int W = a.chunk_keys;
@@ -122,14 +139,15 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void fwd_decode_partial_ke
 
   // Q^T operand: lane (q, g4) holds 16-byte feature chunk 4*ks + g4 at k-step
   // ks (the K operand uses the same chunks, so a K load instruction reads 64
-  // contiguous bytes of each of its 16 rows)
-  u32x4 qf[KS];
+  // contiguous bytes of each of its 16 rows).  fp8: lane (q, g4) holds bytes
+  // 32*g4 .. +31 of the row for the single 16x16x128 product, K the same.
+  u32x4 qf[QR];
   {
-    const uint16_t* qrow = a.q + ((size_t)sq0 * a.Hq + head) * D + 8 * g4;
+    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) + ((size_t)sq0 * a.Hq + head) * D * ESZ;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int ks = 0; ks < QR; ++ks) {
       u32x4 x = {0u, 0u, 0u, 0u};
-      if (col_valid) x = *(const u32x4*)(qrow + 32 * ks);
+      if (col_valid) x = *(const u32x4*)(qrow + (FP8 ? 32 * g4 + 16 * ks : 16 * g4 + 64 * ks));
       qf[ks] = x;
     }
   }
@@ -139,52 +157,70 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void fwd_decode_partial_ke
 
   // K/V rows of this sequence and head, bounded: rows past the end read zeros.
   // With a block table the rows live in pages instead (see load below).
-  const uint32_t rs_bytes = (uint32_t)a.Hkv * D * 2;
-  const uint32_t seq_bytes = (uint32_t)(Lk - 1) * rs_bytes + D * 2;
-  const size_t head_off = ((size_t)sk0 * a.Hkv + g) * D;
-  const __amdgpu_buffer_rsrc_t krs = rows_rsrc(a.k + head_off, seq_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = rows_rsrc(a.v + head_off, seq_bytes);
-  // K operand rows: sub-block bb row r = lane & 15 holds key 8*(r/4) + 4*bb + r%4,
+  const uint32_t rs_bytes = (uint32_t)a.Hkv * D * ESZ;
+  const uint32_t seq_bytes = (uint32_t)(Lk - 1) * rs_bytes + D * ESZ;
+  const size_t head_off = ((size_t)sk0 * a.Hkv + g) * D * ESZ;
+  const __amdgpu_buffer_rsrc_t krs = rows_rsrc(reinterpret_cast<const uint8_t*>(a.k) + head_off, seq_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = rows_rsrc(reinterpret_cast<const uint8_t*>(a.v) + head_off, seq_bytes);
+  // K operand rows: half bb row r = lane & 15 holds key 8*(r/4) + 4*bb + r%4,
   // so that a lane's 8 scores are 8 consecutive keys (the P operand layout)
   uint32_t k_off[2];
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb)
-    k_off[bb] = (uint32_t)(8 * (q >> 2) + 4 * bb + (q & 3)) * rs_bytes + (uint32_t)g4 * 16u;
+    k_off[bb] = (uint32_t)(8 * (q >> 2) + 4 * bb + (q & 3)) * rs_bytes + (uint32_t)g4 * (FP8 ? 32u : 16u);
   // V staging: lane (kq, cv) loads keys 4kq..4kq+3 x feature chunks cv + 8*x
   const int kq = lane & 7, cv = lane >> 3;
   const uint32_t v_off = (uint32_t)(4 * kq) * rs_bytes + (uint32_t)cv * 16u;
   uint16_t* vt = reinterpret_cast<uint16_t*>(smem) + wave * kSlotElems;  // this wave's V^T [D][kVtStride]
 
   struct Regs {
-    u32x4 k[2][KS];
-    u32x4 v[VCH][4];
+    u32x4 k[NSB][2][KR];
+    u32x4 v[NSB][VCH][4];
   };
-  // Block j0 (a multiple of 32) of the sequence.  Paged: the block lies in
-  // one page (page_size is a multiple of 64); its resource is bounded by the
-  // rows of that page the sequence uses, so rows past the sequence's end read
-  // zeros whatever the page holds there.
-  auto load = [&](Regs& R, int j0) {
-    int soff = j0 * (int)rs_bytes;
+  // Block j0 of the sequence.  Paged: the block lies in one page (a multiple
+  // of 32 keys on the sequence's 32-key grid, page_size a multiple of 64);
+  // its resource is bounded by the rows of that page the sequence uses, so
+  // rows past the sequence's end read zeros whatever the page holds there.
+  //
+  // Every call issues the same loads: a block past the end of the wave's
+  // blocks (valid false), or a sub-block wholly past the segment's end, reads
+  // through a resource of zero bytes, so its loads return zeros without a
+  // memory access.  Loads behind a branch would leave the compiler's wait
+  // counts unable to tell the paths apart, and its merged count would wait
+  // for the loads just issued as well as for the block about to be computed.
+  const __amdgpu_buffer_rsrc_t none = rows_rsrc(a.k, 0u);
+  auto load = [&](Regs& R, int j0, bool valid) {
+    int soff = valid ? j0 * (int)rs_bytes : 0;
     __amdgpu_buffer_rsrc_t kr = krs, vr = vrs;
     if constexpr (PAGED) {
-      const int pb = j0 / a.page_size;
-      const int page = a.block_table[(size_t)b * a.max_blocks + pb];
-      const uint32_t rows = (uint32_t)min(a.page_size, Lk - pb * a.page_size);
-      const size_t off = ((size_t)page * a.page_size * a.Hkv + g) * D;
-      kr = rows_rsrc(a.k + off, (rows - 1) * rs_bytes + D * 2);
-      vr = rows_rsrc(a.v + off, (rows - 1) * rs_bytes + D * 2);
-      soff = (j0 - pb * a.page_size) * (int)rs_bytes;
+      if (valid) {
+        const int pb = j0 / a.page_size;
+        const int page = a.block_table[(size_t)b * a.max_blocks + pb];
+        const uint32_t rows = (uint32_t)min(a.page_size, Lk - pb * a.page_size);
+        const size_t off = ((size_t)page * a.page_size * a.Hkv + g) * D;
+        kr = rows_rsrc(a.k + off, (rows - 1) * rs_bytes + D * 2);
+        vr = rows_rsrc(a.v + off, (rows - 1) * rs_bytes + D * 2);
+        soff = (j0 - pb * a.page_size) * (int)rs_bytes;
+      }
     }
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb)
+    for (int sb = 0; sb < NSB; ++sb) {
+      const bool live = valid && (sb == 0 || j0 + kBlk * sb < c1);
+      const __amdgpu_buffer_rsrc_t ks_r = live ? kr : none, vs_r = live ? vr : none;
+      const int so = live ? soff + kBlk * sb * (int)rs_bytes : 0;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        R.k[bb][ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, k_off[bb] + 64 * ks, soff, kStreamPolicy));
+      for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-    for (int x = 0; x < VCH; ++x)
+        for (int ks = 0; ks < KR; ++ks)
+          R.k[sb][bb][ks] = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(ks_r, k_off[bb] + (FP8 ? 16 : 64) * ks, so, kStreamPolicy));
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        R.v[x][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, v_off + i * rs_bytes + x * 128, soff, kStreamPolicy));
+      for (int x = 0; x < VCH; ++x)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          R.v[sb][x][i] = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(vs_r, v_off + i * rs_bytes + x * 128, so, kStreamPolicy));
+    }
   };
 
   f32x4 o[DB];
@@ -192,11 +228,32 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void fwd_decode_partial_ke
   for (int d = 0; d < DB; ++d) o[d] = f32x4{};
   float m_run = kNegInf, l_run = 0.f;
 
-  auto compute = [&](Regs& R, int j0) {
+  // One 32-key sub-block sb of a block at key j0.
+  auto compute_sub = [&](Regs& R, int sb, int j0) {
     // V block -> LDS, transposed (and re-encoded as IEEE half for bfloat16)
+    if constexpr (FP8) {
+      // lane (kq, cv) holds features 16 cv .. + 15 of keys 4 kq .. + 3; word
+      // w of key i widens to the half pairs (4w, 4w + 1) and (4w + 2, 4w + 3)
+      const u32x4 a0 = R.v[sb][0][0], a1 = R.v[sb][0][1], a2 = R.v[sb][0][2], a3 = R.v[sb][0][3];
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int hsel = 0; hsel < 2; ++hsel) {
+          const uint32_t h0 = fp8x2_to_f16x2(a0[w], hsel), h1 = fp8x2_to_f16x2(a1[w], hsel);
+          const uint32_t h2 = fp8x2_to_f16x2(a2[w], hsel), h3 = fp8x2_to_f16x2(a3[w], hsel);
+          const int d = 16 * cv + 4 * w + 2 * hsel;
+          u32x2 even, odd;
+          even[0] = __builtin_amdgcn_perm(h1, h0, 0x05040100u);
+          even[1] = __builtin_amdgcn_perm(h3, h2, 0x05040100u);
+          odd[0] = __builtin_amdgcn_perm(h1, h0, 0x07060302u);
+          odd[1] = __builtin_amdgcn_perm(h3, h2, 0x07060302u);
+          *(u32x2*)(vt + d * kVtStride + 4 * kq) = even;
+          *(u32x2*)(vt + (d + 1) * kVtStride + 4 * kq) = odd;
+        }
+    } else {
 #pragma unroll
     for (int x = 0; x < VCH; ++x) {
-      u32x4 a0 = R.v[x][0], a1 = R.v[x][1], a2 = R.v[x][2], a3 = R.v[x][3];
+      u32x4 a0 = R.v[sb][x][0], a1 = R.v[sb][x][1], a2 = R.v[sb][x][2], a3 = R.v[sb][x][3];
       if constexpr (BF16) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -218,13 +275,18 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void fwd_decode_partial_ke
         *(u32x2*)(vt + (d0 + 2 * w + 1) * kVtStride + 4 * kq) = odd;
       }
     }
+    }
     // scores: lane (q, g4) gets keys j0 + 8*g4 + 0..7 of column q
     f32x4 s[2];
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
       s[bb] = f32x4{};
+      if constexpr (FP8) {
+        s[bb] = mfma_16x16x128_fp8(R.k[sb][bb][0], R.k[sb][bb][1], qf[0], qf[1], s[bb]);
+      } else {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) s[bb] = mfma_16x16x32<BF16>(R.k[bb][ks], qf[ks], s[bb]);
+        for (int ks = 0; ks < KS; ++ks) s[bb] = mfma_16x16x32<BF16>(R.k[sb][bb][ks], qf[ks], s[bb]);
+      }
     }
     const int jlane = j0 + 8 * g4;
     float x[8];
@@ -264,28 +326,57 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void fwd_decode_partial_ke
       o[d] = mfma_16x16x32<false>(vf, pf, o[d]);
     }
   };
+  auto compute = [&](Regs& R, int j0) {
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb) {
+      if (sb > 0 && j0 + kBlk * sb >= c1) break;
+      compute_sub(R, sb, j0 + kBlk * sb);
+    }
+  };
 
-  // this wave's blocks: j = cb + 32 * (stripe + stripes * i).  Paged, the
-  // blocks sit on the sequence's 32-key grid so none crosses a page (keys
-  // before c0 are masked in the first block); packed, they start at c0.
+  // Blocks of kBlkKeys keys from cb (paged: on the sequence's 32-key grid so
+  // that none crosses a page, keys before c0 masked in the first block;
+  // packed: from c0).  The `stripes` waves of a head claim the segment's
+  // blocks one at a time from a counter in LDS: waves that share a SIMD do
+  // not issue at the same rate (the older one is preferred), and with a fixed
+  // split the workgroup would wait for the slower one.
   const int cb = PAGED ? (c0 & ~(kBlk - 1)) : c0;
-  const int nblk = (c1 - cb + kBlk - 1) / kBlk;
-  Regs ra, rb;
-  int i = stripe;
-  if (i < nblk) load(ra, cb + kBlk * i);
-  for (; i < nblk; i += 2 * stripes) {
-    const int inext = i + stripes;
-    if (inext < nblk) load(rb, cb + kBlk * inext);
-    compute(ra, cb + kBlk * i);
-    if (inext >= nblk) break;
-    if (inext + stripes < nblk) load(ra, cb + kBlk * (inext + stripes));
-    compute(rb, cb + kBlk * inext);
+  const int nblk = (c1 - cb + kBlkKeys - 1) / kBlkKeys;
+  auto claim = [&]() -> int {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(&next_blk[hh], 1);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
+  // A ring of NBUF register buffers: buffer u holds block jb[u]; the load of
+  // the block NBUF - 1 places ahead is issued before each compute, so NBUF -
+  // 1 blocks stay in flight.  A wave's claims only grow, so the first block
+  // past the end ends its walk.
+  Regs rg[NBUF];
+  int jb[NBUF];
+#pragma unroll
+  for (int u = 0; u + 1 < NBUF; ++u) {
+    jb[u] = claim();
+    load(rg[u], cb + kBlkKeys * jb[u], jb[u] < nblk);
+  }
+  for (bool more = true; more;) {
+#pragma unroll
+    for (int u = 0; u < NBUF; ++u) {
+      if (jb[u] >= nblk) {
+        more = false;
+        break;
+      }
+      const int un = (u + NBUF - 1) % NBUF;
+      jb[un] = claim();
+      load(rg[un], cb + kBlkKeys * jb[un], jb[un] < nblk);
+      compute(rg[u], cb + kBlkKeys * jb[u]);
+    }
   }
 
   // ---- merge the partial states of the waves that share a head, in LDS
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
   __syncthreads();
+  if (tid < kDcKvPerWgMax) next_blk[tid] = 0;  // every wave is past its last claim of this segment
   float* red = reinterpret_cast<float*>(smem);   // [4][16][kRedStride]
   float* mred = red + kWaves * 16 * kRedStride;  // [4][16]
   float* lred = mred + kWaves * 16;              // [4][16]
@@ -391,7 +482,7 @@ __global__ __launch_bounds__(256) void fwd_decode_combine_kernel(FwdArgs a) {
       for (int f = 0; f < F; ++f) acc[f] += w * o_p[(size_t)ch * ostride + f];
     }
   }
-  const float inv = S > 0.f ? 1.f / S : 0.f;
+  const float inv = (S > 0.f ? 1.f / S : 0.f) * a.out_scale;  // out_scale: 1, or the fp8 V scale
   uint16_t* dst = a.out + ((size_t)sq0 * a.Hq + h) * D + lane * F;
   if constexpr (F == 2) {
     *(uint32_t*)dst = pack_out_x2<BF16>(acc[0] * inv, acc[1] * inv);
@@ -421,6 +512,26 @@ static hipError_t launch_decode_d(const FwdArgs& a, bool alibi, hipStream_t stre
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((fwd_decode_combine_kernel<D, BF16>), dim3((a.Hq + 3) / 4, a.num_seqs), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+// fp8 (OCP e4m3) q, k, v; D = 128; out_bf16 picks the output dtype; packed K/V only.
+hipError_t launch_decode_fp8(const FwdArgs& a, bool out_bf16, bool alibi, hipStream_t stream) {
+  if (a.dc_pieces > 0) {
+    const dim3 grid((unsigned)a.dc_pieces * (unsigned)((a.Hkv / a.kv_per_wg) * a.head_slices));
+    const dim3 block(64 * kWaves);
+    if (out_bf16) {
+      if (alibi) hipLaunchKernelGGL((fwd_decode_partial_kernel<128, true, true, false, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((fwd_decode_partial_kernel<128, true, false, false, true>), grid, block, 0, stream, a);
+    } else {
+      if (alibi) hipLaunchKernelGGL((fwd_decode_partial_kernel<128, false, true, false, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((fwd_decode_partial_kernel<128, false, false, false, true>), grid, block, 0, stream, a);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (out_bf16) hipLaunchKernelGGL((fwd_decode_combine_kernel<128, true>), dim3((a.Hq + 3) / 4, a.num_seqs), dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL((fwd_decode_combine_kernel<128, false>), dim3((a.Hq + 3) / 4, a.num_seqs), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

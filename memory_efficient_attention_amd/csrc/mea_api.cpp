@@ -34,8 +34,8 @@ int gcd_int(int x, int y) {
   return x;
 }
 
-// Key/value heads that one decode workgroup serves together (one wave each).
-int32_t decode_kv_per_wg(int32_t Hkv) { return gcd_int(Hkv, mea::kDcWaves); }
+// Key/value heads of one decode head group (kDcWaves / nh waves serve each).
+int32_t decode_kv_per_wg(int32_t Hkv) { return gcd_int(Hkv, mea::kDcKvPerWgMax); }
 
 int32_t decode_head_groups(int32_t Hq, int32_t Hkv) {
   const int32_t group = Hq / Hkv;
@@ -45,7 +45,7 @@ int32_t decode_head_groups(int32_t Hq, int32_t Hkv) {
 int32_t default_chunk(int32_t total_k, int32_t Hq, int32_t Hkv) {
   // Piece length W of the concatenated key axis: about kDcTargetWgs
   // equal-sized (piece, head group) workgroups in all, i.e. one full round of
-  // two workgroups per CU on 256 CUs: every workgroup starts at once and
+  // one workgroup per CU on 256 CUs: every workgroup starts at once and
   // none is left over for a tail (measured: one round beats two or four,
   // which pay each workgroup's start-up again).  Never below kDcMinPiece keys,
   // so that partial results stay a small fraction of the K/V bytes.
@@ -179,7 +179,7 @@ mea_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, fl
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   hipError_t err;
-  if (max_seqlen_q == 1 && fp8 == nullptr) {
+  if (max_seqlen_q == 1) {
     const int32_t chunk = forced_split ? chunk_keys : default_chunk(total_k, Hq, Hkv);
     const size_t need = decode_ws_bytes(num_seqs, total_k, max_seqlen_k, Hq, D, chunk);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need))
@@ -195,7 +195,7 @@ mea_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, fl
     a.ws_lse = a.ws_o + (size_t)num_seqs * a.max_chunks * Hq * D;
     if ((long long)a.dc_pieces * decode_head_groups(Hq, Hkv) > 0x7fffffffll)
       return fail(MEA_ERR_UNSUPPORTED, "too many decode workgroups (%d pieces of %d keys)", a.dc_pieces, chunk);
-    err = mea::launch_decode(a, D, bf16, alibi, s);
+    err = fp8 != nullptr ? mea::launch_decode_fp8(a, bf16, alibi, s) : mea::launch_decode(a, D, bf16, alibi, s);
   } else {
     const size_t need = prefill_ws_bytes(num_seqs, total_k, Hkv, D);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need))
@@ -398,9 +398,10 @@ mea_status_t mea_fwd_fp8(const void* q, const void* k, const void* v, float q_sc
                   stream, 0, false, nullptr, &sc);
 }
 
-size_t mea_fwd_fp8_workspace_size(int32_t num_seqs, int32_t total_k, int32_t Hkv, int32_t D) {
-  if (num_seqs <= 0 || total_k < 0 || Hkv <= 0 || D != 128) return 0;
-  return prefill_ws_bytes(num_seqs, total_k, Hkv, D);
+size_t mea_fwd_fp8_workspace_size(int32_t num_seqs, int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                  int32_t Hq, int32_t Hkv, int32_t D) {
+  if (D != 128) return 0;
+  return mea_fwd_workspace_size(num_seqs, total_k, max_seqlen_q, max_seqlen_k, Hq, Hkv, D, 0);
 }
 
 mea_status_t mea_swiglu_ffn(const void* x, const void* w_gate, const void* w_up, const void* w_down, void* hidden,

@@ -113,6 +113,16 @@ __device__ __forceinline__ f32x16 mfma_32x32x64_fp8(u32x4 alo, u32x4 ahi, u32x4 
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// 16x16x128 products of OCP e4m3 operands, float32 accumulate.  Lane l holds
+// row (or column) l % 16 and 32 k-values, 16 bytes in each of lo and hi, with
+// the same freedom of k-assignment; the output layout is that of the 16x16x32
+// 16-bit products (lane l: column l % 16, rows 4 (l / 16) .. + 3).
+__device__ __forceinline__ f32x4 mfma_16x16x128_fp8(u32x4 alo, u32x4 ahi, u32x4 blo, u32x4 bhi, f32x4 c) {
+  const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(alo, ahi, 0, 1, 2, 3, 4, 5, 6, 7));
+  const i32x8 b = __builtin_bit_cast(i32x8, __builtin_shufflevector(blo, bhi, 0, 1, 2, 3, 4, 5, 6, 7));
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
 // The other half-wave's value of x (lane l <-> lane l ^ 32), combined.
 __device__ __forceinline__ float halfwave_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
@@ -157,6 +167,16 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
   float lo = __builtin_bit_cast(float, w << 16);
   float hi = __builtin_bit_cast(float, w & 0xffff0000u);
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+}
+
+// Bytes 2 hi and 2 hi + 1 of w, two OCP e4m3 values, widened to a packed pair
+// of IEEE halves (low half from the lower byte).  Exact: every e4m3 value,
+// subnormals included, is a half.
+__device__ __forceinline__ uint32_t fp8x2_to_f16x2(uint32_t w, bool hi) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 r = hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.f, true)
+                  : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.f, false);
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 // MFMA accumulator row of register r in half-wave `hi` (32x32 layout).

@@ -18,10 +18,11 @@ constexpr int kPfBN = 64;          // keys per LDS tile
 // Decode: workgroups of 4 waves; gcd(Hkv, 4) key/value heads per workgroup,
 // each wave streaming its own 32-key blocks of one head's part of a piece of
 // the concatenated key axis.
-constexpr int kDcWaves = 4;
+constexpr int kDcWaves = 8;         // decode workgroup: 8 waves, one workgroup per CU
+constexpr int kDcKvPerWgMax = 4;    // key/value heads per decode workgroup: gcd(Hkv, 4)
 constexpr int kDcPieceAlign = 32;    // piece lengths are multiples of one wave block
 constexpr int kDcMinPiece = 128;     // shortest default piece
-constexpr int kDcTargetWgs = 512;    // default: one round of 2 workgroups per CU on 256 CUs
+constexpr int kDcTargetWgs = 256;    // default: one round of one workgroup per CU on 256 CUs
 constexpr int kDcHeadsPerWg = 16;    // query heads of one group served per workgroup
 
 // Backward: workgroups of 8 waves (two groups of 4).  dK/dV: a wave owns 32
@@ -39,6 +40,7 @@ hipError_t launch_prefill(const FwdArgs& a, int D, bool bf16, bool causal, bool 
 hipError_t launch_prefill_fp8(const FwdArgs& a, bool out_bf16, bool causal, bool alibi, int max_seqlen_k,
                               hipStream_t stream);
 hipError_t launch_decode(const FwdArgs& a, int D, bool bf16, bool alibi, hipStream_t stream);
+hipError_t launch_decode_fp8(const FwdArgs& a, bool out_bf16, bool alibi, hipStream_t stream);
 hipError_t launch_backward(const BwdArgs& a, int D, bool bf16, bool causal, bool alibi, hipStream_t stream);
 hipError_t launch_swiglu_ffn(const void* x, const void* w_gate, const void* w_up, const void* w_down, void* hidden,
                              void* out, int tokens, int d_model, int d_ff, bool bf16, hipStream_t stream);

@@ -48,7 +48,7 @@ def test_every_kernel_stub_is_defined():
 
 
 def test_version_and_strings():
-    assert _native.mea_abi_version() == 6
+    assert _native.mea_abi_version() == 7
     for st in range(4):
         assert _native.mea_status_string(st).startswith("MEA_")
     assert "unknown" in _native.mea_status_string(99)
@@ -150,10 +150,10 @@ def test_workspace_size():
     assert ws(64, 137663, 4085, 4085, 32, 8, 128, 0) == (137663 // 64 + 64) * 8 * 128 * 128
     assert ws(4, 0, 200, 0, 8, 8, 64, 0) == 0
     # decode: float32 partials per (sequence, partial slot, query head); the
-    # key axis is cut into pieces of W keys, ~512 (piece, head group)
+    # key axis is cut into pieces of W keys, ~256 (piece, head group)
     # workgroups in all; here 2 head groups (8 key/value heads, 4 per group)
     W = _native.mea_default_chunk_keys(1101299, 64, 8)
-    assert W == 4320                                   # ceil(1101299 * 2 / 512) -> multiple of 32
+    assert W == 8608                                   # ceil(1101299 * 2 / 256) -> multiple of 32
     slots = -(-32680 // W) + 1                         # a sequence touches at most ceil(L / W) + 1 pieces
     assert ws(64, 1101299, 1, 32680, 64, 8, 128, 0) == 64 * slots * 64 * 129 * 4
     assert ws(64, 1101299, 1, 32680, 64, 8, 128, 256) == 64 * (128 + 1) * 64 * 129 * 4
@@ -161,11 +161,12 @@ def test_workspace_size():
     assert ws(64, 1101299, 1, 32680, 64, 8, 128, 96) == 64 * (341 + 1) * 64 * 129 * 4
     assert ws(2, 200, 1, 100, 6, 4, 128, 0) == 0                            # Hq % Hkv != 0
     assert ws(4, 0, 1, 0, 8, 8, 128, 0) == 0                                # no keys at all
-    assert _native.mea_default_chunk_keys(32768, 64, 8) == 128              # 2 x 32768 / 512 = 128
+    assert _native.mea_default_chunk_keys(32768, 64, 8) == 256              # 2 x 32768 / 256
+    assert _native.mea_default_chunk_keys(16384, 64, 8) == 128              # 2 x 16384 / 256
     assert _native.mea_default_chunk_keys(8192, 64, 8) == 128               # floor of 128 keys
     assert _native.mea_default_chunk_keys(0, 64, 8) == 128
     assert _native.mea_default_chunk_keys(0, 0, 0) == 128
-    assert _native.mea_default_chunk_keys(1 << 24, 32, 1) == (1 << 24) * 2 // 512   # 1 head x 2 slices
+    assert _native.mea_default_chunk_keys(1 << 24, 32, 1) == (1 << 24) * 2 // 256  # 1 head x 2 slices
     for T, Hq, h in [(1000, 1, 1), (8 * 4096, 64, 8), (200 * 32768, 64, 8), (3 * 77, 4, 2)]:
         c = _native.mea_default_chunk_keys(T, Hq, h)
         assert c % 32 == 0 and c >= 128
@@ -247,7 +248,7 @@ def call_fp8(**kw):
     (dict(q=None), MEA_ERR_INVALID, "non-NULL"),
     (dict(out_dtype=9), MEA_ERR_UNSUPPORTED, "dtype"),
     (dict(workspace=None, workspace_bytes=0), MEA_ERR_INVALID, "workspace"),
-    # decode-shaped calls still take the prefill kernel and its workspace
+    # decode-shaped calls take the split-KV kernels and their float32 partials
     (dict(total_q=4, max_seqlen_q=1, workspace=None, workspace_bytes=0), MEA_ERR_INVALID, "workspace"),
 ])
 def test_fp8_rejected_before_launch(kw, status, needle):
@@ -257,10 +258,14 @@ def test_fp8_rejected_before_launch(kw, status, needle):
 
 def test_fp8_workspace_size():
     ws = _native.mea_fwd_fp8_workspace_size
-    assert ws(64, 137663, 8, 128) == (137663 // 64 + 64) * 8 * 128 * 128
-    assert ws(4, 365, 2, 64) == 0
-    assert ws(0, 365, 2, 128) == 0
-    assert ws(4, 0, 2, 128) == 0
+    # prefill-shaped: the V^T tile images of the 16-bit prefill path
+    assert ws(64, 137663, 4094, 4094, 32, 8, 128) == (137663 // 64 + 64) * 8 * 128 * 128
+    # decode-shaped: the 16-bit decode path's float32 partials
+    w16 = _native.mea_fwd_workspace_size(64, 1101299, 1, 32680, 64, 8, 128, 0)
+    assert w16 > 0 and ws(64, 1101299, 1, 32680, 64, 8, 128) == w16
+    assert ws(4, 365, 2, 200, 8, 2, 64) == 0
+    assert ws(0, 365, 2, 200, 8, 2, 128) == 0
+    assert ws(4, 0, 2, 0, 8, 2, 128) == 0
 
 
 def call_ffn(**kw):

@@ -2,6 +2,7 @@
 e4m3 with per-tensor scales; the HIP result is compared with the float64
 oracle on the same codes and scales (``attention_forward_fp8``), with the
 output gates of the 16-bit path for the output dtype."""
+import dataclasses
 import sys
 
 import pytest
@@ -46,7 +47,13 @@ CASES = [
     ("lq_gt_lk_causal", [3, 5, 70, 150], [7, 2, 200, 64], 4, 2, True, False, torch.bfloat16),
     ("lq_lt_lk_causal_alibi", [65, 17, 200], [300, 17, 333], 4, 4, True, True, torch.bfloat16),
     ("empty_sides", [0, 65, 10, 0, 33], [5, 0, 10, 0, 129], 4, 2, True, False, torch.bfloat16),
-    ("decode_shaped", [1, 1, 1, 1], [300, 1, 64, 1000], 8, 2, True, True, torch.bfloat16),
+    # decode-shaped calls (max_seqlen_q == 1) take the split-KV decode kernels
+    ("decode_gqa_alibi", [1, 1, 1, 1], [300, 1, 64, 1000], 8, 2, True, True, torch.bfloat16),
+    ("decode_group8_long", [1] * 6, [5000, 33, 1, 4097, 64, 129], 64, 8, True, False, torch.bfloat16),
+    ("decode_mqa_alibi_fp16", [1, 1, 1], [2000, 65, 700], 16, 1, True, True, torch.float16),
+    ("decode_group20", [1, 1, 1, 1, 1], [1, 130, 0, 3000, 257], 40, 2, True, False, torch.bfloat16),
+    ("decode_empty_rows", [1, 0, 1], [0, 5, 64], 8, 8, True, False, torch.bfloat16),
+    ("decode_tails", [1] * 7, [31, 32, 33, 63, 64, 65, 97], 8, 4, True, True, torch.bfloat16),
 ]
 
 
@@ -86,3 +93,45 @@ def test_fp8_full_size_sampled():
     go = torch.stack([out[t, h] for t, h in rows])
     gl = torch.stack([lse[h, t] for t, h in rows])
     _log(f"  {compare(go, gl, ro, rl, 'bf16', 'fp8 full size sampled')}")
+
+
+def test_fp8_decode_full_size_sampled():
+    """The 64-request decode workload (1.1 M KV tokens, Hq 64 / Hkv 8) in fp8;
+    sampled rows against the oracle on the dequantised values."""
+    inp = generate("decode_splitkv_64req_h64kv8_d128_bf16")
+    f = to_fp8(inp)
+    _log(f"fp8 decode full size, sum Lk={inp.total_k}")
+    out, lse = _run(inp, f, torch.bfloat16)
+    assert not torch.isnan(out).any()
+    rows = sample_rows(inp, 128, seed=9)
+    q = f.q8.to(torch.float64) * f.q_scale
+    k = f.k8.to(torch.float64) * f.k_scale
+    v = f.v8.to(torch.float64) * f.v_scale
+    ro, rl = oracle.attention_rows(q, k, v, inp.seqstart_q, inp.seqstart_k, rows, causal=inp.causal,
+                                   scale=inp.scale)
+    go = torch.stack([out[t, h] for t, h in rows])
+    gl = torch.stack([lse[h, t] for t, h in rows])
+    _log(f"  {compare(go, gl, ro, rl, 'bf16', 'fp8 decode sampled')}")
+
+
+def test_fp8_decode_matches_prefill_kernel_rows():
+    """A decode row is also the last row of a prefill-shaped call over the
+    same keys: with a second query row added to every sequence the call takes
+    the prefill kernel, and its last rows must agree with the decode kernel's
+    to the output tolerance (both are checked against the oracle above; this
+    ties the two fp8 paths to each other on the same codes)."""
+    lk = [300, 1, 64, 1000, 4097]
+    inp = random_case(790, [1] * len(lk), lk, Hq=16, Hkv=4, D=128, dtype="bf16", causal=True)
+    f = to_fp8(inp)
+    out_d, lse_d = _run(inp, f, torch.bfloat16)
+    # prefill-shaped: each sequence gets its decode query as its last of two rows
+    inp2 = random_case(790, [2] * len(lk), lk, Hq=16, Hkv=4, D=128, dtype="bf16", causal=True)
+    f2 = to_fp8(inp2)
+    q8 = f2.q8.clone()
+    q8[1::2] = f.q8
+    f2 = dataclasses.replace(f2, q8=q8, k8=f.k8, v8=f.v8, q_scale=f.q_scale, k_scale=f.k_scale, v_scale=f.v_scale)
+    out_p, lse_p = _run(inp2, f2, torch.bfloat16)
+    d_out = (out_d.double() - out_p[1::2].double()).abs().max().item()
+    d_lse = (lse_d.double() - lse_p[:, 1::2].double()).abs().max().item()
+    _log(f"  decode vs prefill kernel: out {d_out:.2e}, lse {d_lse:.2e}")
+    assert d_out <= 1e-2 and d_lse <= 1e-3
