@@ -260,16 +260,29 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
     f32x16 s = f32x16{}, dp = f32x16{};
     const int rr = 32 * sb + key_of_row(l32);  // query row fed to A-row l32
     const int kr = 32 * wk + l32;              // key row of this lane's K and V operands
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    // fragments of k-step ks: Q, K, dO, V; those of ks + 1 are read while the
+    // products of ks run (two register sets, the order fixed below)
+    auto frags = [&](int ks, u32x4 (&f)[4]) {
       const int at = rr * (D * 2) + kt_pos<D>(rr, 2 * ks + hi) * 16;
       const int kat = kr * (D * 2) + kt_pos<D>(kr, 2 * ks + hi) * 16;
-      const u32x4 qa = *(const u32x4*)(buf + L::offQ + at);
-      const u32x4 kb = *(const u32x4*)(smem + L::offK + kat);
-      const u32x4 da = *(const u32x4*)(buf + L::offDO + at);
-      const u32x4 vb = *(const u32x4*)(smem + L::offV + kat);
-      s = mfma_32x32x16<BF16>(qa, kb, s);
-      dp = mfma_32x32x16<BF16>(da, vb, dp);
+      f[0] = *(const u32x4*)(buf + L::offQ + at);
+      f[1] = *(const u32x4*)(smem + L::offK + kat);
+      f[2] = *(const u32x4*)(buf + L::offDO + at);
+      f[3] = *(const u32x4*)(smem + L::offV + kat);
+    };
+    u32x4 fr[2][4];
+    frags(0, fr[0]);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) frags(ks + 1, fr[(ks + 1) & 1]);
+      s = mfma_32x32x16<BF16>(fr[ks & 1][0], fr[ks & 1][1], s);
+      dp = mfma_32x32x16<BF16>(fr[ks & 1][2], fr[ks & 1][3], dp);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);    // reads of k-step 0
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // reads of ks + 1
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // products of ks
     }
     // register r holds stage row 32 sb + key_of_reg(r, hi); key position minus
     // query position of register r: kd0 - 32 sb - 8 hi - ro(r)
@@ -463,13 +476,25 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
     for (int kb = 0; kb < 2; ++kb) {
       f32x16 s = f32x16{}, dp = f32x16{};
       const int rr = 32 * kb + key_of_row(l32);
+      // K and V fragments of k-step ks + 1 are read while the products of ks run
+      auto frags = [&](int ks, u32x4 (&f)[2]) {
+        const int at = rr * (D * 2) + kt_pos<D>(rr, 2 * ks + hi) * 16;
+        f[0] = *(const u32x4*)(buf + L::offK + at);
+        f[1] = *(const u32x4*)(buf + L::offV + at);
+      };
+      u32x4 fr[2][2];
+      frags(0, fr[0]);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int at = rr * (D * 2) + kt_pos<D>(rr, 2 * ks + hi) * 16;
-        const u32x4 ka = *(const u32x4*)(buf + L::offK + at);
-        const u32x4 va = *(const u32x4*)(buf + L::offV + at);
-        s = mfma_32x32x16<BF16>(ka, qf[ks], s);
-        dp = mfma_32x32x16<BF16>(va, of[ks], dp);
+        if (ks + 1 < KS) frags(ks + 1, fr[(ks + 1) & 1]);
+        s = mfma_32x32x16<BF16>(fr[ks & 1][0], qf[ks], s);
+        dp = mfma_32x32x16<BF16>(fr[ks & 1][1], of[ks], dp);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);    // reads of k-step 0
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 1 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // reads of ks + 1
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // products of ks
       }
       if (need_mask) {  // keys past the end, or after the query row -> -inf, so their weights are 0
 #pragma unroll
