@@ -15,18 +15,16 @@
 // nh = gcd(Hkv, 4) neighbouring key/value heads (with up to 16 query heads of
 // each head's group).  The nh heads of a key are adjacent in memory, so a
 // workgroup reads runs of nh * D * 2 contiguous bytes per key rather than one
-// head's D * 2 bytes out of each token row.  Wave w serves head w % nh; the
-// 8 / nh waves of a head claim the 32-key blocks of the piece's part of a
-// sequence one at a time from a counter in LDS (the two waves of a SIMD do
-// not issue at the same rate, and a fixed split would leave the workgroup
-// waiting for the slower one), each with its own online-softmax state.  Per
-// block, a wave computes
+// head's D * 2 bytes out of each token row.  Wave w serves head w % nh, and
+// the 8 / nh waves of a head take every (8 / nh)-th 32-key block of the
+// piece's part of a sequence, each with its own online-softmax state and no
+// workgroup barrier until the end of that part.  Per block, a wave computes
 //   S^T = K Q^T   16x16x32 products; the query heads of the group are the 16
 //                 columns, so one K/V read serves every head of the group
 //                 (GQA's saving becomes fewer HBM bytes);
 //   O^T += V^T P^T  with V transposed through a per-wave LDS slot.
 // K goes from HBM straight into the product's operand registers; the loads of
-// the next claimed block are in flight while a block is computed.  At the end
+// the wave's next block are in flight while a block is computed.  At the end
 // of each sequence part the waves of a head merge in LDS and write one
 // normalised float32 partial output and its log-sum-exp (log2 units) per
 // query head.
@@ -102,11 +100,6 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void fwd_decode_partial_ke
   const int piece = blockIdx.x / groups, gi = blockIdx.x - piece * groups;
   const int g = (gi / a.head_slices) * nh + hh, hs = gi % a.head_slices;
   const int g0 = (gi / a.head_slices) * nh;  // first head of the group
-
-  // next unclaimed block of the current segment, per head of the group
-  __shared__ int next_blk[kDcKvPerWgMax];
-  if (tid < kDcKvPerWgMax) next_blk[tid] = 0;
-  __syncthreads();
 
   // the piece: keys [k0, k1) of the concatenated key axis
   const int W = a.chunk_keys;
@@ -336,26 +329,27 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void fwd_decode_partial_ke
 
   // Blocks of kBlkKeys keys from cb (paged: on the sequence's 32-key grid so
   // that none crosses a page, keys before c0 masked in the first block;
-  // packed: from c0).  The `stripes` waves of a head claim the segment's
-  // blocks one at a time from a counter in LDS: waves that share a SIMD do
-  // not issue at the same rate (the older one is preferred), and with a fixed
-  // split the workgroup would wait for the slower one.
+  // packed: from c0).  The `stripes` waves of a head take every stripes-th
+  // block, wave w from block w / nh on: a fixed split, so that the result is
+  // the same from run to run (blocks claimed from a shared LDS counter measured
+  // no faster).
   const int cb = PAGED ? (c0 & ~(kBlk - 1)) : c0;
   const int nblk = (c1 - cb + kBlkKeys - 1) / kBlkKeys;
-  auto claim = [&]() -> int {
-    int v = 0;
-    if (lane == 0) v = atomicAdd(&next_blk[hh], 1);
-    return __builtin_amdgcn_readfirstlane(v);
+  int next_own = wave / nh;
+  auto next_block = [&]() -> int {
+    const int v = next_own;
+    next_own += stripes;
+    return v;
   };
   // A ring of NBUF register buffers: buffer u holds block jb[u]; the load of
   // the block NBUF - 1 places ahead is issued before each compute, so NBUF -
-  // 1 blocks stay in flight.  A wave's claims only grow, so the first block
+  // 1 blocks stay in flight.  A wave's blocks only grow, so the first block
   // past the end ends its walk.
   Regs rg[NBUF];
   int jb[NBUF];
 #pragma unroll
   for (int u = 0; u + 1 < NBUF; ++u) {
-    jb[u] = claim();
+    jb[u] = next_block();
     load(rg[u], cb + kBlkKeys * jb[u], jb[u] < nblk);
   }
   for (bool more = true; more;) {
@@ -366,7 +360,7 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void fwd_decode_partial_ke
         break;
       }
       const int un = (u + NBUF - 1) % NBUF;
-      jb[un] = claim();
+      jb[un] = next_block();
       load(rg[un], cb + kBlkKeys * jb[un], jb[un] < nblk);
       compute(rg[u], cb + kBlkKeys * jb[u]);
     }
@@ -376,7 +370,6 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void fwd_decode_partial_ke
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
   __syncthreads();
-  if (tid < kDcKvPerWgMax) next_blk[tid] = 0;  // every wave is past its last claim of this segment
   float* red = reinterpret_cast<float*>(smem);   // [4][16][kRedStride]
   float* mred = red + kWaves * 16 * kRedStride;  // [4][16]
   float* lred = mred + kWaves * 16;              // [4][16]

@@ -135,3 +135,12 @@ def test_fp8_decode_matches_prefill_kernel_rows():
     d_lse = (lse_d.double() - lse_p[:, 1::2].double()).abs().max().item()
     _log(f"  decode vs prefill kernel: out {d_out:.2e}, lse {d_lse:.2e}")
     assert d_out <= 1e-2 and d_lse <= 1e-3
+
+
+def test_fp8_decode_deterministic():
+    inp = random_case(795, [1] * 6, [5000, 33, 1, 4097, 64, 129], Hq=64, Hkv=8, D=128, dtype="bf16", causal=True)
+    f = to_fp8(inp)
+    o1, l1 = _run(inp, f, torch.bfloat16)
+    for _ in range(3):
+        o2, l2 = _run(inp, f, torch.bfloat16)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)

@@ -164,6 +164,17 @@ def test_deterministic_and_lse_optional():
     assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(o1, o3)
 
 
+def test_decode_deterministic():
+    """The split-KV decode path gives the same bits on every call (fixed block
+    split between the waves of a head, fixed merge and combine order)."""
+    inp = generate("decode_splitkv_64req_h64kv8_d128_bf16", num_seqs=16)
+    dev = to_device(inp)
+    o1, l1 = run_gpu(inp, dev)
+    for _ in range(3):
+        o2, l2 = run_gpu(inp, dev)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
 def test_scale_and_slopes_arguments():
     """A non-default scale and arbitrary per-head slopes reach the kernel."""
     inp = random_case(8, [77, 300], Hq=8, Hkv=2, D=64, dtype="fp16", causal=True, alibi=True,
