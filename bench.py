@@ -23,7 +23,9 @@ paged cache (pages of 64 keys in a shuffled order, through mea_fwd_paged),
 ``backward`` the prefill workload's gradients (mea_bwd, dq/dk/dv from a
 seeded dO) at 2.5x the forward's unmasked FLOPs (five products against two),
 ``prefill_fp8`` the prefill workload with q, k, v quantised to OCP e4m3
-(mea_fwd_fp8, per-tensor scales, bf16 output), and ``swiglu_ffn`` the SwiGLU
+(mea_fwd_fp8, per-tensor scales, bf16 output), ``decode_fp8`` and
+``decode_paged_fp8`` the decode workload quantised the same way (packed, and
+in the shuffled 64-key pages through mea_fwd_paged_fp8), and ``swiglu_ffn`` the SwiGLU
 feed-forward layer of the same block on the same 137,663 tokens (d_model
 4096, d_ff 11008, bf16; 6 * T * d_model * d_ff FLOPs).
 """
@@ -165,6 +167,44 @@ class PagedCall:
             self.ws.data_ptr() if self.ws_bytes else None, self.ws_bytes, stream.cuda_stream)
         if st != 0:
             raise RuntimeError(f"mea_fwd_paged: {self.native.mea_status_string(st)}: {self.native.mea_last_error()}")
+
+
+class PagedFp8Call:
+    """Pre-bound mea_fwd_paged_fp8 launch: q, k, v quantised to e4m3 as for
+    Fp8Call, the k/v codes scattered into a paged cache as for PagedCall;
+    bf16 output."""
+
+    def __init__(self, inp, dev, page_size):
+        import dataclasses
+        import torch
+        from memory_efficient_attention_amd import _native
+        from mea_workloads import to_fp8, to_paged
+        f = to_fp8(inp)
+        pk = to_paged(dataclasses.replace(inp, k=f.k8, v=f.v8), page_size, seed=1)
+        self.inp, self.f, self.page_size = inp, f, page_size
+        self.q = f.q8.to(dev)
+        self.kc, self.vc, self.bt = pk.k_cache.to(dev), pk.v_cache.to(dev), pk.block_table.to(dev)
+        self.ssq, self.ssk = inp.seqstart_q.to(dev), inp.seqstart_k.to(dev)
+        self.slopes = None if inp.alibi_slopes is None else inp.alibi_slopes.to(dev)
+        self.out = torch.empty((inp.total_q, inp.Hq, inp.D), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((inp.Hq, inp.total_q), dtype=torch.float32, device=dev)
+        self.ws_bytes = _native.mea_fwd_fp8_workspace_size(len(inp.seqlens_q), inp.total_k, inp.max_seqlen_q,
+                                                            inp.max_seqlen_k, inp.Hq, inp.Hkv, inp.D)
+        self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=dev)
+        self.native = _native
+
+    def __call__(self, stream):
+        inp, f = self.inp, self.f
+        st = self.native.mea_fwd_paged_fp8(
+            self.q.data_ptr(), self.kc.data_ptr(), self.vc.data_ptr(), f.q_scale, f.k_scale, f.v_scale,
+            self.out.data_ptr(), self.lse.data_ptr(), self.ssq.data_ptr(), self.ssk.data_ptr(), self.bt.data_ptr(),
+            len(inp.seqlens_q), inp.total_q, inp.total_k, inp.max_seqlen_q, inp.max_seqlen_k, self.page_size,
+            self.kc.shape[0], self.bt.shape[1], inp.Hq, inp.Hkv, inp.D, self.native.MEA_BF16, int(inp.causal),
+            None if self.slopes is None else self.slopes.data_ptr(), inp.scale,
+            self.ws.data_ptr() if self.ws_bytes else None, self.ws_bytes, stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"mea_fwd_paged_fp8: {self.native.mea_status_string(st)}: "
+                               f"{self.native.mea_last_error()}")
 
 
 class BwdCall:
@@ -347,6 +387,8 @@ def run_part(args, dev):
         call = Fp8Call(generate(name, seed=args.seed), dev)
     elif args.part == "decode_paged":
         call = PagedCall(generate(name, seed=args.seed), dev, PAGE_SIZE)
+    elif args.part == "decode_paged_fp8":
+        call = PagedFp8Call(generate(name, seed=args.seed), dev, PAGE_SIZE)
     elif args.part == "backward":
         call = BwdCall(Call(generate(name, seed=args.seed), dev), dev, args.seed)
     else:
@@ -363,7 +405,7 @@ def run_part(args, dev):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / max(args.steps, 1)
     res = {"part": args.part, "workload": "swiglu_ffn" if args.part == "ffn" else name, "ms": round(ms, 4)}
-    if args.part == "decode_paged":
+    if args.part in ("decode_paged", "decode_paged_fp8"):
         res["page_size"] = PAGE_SIZE
     if args.part in ("prefill", "prefill_fp8"):
         res["tflops"] = round(unmasked_flops(call.inp) / (ms * 1e-3) / 1e12, 2)
@@ -371,7 +413,7 @@ def run_part(args, dev):
         res["tflops"] = round(BWD_GEMMS * unmasked_flops(call.inp) / (ms * 1e-3) / 1e12, 2)
     elif args.part == "ffn":
         res["tflops"] = round(call.flops() / (ms * 1e-3) / 1e12, 2)
-    elif args.part == "decode_fp8":
+    elif args.part in ("decode_fp8", "decode_paged_fp8"):
         res["gbs"] = round(algorithmic_bytes_fp8(call.inp) / (ms * 1e-3) / 1e9, 1)
     else:
         res["gbs"] = round(algorithmic_bytes(call.inp) / (ms * 1e-3) / 1e9, 1)
@@ -392,7 +434,7 @@ def main():
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-ffn", action="store_true")
     ap.add_argument("--part", choices=["all", "prefill", "decode", "decode_paged", "backward", "prefill_fp8",
-                                       "decode_fp8", "ffn", "copy"],
+                                       "decode_fp8", "decode_paged_fp8", "ffn", "copy"],
                     default="all",
                     help="run only one half of the step, or the calibration copy (for profiling); "
                          "the JSON line is for 'all'")
@@ -427,10 +469,12 @@ def main():
     bwd_call = None
     if not args.no_backward:
         bwd_call = BwdCall(Call(pre, dev), dev, args.seed)
-    fp8_call = fp8_dec_call = None
+    fp8_call = fp8_dec_call = fp8_paged_call = None
     if not args.no_fp8:
         fp8_call = Fp8Call(pre, dev)
         fp8_dec_call = Fp8Call(dec, dev)
+        if not args.no_paged_variant:
+            fp8_paged_call = PagedFp8Call(dec, dev, PAGE_SIZE)
     ffn_call = None
     if not args.no_ffn:
         ffn_call = FfnCall(dev, args.seed)
@@ -523,6 +567,13 @@ def main():
                                     "kernel": "mea_fwd_fp8 decode call: fwd_decode_partial_kernel<128,bf16 out,"
                                               "fp8> + fwd_decode_combine_kernel"}}
 
+    fp8_paged_res = None
+    if fp8_paged_call is not None:  # the same in shuffled pages of PAGE_SIZE keys
+        pfms = time_calls(fp8_paged_call, stream, max(5, K // 2))
+        pfgb = algorithmic_bytes_fp8(dec) / (pfms * 1e-3) / 1e9
+        fp8_paged_res = {"page_size": PAGE_SIZE, "ms": round(pfms, 4), "value": round(pfgb, 1), "unit": "GB/s",
+                         "frac": round(pfgb / PEAK_HBM_GBS, 4)}
+
     ffn_res = None
     if ffn_call is not None:  # the SwiGLU feed-forward layer on the prefill workload's tokens
         nms = time_calls(ffn_call, stream, max(3, K // 6))
@@ -580,6 +631,7 @@ def main():
         "decode_fp8": fp8_dec_res,
         "swiglu_ffn": ffn_res,
         "decode_paged": paged_res,
+        "decode_paged_fp8": fp8_paged_res,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

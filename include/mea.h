@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define MEA_ABI_VERSION 7
+#define MEA_ABI_VERSION 8
 
 #if defined(__GNUC__)
 #define MEA_EXPORT __attribute__((visibility("default")))
@@ -227,9 +227,9 @@ MEA_EXPORT size_t mea_fwd_workspace_size(int32_t num_seqs, int32_t total_k, int3
  * Path choice as in mea_fwd: max_seqlen_q == 1 runs the split-KV decode
  * kernels (pieces of mea_default_chunk_keys(total_k, Hq, Hkv) keys, float32
  * partials in the workspace), anything else the prefill kernel (half-precision
- * V^T tile images in the workspace).  No paged variant.  Same ownership and
- * errors as mea_fwd, plus MEA_ERR_UNSUPPORTED for a non-finite or
- * non-positive scale.
+ * V^T tile images in the workspace).  K and V in a paged cache: mea_fwd_paged_fp8.
+ * Same ownership and errors as mea_fwd, plus MEA_ERR_UNSUPPORTED for a
+ * non-finite or non-positive scale.
  */
 MEA_EXPORT mea_status_t mea_fwd_fp8(const void* q, const void* k, const void* v, float q_scale, float k_scale,
                                     float v_scale, void* out, float* lse, const int32_t* seqstart_q,
@@ -237,6 +237,31 @@ MEA_EXPORT mea_status_t mea_fwd_fp8(const void* q, const void* k, const void* v,
                                     int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq, int32_t Hkv, int32_t D,
                                     mea_dtype_t out_dtype, int32_t causal, const float* alibi_slopes, float scale,
                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mea_fwd_paged_fp8 -- mea_fwd_fp8 with K and V in a paged cache, as
+ * mea_fwd_paged does for 16-bit K and V: a serving engine's fp8 KV cache.
+ * Computes exactly what mea_fwd_fp8 computes on the sequences' keys gathered
+ * into the packed layout.
+ *   k_cache, v_cache  [num_pages, page_size, Hkv, D] OCP e4m3 codes (one byte
+ *                     per element), 16-byte aligned
+ *   block_table, page_size, num_pages, max_blocks, seqstart_k
+ *                     as for mea_fwd_paged
+ *   q, q/k/v_scale, out, out_dtype, D
+ *                     as for mea_fwd_fp8
+ * Decode-shaped calls (max_seqlen_q == 1) read 64-key blocks, each within
+ * one page.  Workspace: mea_fwd_fp8_workspace_size with the same sizes.
+ * Same ownership and errors as mea_fwd_fp8 and mea_fwd_paged together.
+ */
+MEA_EXPORT mea_status_t mea_fwd_paged_fp8(const void* q, const void* k_cache, const void* v_cache, float q_scale,
+                                          float k_scale, float v_scale, void* out, float* lse,
+                                          const int32_t* seqstart_q, const int32_t* seqstart_k,
+                                          const int32_t* block_table, int32_t num_seqs, int32_t total_q,
+                                          int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                          int32_t page_size, int32_t num_pages, int32_t max_blocks, int32_t Hq,
+                                          int32_t Hkv, int32_t D, mea_dtype_t out_dtype, int32_t causal,
+                                          const float* alibi_slopes, float scale, void* workspace,
+                                          size_t workspace_bytes, void* stream);
 
 /* Workspace bytes of mea_fwd_fp8: mea_fwd_workspace_size(num_seqs, total_k,
  * max_seqlen_q, max_seqlen_k, Hq, Hkv, D, 0) for D == 128, else 0.  Pure host

@@ -15,8 +15,8 @@ __all__ = [
     "MEA_OK", "MEA_ERR_INVALID", "MEA_ERR_UNSUPPORTED", "MEA_ERR_HIP", "MEA_F16", "MEA_BF16",
     "EXPORTED_SYMBOLS", "library_path", "load", "mea_fwd", "mea_fwd_splitkv", "mea_fwd_paged",
     "mea_fwd_workspace_size", "mea_default_chunk_keys", "mea_bwd", "mea_bwd_workspace_size",
-    "mea_fwd_fp8", "mea_fwd_fp8_workspace_size", "mea_swiglu_ffn", "mea_status_string", "mea_last_error",
-    "mea_abi_version",
+    "mea_fwd_fp8", "mea_fwd_paged_fp8", "mea_fwd_fp8_workspace_size", "mea_swiglu_ffn", "mea_status_string",
+    "mea_last_error", "mea_abi_version",
 ]
 
 MEA_OK, MEA_ERR_INVALID, MEA_ERR_UNSUPPORTED, MEA_ERR_HIP = 0, 1, 2, 3
@@ -24,8 +24,8 @@ MEA_F16, MEA_BF16 = 0, 1
 
 EXPORTED_SYMBOLS = (
     "mea_fwd", "mea_fwd_splitkv", "mea_fwd_paged", "mea_fwd_workspace_size", "mea_default_chunk_keys",
-    "mea_bwd", "mea_bwd_workspace_size", "mea_fwd_fp8", "mea_fwd_fp8_workspace_size", "mea_swiglu_ffn",
-    "mea_status_string", "mea_last_error", "mea_abi_version",
+    "mea_bwd", "mea_bwd_workspace_size", "mea_fwd_fp8", "mea_fwd_paged_fp8", "mea_fwd_fp8_workspace_size",
+    "mea_swiglu_ffn", "mea_status_string", "mea_last_error", "mea_abi_version",
 )
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -60,6 +60,14 @@ _FP8_ARGS = [_vp, _vp, _vp, _f32, _f32, _f32, _vp, _vp,   # q k v q_scale k_scal
              _vp, _f32, _vp, _sz, _vp]                    # slopes scale workspace workspace_bytes stream
 
 
+_PAGED_FP8_ARGS = [_vp, _vp, _vp, _f32, _f32, _f32, _vp, _vp,   # q k_cache v_cache q/k/v_scale out lse
+                   _vp, _vp, _vp,                               # seqstart_q seqstart_k block_table
+                   _i32, _i32, _i32, _i32, _i32,                # num_seqs total_q total_k max_q max_k
+                   _i32, _i32, _i32,                            # page_size num_pages max_blocks
+                   _i32, _i32, _i32, _i32, _i32,                # Hq Hkv D out_dtype causal
+                   _vp, _f32, _vp, _sz, _vp]                    # slopes scale workspace workspace_bytes stream
+
+
 def library_path() -> str:
     return os.environ.get("MEA_LIBRARY", os.path.join(_PKG_DIR, "libmea.so"))
 
@@ -92,6 +100,8 @@ def load() -> ctypes.CDLL:
         lib.mea_bwd_workspace_size.restype = _sz
         lib.mea_fwd_fp8.argtypes = _FP8_ARGS
         lib.mea_fwd_fp8.restype = ctypes.c_int
+        lib.mea_fwd_paged_fp8.argtypes = _PAGED_FP8_ARGS
+        lib.mea_fwd_paged_fp8.restype = ctypes.c_int
         lib.mea_fwd_fp8_workspace_size.argtypes = [_i32] * 7
         lib.mea_fwd_fp8_workspace_size.restype = _sz
         lib.mea_swiglu_ffn.argtypes = [_vp] * 6 + [_i32, _i32, _i32, _i32, _vp]
@@ -160,6 +170,16 @@ def mea_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, out, lse, seqstart_q, seqsta
     return load().mea_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, out, lse, seqstart_q, seqstart_k, num_seqs,
                               total_q, total_k, max_seqlen_q, max_seqlen_k, Hq, Hkv, D, out_dtype, causal,
                               alibi_slopes, scale, workspace, workspace_bytes, stream)
+
+
+def mea_fwd_paged_fp8(q, k_cache, v_cache, q_scale, k_scale, v_scale, out, lse, seqstart_q, seqstart_k,
+                      block_table, num_seqs, total_q, total_k, max_seqlen_q, max_seqlen_k, page_size, num_pages,
+                      max_blocks, Hq, Hkv, D, out_dtype, causal, alibi_slopes, scale, workspace, workspace_bytes,
+                      stream) -> int:
+    return load().mea_fwd_paged_fp8(q, k_cache, v_cache, q_scale, k_scale, v_scale, out, lse, seqstart_q,
+                                    seqstart_k, block_table, num_seqs, total_q, total_k, max_seqlen_q,
+                                    max_seqlen_k, page_size, num_pages, max_blocks, Hq, Hkv, D, out_dtype, causal,
+                                    alibi_slopes, scale, workspace, workspace_bytes, stream)
 
 
 def mea_fwd_fp8_workspace_size(num_seqs, total_k, max_seqlen_q, max_seqlen_k, Hq, Hkv, D) -> int:

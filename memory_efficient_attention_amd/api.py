@@ -23,8 +23,8 @@ from . import _native
 
 __all__ = [
     "BlockDiagonalMask", "BlockDiagonalCausalMask", "memory_efficient_attention",
-    "attention_packed", "attention_paged", "attention_backward_packed", "attention_packed_fp8", "swiglu_ffn",
-    "MeaError",
+    "attention_packed", "attention_paged", "attention_backward_packed", "attention_packed_fp8",
+    "attention_paged_fp8", "swiglu_ffn", "MeaError",
 ]
 
 
@@ -394,6 +394,69 @@ def attention_packed_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, q
             _ptr(q8), _ptr(k8), _ptr(v8), float(q_scale), float(k_scale), float(v_scale), _ptr(out), _ptr(lse),
             _ptr(seqstart_q), _ptr(seqstart_k), num_seqs, Tq, Tk, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv,
             D, _dtype_code(out.dtype), int(bool(causal)), _ptr(slopes), scale,
+            _ptr(workspace) if ws_bytes > 0 else None, ws_bytes, stream.cuda_stream)
+    if st != _native.MEA_OK:
+        raise MeaError(st, _native.mea_last_error())
+    return (out, lse) if return_lse else out
+
+
+def attention_paged_fp8(q8: torch.Tensor, k_cache8: torch.Tensor, v_cache8: torch.Tensor, q_scale: float,
+                        k_scale: float, v_scale: float, block_table: torch.Tensor, seqstart_q: torch.Tensor,
+                        seqstart_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int, *, causal: bool = False,
+                        alibi_slopes: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                        out_dtype: torch.dtype = torch.bfloat16, return_lse: bool = False,
+                        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None, total_k: Optional[int] = None,
+                        stream: Optional[torch.cuda.Stream] = None):
+    """:func:`attention_packed_fp8` over a paged fp8 K/V cache: q8
+    ``[Tq, Hq, 128]`` and caches ``[num_pages, page_size, Hkv, 128]`` of
+    ``torch.float8_e4m3fn``, the ``block_table`` and ``seqstart`` arrays and
+    ``total_k`` as for :func:`attention_paged`."""
+    if q8.dim() != 3 or k_cache8.dim() != 4 or v_cache8.dim() != 4:
+        raise ValueError("q8 must be [tokens, heads, D] and the caches [pages, page_size, heads, D]")
+    Tq, Hq, D = q8.shape
+    num_pages, page_size, Hkv, Dk = k_cache8.shape
+    if Dk != D or tuple(v_cache8.shape) != tuple(k_cache8.shape):
+        raise ValueError(f"shape mismatch: q8 {tuple(q8.shape)} k_cache8 {tuple(k_cache8.shape)} "
+                         f"v_cache8 {tuple(v_cache8.shape)}")
+    if not (q8.dtype == k_cache8.dtype == v_cache8.dtype == torch.float8_e4m3fn):
+        raise TypeError("q8 and the caches must be torch.float8_e4m3fn")
+    dev = q8.device
+    if dev.type != "cuda" or k_cache8.device != dev or v_cache8.device != dev or block_table.device != dev:
+        raise ValueError("q8, the caches and block_table must be on the same GPU")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2:
+        raise TypeError("block_table must be an int32 [num_seqs, max_blocks] tensor")
+    q8, k_cache8, v_cache8 = q8.contiguous(), k_cache8.contiguous(), v_cache8.contiguous()
+    block_table = block_table.contiguous()
+    if seqstart_q.dtype != torch.int32 or seqstart_k.dtype != torch.int32:
+        raise TypeError("seqstart tensors must be int32")
+    num_seqs = seqstart_q.numel() - 1
+    if seqstart_k.numel() != num_seqs + 1 or block_table.shape[0] != num_seqs:
+        raise ValueError("seqstart_q, seqstart_k and block_table disagree on the number of sequences")
+    Tk = int(total_k) if total_k is not None else (int(seqstart_k[-1].item()) if num_seqs > 0 else 0)
+    if out is None:
+        out = torch.empty((Tq, Hq, D), dtype=out_dtype, device=dev)
+    if return_lse and lse is None:
+        lse = torch.empty((Hq, Tq), dtype=torch.float32, device=dev)
+    slopes = None
+    if alibi_slopes is not None:
+        slopes = alibi_slopes.to(device=dev, dtype=torch.float32).contiguous()
+        if slopes.numel() != Hq:
+            raise ValueError(f"alibi_slopes needs {Hq} values (one per query head)")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    scale = float(np.float32(scale))
+    ws_bytes = _native.mea_fwd_fp8_workspace_size(num_seqs, Tk, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, D)
+    if ws_bytes > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        st = _native.mea_fwd_paged_fp8(
+            _ptr(q8), _ptr(k_cache8), _ptr(v_cache8), float(q_scale), float(k_scale), float(v_scale), _ptr(out),
+            _ptr(lse), _ptr(seqstart_q), _ptr(seqstart_k), _ptr(block_table), num_seqs, Tq, Tk,
+            int(max_seqlen_q), int(max_seqlen_k), page_size, num_pages, block_table.shape[1], Hq, Hkv, D,
+            _dtype_code(out.dtype), int(bool(causal)), _ptr(slopes), scale,
             _ptr(workspace) if ws_bytes > 0 else None, ws_bytes, stream.cuda_stream)
     if st != _native.MEA_OK:
         raise MeaError(st, _native.mea_last_error())

@@ -170,8 +170,8 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void fwd_decode_partial_ke
     u32x4 k[NSB][2][KR];
     u32x4 v[NSB][VCH][4];
   };
-  // Block j0 of the sequence.  Paged: the block lies in one page (a multiple
-  // of 32 keys on the sequence's 32-key grid, page_size a multiple of 64);
+  // Block j0 of the sequence.  Paged: the block lies in one page (on the
+  // sequence's grid of kBlkKeys = 32 or 64 keys, page_size a multiple of 64);
   // its resource is bounded by the rows of that page the sequence uses, so
   // rows past the sequence's end read zeros whatever the page holds there.
   //
@@ -190,9 +190,9 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void fwd_decode_partial_ke
         const int pb = j0 / a.page_size;
         const int page = a.block_table[(size_t)b * a.max_blocks + pb];
         const uint32_t rows = (uint32_t)min(a.page_size, Lk - pb * a.page_size);
-        const size_t off = ((size_t)page * a.page_size * a.Hkv + g) * D;
-        kr = rows_rsrc(a.k + off, (rows - 1) * rs_bytes + D * 2);
-        vr = rows_rsrc(a.v + off, (rows - 1) * rs_bytes + D * 2);
+        const size_t off = ((size_t)page * a.page_size * a.Hkv + g) * D * ESZ;
+        kr = rows_rsrc(reinterpret_cast<const uint8_t*>(a.k) + off, (rows - 1) * rs_bytes + D * ESZ);
+        vr = rows_rsrc(reinterpret_cast<const uint8_t*>(a.v) + off, (rows - 1) * rs_bytes + D * ESZ);
         soff = (j0 - pb * a.page_size) * (int)rs_bytes;
       }
     }
@@ -327,13 +327,13 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void fwd_decode_partial_ke
     }
   };
 
-  // Blocks of kBlkKeys keys from cb (paged: on the sequence's 32-key grid so
-  // that none crosses a page, keys before c0 masked in the first block;
-  // packed: from c0).  The `stripes` waves of a head take every stripes-th
+  // Blocks of kBlkKeys keys from cb (paged: on the sequence's kBlkKeys-key
+  // grid so that none crosses a page, keys before c0 masked in the first
+  // block; packed: from c0).  The `stripes` waves of a head take every stripes-th
   // block, wave w from block w / nh on: a fixed split, so that the result is
   // the same from run to run (blocks claimed from a shared LDS counter measured
   // no faster).
-  const int cb = PAGED ? (c0 & ~(kBlk - 1)) : c0;
+  const int cb = PAGED ? (c0 & ~(kBlkKeys - 1)) : c0;
   const int nblk = (c1 - cb + kBlkKeys - 1) / kBlkKeys;
   int next_own = wave / nh;
   auto next_block = [&]() -> int {
@@ -508,17 +508,25 @@ static hipError_t launch_decode_d(const FwdArgs& a, bool alibi, hipStream_t stre
   return hipGetLastError();
 }
 
-// fp8 (OCP e4m3) q, k, v; D = 128; out_bf16 picks the output dtype; packed K/V only.
+// fp8 (OCP e4m3) q, k, v; D = 128; out_bf16 picks the output dtype; K/V packed
+// or in a paged cache (a.block_table).
+template <bool OUT_BF16, bool PAGED>
+static void launch_decode_fp8_partial(const FwdArgs& a, bool alibi, dim3 grid, dim3 block, hipStream_t stream) {
+  if (alibi) hipLaunchKernelGGL((fwd_decode_partial_kernel<128, OUT_BF16, true, PAGED, true>), grid, block, 0, stream, a);
+  else hipLaunchKernelGGL((fwd_decode_partial_kernel<128, OUT_BF16, false, PAGED, true>), grid, block, 0, stream, a);
+}
+
 hipError_t launch_decode_fp8(const FwdArgs& a, bool out_bf16, bool alibi, hipStream_t stream) {
   if (a.dc_pieces > 0) {
     const dim3 grid((unsigned)a.dc_pieces * (unsigned)((a.Hkv / a.kv_per_wg) * a.head_slices));
     const dim3 block(64 * kWaves);
+    const bool paged = a.block_table != nullptr;
     if (out_bf16) {
-      if (alibi) hipLaunchKernelGGL((fwd_decode_partial_kernel<128, true, true, false, true>), grid, block, 0, stream, a);
-      else hipLaunchKernelGGL((fwd_decode_partial_kernel<128, true, false, false, true>), grid, block, 0, stream, a);
+      if (paged) launch_decode_fp8_partial<true, true>(a, alibi, grid, block, stream);
+      else launch_decode_fp8_partial<true, false>(a, alibi, grid, block, stream);
     } else {
-      if (alibi) hipLaunchKernelGGL((fwd_decode_partial_kernel<128, false, true, false, true>), grid, block, 0, stream, a);
-      else hipLaunchKernelGGL((fwd_decode_partial_kernel<128, false, false, false, true>), grid, block, 0, stream, a);
+      if (paged) launch_decode_fp8_partial<false, true>(a, alibi, grid, block, stream);
+      else launch_decode_fp8_partial<false, false>(a, alibi, grid, block, stream);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -184,7 +184,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
       const int pb = kt / a.page_size;
       const int page = a.block_table[(size_t)b * a.max_blocks + pb];
       const uint32_t rows = (uint32_t)min(a.page_size, Lk - pb * a.page_size);
-      kr = rows_rsrc(a.k + ((size_t)page * a.page_size * a.Hkv + g) * D, (rows - 1) * rs_bytes + D * 2);
+      kr = buf_rsrc(reinterpret_cast<const uint8_t*>(a.k) + ((size_t)page * a.page_size * a.Hkv + g) * D * ESZ,
+                    (rows - 1) * rs_bytes + D * ESZ);
       soff = (kt - pb * a.page_size) * (int)rs_bytes;
     }
     uint8_t* dst = kbuf(t);
@@ -438,7 +439,9 @@ __global__ __launch_bounds__(kVtThreads) void vt_images_kernel(FwdArgs a) {
   const int tid = threadIdx.x;
   const int kq = tid % (BN / 4), cv = tid / (BN / 4);
   if (cv >= D / 8) return;
-  const uint32_t rs_bytes = (uint32_t)a.Hkv * D * 2;
+  constexpr int ESZ = FP8 ? 1 : 2;  // bytes per v element
+  const uint32_t rs_bytes = (uint32_t)a.Hkv * D * ESZ;
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v);
   // the tile's rows, bounded so that rows past the sequence's end read zeros
   // (paged: the tile lies in one page, bounded by the rows the sequence uses)
   __amdgpu_buffer_rsrc_t vrs;
@@ -447,21 +450,15 @@ __global__ __launch_bounds__(kVtThreads) void vt_images_kernel(FwdArgs a) {
     const int pb = (i * BN) / a.page_size;
     const int page = a.block_table[(size_t)b * a.max_blocks + pb];
     const uint32_t rows = (uint32_t)min(a.page_size, Lk - pb * a.page_size);
-    vrs = rows_rsrc(a.v + ((size_t)page * a.page_size * a.Hkv + g) * D, (rows - 1) * rs_bytes + D * 2);
+    vrs = buf_rsrc(vbase + ((size_t)page * a.page_size * a.Hkv + g) * D * ESZ, (rows - 1) * rs_bytes + D * ESZ);
     row0 = (uint32_t)(i * BN - pb * a.page_size);
   } else {
-    vrs = rows_rsrc(a.v + ((size_t)sk0 * a.Hkv + g) * D, (uint32_t)(Lk - 1) * rs_bytes + D * 2);
+    vrs = buf_rsrc(vbase + ((size_t)sk0 * a.Hkv + g) * D * ESZ, (uint32_t)(Lk - 1) * rs_bytes + D * ESZ);
     row0 = (uint32_t)(i * BN);
   }
   uint8_t* img = reinterpret_cast<uint8_t*>(a.ws_vt + ((size_t)((sk0 / BN) + b + i) * a.Hkv + g) * (D * BN));
-  if constexpr (FP8) {
-    const uint32_t rs8 = (uint32_t)a.Hkv * D;  // one byte per value
-    const __amdgpu_buffer_rsrc_t v8 =
-        buf_rsrc(reinterpret_cast<const uint8_t*>(a.v) + ((size_t)sk0 * a.Hkv + g) * D, (uint32_t)(Lk - 1) * rs8 + D);
-    write_tile_image_fp8(v8, (uint32_t)(i * BN), rs8, img, kq, cv);
-  } else {
-    write_tile_image<D, BF16>(vrs, row0, rs_bytes, img, kq, cv);
-  }
+  if constexpr (FP8) write_tile_image_fp8(vrs, row0, rs_bytes, img, kq, cv);
+  else write_tile_image<D, BF16>(vrs, row0, rs_bytes, img, kq, cv);
 #endif
 }
 
@@ -509,9 +506,13 @@ hipError_t launch_prefill(const FwdArgs& a, int D, bool bf16, bool causal, bool 
               : launch_prefill_db<128, false>(a, causal, alibi, max_seqlen_k, stream);
 }
 
-// fp8 (OCP e4m3) q, k, v; D = 128; out_bf16 picks the output dtype.
+// fp8 (OCP e4m3) q, k, v; D = 128; out_bf16 picks the output dtype; K/V packed
+// or in a paged cache (a.block_table).
 hipError_t launch_prefill_fp8(const FwdArgs& a, bool out_bf16, bool causal, bool alibi, int max_seqlen_k,
                               hipStream_t stream) {
+  if (a.block_table != nullptr)
+    return out_bf16 ? launch_prefill_dp<128, true, true, true>(a, causal, alibi, max_seqlen_k, stream)
+                    : launch_prefill_dp<128, false, true, true>(a, causal, alibi, max_seqlen_k, stream);
   return out_bf16 ? launch_prefill_dp<128, true, false, true>(a, causal, alibi, max_seqlen_k, stream)
                   : launch_prefill_dp<128, false, false, true>(a, causal, alibi, max_seqlen_k, stream);
 }

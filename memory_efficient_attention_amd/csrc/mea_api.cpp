@@ -398,6 +398,20 @@ mea_status_t mea_fwd_fp8(const void* q, const void* k, const void* v, float q_sc
                   stream, 0, false, nullptr, &sc);
 }
 
+mea_status_t mea_fwd_paged_fp8(const void* q, const void* k_cache, const void* v_cache, float q_scale,
+                               float k_scale, float v_scale, void* out, float* lse, const int32_t* seqstart_q,
+                               const int32_t* seqstart_k, const int32_t* block_table, int32_t num_seqs,
+                               int32_t total_q, int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                               int32_t page_size, int32_t num_pages, int32_t max_blocks, int32_t Hq, int32_t Hkv,
+                               int32_t D, mea_dtype_t out_dtype, int32_t causal, const float* alibi_slopes,
+                               float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  const PagedKv paged{block_table, page_size, num_pages, max_blocks};
+  const Fp8Scales sc{q_scale, k_scale, v_scale};
+  return fwd_impl(q, k_cache, v_cache, out, lse, seqstart_q, seqstart_k, num_seqs, total_q, total_k,
+                  max_seqlen_q, max_seqlen_k, Hq, Hkv, D, out_dtype, causal, alibi_slopes, scale, workspace,
+                  workspace_bytes, stream, 0, false, &paged, &sc);
+}
+
 size_t mea_fwd_fp8_workspace_size(int32_t num_seqs, int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
                                   int32_t Hq, int32_t Hkv, int32_t D) {
   if (D != 128) return 0;

@@ -48,7 +48,7 @@ def test_every_kernel_stub_is_defined():
 
 
 def test_version_and_strings():
-    assert _native.mea_abi_version() == 7
+    assert _native.mea_abi_version() == 8
     for st in range(4):
         assert _native.mea_status_string(st).startswith("MEA_")
     assert "unknown" in _native.mea_status_string(99)
@@ -254,6 +254,35 @@ def call_fp8(**kw):
 def test_fp8_rejected_before_launch(kw, status, needle):
     assert call_fp8(**kw) == status
     assert needle in _native.mea_last_error()
+
+
+def call_paged_fp8(**kw):
+    a = dict(q=P, k_cache=P, v_cache=P, q_scale=0.01, k_scale=0.02, v_scale=0.03, out=P, lse=None, seqstart_q=P,
+             seqstart_k=P, block_table=P, num_seqs=4, total_q=4, total_k=365, max_seqlen_q=1, max_seqlen_k=200,
+             page_size=64, num_pages=10, max_blocks=4, Hq=8, Hkv=2, D=128, out_dtype=MEA_BF16, causal=0,
+             alibi_slopes=None, scale=0.088, workspace=P, workspace_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return _native.mea_fwd_paged_fp8(**a)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(D=64), MEA_ERR_UNSUPPORTED, "D=128"),
+    (dict(k_scale=-1.0), MEA_ERR_UNSUPPORTED, "fp8 scales"),
+    (dict(block_table=None), MEA_ERR_INVALID, "block_table"),
+    (dict(page_size=96), MEA_ERR_UNSUPPORTED, "multiple of 64"),
+    (dict(max_blocks=3), MEA_ERR_INVALID, "max_seqlen_k"),
+    (dict(workspace=None, workspace_bytes=0), MEA_ERR_INVALID, "workspace"),
+    (dict(max_seqlen_q=200, total_q=365, workspace_bytes=100), MEA_ERR_INVALID, "workspace"),
+])
+def test_paged_fp8_rejected_before_launch(kw, status, needle):
+    """Validation of the paged fp8 entry point: the fp8 rules and the page
+    rules both apply, before anything is launched."""
+    assert call_paged_fp8(**kw) == status
+    assert needle in _native.mea_last_error()
+
+
+def test_paged_fp8_empty_call_is_ok():
+    assert call_paged_fp8(num_seqs=0, total_q=0) == MEA_OK
 
 
 def test_fp8_workspace_size():

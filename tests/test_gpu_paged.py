@@ -2,13 +2,15 @@
 input are scattered into shuffled pages (unused slots hold NaN), the HIP path
 runs on the pages, and its result is compared with the float64 oracle on the
 packed input."""
+import dataclasses
 import sys
 
 import numpy as np
 import pytest
 import torch
 
-from mea_workloads import generate, random_case, to_paged
+import oracle
+from mea_workloads import generate, random_case, to_fp8, to_paged
 from parity import compare, compare_rows, oracle_full
 
 pytestmark = pytest.mark.gpu
@@ -69,3 +71,65 @@ def test_paged_prefill_first_sequences_full():
     out, lse = run_paged(inp, 128)
     ref_out, ref_lse = oracle_full(inp)
     _log(f"  {compare(out, lse, ref_out, ref_lse, 'bf16', 'paged prefill 5 seqs')}")
+
+
+# ---------------------------------------------------------------- fp8 caches
+def run_paged_fp8(inp, page_size, seed=0, out_dtype=torch.bfloat16):
+    """q, k, v quantised to e4m3 (per-tensor scales); the k/v codes scattered
+    into shuffled pages (unused slots hold the e4m3 NaN code); returns the
+    GPU result and the fp8 inputs the oracle is to see."""
+    from memory_efficient_attention_amd import attention_paged_fp8
+    f = to_fp8(inp)
+    pk = to_paged(dataclasses.replace(inp, k=f.k8, v=f.v8), page_size, seed=seed)
+    dev = "cuda"
+    out = torch.full((inp.total_q, inp.Hq, inp.D), float("nan"), dtype=out_dtype, device=dev)
+    res = attention_paged_fp8(f.q8.to(dev), pk.k_cache.to(dev), pk.v_cache.to(dev), f.q_scale, f.k_scale, f.v_scale,
+                              pk.block_table.to(dev), inp.seqstart_q.to(dev), inp.seqstart_k.to(dev),
+                              inp.max_seqlen_q, inp.max_seqlen_k, causal=inp.causal,
+                              alibi_slopes=None if inp.alibi_slopes is None else inp.alibi_slopes.to(dev),
+                              scale=inp.scale, out_dtype=out_dtype, return_lse=True, out=out, total_k=inp.total_k)
+    torch.cuda.synchronize()
+    return res[0].cpu(), res[1].cpu(), f
+
+
+def oracle_fp8(inp, f):
+    return oracle.attention_forward_fp8(f.q8, f.k8, f.v8, f.q_scale, f.k_scale, f.v_scale, inp.seqstart_q,
+                                        inp.seqstart_k, causal=inp.causal, alibi_slopes=inp.alibi_slopes,
+                                        scale=inp.scale)
+
+
+PAGED_FP8_CASES = [
+    # (seqlens_q, seqlens_k, Hq, Hkv, causal, alibi, page_size, out dtype)
+    ([1] * 6, [1, 63, 64, 65, 300, 1000], 16, 4, False, True, 64, torch.bfloat16),     # decode
+    ([1] * 5, [700, 0, 129, 2000, 64], 8, 8, True, False, 128, torch.float16),         # decode, empty
+    ([1] * 3, [5000, 4100, 33], 40, 1, False, False, 256, torch.bfloat16),             # decode, MQA
+    ([1] * 4, [95, 130, 2000, 191], 64, 8, True, False, 64, torch.bfloat16),           # decode, group 8
+    ([200, 17, 300], None, 12, 4, True, True, 128, torch.bfloat16),                    # prefill, GQA 3
+    ([40, 7, 90], [100, 7, 300], 8, 2, True, True, 64, torch.float16),                 # L_q < L_k
+]
+
+
+@pytest.mark.parametrize("ci", range(len(PAGED_FP8_CASES)))
+def test_paged_fp8_cases(ci):
+    lq, lk, Hq, Hkv, causal, alibi, ps, odt = PAGED_FP8_CASES[ci]
+    inp = random_case(3100 + ci, lq, lk, Hq=Hq, Hkv=Hkv, D=128, dtype="bf16", causal=causal, alibi=alibi)
+    _log(f"paged fp8 {ci}: {PAGED_FP8_CASES[ci][:-1]}")
+    out, lse, f = run_paged_fp8(inp, ps, seed=ci, out_dtype=odt)
+    ref_out, ref_lse = oracle_fp8(inp, f)
+    _log(f"  {compare(out, lse, ref_out, ref_lse, 'bf16' if odt == torch.bfloat16 else 'fp16', f'paged fp8 {ci}')}")
+
+
+def test_paged_fp8_decode_full_size_sampled():
+    """The 64-request decode workload in e4m3 on shuffled 64-key pages; sampled rows."""
+    inp = generate("decode_splitkv_64req_h64kv8_d128_bf16")
+    _log(f"paged fp8 decode 64 requests, sum Lk={inp.total_k}, page 64")
+    out, lse, f = run_paged_fp8(inp, 64)
+    assert not torch.isnan(out).any()
+    rows = [(t, h) for t in range(64) for h in (0, 9, 63)]
+    q = f.q8.to(torch.float64) * f.q_scale
+    k = f.k8.to(torch.float64) * f.k_scale
+    v = f.v8.to(torch.float64) * f.v_scale
+    ro, rl = oracle.attention_rows(q, k, v, inp.seqstart_q, inp.seqstart_k, rows, causal=inp.causal, scale=inp.scale)
+    go = torch.stack([out[t, h] for t, h in rows])
+    gl = torch.stack([lse[h, t] for t, h in rows])
+    _log(f"  {compare(go, gl, ro, rl, 'bf16', 'paged fp8 decode sampled')}")
