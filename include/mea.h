@@ -117,7 +117,9 @@ typedef enum {
  *                  Its contents on entry do not matter and are clobbered.
  *   stream         hipStream_t to enqueue on.
  *
- * Returns MEA_ERR_INVALID for: a NULL q/k/v/out/seqstart pointer; negative
+ * Returns MEA_ERR_INVALID for: a NULL seqstart pointer, a NULL q or out with
+ * total_q > 0, a NULL k or v with total_k > 0 (k and v are never read when
+ * there are no keys; every query row then gets out = 0 and lse = -inf); negative
  * sizes; Hq or Hkv <= 0 or Hq % Hkv != 0; total_q > 0 with max_seqlen_q == 0;
  * causal not 0/1; a workspace smaller than required.
  * Returns MEA_ERR_UNSUPPORTED for: D not 64/128; dtype not listed; a
@@ -301,8 +303,9 @@ MEA_EXPORT size_t mea_fwd_fp8_workspace_size(int32_t num_seqs, int32_t total_k, 
  *                  bytes, 256-byte aligned; clobbered.
  * dtype applies to q, k, v, out, dout, dq, dk and dv; all 16-byte aligned.
  * Ownership and execution as for mea_fwd (outputs must not alias inputs).
- * Returns MEA_ERR_INVALID for a NULL pointer among q, k, v, out, lse, dout,
- * dq, dk, dv, seqstart_q/k; negative sizes; bad heads; causal not 0/1;
+ * Returns MEA_ERR_INVALID for a NULL pointer among seqstart_q/k, among q,
+ * out, lse, dout, dq with total_q > 0, or among k, v, dk, dv with total_k > 0;
+ * negative sizes; bad heads; causal not 0/1;
  * total_q > 0 with max_seqlen_q == 0 or total_k > 0 with max_seqlen_k == 0;
  * a workspace smaller than required.  MEA_ERR_UNSUPPORTED for D not 64/128,
  * an unknown dtype, a non-finite or non-positive scale, misalignment,

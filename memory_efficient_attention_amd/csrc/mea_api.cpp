@@ -95,8 +95,10 @@ mea_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, fl
                       size_t workspace_bytes, void* stream, int32_t chunk_keys, bool forced_split,
                       const PagedKv* paged = nullptr, const Fp8Scales* fp8 = nullptr) {
   g_last_error[0] = '\0';
-  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
-    return fail(MEA_ERR_INVALID, "q, k, v and out must be non-NULL device pointers");
+  // q and out are read/written only when total_q > 0, k and v only when total_k > 0
+  if (((q == nullptr || out == nullptr) && total_q > 0) || ((k == nullptr || v == nullptr) && total_k > 0))
+    return fail(MEA_ERR_INVALID, "q, k, v and out must be non-NULL device pointers (k and v may be NULL when "
+                "total_k == 0, q and out when total_q == 0)");
   if (seqstart_q == nullptr || seqstart_k == nullptr)
     return fail(MEA_ERR_INVALID, "seqstart_q and seqstart_k must be non-NULL device pointers");
   if (num_seqs < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
@@ -244,10 +246,16 @@ mea_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o
                       mea_dtype_t dtype, int32_t causal, const float* alibi_slopes, float scale,
                       void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error[0] = '\0';
-  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || lse == nullptr || dout == nullptr)
-    return fail(MEA_ERR_INVALID, "q, k, v, out, lse and dout must be non-NULL device pointers");
-  if (dq == nullptr || dk == nullptr || dv == nullptr)
-    return fail(MEA_ERR_INVALID, "dq, dk and dv must be non-NULL device pointers");
+  // the query-side arrays are used only when total_q > 0, the key-side ones only when total_k > 0
+  if ((q == nullptr || out == nullptr || lse == nullptr || dout == nullptr) && total_q > 0)
+    return fail(MEA_ERR_INVALID, "q, k, v, out, lse and dout must be non-NULL device pointers (the query-side "
+                "ones may be NULL when total_q == 0)");
+  if ((k == nullptr || v == nullptr) && total_k > 0)
+    return fail(MEA_ERR_INVALID, "q, k, v, out, lse and dout must be non-NULL device pointers (k and v may be "
+                "NULL when total_k == 0)");
+  if ((dq == nullptr && total_q > 0) || ((dk == nullptr || dv == nullptr) && total_k > 0))
+    return fail(MEA_ERR_INVALID, "dq, dk and dv must be non-NULL device pointers (dq may be NULL when "
+                "total_q == 0, dk and dv when total_k == 0)");
   if (seqstart_q == nullptr || seqstart_k == nullptr)
     return fail(MEA_ERR_INVALID, "seqstart_q and seqstart_k must be non-NULL device pointers");
   if (num_seqs < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)

@@ -106,6 +106,18 @@ def test_rejected_before_launch(kw, status, needle):
     assert needle in _native.mea_last_error()
 
 
+def test_empty_key_side_may_be_null():
+    """No keys at all: k and v are never read, so NULL passes the pointer
+    check (the call below then stops at a later rule, before any launch);
+    with keys, a NULL k is rejected."""
+    assert call(k=None, v=None, total_k=0, max_seqlen_k=0, D=96) == MEA_ERR_UNSUPPORTED
+    assert "D=96" in _native.mea_last_error()
+    assert call(q=None, out=None, num_seqs=4, total_q=0, max_seqlen_q=0, D=96) == MEA_ERR_UNSUPPORTED
+    assert call(k=None, total_k=365) == MEA_ERR_INVALID
+    assert "non-NULL" in _native.mea_last_error()
+    assert call(out=None) == MEA_ERR_INVALID
+
+
 def call_paged(**kw):
     a = dict(q=P, k_cache=P, v_cache=P, out=P, lse=None, seqstart_q=P, seqstart_k=P, block_table=P,
              num_seqs=4, total_q=4, total_k=365, max_seqlen_q=1, max_seqlen_k=200, page_size=64,
