@@ -81,10 +81,16 @@ def algorithmic_bytes_fp8(inp, with_lse=True) -> int:
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources' code: comments and blank space are dropped
+    first, so that an edit of a comment does not orphan the counter runs."""
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "memory_efficient_attention_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "memory_efficient_attention_amd", "csrc", f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -15,9 +15,9 @@ constexpr int kPfGroupWaves = 4;
 constexpr int kPfGroups = 2;
 constexpr int kPfWaves = kPfGroupWaves * kPfGroups;
 constexpr int kPfBN = 64;          // keys per LDS tile
-// Decode: workgroups of 4 waves; gcd(Hkv, 4) key/value heads per workgroup,
-// each wave streaming its own 32-key blocks of one head's part of a piece of
-// the concatenated key axis.
+// Decode: workgroups of 8 waves (one per CU); gcd(Hkv, 4) key/value heads per
+// workgroup, the 8 / gcd waves of a head each streaming every (8 / gcd)-th
+// block of that head's part of a piece of the concatenated key axis.
 constexpr int kDcWaves = 8;         // decode workgroup: 8 waves, one workgroup per CU
 constexpr int kDcKvPerWgMax = 4;    // key/value heads per decode workgroup: gcd(Hkv, 4)
 constexpr int kDcPieceAlign = 32;    // piece lengths are multiples of one wave block
