@@ -195,7 +195,7 @@ mea_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, fl
     a.kv_per_wg = decode_kv_per_wg(Hkv);
     a.ws_o = static_cast<float*>(workspace);
     a.ws_lse = a.ws_o + (size_t)num_seqs * a.max_chunks * Hq * D;
-    if ((long long)a.dc_pieces * decode_head_groups(Hq, Hkv) > 0x7fffffffll)
+    if ((long long)a.dc_pieces * decode_head_groups(Hq, Hkv) > 0x7ffffff8ll)  // the grid is padded to a multiple of 8
       return fail(MEA_ERR_UNSUPPORTED, "too many decode workgroups (%d pieces of %d keys)", a.dc_pieces, chunk);
     err = fp8 != nullptr ? mea::launch_decode_fp8(a, bf16, alibi, s) : mea::launch_decode(a, D, bf16, alibi, s);
   } else {
