@@ -227,9 +227,12 @@ MEA_EXPORT size_t mea_fwd_workspace_size(int32_t num_seqs, int32_t total_k, int3
  *   workspace      mea_fwd_fp8_workspace_size(num_seqs, total_k, max_seqlen_q,
  *                  max_seqlen_k, Hq, Hkv, D) bytes, 256-byte aligned.
  * Path choice as in mea_fwd: max_seqlen_q == 1 runs the split-KV decode
- * kernels (pieces of mea_default_chunk_keys(total_k, Hq, Hkv) keys, float32
- * partials in the workspace), anything else the prefill kernel (half-precision
- * V^T tile images in the workspace).  K and V in a paged cache: mea_fwd_paged_fp8.
+ * kernels (float32 partials in the workspace), anything else the prefill
+ * kernel (half-precision V^T tile images in the workspace).  The decode pieces
+ * are those of mea_default_chunk_keys(total_k, Hq, Hkv), except that with
+ * Hkv a multiple of 8, workgroups take 8 key/value heads (whole 1 KiB token
+ * rows) instead of 4 whenever the pieces for that grouping are still at least
+ * 2048 keys long; mea_fwd_fp8_workspace_size follows the same choice.  K and V in a paged cache: mea_fwd_paged_fp8.
  * Same ownership and errors as mea_fwd, plus MEA_ERR_UNSUPPORTED for a
  * non-finite or non-positive scale.
  */

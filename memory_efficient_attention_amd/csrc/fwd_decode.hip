@@ -12,8 +12,8 @@
 // sequence it touches.
 //
 // Partial kernel: a workgroup of 8 waves (one per CU) takes one piece and
-// nh = gcd(Hkv, 4) neighbouring key/value heads (with up to 16 query heads of
-// each head's group).  The nh heads of a key are adjacent in memory, so a
+// nh neighbouring key/value heads (with up to 16 query heads of each head's
+// group): gcd(Hkv, 4), or gcd(Hkv, 8) for fp8 K/V on long pieces.  The nh heads of a key are adjacent in memory, so a
 // workgroup reads runs of nh * D * 2 contiguous bytes per key rather than one
 // head's D * 2 bytes out of each token row.  Wave w serves head w % nh, and
 // the 8 / nh waves of a head take every (8 / nh)-th 32-key block of the
@@ -429,13 +429,19 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void fwd_decode_partial_ke
 #endif
 }
 
-// One wave per (sequence, query head); a lane owns D/64 features.  The chunk
-// log-sum-exps are reduced across the wave first, then every lane sums its
-// features over the chunks with several partial rows in flight.
+// One wave per (sequence, query head).  The wave reads D/8 lanes to a partial
+// row (8 features, 32 bytes a lane), 512/D rows side by side and four such
+// loads in flight, so that a sequence split into hundreds of pieces is
+// combined with 16 (D 128) or 32 (D 64) rows in flight instead of a row at a
+// time.  The chunk log-sum-exps are reduced across the wave first; the lane
+// groups' sums are added with cross-lane shuffles at the end.
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void fwd_decode_combine_kernel(FwdArgs a) {
-  constexpr int F = D / 64;  // features per lane
+  constexpr int LPR = D / 8;    // lanes per partial row
+  constexpr int RPL = 64 / LPR;  // partial rows per wave-wide load
+  constexpr int U = 4;           // wave-wide loads in flight
   const int lane = threadIdx.x & 63;
+  const int grp = lane / LPR, f0 = (lane % LPR) * 8;
   const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int b = blockIdx.y;
   if (h >= a.Hq) return;
@@ -451,46 +457,50 @@ __global__ __launch_bounds__(256) void fwd_decode_combine_kernel(FwdArgs a) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) M = __builtin_fmaxf(M, __shfl_xor(M, m));
   float S = 0.f;
-  float acc[F];
+  float acc[8];
 #pragma unroll
-  for (int f = 0; f < F; ++f) acc[f] = 0.f;
+  for (int f = 0; f < 8; ++f) acc[f] = 0.f;
   if (M != kNegInf) {
-    const float* o_p = a.ws_o + row0 * D + lane * F;             // chunk c at [c * Hq * D]
+    const float* o_p = a.ws_o + row0 * D + f0;  // chunk c at [c * Hq * D]
     const size_t ostride = (size_t)a.Hq * D;
-    int ch = 0;
-    for (; ch + 4 <= nch; ch += 4) {
-      float lc[4], ov[4][F];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        lc[u] = lse_p[(size_t)(ch + u) * a.Hq];
-#pragma unroll
-        for (int f = 0; f < F; ++f) ov[u][f] = o_p[(size_t)(ch + u) * ostride + f];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float w = (lc[u] == kNegInf) ? 0.f : fast_exp2(lc[u] - M);
-        S += w;
-#pragma unroll
-        for (int f = 0; f < F; ++f) acc[f] += w * ov[u][f];
-      }
-    }
-    for (; ch < nch; ++ch) {
-      const float lc = lse_p[(size_t)ch * a.Hq];
+    auto add = [&](float lc, const float4& x0, const float4& x1) {
       const float w = (lc == kNegInf) ? 0.f : fast_exp2(lc - M);
       S += w;
+      acc[0] += w * x0.x; acc[1] += w * x0.y; acc[2] += w * x0.z; acc[3] += w * x0.w;
+      acc[4] += w * x1.x; acc[5] += w * x1.y; acc[6] += w * x1.z; acc[7] += w * x1.w;
+    };
+    int ch = grp;
+    for (; ch + (U - 1) * RPL < nch; ch += U * RPL) {
+      float lc[U];
+      float4 x[U][2];
 #pragma unroll
-      for (int f = 0; f < F; ++f) acc[f] += w * o_p[(size_t)ch * ostride + f];
+      for (int u = 0; u < U; ++u) {
+        const size_t c = (size_t)(ch + u * RPL);
+        lc[u] = lse_p[c * a.Hq];
+        x[u][0] = *(const float4*)(o_p + c * ostride);
+        x[u][1] = *(const float4*)(o_p + c * ostride + 4);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) add(lc[u], x[u][0], x[u][1]);
     }
+    for (; ch < nch; ch += RPL)
+      add(lse_p[(size_t)ch * a.Hq], *(const float4*)(o_p + (size_t)ch * ostride),
+          *(const float4*)(o_p + (size_t)ch * ostride + 4));
+  }
+#pragma unroll
+  for (int m = LPR; m < 64; m <<= 1) {
+    S += __shfl_xor(S, m);
+#pragma unroll
+    for (int f = 0; f < 8; ++f) acc[f] += __shfl_xor(acc[f], m);
   }
   const float inv = (S > 0.f ? 1.f / S : 0.f) * a.out_scale;  // out_scale: 1, or the fp8 V scale
-  uint16_t* dst = a.out + ((size_t)sq0 * a.Hq + h) * D + lane * F;
-  if constexpr (F == 2) {
-    *(uint32_t*)dst = pack_out_x2<BF16>(acc[0] * inv, acc[1] * inv);
-  } else {
-    uint16_t bits;
-    if constexpr (BF16) bits = __builtin_bit_cast(uint16_t, (__bf16)(acc[0] * inv));
-    else bits = __builtin_bit_cast(uint16_t, (_Float16)(acc[0] * inv));
-    *dst = bits;
+  if (grp == 0) {
+    uint4 o;
+    o.x = pack_out_x2<BF16>(acc[0] * inv, acc[1] * inv);
+    o.y = pack_out_x2<BF16>(acc[2] * inv, acc[3] * inv);
+    o.z = pack_out_x2<BF16>(acc[4] * inv, acc[5] * inv);
+    o.w = pack_out_x2<BF16>(acc[6] * inv, acc[7] * inv);
+    *(uint4*)(a.out + ((size_t)sq0 * a.Hq + h) * D + f0) = o;
   }
   if (lane == 0 && a.lse != nullptr)
     a.lse[(size_t)h * a.total_q + sq0] = S > 0.f ? (M + fast_log2(S)) * kLn2 : kNegInf;

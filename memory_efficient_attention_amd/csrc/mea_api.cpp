@@ -34,27 +34,50 @@ int gcd_int(int x, int y) {
   return x;
 }
 
-// Key/value heads of one decode head group (kDcWaves / nh waves serve each).
-int32_t decode_kv_per_wg(int32_t Hkv) { return gcd_int(Hkv, mea::kDcKvPerWgMax); }
-
-int32_t decode_head_groups(int32_t Hq, int32_t Hkv) {
+// Decode head groups: nh = kv neighbouring key/value heads (kDcWaves / nh
+// waves serve each) times the slices of 16 query heads of each head's group.
+int32_t decode_head_groups(int32_t Hq, int32_t Hkv, int32_t kv) {
   const int32_t group = Hq / Hkv;
-  return (Hkv / decode_kv_per_wg(Hkv)) * ((group + mea::kDcHeadsPerWg - 1) / mea::kDcHeadsPerWg);
+  return (Hkv / kv) * ((group + mea::kDcHeadsPerWg - 1) / mea::kDcHeadsPerWg);
 }
 
-int32_t default_chunk(int32_t total_k, int32_t Hq, int32_t Hkv) {
+int32_t default_chunk(int32_t total_k, int32_t Hq, int32_t Hkv, int32_t kv) {
   // Piece length W of the concatenated key axis: about kDcTargetWgs
   // equal-sized (piece, head group) workgroups in all, i.e. one full round of
   // one workgroup per CU on 256 CUs: every workgroup starts at once and
   // none is left over for a tail (measured: one round beats two or four,
   // which pay each workgroup's start-up again).  Never below kDcMinPiece keys,
   // so that partial results stay a small fraction of the K/V bytes.
-  const long long work = (long long)total_k * (long long)decode_head_groups(Hq, Hkv);
+  const long long work = (long long)total_k * (long long)decode_head_groups(Hq, Hkv, kv);
   long long w = (work + mea::kDcTargetWgs - 1) / mea::kDcTargetWgs;
   w = (w + mea::kDcPieceAlign - 1) / mea::kDcPieceAlign * mea::kDcPieceAlign;
   if (w < mea::kDcMinPiece) w = mea::kDcMinPiece;
   if (w > (1ll << 30)) w = 1ll << 30;
   return (int32_t)w;
+}
+
+// Key/value heads per decode head group and the default piece length.  16-bit
+// K/V: gcd(Hkv, 4) heads, runs of up to 1 KiB of each 2 KiB token row (8 heads
+// of D 128).  fp8 K/V: the token row of 8 heads is 1 KiB, and groups of 4
+// heads read its halves at unequal rates (measured: the workgroups on the
+// first half of the rows took ~13 % longer); gcd(Hkv, 8) heads read whole
+// rows, 5-7 % faster, as long as the pieces stay long (>= kDcFp8WidePiece
+// keys).  On
+// short pieces (one long sequence: the default splits it into pieces of a
+// few hundred keys) the wide groups' halved piece length costs more than they
+// save, so fp8 keeps gcd(Hkv, 4) there.
+struct DecodeSplit {
+  int32_t kv_per_wg, chunk;
+};
+
+DecodeSplit decode_split(int32_t total_k, int32_t Hq, int32_t Hkv, bool fp8) {
+  const int32_t kv4 = gcd_int(Hkv, mea::kDcKvPerWgMax);
+  if (fp8) {
+    const int32_t kv8 = gcd_int(Hkv, mea::kDcKvPerWgMaxFp8);
+    const int32_t w = default_chunk(total_k, Hq, Hkv, kv8);
+    if (kv8 > kv4 && w >= mea::kDcFp8WidePiece) return {kv8, w};
+  }
+  return {kv4, default_chunk(total_k, Hq, Hkv, kv4)};
 }
 
 // Partial slots per sequence: the pieces a sequence of L keys touches are at
@@ -83,6 +106,17 @@ struct PagedKv {
 
 // fp8 (OCP e4m3) q, k, v with per-tensor scales: the values are q_scale * q8
 // etc.  q_scale * k_scale folds into the score scale, v_scale into the output.
+size_t fwd_ws_size(int32_t num_seqs, int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq,
+                   int32_t Hkv, int32_t D, int32_t chunk_keys, bool fp8) {
+  if (num_seqs <= 0 || total_k < 0 || max_seqlen_q <= 0 || max_seqlen_k < 0 || Hq <= 0 || Hkv <= 0 ||
+      Hq % Hkv != 0 || (D != 64 && D != 128) || chunk_keys < 0 ||
+      (chunk_keys > 0 && chunk_keys % mea::kDcPieceAlign != 0))
+    return 0;
+  if (max_seqlen_q != 1) return prefill_ws_bytes(num_seqs, total_k, Hkv, D);
+  const int32_t chunk = chunk_keys > 0 ? chunk_keys : decode_split(total_k, Hq, Hkv, fp8).chunk;
+  return decode_ws_bytes(num_seqs, total_k, max_seqlen_k, Hq, D, chunk);
+}
+
 struct Fp8Scales {
   float q, k, v;
 };
@@ -182,7 +216,9 @@ mea_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, fl
 
   hipError_t err;
   if (max_seqlen_q == 1) {
-    const int32_t chunk = forced_split ? chunk_keys : default_chunk(total_k, Hq, Hkv);
+    const DecodeSplit sp = forced_split ? DecodeSplit{gcd_int(Hkv, mea::kDcKvPerWgMax), chunk_keys}
+                                        : decode_split(total_k, Hq, Hkv, fp8 != nullptr);
+    const int32_t chunk = sp.chunk;
     const size_t need = decode_ws_bytes(num_seqs, total_k, max_seqlen_k, Hq, D, chunk);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need))
       return fail(MEA_ERR_INVALID, "workspace of %zu bytes is smaller than the %zu bytes required", workspace_bytes, need);
@@ -192,10 +228,10 @@ mea_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, fl
     a.max_chunks = need > 0 ? decode_slots(max_seqlen_k, chunk) : 0;
     a.head_slices = (a.group + mea::kDcHeadsPerWg - 1) / mea::kDcHeadsPerWg;
     a.heads_per_wg = mea::kDcHeadsPerWg;
-    a.kv_per_wg = decode_kv_per_wg(Hkv);
+    a.kv_per_wg = sp.kv_per_wg;
     a.ws_o = static_cast<float*>(workspace);
     a.ws_lse = a.ws_o + (size_t)num_seqs * a.max_chunks * Hq * D;
-    if ((long long)a.dc_pieces * decode_head_groups(Hq, Hkv) > 0x7ffffff8ll)  // the grid is padded to a multiple of 8
+    if ((long long)a.dc_pieces * decode_head_groups(Hq, Hkv, sp.kv_per_wg) > 0x7ffffff8ll)  // the grid is padded to a multiple of 8
       return fail(MEA_ERR_UNSUPPORTED, "too many decode workgroups (%d pieces of %d keys)", a.dc_pieces, chunk);
     err = fp8 != nullptr ? mea::launch_decode_fp8(a, bf16, alibi, s) : mea::launch_decode(a, D, bf16, alibi, s);
   } else {
@@ -423,7 +459,7 @@ mea_status_t mea_fwd_paged_fp8(const void* q, const void* k_cache, const void* v
 size_t mea_fwd_fp8_workspace_size(int32_t num_seqs, int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
                                   int32_t Hq, int32_t Hkv, int32_t D) {
   if (D != 128) return 0;
-  return mea_fwd_workspace_size(num_seqs, total_k, max_seqlen_q, max_seqlen_k, Hq, Hkv, D, 0);
+  return fwd_ws_size(num_seqs, total_k, max_seqlen_q, max_seqlen_k, Hq, Hkv, D, 0, true);
 }
 
 mea_status_t mea_swiglu_ffn(const void* x, const void* w_gate, const void* w_up, const void* w_down, void* hidden,
@@ -451,18 +487,12 @@ mea_status_t mea_swiglu_ffn(const void* x, const void* w_gate, const void* w_up,
 
 size_t mea_fwd_workspace_size(int32_t num_seqs, int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
                               int32_t Hq, int32_t Hkv, int32_t D, int32_t chunk_keys) {
-  if (num_seqs <= 0 || total_k < 0 || max_seqlen_q <= 0 || max_seqlen_k < 0 || Hq <= 0 || Hkv <= 0 ||
-      Hq % Hkv != 0 || (D != 64 && D != 128) || chunk_keys < 0 ||
-      (chunk_keys > 0 && chunk_keys % mea::kDcPieceAlign != 0))
-    return 0;
-  if (max_seqlen_q != 1) return prefill_ws_bytes(num_seqs, total_k, Hkv, D);
-  const int32_t chunk = chunk_keys > 0 ? chunk_keys : default_chunk(total_k, Hq, Hkv);
-  return decode_ws_bytes(num_seqs, total_k, max_seqlen_k, Hq, D, chunk);
+  return fwd_ws_size(num_seqs, total_k, max_seqlen_q, max_seqlen_k, Hq, Hkv, D, chunk_keys, false);
 }
 
 int32_t mea_default_chunk_keys(int32_t total_k, int32_t Hq, int32_t Hkv) {
   if (Hkv < 1 || Hq < Hkv || Hq % Hkv != 0) return mea::kDcMinPiece;
-  return default_chunk(total_k < 0 ? 0 : total_k, Hq, Hkv);
+  return decode_split(total_k < 0 ? 0 : total_k, Hq, Hkv, false).chunk;
 }
 
 const char* mea_status_string(mea_status_t status) {

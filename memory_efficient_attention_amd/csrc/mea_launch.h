@@ -15,11 +15,14 @@ constexpr int kPfGroupWaves = 4;
 constexpr int kPfGroups = 2;
 constexpr int kPfWaves = kPfGroupWaves * kPfGroups;
 constexpr int kPfBN = 64;          // keys per LDS tile
-// Decode: workgroups of 8 waves (one per CU); gcd(Hkv, 4) key/value heads per
-// workgroup, the 8 / gcd waves of a head each streaming every (8 / gcd)-th
-// block of that head's part of a piece of the concatenated key axis.
+// Decode: workgroups of 8 waves (one per CU); nh = gcd(Hkv, 4) key/value heads
+// per workgroup (gcd(Hkv, 8) for fp8 K/V when the default pieces are at least
+// kDcFp8WidePiece keys), the 8 / nh waves of a head each streaming every
+// (8 / nh)-th block of that head's part of a piece of the concatenated key axis.
 constexpr int kDcWaves = 8;         // decode workgroup: 8 waves, one workgroup per CU
-constexpr int kDcKvPerWgMax = 4;    // key/value heads per decode workgroup: gcd(Hkv, 4)
+constexpr int kDcKvPerWgMax = 4;      // key/value heads per decode workgroup: gcd(Hkv, 4)
+constexpr int kDcKvPerWgMaxFp8 = 8;   // fp8 K/V on long pieces: gcd(Hkv, 8)
+constexpr int kDcFp8WidePiece = 2048; // shortest default piece on which fp8 takes gcd(Hkv, 8)
 constexpr int kDcPieceAlign = 32;    // piece lengths are multiples of one wave block
 constexpr int kDcMinPiece = 128;     // shortest default piece
 constexpr int kDcTargetWgs = 256;    // default: one round of one workgroup per CU on 256 CUs

@@ -301,9 +301,19 @@ def test_fp8_workspace_size():
     ws = _native.mea_fwd_fp8_workspace_size
     # prefill-shaped: the V^T tile images of the 16-bit prefill path
     assert ws(64, 137663, 4094, 4094, 32, 8, 128) == (137663 // 64 + 64) * 8 * 128 * 128
-    # decode-shaped: the 16-bit decode path's float32 partials
-    w16 = _native.mea_fwd_workspace_size(64, 1101299, 1, 32680, 64, 8, 128, 0)
-    assert w16 > 0 and ws(64, 1101299, 1, 32680, 64, 8, 128) == w16
+    # decode-shaped: float32 partials, num_seqs x slots x Hq x (D + 1) floats,
+    # slots = ceil(max_seqlen_k / W) + 1 for pieces of W keys.  16-bit: two
+    # groups of 4 key/value heads, W = 1101299 * 2 / 256 -> 8608 (a multiple
+    # of 32); fp8 with 8 key/value heads: one group of 8 heads since
+    # W = 1101299 / 256 -> 4320 is at least 2048 keys
+    part = lambda slots: 64 * slots * 64 * 129 * 4
+    assert _native.mea_fwd_workspace_size(64, 1101299, 1, 32680, 64, 8, 128, 0) == part(-(-32680 // 8608) + 1)
+    assert ws(64, 1101299, 1, 32680, 64, 8, 128) == part(-(-32680 // 4320) + 1)
+    # one 131072-key sequence: the 8-head pieces would be 512 keys, so fp8
+    # keeps the 16-bit grouping and size; likewise with 4 key/value heads
+    for args in [(1, 131072, 1, 131072, 64, 8, 128), (64, 1101299, 1, 32680, 32, 4, 128)]:
+        w16 = _native.mea_fwd_workspace_size(*args, 0)
+        assert w16 > 0 and ws(*args) == w16
     assert ws(4, 365, 2, 200, 8, 2, 64) == 0
     assert ws(0, 365, 2, 200, 8, 2, 128) == 0
     assert ws(4, 0, 2, 0, 8, 2, 128) == 0

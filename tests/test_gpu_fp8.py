@@ -137,6 +137,32 @@ def test_fp8_decode_matches_prefill_kernel_rows():
     assert d_out <= 1e-2 and d_lse <= 1e-3
 
 
+def test_fp8_decode_wide_head_groups():
+    """Decode with 8 key/value heads and over half a million keys, so that the
+    pieces stay at least 2048 keys long and each fp8 decode workgroup takes
+    all 8 heads of a token row.  Every row is checked against the oracle, one
+    key/value head (and its two query heads) at a time, so that the oracle
+    holds one head's keys in float64; a second call must give the same bits."""
+    lk = [0, 1, 31, 33, 2047, 2049, 100000, 65, 250000, 4097, 200000, 129]
+    inp = random_case(797, [1] * len(lk), lk, Hq=16, Hkv=8, D=128, dtype="bf16", causal=True, alibi=True)
+    f = to_fp8(inp)
+    _log(f"fp8 decode, 8-head groups: {len(lk)} requests, sum Lk={inp.total_k}, Hq 16 / Hkv 8")
+    out, lse = _run(inp, f, torch.bfloat16)
+    out2, lse2 = _run(inp, f, torch.bfloat16)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    for g in range(8):
+        hs = [2 * g, 2 * g + 1]
+        q = f.q8[:, hs].to(torch.float64) * f.q_scale
+        k = f.k8[:, [g]].to(torch.float64) * f.k_scale
+        v = f.v8[:, [g]].to(torch.float64) * f.v_scale
+        rows = [(t, j) for t in range(inp.total_q) for j in range(2)]
+        ro, rl = oracle.attention_rows(q, k, v, inp.seqstart_q, inp.seqstart_k, rows, causal=True,
+                                       alibi_slopes=inp.alibi_slopes[hs], scale=inp.scale)
+        go = torch.stack([out[t, hs[j]] for t, j in rows])
+        gl = torch.stack([lse[hs[j], t] for t, j in rows])
+        _log(f"  {compare(go, gl, ro, rl, 'bf16', f'8-head groups, key/value head {g}')}")
+
+
 def test_fp8_decode_deterministic():
     inp = random_case(795, [1] * 6, [5000, 33, 1, 4097, 64, 129], Hq=64, Hkv=8, D=128, dtype="bf16", causal=True)
     f = to_fp8(inp)
