@@ -126,6 +126,19 @@ def test_decode_pieces_spanning_many_sequences(piece):
     _log(f"  {compare(out, lse, ref_out, ref_lse, 'bf16', f'decode short piece={piece}')}")
 
 
+@pytest.mark.parametrize("D,dtype", [(64, "fp16"), (128, "bf16")])
+def test_decode_combine_many_pieces(D, dtype):
+    """Pieces of 32 keys: a 9,000-key request has 282 partial rows to combine,
+    which the combine kernel reads 512 / D rows per wave-wide load, four loads
+    in flight, plus a ragged remainder (row counts 1, 2, 29, 95, 282 here)."""
+    lk = [9000, 1, 0, 40, 3000, 900]
+    inp = random_case(4300 + D, [1] * len(lk), lk, Hq=8, Hkv=2, D=D, dtype=dtype, causal=True, alibi=True)
+    _log(f"decode many pieces, D={D} {dtype}, Lk={lk}")
+    out, lse = run_gpu(inp, chunk_keys=32)
+    ref_out, ref_lse = oracle_full(inp)
+    _log(f"  {compare(out, lse, ref_out, ref_lse, dtype, f'decode 32-key pieces D={D}')}")
+
+
 # ----------------------------------------------------------------------------- edge cases
 EDGE = [
     # (seqlens_q, seqlens_k, Hq, Hkv, D, dtype, causal, alibi)
