@@ -171,8 +171,12 @@ MEA_EXPORT mea_status_t mea_fwd_splitkv(const void* q, const void* k, const void
  *                     has seqstart_k[b+1] - seqstart_k[b] keys; total_k is
  *                     their sum), used for the work split only
  * page_size must be a positive multiple of 64.  Rows of a sequence's last
- * page past its length are never read.  Preconditions, not checked (device
- * memory): every block_table entry a sequence uses is in [0, num_pages).
+ * page past its length are never read.  Every block_table entry a sequence
+ * uses should be in [0, num_pages); the table is device memory and is not
+ * checked on the host, but the kernels never dereference an entry outside
+ * that range (nor a block past max_blocks): its keys and values read as
+ * zeros, so the call touches no memory outside the cache, and that
+ * sequence's result is meaningless.
  * Workspace: mea_fwd_workspace_size with the same sizes.  Same ownership and
  * errors as mea_fwd, plus MEA_ERR_INVALID for a NULL block_table, a
  * non-positive page_size, num_pages or max_blocks, or max_blocks *

@@ -194,12 +194,16 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void fwd_decode_partial_ke
     __amdgpu_buffer_rsrc_t kr = krs, vr = vrs;
     if constexpr (PAGED) {
       if (valid) {
+        // a block past the table's row or a page outside [0, num_pages)
+        // reads zeros through a zero-byte resource
         const int pb = j0 / a.page_size;
-        const int page = a.block_table[(size_t)b * a.max_blocks + pb];
+        const int page = pb < a.max_blocks ? a.block_table[(size_t)b * a.max_blocks + pb] : -1;
+        const bool ok = (uint32_t)page < (uint32_t)a.num_pages;
         const uint32_t rows = (uint32_t)min(a.page_size, Lk - pb * a.page_size);
-        const size_t off = ((size_t)page * a.page_size * a.Hkv + g) * D * ESZ;
-        kr = rows_rsrc(reinterpret_cast<const uint8_t*>(a.k) + off, (rows - 1) * rs_bytes + D * ESZ);
-        vr = rows_rsrc(reinterpret_cast<const uint8_t*>(a.v) + off, (rows - 1) * rs_bytes + D * ESZ);
+        const uint32_t bytes = ok ? (rows - 1) * rs_bytes + D * ESZ : 0u;
+        const size_t off = ((size_t)(ok ? page : 0) * a.page_size * a.Hkv + g) * D * ESZ;
+        kr = rows_rsrc(reinterpret_cast<const uint8_t*>(a.k) + off, bytes);
+        vr = rows_rsrc(reinterpret_cast<const uint8_t*>(a.v) + off, bytes);
         soff = (j0 - pb * a.page_size) * (int)rs_bytes;
       }
     }

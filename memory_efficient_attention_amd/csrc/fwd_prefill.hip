@@ -175,17 +175,20 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
 
   // K tile of step t.  Paged: the 64-key tile lies in one page (page_size
   // is a multiple of 64); its resource is bounded by the rows of that page
-  // the sequence uses, so rows past the sequence's end read zeros.
+  // the sequence uses, so rows past the sequence's end read zeros.  A block
+  // past the table's row or a page index outside [0, num_pages) gets a
+  // zero-byte resource: its rows read zeros and no memory is touched.
   auto issue_k = [&](int t) {
     const int kt = tile_of(t) * BN;
     int soff = kt * (int)rs_bytes;
     __amdgpu_buffer_rsrc_t kr = krs;
     if constexpr (PAGED) {
       const int pb = kt / a.page_size;
-      const int page = a.block_table[(size_t)b * a.max_blocks + pb];
+      const int page = pb < a.max_blocks ? a.block_table[(size_t)b * a.max_blocks + pb] : -1;
+      const bool ok = (uint32_t)page < (uint32_t)a.num_pages;
       const uint32_t rows = (uint32_t)min(a.page_size, Lk - pb * a.page_size);
-      kr = buf_rsrc(reinterpret_cast<const uint8_t*>(a.k) + ((size_t)page * a.page_size * a.Hkv + g) * D * ESZ,
-                    (rows - 1) * rs_bytes + D * ESZ);
+      kr = buf_rsrc(reinterpret_cast<const uint8_t*>(a.k) + ((size_t)(ok ? page : 0) * a.page_size * a.Hkv + g) * D * ESZ,
+                    ok ? (rows - 1) * rs_bytes + D * ESZ : 0u);
       soff = (kt - pb * a.page_size) * (int)rs_bytes;
     }
     uint8_t* dst = kbuf(t);
@@ -447,10 +450,13 @@ __global__ __launch_bounds__(kVtThreads) void vt_images_kernel(FwdArgs a) {
   __amdgpu_buffer_rsrc_t vrs;
   uint32_t row0;
   if constexpr (PAGED) {
+    // a block past the table's row or a page outside [0, num_pages) reads zeros
     const int pb = (i * BN) / a.page_size;
-    const int page = a.block_table[(size_t)b * a.max_blocks + pb];
+    const int page = pb < a.max_blocks ? a.block_table[(size_t)b * a.max_blocks + pb] : -1;
+    const bool ok = (uint32_t)page < (uint32_t)a.num_pages;
     const uint32_t rows = (uint32_t)min(a.page_size, Lk - pb * a.page_size);
-    vrs = buf_rsrc(vbase + ((size_t)page * a.page_size * a.Hkv + g) * D * ESZ, (rows - 1) * rs_bytes + D * ESZ);
+    vrs = buf_rsrc(vbase + ((size_t)(ok ? page : 0) * a.page_size * a.Hkv + g) * D * ESZ,
+                   ok ? (rows - 1) * rs_bytes + D * ESZ : 0u);
     row0 = (uint32_t)(i * BN - pb * a.page_size);
   } else {
     vrs = buf_rsrc(vbase + ((size_t)sk0 * a.Hkv + g) * D * ESZ, (uint32_t)(Lk - 1) * rs_bytes + D * ESZ);

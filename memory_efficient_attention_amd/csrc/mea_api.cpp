@@ -209,6 +209,7 @@ mea_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, fl
     a.block_table = paged->block_table;
     a.page_size = paged->page_size;
     a.max_blocks = paged->max_blocks;
+    a.num_pages = paged->num_pages;
   }
   const bool bf16 = dtype == MEA_BF16;
   const bool alibi = alibi_slopes != nullptr;

@@ -35,6 +35,7 @@ struct FwdArgs {
   const int32_t* block_table;  // paged K/V: [num_seqs, max_blocks] page of each page_size-key block, or nullptr
   int32_t page_size;         // paged K/V: keys per page (a multiple of 64)
   int32_t max_blocks;        // paged K/V: row length of block_table
+  int32_t num_pages;         // paged K/V: pages in the cache; entries outside [0, num_pages) read as zeros
   float scale_log2;          // scale * log2(e)
   int32_t num_seqs;
   int32_t total_q;

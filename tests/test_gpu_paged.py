@@ -133,3 +133,69 @@ def test_paged_fp8_decode_full_size_sampled():
     go = torch.stack([out[t, h] for t, h in rows])
     gl = torch.stack([lse[h, t] for t, h in rows])
     _log(f"  {compare(go, gl, ro, rl, 'bf16', 'paged fp8 decode sampled')}")
+
+
+# ------------------------------------------------------ out-of-range entries
+BAD_PAGE_CASES = [
+    # (seqlens_q, seqlens_k, Hq, Hkv, D, dtype, causal, alibi, page_size, fp8, {(sequence, block): entry})
+    ([1] * 4, [300, 64, 1000, 129], 16, 4, 128, "bf16", True, True, 64, False,
+     {(0, 2): "num_pages", (2, 0): -1, (2, 15): 2**31 - 1, (3, 2): "num_pages+5"}),              # decode
+    ([37, 120, 200], None, 8, 2, 64, "fp16", True, False, 64, False,
+     {(1, 1): -1, (2, 0): "num_pages", (2, 3): 2**31 - 1}),                                     # prefill
+    ([1] * 4, [300, 64, 1000, 129], 16, 4, 128, "bf16", True, False, 64, True,
+     {(0, 2): "num_pages", (2, 0): -1, (2, 15): 2**31 - 1}),                                    # fp8 decode
+    ([40, 7, 90], [100, 7, 300], 8, 2, 128, "bf16", True, True, 64, True,
+     {(0, 1): "num_pages", (2, 2): -1}),                                                       # fp8 prefill
+]
+
+
+def _zero_blocks(x, inp, blocks, page_size):
+    x = x.clone()
+    sk = inp.seqstart_k.tolist()
+    for b, i in blocks:
+        x[sk[b] + i * page_size:min(sk[b] + (i + 1) * page_size, sk[b + 1])] = 0
+    return x
+
+
+@pytest.mark.parametrize("ci", range(len(BAD_PAGE_CASES)))
+def test_out_of_range_entries_read_as_zeros(ci):
+    """Block-table entries outside [0, num_pages) (num_pages itself, past it,
+    -1 and 2^31 - 1) are never dereferenced: the keys and values of those
+    blocks read as zeros.  The result equals the oracle on the packed input
+    with those keys and values set to zero (e4m3 code 0 is +0)."""
+    from memory_efficient_attention_amd import attention_paged, attention_paged_fp8
+    lq, lk, Hq, Hkv, D, dt, causal, alibi, ps, fp8, bad = BAD_PAGE_CASES[ci]
+    inp = random_case(3200 + ci, lq, lk, Hq=Hq, Hkv=Hkv, D=D, dtype=dt, causal=causal, alibi=alibi)
+    _log(f"out-of-range block-table entries {ci}: {bad}")
+    dev = "cuda"
+    slopes = None if inp.alibi_slopes is None else inp.alibi_slopes.to(dev)
+    if fp8:
+        f = to_fp8(inp)
+        pk = to_paged(dataclasses.replace(inp, k=f.k8, v=f.v8), ps, seed=ci)
+    else:
+        pk = to_paged(inp, ps, seed=ci)
+    num_pages = pk.k_cache.shape[0]
+    table = pk.block_table.clone()
+    for (b, i), e in bad.items():
+        assert i * ps < inp.seqlens_k[b]
+        table[b, i] = {"num_pages": num_pages, "num_pages+5": num_pages + 5}.get(e, e)
+    out = torch.full((inp.total_q, Hq, D), float("nan"), dtype=torch.bfloat16 if dt == "bf16" else torch.float16,
+                     device=dev)
+    common = dict(causal=causal, alibi_slopes=slopes, scale=inp.scale, return_lse=True, out=out, total_k=inp.total_k)
+    if fp8:
+        res = attention_paged_fp8(f.q8.to(dev), pk.k_cache.to(dev), pk.v_cache.to(dev), f.q_scale, f.k_scale,
+                                  f.v_scale, table.to(dev), inp.seqstart_q.to(dev), inp.seqstart_k.to(dev),
+                                  inp.max_seqlen_q, inp.max_seqlen_k, out_dtype=out.dtype, **common)
+    else:
+        res = attention_paged(inp.q.to(dev), pk.k_cache.to(dev), pk.v_cache.to(dev), table.to(dev),
+                              inp.seqstart_q.to(dev), inp.seqstart_k.to(dev), inp.max_seqlen_q, inp.max_seqlen_k,
+                              **common)
+    torch.cuda.synchronize()
+    got_out, got_lse = res[0].cpu(), res[1].cpu()
+    if fp8:
+        fz = dataclasses.replace(f, k8=_zero_blocks(f.k8, inp, bad, ps), v8=_zero_blocks(f.v8, inp, bad, ps))
+        ref_out, ref_lse = oracle_fp8(inp, fz)
+    else:
+        inz = dataclasses.replace(inp, k=_zero_blocks(inp.k, inp, bad, ps), v=_zero_blocks(inp.v, inp, bad, ps))
+        ref_out, ref_lse = oracle_full(inz)
+    _log(f"  {compare(got_out, got_lse, ref_out, ref_lse, dt, f'out-of-range entries {ci}')}")
