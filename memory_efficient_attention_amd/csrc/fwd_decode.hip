@@ -298,13 +298,18 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void fwd_decode_partial_ke
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float sc = s[e / 4][e % 4];
-      float v;
-      if constexpr (ALIBI) v = __builtin_fmaf(sc, c, slope2 * (float)(jlane + e - qpos));
-      else v = sc * c;
-      if (jlane + e >= c1 || (PAGED && jlane + e < c0)) v = kNegInf;
-      x[e] = v;
-      mx = __builtin_fmaxf(mx, v);
+      if constexpr (ALIBI) x[e] = __builtin_fmaf(sc, c, slope2 * (float)(jlane + e - qpos));
+      else x[e] = sc * c;
     }
+    // element tests only on a segment's last block (and, paged, its first):
+    // a wave-uniform branch
+    if (j0 + kBlk > c1 || (PAGED && j0 < c0)) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (jlane + e >= c1 || (PAGED && jlane + e < c0)) x[e] = kNegInf;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mx = __builtin_fmaxf(mx, x[e]);
     mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16));
     mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
     if (__any(mx > m_run + 8.f)) {
