@@ -136,3 +136,93 @@ def test_unmutated_ffn_oracle_passes_pins():
 @pytest.mark.parametrize("mi", range(len(MUTATIONS)))
 def test_planted_ffn_mistake_fails_pins(mi):
     assert not _pins_pass(_mutant(*MUTATIONS[mi]))
+
+
+# ---- out_abs and the row-sampled form (the full-size GPU check uses both) ----
+
+def brute_out_abs(x, wg, wu, wd):
+    """sum_f |hidden[t, f] * w_down[j, f]| by scalar loops and math.fsum."""
+    h, _ = brute(x, wg, wu, wd)
+    H, Dn = h.tolist(), wd.double().tolist()
+    T, df, dm = len(H), len(H[0]), len(Dn)
+    return torch.tensor([[math.fsum(abs(H[t][f] * Dn[j][f]) for f in range(df)) for j in range(dm)]
+                         for t in range(T)], dtype=torch.float64)
+
+
+def _out_abs_ok(fn):
+    for ci in range(len(CASES)):
+        T, dm, df = CASES[ci]
+        f = swiglu_case(200 + ci, T, dm, df, dtype="bf16")
+        _, _, a = fn(f.x, f.w_gate, f.w_up, f.w_down)
+        ba = brute_out_abs(f.x, f.w_gate, f.w_up, f.w_down)
+        # equal in both directions, relative to each element's own size
+        if not bool(((a - ba).abs() <= 1e-12 * ba.abs().clamp_min(1e-300)).all()):
+            return False
+    return True
+
+
+ROWS = [6, 0, 6, 12, 3, 0]   # unsorted, repeated, the first (0) and the last (12) token
+
+
+def _rows_ok(fn_rows):
+    f = swiglu_case(300, 13, 8, 10, dtype="bf16")
+    idx = torch.tensor(ROWS)
+    h, o, a = fn_rows(f.x, f.w_gate, f.w_up, f.w_down, ROWS)
+    bh, bo = brute(f.x[idx], f.w_gate, f.w_up, f.w_down)
+    ba = brute_out_abs(f.x[idx], f.w_gate, f.w_up, f.w_down)
+    if h.shape != (len(ROWS), 10) or o.shape != (len(ROWS), 8) or a.shape != (len(ROWS), 8):
+        return False
+    return ((h - bh).abs().max().item() < 1e-12 and (o - bo).abs().max().item() < 1e-12
+            and (a - ba).abs().max().item() < 1e-12)
+
+
+def test_out_abs_brute_force():
+    assert _out_abs_ok(swiglu_ffn)
+
+
+def test_rows_brute_force():
+    assert _rows_ok(oracle.swiglu_ffn_rows)
+
+
+def test_rows_equal_full_rows():
+    """The row-sampled form returns the full layer's rows (same float64 arithmetic)."""
+    f = swiglu_case(301, 40, 16, 24, dtype="bf16")
+    rows = [39, 0, 17, 17, 5]
+    full = swiglu_ffn(f.x, f.w_gate, f.w_up, f.w_down)
+    part = oracle.swiglu_ffn_rows(f.x, f.w_gate, f.w_up, f.w_down, rows)
+    for a, b in zip(part, full):
+        assert (a - b[torch.tensor(rows)]).abs().max().item() < 1e-12
+
+
+ROW_MUTATIONS = [
+    # the error scale of each output element inflated: it loosens every GPU bound built on it
+    ("out_abs = hidden.abs() @ Wd.abs().transpose(0, 1)", "out_abs = 100 * (hidden.abs() @ Wd.abs().transpose(0, 1))"),
+    # the scale without absolute values inside the sum
+    ("out_abs = hidden.abs() @ Wd.abs().transpose(0, 1)", "out_abs = (hidden @ Wd.transpose(0, 1)).abs()"),
+    # the first len(rows) tokens instead of the selected ones
+    ("return swiglu_ffn(x[idx], w_gate, w_up, w_down)", "return swiglu_ffn(x[:len(idx)], w_gate, w_up, w_down)"),
+]
+
+
+def _mutant_module(old, new):
+    src = open(FFN_SRC).read()
+    assert src.count(old) == 1, old
+    mod = types.ModuleType("ffn_mutant")
+    exec(compile(src.replace(old, new), "ffn_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+def _row_pins_pass(mod):
+    try:
+        return _out_abs_ok(mod.swiglu_ffn) and _rows_ok(mod.swiglu_ffn_rows)
+    except Exception:
+        return False
+
+
+def test_unmutated_row_pins_pass():
+    assert _row_pins_pass(oracle.ffn)
+
+
+@pytest.mark.parametrize("mi", range(len(ROW_MUTATIONS)))
+def test_planted_row_mistake_fails_pins(mi):
+    assert not _row_pins_pass(_mutant_module(*ROW_MUTATIONS[mi]))
