@@ -129,9 +129,13 @@ typedef enum {
  *
  * Numerics: Q K^T runs on the matrix cores in the input dtype with float32
  * accumulation; the softmax is float32; the softmax weights enter P V as
- * IEEE half with V converted to half (exact for bfloat16 V with
- * 2^-14 <= |v| <= 65504; larger magnitudes saturate, smaller lose bits
- * below 2^-24); out is rounded to nearest even from float32.
+ * IEEE halves, with bfloat16 V re-encoded as halves, which is exact for
+ * 2^-14 <= |v| <= 65504.  Wherever a block of bfloat16 V holds a larger
+ * magnitude, or only magnitudes below 2^-14 (where the re-encoding would
+ * lose precision), that block keeps bfloat16 V and bfloat16 weights instead
+ * (prefill: a 64-key tile, and then the whole query tile that reads it;
+ * decode: a 32-key block of one wave), so any finite bfloat16 V is served.
+ * out is rounded to nearest even from float32.
  */
 MEA_EXPORT mea_status_t mea_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                      const int32_t* seqstart_q, const int32_t* seqstart_k, int32_t num_seqs,
@@ -200,9 +204,10 @@ MEA_EXPORT mea_status_t mea_fwd_paged(const void* q, const void* k_cache, const 
  *     (D + 1) * 4, W = the piece length (chunk_keys, or the library's choice
  *     mea_default_chunk_keys(total_k, Hq, Hkv)) -- float32 partial outputs
  *     and log-sum-exps; 0 when total_k or max_seqlen_k is 0;
- *   max_seqlen_q > 1 (prefill): (total_k / 64 + num_seqs) * Hkv * D * 128 --
- *     one transposed half-precision copy of every 64-key tile of V (0 when
- *     total_k == 0).
+ *   max_seqlen_q > 1 (prefill): with S = (total_k / 64 + num_seqs) * Hkv,
+ *     round256(S * D * 128) + round256(S * 4) -- one transposed 16-bit copy
+ *     of every 64-key tile of V and one int32 flag per copy (round256 rounds
+ *     up to a multiple of 256; 0 when total_k == 0).
  */
 MEA_EXPORT size_t mea_fwd_workspace_size(int32_t num_seqs, int32_t total_k, int32_t max_seqlen_q,
                                          int32_t max_seqlen_k, int32_t Hq, int32_t Hkv, int32_t D,

@@ -132,6 +132,38 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _check_out(t: Optional[torch.Tensor], name: str, shape, dtype: torch.dtype, dev: torch.device) -> None:
+    """A caller-supplied output buffer must be exactly what the kernels write:
+    the kernels store full-size rows through its raw pointer, so a short,
+    strided, wrongly typed or foreign-device buffer would be written out of
+    bounds or scrambled."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != dev:
+        raise ValueError(f"{name} must be on {dev}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _workspace(ws: Optional[torch.Tensor], need: int, dev: torch.device) -> Optional[torch.Tensor]:
+    """The caller's workspace if it is a usable one of at least ``need`` bytes,
+    else a new one (``None`` when nothing is needed)."""
+    if need <= 0:
+        return None
+    if ws is not None:
+        if ws.device != dev:
+            raise ValueError(f"workspace must be on {dev}, got {ws.device}")
+        if not ws.is_contiguous():
+            raise ValueError("workspace must be contiguous")
+        if ws.numel() * ws.element_size() >= need:
+            return ws
+    return torch.empty(need, dtype=torch.uint8, device=dev)
+
+
 def attention_packed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                      seqstart_q: torch.Tensor, seqstart_k: torch.Tensor,
                      max_seqlen_q: int, max_seqlen_k: int, *, causal: bool = False,
@@ -162,6 +194,8 @@ def attention_packed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     num_seqs = seqstart_q.numel() - 1
     if seqstart_k.numel() != num_seqs + 1:
         raise ValueError("seqstart_q and seqstart_k differ in length")
+    _check_out(out, "out", (Tq, Hq, D), q.dtype, dev)
+    _check_out(lse, "lse", (Hq, Tq), torch.float32, dev)
     if out is None:
         out = torch.empty_like(q)
     if return_lse and lse is None:
@@ -176,13 +210,12 @@ def attention_packed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     scale = float(np.float32(scale))
     ws_bytes = _native.mea_fwd_workspace_size(num_seqs, Tk, max_seqlen_q, max_seqlen_k, Hq, Hkv, D,
                                               int(chunk_keys or 0))
-    if ws_bytes > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, ws_bytes, dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(seqstart_q), _ptr(seqstart_k),
             num_seqs, Tq, Tk, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, D, _dtype_code(q.dtype),
-            int(bool(causal)), _ptr(slopes), scale, _ptr(workspace) if ws_bytes > 0 else None,
+            int(bool(causal)), _ptr(slopes), scale, _ptr(workspace),
             ws_bytes, stream.cuda_stream)
     with torch.cuda.device(dev):
         if chunk_keys is None:
@@ -230,6 +263,8 @@ def attention_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
     if seqstart_k.numel() != num_seqs + 1 or block_table.shape[0] != num_seqs:
         raise ValueError("seqstart_q, seqstart_k and block_table disagree on the number of sequences")
     Tk = int(total_k) if total_k is not None else (int(seqstart_k[-1].item()) if num_seqs > 0 else 0)
+    _check_out(out, "out", (Tq, Hq, D), q.dtype, dev)
+    _check_out(lse, "lse", (Hq, Tq), torch.float32, dev)
     if out is None:
         out = torch.empty_like(q)
     if return_lse and lse is None:
@@ -243,8 +278,7 @@ def attention_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
         scale = 1.0 / math.sqrt(D)
     scale = float(np.float32(scale))
     ws_bytes = _native.mea_fwd_workspace_size(num_seqs, Tk, max_seqlen_q, max_seqlen_k, Hq, Hkv, D, 0)
-    if ws_bytes > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, ws_bytes, dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     with torch.cuda.device(dev):
@@ -252,7 +286,7 @@ def attention_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
             _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), _ptr(seqstart_q),
             _ptr(seqstart_k), _ptr(block_table), num_seqs, Tq, Tk, int(max_seqlen_q), int(max_seqlen_k),
             page_size, num_pages, block_table.shape[1], Hq, Hkv, D, _dtype_code(q.dtype),
-            int(bool(causal)), _ptr(slopes), scale, _ptr(workspace) if ws_bytes > 0 else None,
+            int(bool(causal)), _ptr(slopes), scale, _ptr(workspace),
             ws_bytes, stream.cuda_stream)
     if st != _native.MEA_OK:
         raise MeaError(st, _native.mea_last_error())
@@ -292,6 +326,9 @@ def attention_backward_packed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     num_seqs = seqstart_q.numel() - 1
     if seqstart_k.numel() != num_seqs + 1:
         raise ValueError("seqstart_q and seqstart_k differ in length")
+    _check_out(dq, "dq", q.shape, q.dtype, dev)
+    _check_out(dk, "dk", k.shape, k.dtype, dev)
+    _check_out(dv, "dv", v.shape, v.dtype, dev)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
@@ -304,8 +341,7 @@ def attention_backward_packed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         scale = 1.0 / math.sqrt(D)
     scale = float(np.float32(scale))
     ws_bytes = _native.mea_bwd_workspace_size(num_seqs, Tq, Tk, Hq, Hkv, D)
-    if ws_bytes > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, ws_bytes, dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     with torch.cuda.device(dev):
@@ -313,7 +349,7 @@ def attention_backward_packed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
             _ptr(seqstart_q), _ptr(seqstart_k), num_seqs, Tq, Tk, int(max_seqlen_q), int(max_seqlen_k),
             Hq, Hkv, D, _dtype_code(q.dtype), int(bool(causal)), _ptr(slopes), scale,
-            _ptr(workspace) if ws_bytes > 0 else None, ws_bytes, stream.cuda_stream)
+            _ptr(workspace), ws_bytes, stream.cuda_stream)
     if st != _native.MEA_OK:
         raise MeaError(st, _native.mea_last_error())
     return dq, dk, dv
@@ -372,6 +408,8 @@ def attention_packed_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, q
     num_seqs = seqstart_q.numel() - 1
     if seqstart_k.numel() != num_seqs + 1:
         raise ValueError("seqstart_q and seqstart_k differ in length")
+    _check_out(out, "out", (Tq, Hq, D), out_dtype, dev)
+    _check_out(lse, "lse", (Hq, Tq), torch.float32, dev)
     if out is None:
         out = torch.empty((Tq, Hq, D), dtype=out_dtype, device=dev)
     if return_lse and lse is None:
@@ -385,8 +423,7 @@ def attention_packed_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, q
         scale = 1.0 / math.sqrt(D)
     scale = float(np.float32(scale))
     ws_bytes = _native.mea_fwd_fp8_workspace_size(num_seqs, Tk, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, D)
-    if ws_bytes > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, ws_bytes, dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     with torch.cuda.device(dev):
@@ -394,7 +431,7 @@ def attention_packed_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, q
             _ptr(q8), _ptr(k8), _ptr(v8), float(q_scale), float(k_scale), float(v_scale), _ptr(out), _ptr(lse),
             _ptr(seqstart_q), _ptr(seqstart_k), num_seqs, Tq, Tk, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv,
             D, _dtype_code(out.dtype), int(bool(causal)), _ptr(slopes), scale,
-            _ptr(workspace) if ws_bytes > 0 else None, ws_bytes, stream.cuda_stream)
+            _ptr(workspace), ws_bytes, stream.cuda_stream)
     if st != _native.MEA_OK:
         raise MeaError(st, _native.mea_last_error())
     return (out, lse) if return_lse else out
@@ -434,6 +471,8 @@ def attention_paged_fp8(q8: torch.Tensor, k_cache8: torch.Tensor, v_cache8: torc
     if seqstart_k.numel() != num_seqs + 1 or block_table.shape[0] != num_seqs:
         raise ValueError("seqstart_q, seqstart_k and block_table disagree on the number of sequences")
     Tk = int(total_k) if total_k is not None else (int(seqstart_k[-1].item()) if num_seqs > 0 else 0)
+    _check_out(out, "out", (Tq, Hq, D), out_dtype, dev)
+    _check_out(lse, "lse", (Hq, Tq), torch.float32, dev)
     if out is None:
         out = torch.empty((Tq, Hq, D), dtype=out_dtype, device=dev)
     if return_lse and lse is None:
@@ -447,8 +486,7 @@ def attention_paged_fp8(q8: torch.Tensor, k_cache8: torch.Tensor, v_cache8: torc
         scale = 1.0 / math.sqrt(D)
     scale = float(np.float32(scale))
     ws_bytes = _native.mea_fwd_fp8_workspace_size(num_seqs, Tk, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, D)
-    if ws_bytes > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, ws_bytes, dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     with torch.cuda.device(dev):
@@ -457,7 +495,7 @@ def attention_paged_fp8(q8: torch.Tensor, k_cache8: torch.Tensor, v_cache8: torc
             _ptr(lse), _ptr(seqstart_q), _ptr(seqstart_k), _ptr(block_table), num_seqs, Tq, Tk,
             int(max_seqlen_q), int(max_seqlen_k), page_size, num_pages, block_table.shape[1], Hq, Hkv, D,
             _dtype_code(out.dtype), int(bool(causal)), _ptr(slopes), scale,
-            _ptr(workspace) if ws_bytes > 0 else None, ws_bytes, stream.cuda_stream)
+            _ptr(workspace), ws_bytes, stream.cuda_stream)
     if st != _native.MEA_OK:
         raise MeaError(st, _native.mea_last_error())
     return (out, lse) if return_lse else out
@@ -484,6 +522,8 @@ def swiglu_ffn(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, w_down
     if dev.type != "cuda" or any(t.device != dev for t in (w_gate, w_up, w_down)):
         raise ValueError("x and the weights must be on the same GPU")
     x, w_gate, w_up, w_down = (t.contiguous() for t in (x, w_gate, w_up, w_down))
+    _check_out(hidden, "hidden", (T, d_ff), x.dtype, dev)
+    _check_out(out, "out", (T, d_model), x.dtype, dev)
     if hidden is None:
         hidden = torch.empty((T, d_ff), dtype=x.dtype, device=dev)
     if out is None:

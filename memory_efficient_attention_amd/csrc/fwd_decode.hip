@@ -189,9 +189,12 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void fwd_decode_partial_ke
   // counts unable to tell the paths apart, and its merged count would wait
   // for the loads just issued as well as for the block about to be computed.
   const __amdgpu_buffer_rsrc_t none = rows_rsrc(a.k, 0u);
-  auto load = [&](Regs& R, int j0, bool valid) {
-    int soff = valid ? j0 * (int)rs_bytes : 0;
-    __amdgpu_buffer_rsrc_t kr = krs, vr = vrs;
+  struct Src {
+    __amdgpu_buffer_rsrc_t k, v;
+    int soff;
+  };
+  auto src_of = [&](int j0, bool valid) -> Src {
+    Src r{krs, vrs, valid ? j0 * (int)rs_bytes : 0};
     if constexpr (PAGED) {
       if (valid) {
         // a block past the table's row or a page outside [0, num_pages)
@@ -202,11 +205,17 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void fwd_decode_partial_ke
         const uint32_t rows = (uint32_t)min(a.page_size, Lk - pb * a.page_size);
         const uint32_t bytes = ok ? (rows - 1) * rs_bytes + D * ESZ : 0u;
         const size_t off = ((size_t)(ok ? page : 0) * a.page_size * a.Hkv + g) * D * ESZ;
-        kr = rows_rsrc(reinterpret_cast<const uint8_t*>(a.k) + off, bytes);
-        vr = rows_rsrc(reinterpret_cast<const uint8_t*>(a.v) + off, bytes);
-        soff = (j0 - pb * a.page_size) * (int)rs_bytes;
+        r.k = rows_rsrc(reinterpret_cast<const uint8_t*>(a.k) + off, bytes);
+        r.v = rows_rsrc(reinterpret_cast<const uint8_t*>(a.v) + off, bytes);
+        r.soff = (j0 - pb * a.page_size) * (int)rs_bytes;
       }
     }
+    return r;
+  };
+  auto load = [&](Regs& R, int j0, bool valid) {
+    const Src sr = src_of(j0, valid);
+    const int soff = sr.soff;
+    const __amdgpu_buffer_rsrc_t kr = sr.k, vr = sr.v;
 #pragma unroll
     for (int sb = 0; sb < NSB; ++sb) {
       const bool live = valid && (sb == 0 || j0 + kBlk * sb < c1);
@@ -231,9 +240,17 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void fwd_decode_partial_ke
 #pragma unroll
   for (int d = 0; d < DB; ++d) o[d] = f32x4{};
   float m_run = kNegInf, l_run = 0.f;
+  bool redo = false;  // a block of this wave was left to the second walk
 
-  // One 32-key sub-block sb of a block at key j0.
-  auto compute_sub = [&](Regs& R, int sb, int j0) {
+  // One 32-key sub-block sb of a block at key j0.  bfloat16 V normally
+  // enters P V as IEEE halves.  A block that holds a value outside the range
+  // where that is exact (v_needs_bf16 of its largest |v|, decided per wave)
+  // is skipped by the main walk (REDO false), which only notes that there is
+  // one, and computed in a second walk over the wave's blocks (REDO true)
+  // that takes just such blocks, with V and P in bfloat16.  Keeping the rare
+  // case out of the main walk keeps that walk within the register budget.
+  auto compute_sub = [&](auto redo_c, Regs& R, int sb, int j0) {
+    constexpr bool REDO = decltype(redo_c)::value;
     // V block -> LDS, transposed (and re-encoded as IEEE half for bfloat16)
     if constexpr (FP8) {
       // lane (kq, cv) holds features 16 cv .. + 15 of keys 4 kq .. + 3; word
@@ -255,18 +272,8 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void fwd_decode_partial_ke
           *(u32x2*)(vt + (d + 1) * kVtStride + 4 * kq) = odd;
         }
     } else {
-#pragma unroll
-    for (int x = 0; x < VCH; ++x) {
-      u32x4 a0 = R.v[sb][x][0], a1 = R.v[sb][x][1], a2 = R.v[sb][x][2], a3 = R.v[sb][x][3];
-      if constexpr (BF16) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          a0[w] = bf16x2_to_f16x2(a0[w]);
-          a1[w] = bf16x2_to_f16x2(a1[w]);
-          a2[w] = bf16x2_to_f16x2(a2[w]);
-          a3[w] = bf16x2_to_f16x2(a3[w]);
-        }
-      }
+    // transposed store of lane (kq, cv)'s 4 keys x 8 features of chunk x
+    auto store_vt = [&](const u32x4& a0, const u32x4& a1, const u32x4& a2, const u32x4& a3, int x) {
       const int d0 = 8 * (cv + 8 * x);
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -277,6 +284,41 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void fwd_decode_partial_ke
         odd[1] = __builtin_amdgcn_perm(a3[w], a2[w], 0x07060302u);
         *(u32x2*)(vt + (d0 + 2 * w) * kVtStride + 4 * kq) = even;
         *(u32x2*)(vt + (d0 + 2 * w + 1) * kVtStride + 4 * kq) = odd;
+      }
+    };
+    float vmax = 0.f;  // bfloat16: the block's largest |v|
+    if constexpr (REDO) {
+#pragma unroll
+      for (int x = 0; x < VCH; ++x)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) vmax = bf16x2_absmax(vmax, R.v[sb][x][i][w]);
+      if (!__any(v_needs_bf16(vmax))) return;  // done in the main walk
+#pragma unroll
+      for (int x = 0; x < VCH; ++x) store_vt(R.v[sb][x][0], R.v[sb][x][1], R.v[sb][x][2], R.v[sb][x][3], x);
+    } else {
+#pragma unroll
+      for (int x = 0; x < VCH; ++x) {
+        u32x4 a0 = R.v[sb][x][0], a1 = R.v[sb][x][1], a2 = R.v[sb][x][2], a3 = R.v[sb][x][3];
+        if constexpr (BF16) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            vmax = bf16x2_absmax(bf16x2_absmax(vmax, a0[w]), a1[w]);
+            vmax = bf16x2_absmax(bf16x2_absmax(vmax, a2[w]), a3[w]);
+            a0[w] = bf16x2_to_f16x2(a0[w]);
+            a1[w] = bf16x2_to_f16x2(a1[w]);
+            a2[w] = bf16x2_to_f16x2(a2[w]);
+            a3[w] = bf16x2_to_f16x2(a3[w]);
+          }
+        }
+        store_vt(a0, a1, a2, a3, x);
+      }
+      if constexpr (BF16) {
+        if (__any(v_needs_bf16(vmax))) {  // left to the second walk
+          redo = true;
+          return;
+        }
       }
     }
     }
@@ -326,20 +368,20 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void fwd_decode_partial_ke
     for (int e = 0; e < 8; e += 2) {
       const float p0 = fast_exp2(x[e] - m_use), p1 = fast_exp2(x[e + 1] - m_use);
       l_run += p0 + p1;
-      pf[e / 2] = pack_f16x2(p0, p1);
+      pf[e / 2] = REDO ? pack_out_x2<true>(p0, p1) : pack_f16x2(p0, p1);
     }
     // O^T += V^T P^T: V^T fragment of feature block d is row 16d + q, keys 8*g4..+7
 #pragma unroll
     for (int d = 0; d < DB; ++d) {
       const u32x4 vf = *(const u32x4*)(vt + (16 * d + q) * kVtStride + 8 * g4);
-      o[d] = mfma_16x16x32<false>(vf, pf, o[d]);
+      o[d] = mfma_16x16x32<REDO>(vf, pf, o[d]);
     }
   };
   auto compute = [&](Regs& R, int j0) {
 #pragma unroll
     for (int sb = 0; sb < NSB; ++sb) {
       if (sb > 0 && j0 + kBlk * sb >= c1) break;
-      compute_sub(R, sb, j0 + kBlk * sb);
+      compute_sub(std::false_type{}, R, sb, j0 + kBlk * sb);
     }
   };
 
@@ -379,6 +421,17 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void fwd_decode_partial_ke
       jb[un] = next_block();
       load(rg[un], cb + kBlkKeys * jb[un], jb[un] < nblk);
       compute(rg[u], cb + kBlkKeys * jb[u]);
+    }
+  }
+
+  // The second walk (bfloat16 only, rare): the wave's blocks again, those
+  // that need bfloat16 V computed.  redo is wave-uniform.
+  if constexpr (BF16 && !FP8) {
+    if (redo) {
+      for (int jw = wave / nh; jw < nblk; jw += stripes) {
+        load(rg[0], cb + kBlkKeys * jw, true);
+        compute_sub(std::true_type{}, rg[0], 0, cb + kBlkKeys * jw);
+      }
     }
   }
 

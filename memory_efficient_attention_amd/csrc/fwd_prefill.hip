@@ -288,8 +288,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
     }
   };
 
-  // Probabilities of the prepared scores, packed as the P operand.
-  auto probs = [&](f32x16 (&s)[2], u32x4 (&pf)[4], float& lsum) {
+  // Probabilities of the prepared scores, packed as the P operand: IEEE
+  // halves, or bfloat16 where the V^T tiles stayed bfloat16 (vbf_c).
+  auto probs = [&](auto vbf_c, f32x16 (&s)[2], u32x4 (&pf)[4], float& lsum) {
+    constexpr bool VBF = decltype(vbf_c)::value;
     const float m_use = (m_run == kNegInf) ? 0.f : m_run;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -304,18 +306,19 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
           p1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], c, -m_use));
         }
         lsum += p0 + p1;
-        pf[2 * kb + r / 8][(r % 8) / 2] = pack_f16x2(p0, p1);
+        pf[2 * kb + r / 8][(r % 8) / 2] = VBF ? pack_out_x2<true>(p0, p1) : pack_f16x2(p0, p1);
       }
   };
 
   // O^T += V^T P^T for tile t: V^T fragment of 16-key chunk ch, feature block d
-  auto pv = [&](int t, const u32x4 (&pf)[4]) {
+  auto pv = [&](auto vbf_c, int t, const u32x4 (&pf)[4]) {
+    constexpr bool VBF = decltype(vbf_c)::value;
     const uint8_t* Vt = vbuf(t);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int ch = i / (D / 32), d = i % (D / 32);
       const u32x4 vf = *(const u32x4*)(Vt + vt_off(32 * d + l32, 2 * ch + hi));
-      o[d] = mfma_32x32x16<false>(vf, pf[ch], o[d]);
+      o[d] = mfma_32x32x16<VBF>(vf, pf[ch], o[d]);
     }
     interleave_reads_and_products<NV>();
   };
@@ -339,10 +342,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
   // own loop, so that within a loop the phase kinds are fixed and the scores
   // and P are never both carried around it.  Both loops pass the same
   // barriers: two per tile and two at the end.
-  auto softmax = [&](int t, f32x16 (&s)[2], u32x4 (&pf)[4]) {
+  auto softmax = [&](auto vbf_c, int t, f32x16 (&s)[2], u32x4 (&pf)[4]) {
     prepare(t, s);
     float lsum = 0.f;
-    probs(s, pf, lsum);
+    probs(vbf_c, s, pf, lsum);
     l_run += lsum;
   };
   auto request = [&](int j) {
@@ -354,7 +357,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
   constexpr int kWaitV = 0xF70 | L::vLoads;
   constexpr int kWaitKV = 0xF70 | (L::kLoads + L::vLoads);
   static_assert(L::kLoads + L::vLoads < 16, "vmcnt immediate");
-  if (nkt > 0) {
+  // The loop, with P in IEEE halves or (vbf_c) in bfloat16.
+  auto run = [&](auto vbf_c) {
     issue_k(0);
     if (grp == 0) request(0);
     __builtin_amdgcn_s_waitcnt(0);
@@ -363,34 +367,48 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
     u32x4 pf[4];
     if (grp == 0) {
       for (int j = 0; j < nkt; ++j) {
-        if (j >= 1) pv(j - 1, pf);       // phase 2j: M(j)
+        if (j >= 1) pv(vbf_c, j - 1, pf);       // phase 2j: M(j)
         qk(j, s);
         __syncthreads();
         request(j + 1);                  // phase 2j+1: V(j), and this wave's share of R(j+1)
-        softmax(j, s, pf);
+        softmax(vbf_c, j, s, pf);
         // this wave's share of R(j) landed; R(j+1) may stay in flight
         if (j + 2 < nkt) __builtin_amdgcn_s_waitcnt(kWaitKV);
         else if (j + 1 < nkt) __builtin_amdgcn_s_waitcnt(kWaitV);
         else __builtin_amdgcn_s_waitcnt(kWaitNone);
         __syncthreads();
       }
-      pv(nkt - 1, pf);                   // phase 2 nkt: M(nkt)
+      pv(vbf_c, nkt - 1, pf);                   // phase 2 nkt: M(nkt)
       __syncthreads();
       __syncthreads();                   // phase 2 nkt + 1
     } else {
       for (int j = 0; j < nkt; ++j) {
         request(j);                      // phase 2j: V(j-1), and this wave's share of R(j)
-        if (j >= 1) softmax(j - 1, s, pf);
+        if (j >= 1) softmax(vbf_c, j - 1, s, pf);
         __syncthreads();
-        if (j >= 1) pv(j - 1, pf);       // phase 2j+1: M(j)
+        if (j >= 1) pv(vbf_c, j - 1, pf);       // phase 2j+1: M(j)
         qk(j, s);
         __builtin_amdgcn_s_waitcnt(0);   // this wave's share of R(j) landed
         __syncthreads();
       }
-      softmax(nkt - 1, s, pf);           // phase 2 nkt: V(nkt-1)
+      softmax(vbf_c, nkt - 1, s, pf);           // phase 2 nkt: V(nkt-1)
       __syncthreads();
-      pv(nkt - 1, pf);                   // phase 2 nkt + 1: M(nkt)
+      pv(vbf_c, nkt - 1, pf);                   // phase 2 nkt + 1: M(nkt)
       __syncthreads();
+    }
+  };
+  // bfloat16 V: P V in bfloat16 for the whole workgroup if any V^T tile it
+  // reads stayed bfloat16 (the pre-pass flags them); otherwise, the normal
+  // case, in IEEE halves.
+  if (nkt > 0) {
+    if constexpr (BF16 && !FP8) {
+      const int32_t* fl = a.ws_vflag + ((size_t)(sk0 / BN) + b) * a.Hkv + g;
+      int any = 0;
+      for (int t = lane; t < nkt; t += 64) any |= fl[(size_t)t * a.Hkv];
+      if (__any(any != 0)) run(std::true_type{});
+      else run(std::false_type{});
+    } else {
+      run(std::false_type{});
     }
   }
 
@@ -427,21 +445,24 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
 }
 
 // V pre-pass: the 64 keys of tile i of sequence b and key/value head g become
-// one V^T image [D][64] of IEEE halves at slot (seqstart_k[b] / 64 + b + i) *
-// Hkv + g of the workspace (the slots of consecutive sequences never overlap,
-// since a sequence of L keys has at most L / 64 + 1 tiles).  Keys past the
+// one V^T image [D][64] at slot (seqstart_k[b] / 64 + b + i) * Hkv + g of the
+// workspace (the slots of consecutive sequences never overlap, since a
+// sequence of L keys has at most L / 64 + 1 tiles).  Keys past the
 // sequence's end are zero.  Thread (kq, cv) transposes 4 keys x 8 features in
-// registers.
+// registers.  The image holds IEEE halves (fp16 V as is, fp8 V widened,
+// bfloat16 V re-encoded); a bfloat16 tile whose values the re-encoding would
+// not keep (v_needs_bf16) stays bfloat16, and the slot's flag in ws_vflag
+// says which (bfloat16 inputs only).
 template <int D, bool BF16, bool PAGED, bool FP8 = false>
 __global__ __launch_bounds__(kVtThreads) void vt_images_kernel(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int BN = kPfBN;
   const int g = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
   const int sk0 = a.seqstart_k[b], Lk = a.seqstart_k[b + 1] - sk0;
-  if (i * BN >= Lk) return;
+  if (i * BN >= Lk) return;  // uniform over the workgroup
   const int tid = threadIdx.x;
   const int kq = tid % (BN / 4), cv = tid / (BN / 4);
-  if (cv >= D / 8) return;
+  const bool active = cv < D / 8;  // D = 64: half the threads hold no part of the tile
   constexpr int ESZ = FP8 ? 1 : 2;  // bytes per v element
   const uint32_t rs_bytes = (uint32_t)a.Hkv * D * ESZ;
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v);
@@ -462,9 +483,20 @@ __global__ __launch_bounds__(kVtThreads) void vt_images_kernel(FwdArgs a) {
     vrs = buf_rsrc(vbase + ((size_t)sk0 * a.Hkv + g) * D * ESZ, (uint32_t)(Lk - 1) * rs_bytes + D * ESZ);
     row0 = (uint32_t)(i * BN);
   }
-  uint8_t* img = reinterpret_cast<uint8_t*>(a.ws_vt + ((size_t)((sk0 / BN) + b + i) * a.Hkv + g) * (D * BN));
-  if constexpr (FP8) write_tile_image_fp8(vrs, row0, rs_bytes, img, kq, cv);
-  else write_tile_image<D, BF16>(vrs, row0, rs_bytes, img, kq, cv);
+  const size_t slot = ((size_t)(sk0 / BN) + b + i) * a.Hkv + g;
+  uint8_t* img = reinterpret_cast<uint8_t*>(a.ws_vt + slot * (D * BN));
+  if constexpr (FP8) {
+    if (active) write_tile_image_fp8(vrs, row0, rs_bytes, img, kq, cv);
+  } else {
+    u32x4 r[4] = {};
+    if (active) load_tile_part(vrs, row0, rs_bytes, kq, cv, r);
+    if constexpr (BF16) {
+      const bool keep_bf16 = __syncthreads_or(active && v_needs_bf16(tile_part_absmax_bf16(r))) != 0;
+      if (!keep_bf16) tile_part_to_f16(r);
+      if (tid == 0) a.ws_vflag[slot] = keep_bf16 ? 1 : 0;
+    }
+    if (active) store_tile_image(r, img, kq, cv);
+  }
 #endif
 }
 

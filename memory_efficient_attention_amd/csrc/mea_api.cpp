@@ -89,12 +89,21 @@ size_t decode_ws_bytes(int32_t num_seqs, int32_t total_k, int32_t max_seqlen_k, 
   return (size_t)num_seqs * (size_t)decode_slots(max_seqlen_k, w) * (size_t)Hq * (size_t)(D + 1) * sizeof(float);
 }
 
-// Prefill: one half-precision V^T image of D x 64 keys per key/value head and
-// key tile; sequence b's tiles start at slot seqstart_k[b] / 64 + b, so
-// total_k / 64 + num_seqs slots per head cover every sequence.
+// Prefill: one 16-bit V^T image of D x 64 keys per key/value head and key
+// tile, then one int32 flag per image (1: the image stayed bfloat16);
+// sequence b's tiles start at slot seqstart_k[b] / 64 + b, so total_k / 64 +
+// num_seqs slots per head cover every sequence.  Each part is 256-byte
+// aligned.
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+size_t prefill_slots(int32_t num_seqs, int32_t total_k, int32_t Hkv) {
+  return ((size_t)total_k / mea::kPfBN + (size_t)num_seqs) * (size_t)Hkv;
+}
+
 size_t prefill_ws_bytes(int32_t num_seqs, int32_t total_k, int32_t Hkv, int32_t D) {
   if (total_k == 0) return 0;
-  return ((size_t)total_k / mea::kPfBN + (size_t)num_seqs) * (size_t)Hkv * (size_t)D * mea::kPfBN * 2;
+  const size_t slots = prefill_slots(num_seqs, total_k, Hkv);
+  return align256(slots * (size_t)D * mea::kPfBN * 2) + align256(slots * sizeof(int32_t));
 }
 
 // Paged K/V cache: block_table[b * max_blocks + i] is the page holding keys
@@ -243,6 +252,9 @@ mea_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, fl
     if ((long long)max_seqlen_k / mea::kPfBN + 1 > 65535)
       return fail(MEA_ERR_UNSUPPORTED, "max_seqlen_k=%d needs more than 65535 key tiles", max_seqlen_k);
     a.ws_vt = static_cast<uint16_t*>(workspace);
+    if (need > 0)
+      a.ws_vflag = reinterpret_cast<int32_t*>(
+          static_cast<uint8_t*>(workspace) + align256(prefill_slots(num_seqs, total_k, Hkv) * (size_t)D * mea::kPfBN * 2));
     a.heads_per_wg = gcd_int(a.group, mea::kPfGroupWaves);
     a.head_slices = a.group / a.heads_per_wg;
     const int bt = mea::kPfGroups * 32 * (mea::kPfGroupWaves / a.heads_per_wg);
@@ -261,7 +273,6 @@ mea_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, fl
 
 // Backward workspace: lse2 and Dsum [Hq, total_q] float32, each part
 // 256-byte aligned.
-size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct BwdWs {
   size_t lse2, dsum, total;

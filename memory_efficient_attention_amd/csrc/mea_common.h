@@ -32,6 +32,7 @@ struct FwdArgs {
   float* ws_o;               // decode: [num_seqs, max_chunks, Hq, D] float32 partials
   float* ws_lse;             // decode: [num_seqs, max_chunks, Hq] float32 (log2 units)
   uint16_t* ws_vt;           // prefill: transposed half-precision V tile images (see fwd_prefill.hip)
+  int32_t* ws_vflag;         // prefill, bfloat16: per V^T image, 1 if it was kept in bfloat16
   const int32_t* block_table;  // paged K/V: [num_seqs, max_blocks] page of each page_size-key block, or nullptr
   int32_t page_size;         // paged K/V: keys per page (a multiple of 64)
   int32_t max_blocks;        // paged K/V: row length of block_table
@@ -168,6 +169,31 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
   float lo = __builtin_bit_cast(float, w << 16);
   float hi = __builtin_bit_cast(float, w & 0xffff0000u);
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+}
+
+// A packed pair of IEEE halves re-encoded as a packed pair of bfloat16
+// values, round to nearest even.
+__device__ __forceinline__ uint32_t f16x2_to_bf16x2(uint32_t w) {
+  const f16x2 h = __builtin_bit_cast(f16x2, w);
+  return pack_out_x2<true>((float)h[0], (float)h[1]);
+}
+
+// Running maximum magnitude of the two bfloat16 values packed in w.
+__device__ __forceinline__ float bf16x2_absmax(float m, uint32_t w) {
+  const float lo = __builtin_bit_cast(float, w << 16);
+  const float hi = __builtin_bit_cast(float, w & 0xffff0000u);
+  return __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(lo), __builtin_fabsf(hi)));
+}
+
+// Whether a block of bfloat16 V values whose largest magnitude is m must stay
+// in bfloat16 for P V.  bf16x2_to_f16x2 is exact for every bfloat16 value
+// with 2^-14 <= |v| <= 65504 and errs by less than 2^-24 below that, i.e. by
+// less than 2^-10 of the block's largest magnitude whenever that is at least
+// 2^-14.  Blocks with a larger magnitude (which would saturate) or with only
+// smaller ones (which would lose their precision) keep bfloat16 and use
+// bfloat16 weights instead.  (A NaN converts to a NaN either way.)
+__device__ __forceinline__ bool v_needs_bf16(float m) {
+  return !(m <= 65504.f) || (m > 0.f && m < 0x1p-14f);
 }
 
 // Bytes 2 hi and 2 hi + 1 of w, two OCP e4m3 values, widened to a packed pair

@@ -123,23 +123,31 @@ __device__ __forceinline__ void store_tile_image(const u32x4 (&r)[4], uint8_t* i
 
 // Rows row0 + 4kq .. + 3 and columns 8cv .. 8cv + 7 of a 64-row tile of 16-bit
 // values, read through `rs` (row stride rs_bytes; rows past the resource's end
-// read zeros), into the [D][64] image.  TO_F16: the values are bfloat16 and
-// are re-encoded as IEEE halves.
-template <int D, bool TO_F16>
-__device__ __forceinline__ void write_tile_image(__amdgpu_buffer_rsrc_t rs, uint32_t row0, uint32_t rs_bytes,
-                                                 uint8_t* img, int kq, int cv) {
-  u32x4 r[4];
+// read zeros), as store_tile_image takes them.
+__device__ __forceinline__ void load_tile_part(__amdgpu_buffer_rsrc_t rs, uint32_t row0, uint32_t rs_bytes,
+                                               int kq, int cv, u32x4 (&r)[4]) {
 #pragma unroll
   for (int k = 0; k < 4; ++k)
     r[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                          rs, (row0 + 4 * kq + k) * rs_bytes + cv * 16u, 0, 0));
-  if constexpr (TO_F16) {
+}
+
+// Largest magnitude among the 32 bfloat16 values of a load_tile_part share.
+__device__ __forceinline__ float tile_part_absmax_bf16(const u32x4 (&r)[4]) {
+  float m = 0.f;
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
+  for (int k = 0; k < 4; ++k)
 #pragma unroll
-      for (int w = 0; w < 4; ++w) r[k][w] = bf16x2_to_f16x2(r[k][w]);
-  }
-  store_tile_image(r, img, kq, cv);
+    for (int w = 0; w < 4; ++w) m = bf16x2_absmax(m, r[k][w]);
+  return m;
+}
+
+// The share's bfloat16 values re-encoded as IEEE halves.
+__device__ __forceinline__ void tile_part_to_f16(u32x4 (&r)[4]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) r[k][w] = bf16x2_to_f16x2(r[k][w]);
 }
 
 // The same for a tile of OCP e4m3 (fp8) values, re-encoded as IEEE halves

@@ -14,8 +14,10 @@ passages of the pages it follows.  Every function here is pinned by
 routine) except the readings listed as "parity unpinned" in
 ``oracle.attention``'s module docstring.
 """
-from .attention import attention_backward, attention_forward, attention_forward_fp8, attention_rows
+from .attention import (attention_backward, attention_backward_scales, attention_forward,
+                        attention_forward_fp8, attention_rows)
 from .ffn import silu, swiglu_ffn, swiglu_ffn_rows
 
-__all__ = ["attention_forward", "attention_rows", "attention_backward", "attention_forward_fp8", "silu",
+__all__ = ["attention_forward", "attention_rows", "attention_backward", "attention_backward_scales",
+           "attention_forward_fp8", "silu",
            "swiglu_ffn", "swiglu_ffn_rows"]

@@ -53,7 +53,8 @@ from typing import List, Optional, Sequence, Tuple
 
 import torch
 
-__all__ = ["attention_forward", "attention_rows", "attention_backward", "attention_forward_fp8"]
+__all__ = ["attention_forward", "attention_rows", "attention_backward", "attention_backward_scales",
+           "attention_forward_fp8"]
 
 
 def _f64(x: torch.Tensor) -> torch.Tensor:
@@ -217,6 +218,67 @@ def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: 
             dq[sq[b]:sq[b + 1], h, :] = scale * (dS @ Kg)
             dk[sk[b]:sk[b + 1], g, :] += scale * (dS.transpose(0, 1) @ Qh)
     return dq, dk, dv
+
+
+def attention_backward_scales(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor,
+                              seqstart_q, seqstart_k, *, causal: bool = False,
+                              alibi_slopes: Optional[torch.Tensor] = None,
+                              scale: Optional[float] = None, floor: float = 0.0
+                              ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Error scales of the gradients: for every element of dq, dk and dv, the
+    sum of the absolute values of the terms ``attention_backward`` adds up for
+    it, for element-wise error bounds (not part of the method).
+
+    An implementation that rounds the softmax weights P and dS to a 16-bit
+    type with unit roundoff u, and forms rowsum(dO * out) from a rounded out,
+    errs on each term by at most u times that term's size, taking P and |dS|
+    no smaller than ``floor`` (the smallest normal number of the type: below
+    it a rounding errs by up to u * floor) on allowed (query, key) pairs.
+    With p = max(P, floor) and d = max(|dS|, floor) there, 0 on masked pairs,
+    and E_i = sum_d |dO[i, d] out[i, d]| (the size of the row term):
+      av_g += p^T |dO_h|
+      aq_h  = scale * (d |K_g| + (p * E) |K_g|)
+      ak_g += scale * (d^T |Q_h| + (p * E)^T |Q_h|)
+    Returns float64 (aq [Tq, Hq, D], ak [Tk, Hkv, D], av [Tk, Hkv, D]).
+    """
+    Q64, K64, V64, dO64 = _f64(q), _f64(k), _f64(v), _f64(dout)
+    Tq, Hq, D = Q64.shape
+    Tk, Hkv, _ = K64.shape
+    if scale is None:
+        scale = D ** -0.5
+    slopes = None if alibi_slopes is None else [float(s) for s in _f64(alibi_slopes)]
+    sq, sk = _starts(seqstart_q), _starts(seqstart_k)
+    per_group = Hq // Hkv
+    aq = torch.zeros((Tq, Hq, D), dtype=torch.float64)
+    ak = torch.zeros((Tk, Hkv, D), dtype=torch.float64)
+    av = torch.zeros((Tk, Hkv, D), dtype=torch.float64)
+    for b in range(len(sq) - 1):
+        L_q, L_k = sq[b + 1] - sq[b], sk[b + 1] - sk[b]
+        if L_q == 0 or L_k == 0:
+            continue
+        qpos = torch.arange(L_q, dtype=torch.float64) + (L_k - L_q)
+        kpos = torch.arange(L_k, dtype=torch.float64)
+        allowed = torch.ones((L_q, L_k), dtype=torch.bool)
+        if causal:
+            allowed = kpos[None, :] <= qpos[:, None]
+        for h in range(Hq):
+            g = h // per_group
+            Qh = Q64[sq[b]:sq[b + 1], h, :]
+            Kg = K64[sk[b]:sk[b + 1], g, :]
+            Vg = V64[sk[b]:sk[b + 1], g, :]
+            dOh = dO64[sq[b]:sq[b + 1], h, :]
+            P, _ = _softmax_block(Qh, Kg, qpos, causal, None if slopes is None else slopes[h],
+                                  float(scale))
+            dP = dOh @ Vg.transpose(0, 1)
+            dS = P * (dP - (P * dP).sum(dim=1, keepdim=True))
+            E = (dOh * (P @ Vg)).abs().sum(dim=1, keepdim=True)
+            live = allowed & (P.sum(dim=1, keepdim=True) > 0)       # rows with no key stay 0
+            p = torch.where(live, P.clamp_min(floor), 0.0)
+            d = torch.where(live, dS.abs().clamp_min(floor), 0.0)
+            av[sk[b]:sk[b + 1], g, :] += p.transpose(0, 1) @ dOh.abs()
+            aq[sq[b]:sq[b + 1], h, :] = scale * ((d + p * E) @ Kg.abs())
+            ak[sk[b]:sk[b + 1], g, :] += scale * ((d + p * E).transpose(0, 1) @ Qh.abs())
+    return aq, ak, av
 
 
 def attention_forward_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, q_scale: float,

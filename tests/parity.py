@@ -82,11 +82,19 @@ def compare_rows(out_gpu: torch.Tensor, lse_gpu: torch.Tensor, inp: Inputs,
 
 # Backward tolerance.  Q K^T and dO V^T run in the input precision with
 # float32 accumulation; P and dS are rounded to the input precision (unit
-# roundoff u: 2^-11 for fp16, 2^-8 for bf16) before the second products, and
-# dq, dk, dv are rounded once more on output, so each element carries a few u
-# of relative error on its largest terms.  The bound is 4 u of the largest
-# reference magnitude of that gradient, plus 1e-6 absolute for all-zero ones.
+# roundoff u: 2^-11 for fp16, 2^-8 for bf16) before the second products,
+# rowsum(dO * out) is formed from the rounded forward output, and dq, dk, dv
+# are rounded once more on output.  Two bounds must both hold:
+#   per tensor:  |g - g_ref| <= 4u max|g_ref| + 1e-6
+#   per element: |g - g_ref| <= 4u A + 2u |g_ref| + 1e-6
+# where A is the oracle's error scale of that element (the sum of the sizes
+# of its terms, P and |dS| taken no smaller than the type's smallest normal
+# number, below which a rounding errs by up to u times that number).  The
+# element-wise bound catches a row left wrong or zero whose values sit far
+# below the tensor's largest.
 GRAD_TOL_REL = {"fp16": 4 * 2.0 ** -11, "bf16": 4 * 2.0 ** -8}
+UNIT_ROUNDOFF = {"fp16": 2.0 ** -11, "bf16": 2.0 ** -8}
+SMALLEST_NORMAL = {"fp16": 2.0 ** -14, "bf16": 2.0 ** -126}
 
 
 def run_gpu_backward(inp: Inputs, dout: torch.Tensor, dev: Optional[dict] = None):
@@ -108,21 +116,39 @@ def run_gpu_backward(inp: Inputs, dout: torch.Tensor, dev: Optional[dict] = None
     return dq.cpu(), dk.cpu(), dv.cpu()
 
 
-def oracle_backward(inp: Inputs, dout: torch.Tensor):
-    return oracle.attention_backward(inp.q, inp.k, inp.v, dout, inp.seqstart_q, inp.seqstart_k,
-                                     causal=inp.causal, alibi_slopes=inp.alibi_slopes, scale=inp.scale)
+class GradRef(tuple):
+    """The oracle's (dq, dk, dv), with their element-wise error scales in
+    ``.scales``."""
+    scales = None
+
+
+def oracle_backward(inp: Inputs, dout: torch.Tensor) -> GradRef:
+    kw = dict(causal=inp.causal, alibi_slopes=inp.alibi_slopes, scale=inp.scale)
+    args = (inp.q, inp.k, inp.v, dout, inp.seqstart_q, inp.seqstart_k)
+    ref = GradRef(oracle.attention_backward(*args, **kw))
+    ref.scales = oracle.attention_backward_scales(*args, **kw, floor=SMALLEST_NORMAL[inp.dtype])
+    return ref
 
 
 def compare_grads(got, ref, dtype: str, what: str = "") -> dict:
-    """Assert parity of (dq, dk, dv) with the oracle's; returns error figures."""
+    """Assert parity of (dq, dk, dv) with the oracle's; returns error figures
+    (max error, max |ref|, and the worst error over its element-wise bound)."""
     res = {}
-    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+    u = UNIT_ROUNDOFF[dtype]
+    scales = getattr(ref, "scales", None)
+    assert scales is not None, f"{what}: the oracle reference carries no error scales"
+    for name, g, r, a in zip(("dq", "dk", "dv"), got, ref, scales):
         assert g.shape == r.shape, (what, name, g.shape, r.shape)
         gd = g.double()
         assert not torch.isnan(gd).any(), f"{what}: NaN in {name} (unwritten or invalid rows)"
         scale = r.abs().max().item() if r.numel() else 0.0
         tol = GRAD_TOL_REL[dtype] * scale + 1e-6
-        err = (gd - r).abs().max().item() if r.numel() else 0.0
-        res[name] = (err, scale)
+        e = (gd - r).abs()
+        err = e.max().item() if r.numel() else 0.0
+        elem_bound = 4 * u * a + 2 * u * r.abs() + 1e-6
+        worst = (e / elem_bound).max().item() if r.numel() else 0.0
+        res[name] = (err, scale, round(worst, 3))
         assert err <= tol, f"{what}: {name} error {err:.3e} > {tol:.3e} (max |ref| {scale:.3e})"
+        assert worst <= 1.0, (f"{what}: {name} exceeds its element-wise bound by {worst:.2f}x "
+                              f"(max error {err:.3e})")
     return res

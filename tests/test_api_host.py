@@ -72,3 +72,41 @@ def test_to_paged_round_trip():
     spare = [p for p in range(pk.k_cache.shape[0]) if p not in used]
     assert len(spare) == 2 and all(torch.isnan(pk.v_cache[p].float()).all() for p in spare)
     assert not _m.isnan(float(pk.block_table.sum()))
+
+
+def test_output_buffer_checks():
+    """Caller-supplied outputs are validated before any pointer reaches the
+    kernels (they store full-size rows through it)."""
+    from memory_efficient_attention_amd.api import _check_out
+    dev = torch.device("cpu")
+    good = torch.empty(5, 4, 64, dtype=torch.bfloat16)
+    _check_out(good, "out", (5, 4, 64), torch.bfloat16, dev)
+    _check_out(None, "out", (5, 4, 64), torch.bfloat16, dev)
+    with pytest.raises(ValueError, match="shape"):
+        _check_out(torch.empty(4, 4, 64, dtype=torch.bfloat16), "out", (5, 4, 64), torch.bfloat16, dev)
+    with pytest.raises(TypeError, match="must be torch.bfloat16"):
+        _check_out(torch.empty(5, 4, 64, dtype=torch.float32), "out", (5, 4, 64), torch.bfloat16, dev)
+    with pytest.raises(ValueError, match="contiguous"):
+        _check_out(torch.empty(4, 5, 64, dtype=torch.bfloat16).transpose(0, 1), "out", (5, 4, 64),
+                   torch.bfloat16, dev)
+    with pytest.raises(ValueError, match="must be on"):
+        _check_out(torch.empty(5, 4, 64, dtype=torch.bfloat16, device="meta"), "out", (5, 4, 64),
+                   torch.bfloat16, dev)
+    with pytest.raises(ValueError, match="lse must have shape"):
+        _check_out(torch.empty(5, 4, dtype=torch.float32), "lse", (4, 5), torch.float32, dev)
+
+
+def test_workspace_checks():
+    from memory_efficient_attention_amd.api import _workspace
+    dev = torch.device("cpu")
+    assert _workspace(None, 0, dev) is None
+    ws = torch.empty(4096, dtype=torch.uint8)
+    assert _workspace(ws, 4096, dev) is ws
+    assert _workspace(ws, 1000, dev) is ws
+    bigger = _workspace(ws, 4097, dev)                   # too small: a new one
+    assert bigger is not ws and bigger.numel() == 4097
+    assert _workspace(torch.empty(1024, dtype=torch.float32), 4096, dev).numel() == 1024  # bytes, not elements
+    with pytest.raises(ValueError, match="contiguous"):
+        _workspace(torch.empty(64, 128, dtype=torch.uint8).t(), 16, dev)
+    with pytest.raises(ValueError, match="must be on"):
+        _workspace(torch.empty(64, dtype=torch.uint8, device="meta"), 16, dev)

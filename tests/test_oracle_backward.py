@@ -233,3 +233,123 @@ def test_unmutated_backward_passes_pins():
 def test_planted_backward_mistake_fails_pins(mi):
     old, new = MUTATIONS[mi]
     assert not _pins_pass(_mutant(old, new))
+
+
+# ----------------------------------------------------------------------------- error scales
+# ``attention_backward_scales`` sums the absolute values of the terms of each
+# gradient element (the element-wise GPU bounds are built on it).  Its pins:
+# a scalar brute force that lists every term of every element, checks that the
+# terms add up to the (finite-difference-pinned) gradient, and sums their
+# absolute values; and |gradient| <= its scale.
+
+def _brute_terms(inp, dout, floor):
+    """Per element: (sum of the terms, sum of their sizes), by scalar loops."""
+    from oracle import attention_forward
+    out, _ = attention_forward(inp.q, inp.k, inp.v, inp.seqstart_q, inp.seqstart_k, causal=inp.causal,
+                               alibi_slopes=inp.alibi_slopes, scale=inp.scale)
+    Q, K, V, dO, O = (t.double().tolist() for t in (inp.q, inp.k, inp.v, dout, out))
+    Hq, Hkv, D, sc = inp.Hq, inp.Hkv, inp.D, inp.scale
+    sl = None if inp.alibi_slopes is None else inp.alibi_slopes.double().tolist()
+    sq, sk = inp.seqstart_q.tolist(), inp.seqstart_k.tolist()
+    tq = {}
+    tk = {}
+    tv = {}
+    for b in range(len(sq) - 1):
+        Lq, Lk = sq[b + 1] - sq[b], sk[b + 1] - sk[b]
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            for r in range(Lq):
+                i = sq[b] + r
+                pos = r + Lk - Lq
+                keys = [j for j in range(Lk) if not (inp.causal and j > pos)]
+                if not keys:
+                    continue
+                s = {}
+                for j in keys:
+                    x = sc * math.fsum(Q[i][h][d] * K[sk[b] + j][g][d] for d in range(D))
+                    if sl is not None:
+                        x -= sl[h] * abs(pos - j)
+                    s[j] = x
+                m = max(s.values())
+                z = math.fsum(math.exp(s[j] - m) for j in keys)
+                P = {j: math.exp(s[j] - m) / z for j in keys}
+                dP = {j: math.fsum(dO[i][h][d] * V[sk[b] + j][g][d] for d in range(D)) for j in keys}
+                rs = math.fsum(P[j] * dP[j] for j in keys)
+                dS = {j: P[j] * (dP[j] - rs) for j in keys}
+                E = math.fsum(abs(dO[i][h][d] * O[i][h][d]) for d in range(D))
+                for j in keys:
+                    kj = sk[b] + j
+                    p, dd = max(P[j], floor), max(abs(dS[j]), floor)
+                    for d in range(D):
+                        tq.setdefault((i, h, d), []).append((sc * dS[j] * K[kj][g][d],
+                                                             sc * (dd + p * E) * abs(K[kj][g][d])))
+                        tk.setdefault((kj, g, d), []).append((sc * dS[j] * Q[i][h][d],
+                                                              sc * (dd + p * E) * abs(Q[i][h][d])))
+                        tv.setdefault((kj, g, d), []).append((P[j] * dO[i][h][d], p * abs(dO[i][h][d])))
+    return tq, tk, tv
+
+
+def _scales_ok(scales_fn, ci, seed, floor):
+    inp, dout = _case(ci, seed)
+    args = (inp.q, inp.k, inp.v, dout, inp.seqstart_q, inp.seqstart_k)
+    kw = dict(causal=inp.causal, alibi_slopes=inp.alibi_slopes, scale=inp.scale)
+    grads = attention_backward(*args, **kw)
+    scales = scales_fn(*args, **kw, floor=floor)
+    for grad, scl, terms in zip(grads, scales, _brute_terms(inp, dout, floor)):
+        want_g = torch.zeros_like(grad)
+        want_s = torch.zeros_like(scl)
+        for idx, ts in terms.items():
+            want_g[idx] = math.fsum(t for t, _ in ts)
+            want_s[idx] = math.fsum(a for _, a in ts)
+        if (want_g - grad).abs().max().item() > 1e-12:      # the terms are those of the gradient
+            return False
+        if not bool(((scl - want_s).abs() <= 1e-12 * want_s.abs().clamp_min(1.0)).all()):
+            return False
+        if floor == 0.0 and not bool((grad.abs() <= scl + 1e-12).all()):
+            return False
+    return True
+
+
+SCALE_CASES = [0, 2, 4, 5, 6, 7]   # plain, MQA + empty sequence, decode rows, rows with no key, L_q < L_k, empty K
+
+
+@pytest.mark.parametrize("ci", SCALE_CASES)
+@pytest.mark.parametrize("floor", [0.0, 2.0 ** -6])
+def test_backward_scales_brute_force(ci, floor):
+    assert _scales_ok(oracle.attention_backward_scales, ci, 700 + ci, floor)
+
+
+SCALE_MUTATIONS = [
+    ("d = torch.where(live, dS.abs().clamp_min(floor), 0.0)", "d = torch.where(live, dS.clamp_min(floor), 0.0)"),
+    ("aq[sq[b]:sq[b + 1], h, :] = scale * ((d + p * E) @ Kg.abs())",
+     "aq[sq[b]:sq[b + 1], h, :] = scale * (d @ Kg.abs())"),                  # row term dropped
+    ("p = torch.where(live, P.clamp_min(floor), 0.0)", "p = P.clamp_min(floor)"),   # floor on masked pairs
+    ("av[sk[b]:sk[b + 1], g, :] += p.transpose(0, 1) @ dOh.abs()",
+     "av[sk[b]:sk[b + 1], g, :] += 100 * (p.transpose(0, 1) @ dOh.abs())"),  # inflated scale
+    ("ak[sk[b]:sk[b + 1], g, :] += scale * ((d + p * E).transpose(0, 1) @ Qh.abs())",
+     "ak[sk[b]:sk[b + 1], g, :] = scale * ((d + p * E).transpose(0, 1) @ Qh.abs())"),  # group sum dropped
+]
+
+
+def _scales_mutant(old, new):
+    src = open(ORACLE_SRC).read()
+    assert src.count(old) == 1, old
+    mod = types.ModuleType("oracle_scales_mutant")
+    exec(compile(src.replace(old, new), "oracle_scales_mutant", "exec"), mod.__dict__)
+    return mod.attention_backward_scales
+
+
+def _scale_pins_pass(fn):
+    try:
+        return all(_scales_ok(fn, ci, 800 + ci, fl) for ci in SCALE_CASES for fl in (0.0, 2.0 ** -6))
+    except Exception:
+        return False
+
+
+def test_unmutated_scales_pass_pins():
+    assert _scale_pins_pass(oracle.attention_backward_scales)
+
+
+@pytest.mark.parametrize("mi", range(len(SCALE_MUTATIONS)))
+def test_planted_scale_mistake_fails_pins(mi):
+    assert not _scale_pins_pass(_scales_mutant(*SCALE_MUTATIONS[mi]))
