@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define MEA_ABI_VERSION 8
+#define MEA_ABI_VERSION 9
 
 #if defined(__GNUC__)
 #define MEA_EXPORT __attribute__((visibility("default")))
@@ -143,6 +143,33 @@ MEA_EXPORT mea_status_t mea_fwd(const void* q, const void* k, const void* v, voi
                      int32_t Hkv, int32_t D, mea_dtype_t dtype, int32_t causal,
                      const float* alibi_slopes, float scale, void* workspace,
                      size_t workspace_bytes, void* stream);
+
+/*
+ * mea_fwd_noalloc -- mea_fwd for callers that cannot allocate memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments, computation and errors, without the
+ * workspace.  The scratch it needs (the V^T tile images of a prefill call,
+ * the float32 partials of a decode call: mea_fwd_workspace_size with the
+ * same sizes and chunk_keys = 0) lives in one fixed device array of
+ * MEA_NOALLOC_SCRATCH_BYTES per GPU, part of the library's device code:
+ * every GPU the library runs on holds it until the process ends.  The call
+ * allocates nothing and calls no hipMalloc or hipFree.
+ *   stream   must belong to the current device (MEA_ERR_INVALID otherwise).
+ * Returns MEA_ERR_UNSUPPORTED when the call needs more than
+ * MEA_NOALLOC_SCRATCH_BYTES of scratch (mea_fwd with a caller workspace has
+ * no such limit), and everything mea_fwd returns.
+ * Every call on one GPU uses that GPU's one array: calls that may overlap on
+ * one GPU (different streams, different host threads) race and must be
+ * ordered by the caller.  The array keeps the last call's contents; no call
+ * depends on them.
+ */
+#define MEA_NOALLOC_SCRATCH_BYTES (32u << 20)
+MEA_EXPORT mea_status_t mea_fwd_noalloc(const void* q, const void* k, const void* v, void* out, float* lse,
+                                        const int32_t* seqstart_q, const int32_t* seqstart_k, int32_t num_seqs,
+                                        int32_t total_q, int32_t total_k, int32_t max_seqlen_q,
+                                        int32_t max_seqlen_k, int32_t Hq, int32_t Hkv, int32_t D,
+                                        mea_dtype_t dtype, int32_t causal, const float* alibi_slopes, float scale,
+                                        void* stream);
 
 /*
  * mea_fwd_splitkv -- mea_fwd for the decode case (max_seqlen_q must be 1)

@@ -8,8 +8,17 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdint>
+#include <mutex>
 
 #include "mea_launch.h"
+
+// Scratch of mea_fwd_noalloc: one fixed array per device, in the library's
+// device code (it exists on every GPU the library runs on, for the life of the
+// process).  Host code never passes `scratch` itself to a kernel: in host
+// code that name is a stand-in, not a device address.  The device address is
+// taken once per device with hipGetSymbolAddress, that device current, and
+// kept in g_scratch_ptr (noalloc_scratch below).
+static __device__ __align__(256) uint8_t scratch[MEA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -271,6 +280,36 @@ mea_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, fl
   return MEA_OK;
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's device address on the device of `stream`, which must be
+// the current device.
+mea_status_t noalloc_scratch(void* stream, void** out) {
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return fail(MEA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  hipDevice_t sdev = cur;
+  if (stream != nullptr) {
+    e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev);
+    if (e != hipSuccess) return fail(MEA_ERR_HIP, "hipStreamGetDevice failed: %s", hipGetErrorString(e));
+  }
+  if (sdev != cur)
+    return fail(MEA_ERR_INVALID, "the stream belongs to device %d but device %d is current", (int)sdev, cur);
+  if (cur < 0 || cur >= kMaxDevices) return fail(MEA_ERR_UNSUPPORTED, "device %d: at most %d devices", cur, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[cur] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(MEA_ERR_HIP, "hipGetSymbolAddress of the scratch array failed: %s", hipGetErrorString(e));
+    g_scratch_ptr[cur] = p;
+  }
+  *out = g_scratch_ptr[cur];
+  return MEA_OK;
+}
+
 // Backward workspace: lse2 and Dsum [Hq, total_q] float32, each part
 // 256-byte aligned.
 
@@ -396,6 +435,26 @@ mea_status_t mea_fwd(const void* q, const void* k, const void* v, void* out, flo
   return fwd_impl(q, k, v, out, lse, seqstart_q, seqstart_k, num_seqs, total_q, total_k, max_seqlen_q,
                   max_seqlen_k, Hq, Hkv, D, dtype, causal, alibi_slopes, scale, workspace,
                   workspace_bytes, stream, 0, false);
+}
+
+mea_status_t mea_fwd_noalloc(const void* q, const void* k, const void* v, void* out, float* lse,
+                             const int32_t* seqstart_q, const int32_t* seqstart_k, int32_t num_seqs,
+                             int32_t total_q, int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                             int32_t Hq, int32_t Hkv, int32_t D, mea_dtype_t dtype, int32_t causal,
+                             const float* alibi_slopes, float scale, void* stream) {
+  g_last_error[0] = '\0';
+  const size_t need = fwd_ws_size(num_seqs, total_k, max_seqlen_q, max_seqlen_k, Hq, Hkv, D, 0, false);
+  if (need > (size_t)MEA_NOALLOC_SCRATCH_BYTES)
+    return fail(MEA_ERR_UNSUPPORTED, "this call needs %zu bytes of scratch, more than the %zu bytes mea_fwd_noalloc "
+                "holds per device (use mea_fwd with a workspace)", need, (size_t)MEA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (need > 0) {
+    const mea_status_t st = noalloc_scratch(stream, &ws);
+    if (st != MEA_OK) return st;
+  }
+  return fwd_impl(q, k, v, out, lse, seqstart_q, seqstart_k, num_seqs, total_q, total_k, max_seqlen_q,
+                  max_seqlen_k, Hq, Hkv, D, dtype, causal, alibi_slopes, scale, ws,
+                  need > 0 ? (size_t)MEA_NOALLOC_SCRATCH_BYTES : 0, stream, 0, false);
 }
 
 mea_status_t mea_fwd_splitkv(const void* q, const void* k, const void* v, void* out, float* lse,

@@ -48,7 +48,7 @@ def test_every_kernel_stub_is_defined():
 
 
 def test_version_and_strings():
-    assert _native.mea_abi_version() == 8
+    assert _native.mea_abi_version() == 9
     for st in range(4):
         assert _native.mea_status_string(st).startswith("MEA_")
     assert "unknown" in _native.mea_status_string(99)
@@ -349,3 +349,20 @@ def test_ffn_rejected_before_launch(kw, status, needle):
 
 def test_ffn_empty_is_a_noop():
     assert call_ffn(tokens=0) == MEA_OK
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch():
+    """mea_fwd_noalloc checks the scratch a call needs against its fixed array
+    before touching any device."""
+    big = dict(num_seqs=64, total_q=137663, total_k=137663, max_seqlen_q=4085, max_seqlen_k=4085, Hq=32, Hkv=8,
+               D=128)
+    need = _native.mea_fwd_workspace_size(64, 137663, 4085, 4085, 32, 8, 128, 0)
+    assert need > (32 << 20)
+    st = _native.mea_fwd_noalloc(P, P, P, P, P, P, P, big["num_seqs"], big["total_q"], big["total_k"],
+                                 big["max_seqlen_q"], big["max_seqlen_k"], big["Hq"], big["Hkv"], big["D"],
+                                 MEA_BF16, 1, None, 0.088, None)
+    assert st == MEA_ERR_UNSUPPORTED
+    assert "scratch" in _native.mea_last_error() and str(need) in _native.mea_last_error()
+    # malformed arguments are rejected by the usual validation, still before any device call
+    st = _native.mea_fwd_noalloc(P, P, P, P, P, P, P, 2, 10, 10, 5, 5, 6, 4, 64, MEA_F16, 0, None, 0.125, None)
+    assert st == MEA_ERR_INVALID
