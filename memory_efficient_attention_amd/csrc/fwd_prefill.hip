@@ -71,7 +71,18 @@ struct PfLayout {
 // FP8: q, k and v hold OCP e4m3 values (one byte each) and BF16 names the
 // output dtype; Q K^T runs on the fp8 matrix cores, V enters P V as halves
 // (the pre-pass widens it exactly), and the output is scaled by out_scale.
-template <int D, bool BF16, bool CAUSAL, bool ALIBI, bool PAGED, bool FP8 = false>
+//
+// VBF: bfloat16 V outside the range where IEEE halves are exact.  The
+// pre-pass keeps such V^T tiles in bfloat16 and flags them; the normal
+// launch (VBF false) runs every work item as usual, and its result for an
+// item that reads a flagged tile is wrong.  A second launch with VBF true,
+// one workgroup per (sequence, key/value head), computes exactly those items
+// again with P V in bfloat16 (V and weights), overwriting their rows: all its
+// threads read the sequence's flags at once, so a sequence with none (the
+// normal case) costs that one read; otherwise the workgroup runs the items
+// of its sequence and head whose key tiles reach the first flagged one, in
+// turn.
+template <int D, bool BF16, bool CAUSAL, bool ALIBI, bool PAGED, bool FP8 = false, bool VBF = false>
 __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the body uses buffer-resource types that exist only for the GPU target
   constexpr int ESZ = FP8 ? 1 : 2;        // bytes per q/k element
@@ -83,9 +94,45 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
   constexpr int kSmemBytes = kBufs * L::bufBytes > kStageBytes ? kBufs * L::bufBytes : kStageBytes;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmemBytes];
 
-  // ---- work item: XCD-aware remap of the linear workgroup index
+  // VBF: the sequence vb and key/value head vg of this workgroup, the first
+  // flagged key tile vfirst of them, and the number of candidate items
+  int vb = 0, vg = 0, vfirst = 0, vcand = 0;
+  if constexpr (VBF) {
+    __shared__ int first_flagged;
+    vb = (int)blockIdx.x / a.Hkv;
+    vg = (int)blockIdx.x % a.Hkv;
+    const int sk = a.seqstart_k[vb], lk = a.seqstart_k[vb + 1] - sk;
+    const int lq = a.seqstart_q[vb + 1] - a.seqstart_q[vb];
+    const int ntk = (lk + BN - 1) / BN;
+    if (threadIdx.x == 0) first_flagged = ntk;
+    __syncthreads();
+    const int32_t* fl = a.ws_vflag + ((size_t)(sk / BN) + vb) * a.Hkv + vg;
+    for (int t = (int)threadIdx.x; t < ntk; t += kThreads)
+      if (fl[(size_t)t * a.Hkv] != 0) atomicMin(&first_flagged, t);
+    __syncthreads();
+    vfirst = first_flagged;
+    if (vfirst >= ntk || lq == 0) return;  // uniform over the workgroup
+    const int bt = kPfGroups * 32 * (kPfGroupWaves / a.heads_per_wg);
+    vcand = a.head_slices * ((lq + bt - 1) / bt);
+  }
+  for (int vi = 0;; ++vi) {  // VBF: candidate vi; otherwise one pass
+  // ---- work item: XCD-aware remap of the linear workgroup index (VBF:
+  // candidate vi of (vb, vg), or -1 when it reads no flagged tile)
   const int per_xcd = (int)gridDim.x >> 3;
-  const int w = ((int)blockIdx.x & 7) * per_xcd + ((int)blockIdx.x >> 3);
+  int w = ((int)blockIdx.x & 7) * per_xcd + ((int)blockIdx.x >> 3);
+  if constexpr (VBF) {
+    if (vi >= vcand) return;
+    const int lq = a.seqstart_q[vb + 1] - a.seqstart_q[vb];
+    const int lk = a.seqstart_k[vb + 1] - a.seqstart_k[vb];
+    const int bt = kPfGroups * 32 * (kPfGroupWaves / a.heads_per_wg);
+    const int nt = (lq + bt - 1) / bt;
+    const int t_r = vi % nt, h_s = vi / nt;
+    const int first_tok = (nt - 1 - t_r) * bt;
+    const int end = CAUSAL ? min(lk, min(first_tok + bt, lq) + lk - lq) : lk;
+    const int tiles = end > 0 ? (end + BN - 1) / BN : 0;
+    w = tiles > vfirst ? ((vg * a.head_slices + h_s) * a.num_seqs + vb) * a.pf_max_tiles + t_r : -1;
+    if (w < 0) continue;
+  }
   if (w >= a.pf_items) return;
   const int t_rev = w % a.pf_max_tiles;
   const int rest = w / a.pf_max_tiles;
@@ -288,10 +335,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
     }
   };
 
-  // Probabilities of the prepared scores, packed as the P operand: IEEE
-  // halves, or bfloat16 where the V^T tiles stayed bfloat16 (vbf_c).
-  auto probs = [&](auto vbf_c, f32x16 (&s)[2], u32x4 (&pf)[4], float& lsum) {
-    constexpr bool VBF = decltype(vbf_c)::value;
+  // Probabilities of the prepared scores, packed as the P operand.
+  auto probs = [&](f32x16 (&s)[2], u32x4 (&pf)[4], float& lsum) {
     const float m_use = (m_run == kNegInf) ? 0.f : m_run;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -311,8 +356,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
   };
 
   // O^T += V^T P^T for tile t: V^T fragment of 16-key chunk ch, feature block d
-  auto pv = [&](auto vbf_c, int t, const u32x4 (&pf)[4]) {
-    constexpr bool VBF = decltype(vbf_c)::value;
+  auto pv = [&](int t, const u32x4 (&pf)[4]) {
     const uint8_t* Vt = vbuf(t);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -342,10 +386,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
   // own loop, so that within a loop the phase kinds are fixed and the scores
   // and P are never both carried around it.  Both loops pass the same
   // barriers: two per tile and two at the end.
-  auto softmax = [&](auto vbf_c, int t, f32x16 (&s)[2], u32x4 (&pf)[4]) {
+  auto softmax = [&](int t, f32x16 (&s)[2], u32x4 (&pf)[4]) {
     prepare(t, s);
     float lsum = 0.f;
-    probs(vbf_c, s, pf, lsum);
+    probs(s, pf, lsum);
     l_run += lsum;
   };
   auto request = [&](int j) {
@@ -357,8 +401,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
   constexpr int kWaitV = 0xF70 | L::vLoads;
   constexpr int kWaitKV = 0xF70 | (L::kLoads + L::vLoads);
   static_assert(L::kLoads + L::vLoads < 16, "vmcnt immediate");
-  // The loop, with P in IEEE halves or (vbf_c) in bfloat16.
-  auto run = [&](auto vbf_c) {
+  if (nkt > 0) {
     issue_k(0);
     if (grp == 0) request(0);
     __builtin_amdgcn_s_waitcnt(0);
@@ -367,48 +410,34 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
     u32x4 pf[4];
     if (grp == 0) {
       for (int j = 0; j < nkt; ++j) {
-        if (j >= 1) pv(vbf_c, j - 1, pf);       // phase 2j: M(j)
+        if (j >= 1) pv(j - 1, pf);       // phase 2j: M(j)
         qk(j, s);
         __syncthreads();
         request(j + 1);                  // phase 2j+1: V(j), and this wave's share of R(j+1)
-        softmax(vbf_c, j, s, pf);
+        softmax(j, s, pf);
         // this wave's share of R(j) landed; R(j+1) may stay in flight
         if (j + 2 < nkt) __builtin_amdgcn_s_waitcnt(kWaitKV);
         else if (j + 1 < nkt) __builtin_amdgcn_s_waitcnt(kWaitV);
         else __builtin_amdgcn_s_waitcnt(kWaitNone);
         __syncthreads();
       }
-      pv(vbf_c, nkt - 1, pf);                   // phase 2 nkt: M(nkt)
+      pv(nkt - 1, pf);                   // phase 2 nkt: M(nkt)
       __syncthreads();
       __syncthreads();                   // phase 2 nkt + 1
     } else {
       for (int j = 0; j < nkt; ++j) {
         request(j);                      // phase 2j: V(j-1), and this wave's share of R(j)
-        if (j >= 1) softmax(vbf_c, j - 1, s, pf);
+        if (j >= 1) softmax(j - 1, s, pf);
         __syncthreads();
-        if (j >= 1) pv(vbf_c, j - 1, pf);       // phase 2j+1: M(j)
+        if (j >= 1) pv(j - 1, pf);       // phase 2j+1: M(j)
         qk(j, s);
         __builtin_amdgcn_s_waitcnt(0);   // this wave's share of R(j) landed
         __syncthreads();
       }
-      softmax(vbf_c, nkt - 1, s, pf);           // phase 2 nkt: V(nkt-1)
+      softmax(nkt - 1, s, pf);           // phase 2 nkt: V(nkt-1)
       __syncthreads();
-      pv(vbf_c, nkt - 1, pf);                   // phase 2 nkt + 1: M(nkt)
+      pv(nkt - 1, pf);                   // phase 2 nkt + 1: M(nkt)
       __syncthreads();
-    }
-  };
-  // bfloat16 V: P V in bfloat16 for the whole workgroup if any V^T tile it
-  // reads stayed bfloat16 (the pre-pass flags them); otherwise, the normal
-  // case, in IEEE halves.
-  if (nkt > 0) {
-    if constexpr (BF16 && !FP8) {
-      const int32_t* fl = a.ws_vflag + ((size_t)(sk0 / BN) + b) * a.Hkv + g;
-      int any = 0;
-      for (int t = lane; t < nkt; t += 64) any |= fl[(size_t)t * a.Hkv];
-      if (__any(any != 0)) run(std::true_type{});
-      else run(std::false_type{});
-    } else {
-      run(std::false_type{});
     }
   }
 
@@ -440,6 +469,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
       const u32x4 val = *(const u32x4*)(ot + row * (D + 8) + ch * 8);
       *(u32x4*)(a.out + ((size_t)(sq0 + tok0 + row) * a.Hq + head) * D + ch * 8) = val;
     }
+  }
+  if constexpr (!VBF) break;
+  __syncthreads();  // VBF: the next item reuses the LDS
   }
 #endif
 }
@@ -511,7 +543,22 @@ static hipError_t launch_prefill_d(const FwdArgs& a, bool causal, bool alibi, di
     if (alibi) hipLaunchKernelGGL((fwd_prefill_kernel<D, BF16, false, true, PAGED, FP8>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((fwd_prefill_kernel<D, BF16, false, false, PAGED, FP8>), grid, block, 0, stream, a);
   }
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if constexpr (BF16 && !FP8) {
+    // items that read a V^T tile kept in bfloat16, again (one workgroup per
+    // sequence and key/value head; almost all of them exit at once)
+    const dim3 fgrid((unsigned)a.num_seqs * (unsigned)a.Hkv);
+    if (causal) {
+      if (alibi) hipLaunchKernelGGL((fwd_prefill_kernel<D, true, true, true, PAGED, false, true>), fgrid, block, 0, stream, a);
+      else hipLaunchKernelGGL((fwd_prefill_kernel<D, true, true, false, PAGED, false, true>), fgrid, block, 0, stream, a);
+    } else {
+      if (alibi) hipLaunchKernelGGL((fwd_prefill_kernel<D, true, false, true, PAGED, false, true>), fgrid, block, 0, stream, a);
+      else hipLaunchKernelGGL((fwd_prefill_kernel<D, true, false, false, PAGED, false, true>), fgrid, block, 0, stream, a);
+    }
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 template <int D, bool BF16, bool PAGED, bool FP8 = false>
