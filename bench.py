@@ -25,9 +25,18 @@ seeded dO) at 2.5x the forward's unmasked FLOPs (five products against two),
 ``prefill_fp8`` the prefill workload with q, k, v quantised to OCP e4m3
 (mea_fwd_fp8, per-tensor scales, bf16 output), ``decode_fp8`` and
 ``decode_paged_fp8`` the decode workload quantised the same way (packed, and
-in the shuffled 64-key pages through mea_fwd_paged_fp8), and ``swiglu_ffn`` the SwiGLU
+in the shuffled 64-key pages through mea_fwd_paged_fp8), ``swiglu_ffn`` the SwiGLU
 feed-forward layer of the same block on the same 137,663 tokens (d_model
-4096, d_ff 11008, bf16; 6 * T * d_model * d_ff FLOPs).
+4096, d_ff 11008, bf16; 6 * T * d_model * d_ff FLOPs), and ``prefill_4x2048``
+the 4 x 2048-token causal ALiBi GQA prefill (32 query / 8 key-value heads,
+D = 128, bf16) with its own roofline.  ``cpu_baseline`` also times the oracle
+on samples of the decode workload and on the small parity workloads, and
+records the host's CPU model and core count.
+
+``python bench.py --write-traffic DIR`` turns rocprofv3 FETCH_SIZE /
+WRITE_SIZE counter runs of the parts (``DIR/pmc_<part>_<COUNTER>/``, one
+counter per run, the ``copy`` part included for calibration) into
+profiles/hbm_traffic.json, keyed by the kernel-source hash.
 """
 from __future__ import annotations
 
@@ -46,6 +55,8 @@ PEAK_MFMA_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/C
 PEAK_HBM_GBS = 8000.0            # HBM3E
 PREFILL = "varlen_causal_gqa_64seq_h32kv8_d128_bf16"
 DECODE = "decode_splitkv_64req_h64kv8_d128_bf16"
+PREFILL_4X2048 = "causal_alibi_gqa_4x2048_h32kv8_d128_bf16"
+SMALL_WORKLOADS = ["packed_varlen_h8_d64_fp16", "bmghk_gqa_b2_m256_g2x4_d64_fp16"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = ["fwd_prefill.hip", "fwd_decode.hip", "bwd.hip", "ffn.hip", "mea_common.h", "mea_launch.h",
                   "mea_tiles.h"]
@@ -327,13 +338,54 @@ def time_calls(call, stream, reps):
     return e0.elapsed_time(e1) / reps
 
 
-def cpu_baseline(pre_inp, gpu_out, gpu_lse, budget_s: float):
+def host_cpu():
+    """CPU model and core counts of this host (Linux /proc and the process's affinity)."""
+    model, cores = None, set()
+    phys, core = None, None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                k, _, v = ln.partition(":")
+                k, v = k.strip(), v.strip()
+                if k == "model name" and model is None:
+                    model = v
+                elif k == "physical id":
+                    phys = v
+                elif k == "core id":
+                    core = v
+                elif not k and phys is not None:
+                    cores.add((phys, core))
+                    phys = core = None
+    except OSError:
+        pass
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        allowed = None
+    return {"cpu_model": model, "physical_cores": len(cores) or None, "logical_cpus": os.cpu_count(),
+            "cpus_allowed": allowed}
+
+
+def _time_oracle(inp):
+    import oracle
+    t0 = time.perf_counter()
+    out, lse = oracle.attention_forward(inp.q, inp.k, inp.v, inp.seqstart_q, inp.seqstart_k, causal=inp.causal,
+                                        alibi_slopes=inp.alibi_slopes, scale=inp.scale)
+    return time.perf_counter() - t0, out, lse
+
+
+def cpu_baseline(pre_inp, gpu_out, gpu_lse, budget_s: float, dec_inp=None, dec_budget_s: float = 4.0,
+                 small=None, cfg3=None):
     """Time the float64 CPU oracle on the prefill workload's sequences, one at
     a time in order, until about budget_s seconds have been spent (the budget
-    plus at most one sequence), and check the GPU rows of those sequences."""
+    plus at most one sequence), and check the GPU rows of those sequences.
+    Also: the decode workload's requests the same way (dec_inp, dec_budget_s),
+    each small parity workload whole (small: name -> Inputs) and the 4 x 2048
+    prefill whole (cfg3), and the host's CPU model and core count.  The
+    oracle runs on torch's CPU threads: the host share this process was given
+    (OMP_NUM_THREADS), which ``cores`` reports."""
     import torch
     import oracle
-    # threads: torch's default (OMP_NUM_THREADS), i.e. the host share this process was given
     sq, sk = pre_inp.seqstart_q.tolist(), pre_inp.seqstart_k.tolist()
     n_done, flops, dt, err, lerr = 0, 0, 0.0, 0.0, 0.0
     for b in range(len(pre_inp.seqlens_q)):
@@ -349,16 +401,130 @@ def cpu_baseline(pre_inp, gpu_out, gpu_lse, budget_s: float):
         err = max(err, (gpu_out[sq[b]:sq[b + 1]].double() - ref_out).abs().max().item())
         lerr = max(lerr, (gpu_lse[:, sq[b]:sq[b + 1]].double() - ref_lse).abs().max().item())
         n_done += 1
-    return {
+    res = {
         "value": flops / dt / 1e12, "unit": "TFLOP/s",
         "cores": torch.get_num_threads(), "kind": "oracle",
         "sample": f"first {n_done} of {len(pre_inp.seqlens_q)} sequences of the prefill workload "
                   f"({sq[n_done]} tokens, {flops / 1e9:.1f} unmasked GFLOP), float64, {dt:.1f} s",
         "gpu_vs_oracle_on_sample": {"max_abs_out": err, "max_abs_lse": lerr},
+        "host": host_cpu(),
     }
+    if dec_inp is not None:
+        n, dbytes, ddt = 0, 0, 0.0
+        while n < len(dec_inp.seqlens_q) and ddt < dec_budget_s:
+            one = one_sequence(dec_inp, n)
+            t, _, _ = _time_oracle(one)
+            ddt += t
+            dbytes += algorithmic_bytes(one)
+            n += 1
+        res["decode"] = {"value": dbytes / ddt / 1e9, "unit": "GB/s",
+                         "sample": f"first {n} of {len(dec_inp.seqlens_q)} requests of the decode workload "
+                                   f"({dec_inp.seqstart_k.tolist()[n]} keys), float64, {ddt:.1f} s"}
+    per_config = {}
+    for name, inp in (small or {}).items():
+        t, _, _ = _time_oracle(inp)
+        per_config[name] = {"seconds": round(t, 4), "tflops": unmasked_flops(inp) / t / 1e12}
+    if cfg3 is not None:
+        t, _, _ = _time_oracle(cfg3)
+        per_config[PREFILL_4X2048] = {"seconds": round(t, 3), "tflops": unmasked_flops(cfg3) / t / 1e12}
+    if per_config:
+        res["per_config"] = per_config
+    return res
+
+
+def one_sequence(inp, b):
+    """Sequence b of ``inp`` on its own (views of the same tensors)."""
+    import dataclasses
+    from mea_workloads import seqstart_from_lengths
+    sq, sk = inp.seqstart_q.tolist(), inp.seqstart_k.tolist()
+    lq, lk = sq[b + 1] - sq[b], sk[b + 1] - sk[b]
+    return dataclasses.replace(inp, q=inp.q[sq[b]:sq[b + 1]], k=inp.k[sk[b]:sk[b + 1]], v=inp.v[sk[b]:sk[b + 1]],
+                               seqstart_q=seqstart_from_lengths([lq]), seqstart_k=seqstart_from_lengths([lk]),
+                               seqlens_q=[lq], seqlens_k=[lk], bmghk=None)
 
 
 COPY_BYTES = 1 << 30   # calibration copy: 1 GiB read + 1 GiB written per launch
+
+# Parts whose counter runs make up each reported traffic figure: the kernels of
+# one call (warm-up included, averaged per dispatch) and the parts that ran them.
+TRAFFIC_PARTS = {
+    "fwd_prefill": ("prefill", ["vt_images_kernel<128, true, false, false>",
+                                "fwd_prefill_kernel<128, true, true, false, false, false, false>",
+                                "fwd_prefill_kernel<128, true, true, false, false, false, true>"]),
+    "fwd_prefill_alibi": ("prefill_alibi", ["vt_images_kernel<128, true, false, false>",
+                                            "fwd_prefill_kernel<128, true, true, true, false, false, false>",
+                                            "fwd_prefill_kernel<128, true, true, true, false, false, true>"]),
+    "fwd_prefill_4x2048": ("prefill_4x2048", ["vt_images_kernel<128, true, false, false>",
+                                              "fwd_prefill_kernel<128, true, true, true, false, false, false>",
+                                              "fwd_prefill_kernel<128, true, true, true, false, false, true>"]),
+    "fwd_decode": ("decode", ["fwd_decode_partial_kernel<128, true, false, false, false>",
+                              "fwd_decode_combine_kernel<128, true>"]),
+    "bwd": ("backward", ["bwd_prep_kernel<128, true>", "bwd_dkdv_kernel<128, true, true, false>",
+                         "bwd_dq_kernel<128, true, true, false>"]),
+    "fwd_prefill_fp8": ("prefill_fp8", ["vt_images_kernel<128, true, false, true>",
+                                        "fwd_prefill_kernel<128, true, true, false, false, true, false>"]),
+    "fwd_decode_fp8": ("decode_fp8", ["fwd_decode_partial_kernel<128, true, false, false, true>",
+                                      "fwd_decode_combine_kernel<128, true>"]),
+    "ffn": ("ffn", ["ffn_gemm_kernel<true, true>", "ffn_gemm_kernel<true, false>"]),
+}
+
+
+def _counter_means(path, counter):
+    """Mean counter value (KiB) per dispatch of each kernel in one rocprofv3
+    --pmc CSV (counter_collection), keyed by the kernel name without the
+    namespace and argument list."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {path}")
+    sums, counts = {}, {}
+    for f in files:
+        with open(f, newline="") as fh:
+            for row in csv.DictReader(fh):
+                if row.get("Counter_Name") != counter:
+                    continue
+                name = row["Kernel_Name"]
+                name = name[name.find("::") + 2:] if name.startswith("void mea::") or name.startswith("mea::") else name
+                name = name.split("(")[0].strip()
+                sums[name] = sums.get(name, 0.0) + float(row["Counter_Value"])
+                counts[name] = counts.get(name, 0) + 1
+    return {k: sums[k] / counts[k] for k in sums}, counts
+
+
+def write_traffic(root):
+    """profiles/hbm_traffic.json from the FETCH_SIZE / WRITE_SIZE runs under
+    root: each counter scaled by what it reads for the copy of known size."""
+    fetch_copy, _ = _counter_means(os.path.join(root, "pmc_copy_FETCH_SIZE"), "FETCH_SIZE")
+    write_copy, _ = _counter_means(os.path.join(root, "pmc_copy_WRITE_SIZE"), "WRITE_SIZE")
+    fk = max(fetch_copy.values())
+    wk = max(write_copy.values())
+    fetch_factor = COPY_BYTES / (fk * 1024)
+    write_factor = COPY_BYTES / (wk * 1024)
+    rec = {"source_hash": kernel_source_hash(),
+           "calibration": {"copy_bytes_each_way": COPY_BYTES, "fetch_kib_per_dispatch": fk,
+                           "write_kib_per_dispatch": wk, "fetch_factor": round(fetch_factor, 4),
+                           "write_factor": round(write_factor, 4)},
+           "per_kernel": {}, "kernels": {}}
+    for key, (part, kernels) in TRAFFIC_PARTS.items():
+        try:
+            fetch, nf = _counter_means(os.path.join(root, f"pmc_{part}_FETCH_SIZE"), "FETCH_SIZE")
+            write, _ = _counter_means(os.path.join(root, f"pmc_{part}_WRITE_SIZE"), "WRITE_SIZE")
+        except FileNotFoundError:
+            continue
+        per, total = {}, 0
+        for k in kernels:
+            if k not in fetch:
+                continue
+            rb = int(fetch[k] * 1024 * fetch_factor)
+            wb = int(write.get(k, 0.0) * 1024 * write_factor)
+            per[k] = {"read_bytes": rb, "write_bytes": wb, "dispatches": nf[k]}
+            total += rb + wb
+        rec["per_kernel"][key] = per
+        rec["kernels"][key] = total
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec["kernels"]))
 
 
 def run_part(args, dev):
@@ -387,7 +553,11 @@ def run_part(args, dev):
               flush=True)
         return
     name = PREFILL if args.part in ("prefill", "backward", "prefill_fp8") else DECODE
-    if args.part == "ffn":
+    if args.part == "prefill_alibi":
+        call = Call(generate(PREFILL, seed=args.seed, alibi=True), dev)
+    elif args.part == "prefill_4x2048":
+        call = Call(generate(PREFILL_4X2048, seed=args.seed), dev)
+    elif args.part == "ffn":
         call = FfnCall(dev, args.seed)
     elif args.part in ("prefill_fp8", "decode_fp8"):
         call = Fp8Call(generate(name, seed=args.seed), dev)
@@ -410,10 +580,11 @@ def run_part(args, dev):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / max(args.steps, 1)
-    res = {"part": args.part, "workload": "swiglu_ffn" if args.part == "ffn" else name, "ms": round(ms, 4)}
+    workload = {"ffn": "swiglu_ffn", "prefill_4x2048": PREFILL_4X2048, "prefill_alibi": PREFILL + " + alibi"}
+    res = {"part": args.part, "workload": workload.get(args.part, name), "ms": round(ms, 4)}
     if args.part in ("decode_paged", "decode_paged_fp8"):
         res["page_size"] = PAGE_SIZE
-    if args.part in ("prefill", "prefill_fp8"):
+    if args.part in ("prefill", "prefill_fp8", "prefill_alibi", "prefill_4x2048"):
         res["tflops"] = round(unmasked_flops(call.inp) / (ms * 1e-3) / 1e12, 2)
     elif args.part == "backward":
         res["tflops"] = round(BWD_GEMMS * unmasked_flops(call.inp) / (ms * 1e-3) / 1e12, 2)
@@ -439,12 +610,19 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-ffn", action="store_true")
+    ap.add_argument("--write-traffic", metavar="DIR", default=None,
+                    help="write profiles/hbm_traffic.json from the rocprofv3 counter runs under DIR and exit "
+                         "(no GPU needed)")
     ap.add_argument("--part", choices=["all", "prefill", "decode", "decode_paged", "backward", "prefill_fp8",
-                                       "decode_fp8", "decode_paged_fp8", "ffn", "copy"],
+                                       "decode_fp8", "decode_paged_fp8", "ffn", "prefill_alibi", "prefill_4x2048",
+                                       "copy"],
                     default="all",
                     help="run only one half of the step, or the calibration copy (for profiling); "
                          "the JSON line is for 'all'")
     args = ap.parse_args()
+    if args.write_traffic is not None:
+        write_traffic(args.write_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
@@ -484,6 +662,8 @@ def main():
     ffn_call = None
     if not args.no_ffn:
         ffn_call = FfnCall(dev, args.seed)
+    cfg3 = generate(PREFILL_4X2048, seed=args.seed)
+    cfg3_call = Call(cfg3, dev)
     torch.cuda.synchronize()
     print(f"[bench] inputs generated and resident in HBM in {time.perf_counter() - t_gen:.1f} s",
           file=sys.stderr, flush=True)
@@ -528,7 +708,25 @@ def main():
         ams = e0.elapsed_time(e1) / max(3, K // 3)
         atf = unmasked_flops(pre_alibi.inp) / (ams * 1e-3) / 1e12
         alibi_res = {"ms": round(ams, 4), "tflops": round(atf, 2),
-                     "frac": round(atf / PEAK_MFMA_BF16_TFLOPS, 4)}
+                     "frac": round(atf / PEAK_MFMA_BF16_TFLOPS, 4),
+                     "roofline": {"bound": "mfma", "achieved": round(atf, 2), "peak": PEAK_MFMA_BF16_TFLOPS,
+                                  "unit": "TFLOP/s", "frac": round(atf / PEAK_MFMA_BF16_TFLOPS, 4),
+                                  "traffic": measured_traffic("fwd_prefill_alibi"),
+                                  "kernel": "mea_fwd prefill call with ALiBi: vt_images_kernel + "
+                                            "fwd_prefill_kernel<128,bf16,causal,alibi>"}}
+
+    # the 4 x 2048 causal ALiBi GQA prefill: short sequences, so the grid is
+    # four rounds of workgroups and its fixed costs weigh more
+    c3ms = time_calls(cfg3_call, stream, max(20, 2 * K))
+    c3tf = unmasked_flops(cfg3) / (c3ms * 1e-3) / 1e12
+    cfg3_res = {"ms": round(c3ms, 4), "value": round(c3tf, 2), "unit": "TFLOP/s",
+                "config": {"seqs": 4, "tokens": cfg3.total_q, "Hq": 32, "Hkv": 8, "D": 128, "dtype": "bf16",
+                           "mask": "block-diagonal causal", "alibi": True, "unmasked_flops": unmasked_flops(cfg3)},
+                "roofline": {"bound": "mfma", "achieved": round(c3tf, 2), "peak": PEAK_MFMA_BF16_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(c3tf / PEAK_MFMA_BF16_TFLOPS, 4),
+                             "traffic": measured_traffic("fwd_prefill_4x2048"),
+                             "kernel": "mea_fwd prefill call with ALiBi: vt_images_kernel + "
+                                       "fwd_prefill_kernel<128,bf16,causal,alibi>"}}
 
     paged_res = None
     if dec_paged is not None:  # the decode workload with K/V in shuffled pages of PAGE_SIZE keys
@@ -632,6 +830,7 @@ def main():
                          "kernel": "fwd_decode_partial_kernel + fwd_decode_combine_kernel"},
         },
         "prefill_alibi": alibi_res,
+        "prefill_4x2048": cfg3_res,
         "backward": bwd_res,
         "prefill_fp8": fp8_res,
         "decode_fp8": fp8_dec_res,
@@ -641,7 +840,9 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(pre, pre_call.out.cpu(), pre_call.lse.cpu(), args.cpu_budget)
+        line["cpu_baseline"] = cpu_baseline(pre, pre_call.out.cpu(), pre_call.lse.cpu(), args.cpu_budget,
+                                            dec_inp=dec, small={n: generate(n, seed=args.seed) for n in SMALL_WORKLOADS},
+                                            cfg3=cfg3)
     print(json.dumps(line), flush=True)
 
 
