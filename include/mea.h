@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define MEA_ABI_VERSION 9
+#define MEA_ABI_VERSION 10
 
 #if defined(__GNUC__)
 #define MEA_EXPORT __attribute__((visibility("default")))
@@ -143,6 +143,53 @@ MEA_EXPORT mea_status_t mea_fwd(const void* q, const void* k, const void* v, voi
                      int32_t Hkv, int32_t D, mea_dtype_t dtype, int32_t causal,
                      const float* alibi_slopes, float scale, void* workspace,
                      size_t workspace_bytes, void* stream);
+
+/*
+ * mea_fwd_mixed -- mea_fwd on a mixed batch of prefills and decode steps, as a
+ * serving engine batches requests of different lengths (section 4 of the
+ * 7minutos.es tutorial names vLLM-style batching as the use of packed
+ * sequences): the first num_prefill_seqs sequences are prefills (any number
+ * of queries), the remaining ones decode steps of exactly one query each.
+ * Computes exactly what mea_fwd computes on the whole batch, but serves the
+ * two parts with their own kernels, one after the other on `stream`: the
+ * prefills with the tiled prefill kernels, the decode steps with the
+ * split-KV kernels over their own keys (mea_fwd sends a batch with any
+ * sequence of more than one query wholly to the prefill kernels, where a
+ * decode step fills one row of a 64-token tile and one workgroup walks its
+ * whole key history).
+ *   num_prefill_seqs     sequences 0 .. num_prefill_seqs - 1 are the prefills
+ *   prefill_total_q/k    seqstart_q[num_prefill_seqs] and
+ *                        seqstart_k[num_prefill_seqs] (host copies)
+ *   decode_max_seqlen_k  an upper bound of the decode sequences' key counts
+ *   max_seqlen_q/k       as for mea_fwd (max_seqlen_q bounds the prefills)
+ *   workspace            mea_fwd_mixed_workspace_size(...) bytes: the prefill
+ *                        part's V^T images, then (256-byte aligned) the decode
+ *                        part's partials
+ * Other arguments, ownership and errors as for mea_fwd, plus MEA_ERR_INVALID
+ * when num_prefill_seqs is outside [0, num_seqs], prefill_total_q/k outside
+ * [0, total_q/k], decode_max_seqlen_k outside [0, max_seqlen_k], or total_q -
+ * prefill_total_q differs from the number of decode sequences.  Preconditions
+ * as for mea_fwd, plus: every decode sequence has exactly one query, and the
+ * prefill_total_q/k values equal the device seqstart entries.
+ */
+MEA_EXPORT mea_status_t mea_fwd_mixed(const void* q, const void* k, const void* v, void* out, float* lse,
+                                      const int32_t* seqstart_q, const int32_t* seqstart_k, int32_t num_seqs,
+                                      int32_t total_q, int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                      int32_t num_prefill_seqs, int32_t prefill_total_q, int32_t prefill_total_k,
+                                      int32_t decode_max_seqlen_k, int32_t Hq, int32_t Hkv, int32_t D,
+                                      mea_dtype_t dtype, int32_t causal, const float* alibi_slopes, float scale,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of mea_fwd_mixed (0 for arguments it would reject, or when
+ * nothing is needed): the prefill part's mea_fwd_workspace_size-style V^T
+ * images for sequences 0 .. num_prefill_seqs - 1 (prefill_total_k keys), then,
+ * rounded up to 256 bytes, the decode part's partials for the other sequences
+ * (total_k - prefill_total_k keys, pieces chosen as mea_default_chunk_keys
+ * does for that key count).  Pure host function. */
+MEA_EXPORT size_t mea_fwd_mixed_workspace_size(int32_t num_seqs, int32_t total_k, int32_t max_seqlen_q,
+                                               int32_t max_seqlen_k, int32_t num_prefill_seqs,
+                                               int32_t prefill_total_k, int32_t decode_max_seqlen_k, int32_t Hq,
+                                               int32_t Hkv, int32_t D);
 
 /*
  * mea_fwd_noalloc -- mea_fwd for callers that cannot allocate memory (code

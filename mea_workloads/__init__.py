@@ -33,7 +33,8 @@ import torch
 __all__ = [
     "Workload", "Inputs", "WORKLOADS", "get_workload", "generate", "random_case",
     "alibi_slopes", "seqstart_from_lengths", "sample_rows", "prefix", "PagedKV", "to_paged",
-    "random_dout", "Fp8Inputs", "to_fp8", "FfnInputs", "swiglu_case", "FFN_WORKLOAD",
+    "random_dout", "Fp8Inputs", "to_fp8", "FfnInputs", "swiglu_case", "FFN_WORKLOAD", "mixed_case",
+    "MIXED_WORKLOAD",
 ]
 
 _DTYPES = {"fp16": torch.float16, "bf16": torch.bfloat16}
@@ -229,6 +230,25 @@ def random_case(seed: int, seqlens_q: Sequence[int], seqlens_k: Optional[Sequenc
         alibi_slopes=slopes if alibi else None,
         scale=default_scale(D) if scale is None else float(np.float32(scale)),
         dtype=dtype if isinstance(dtype, str) else {v_: k_ for k_, v_ in _DTYPES.items()}[dt])
+
+
+MIXED_WORKLOAD = dict(prefills=8, prefill_lo=128, prefill_hi=4096, decodes=56, decode_lo=1024, decode_hi=32768,
+                      Hq=32, Hkv=8, D=128, dtype="bf16")
+
+
+def mixed_case(seed: int = 0, prefills: int = 8, decodes: int = 56, prefill_lo: int = 128, prefill_hi: int = 4096,
+               decode_lo: int = 1024, decode_hi: int = 32768, Hq: int = 32, Hkv: int = 8, D: int = 128,
+               dtype: str = "bf16", causal: bool = True, alibi: bool = False) -> Inputs:
+    """A serving engine's mixed batch: ``prefills`` prompts with lengths
+    U[prefill_lo, prefill_hi] (queries = keys), then ``decodes`` decode steps
+    of one query each over KV histories of lengths U[decode_lo, decode_hi];
+    lengths from ``numpy.random.default_rng(seed)`` (prefills first), tensors
+    as for every workload."""
+    rng = np.random.default_rng(seed)
+    pre = [int(x) for x in rng.integers(prefill_lo, prefill_hi, size=prefills, endpoint=True)]
+    dec = [int(x) for x in rng.integers(decode_lo, decode_hi, size=decodes, endpoint=True)]
+    return random_case(seed, pre + [1] * decodes, pre + dec, Hq=Hq, Hkv=Hkv, D=D, dtype=dtype, causal=causal,
+                       alibi=alibi)
 
 
 def random_dout(seed: int, inp: Inputs, std: float = 1.0) -> torch.Tensor:

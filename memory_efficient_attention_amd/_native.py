@@ -13,7 +13,8 @@ import threading
 
 __all__ = [
     "MEA_OK", "MEA_ERR_INVALID", "MEA_ERR_UNSUPPORTED", "MEA_ERR_HIP", "MEA_F16", "MEA_BF16",
-    "EXPORTED_SYMBOLS", "library_path", "load", "mea_fwd", "mea_fwd_noalloc", "mea_fwd_splitkv", "mea_fwd_paged",
+    "EXPORTED_SYMBOLS", "library_path", "load", "mea_fwd", "mea_fwd_mixed", "mea_fwd_mixed_workspace_size",
+    "mea_fwd_noalloc", "mea_fwd_splitkv", "mea_fwd_paged",
     "mea_fwd_workspace_size", "mea_default_chunk_keys", "mea_bwd", "mea_bwd_workspace_size",
     "mea_fwd_fp8", "mea_fwd_paged_fp8", "mea_fwd_fp8_workspace_size", "mea_swiglu_ffn", "mea_status_string",
     "mea_last_error", "mea_abi_version",
@@ -23,7 +24,7 @@ MEA_OK, MEA_ERR_INVALID, MEA_ERR_UNSUPPORTED, MEA_ERR_HIP = 0, 1, 2, 3
 MEA_F16, MEA_BF16 = 0, 1
 
 EXPORTED_SYMBOLS = (
-    "mea_fwd", "mea_fwd_noalloc", "mea_fwd_splitkv", "mea_fwd_paged", "mea_fwd_workspace_size", "mea_default_chunk_keys",
+    "mea_fwd", "mea_fwd_mixed", "mea_fwd_mixed_workspace_size", "mea_fwd_noalloc", "mea_fwd_splitkv", "mea_fwd_paged", "mea_fwd_workspace_size", "mea_default_chunk_keys",
     "mea_bwd", "mea_bwd_workspace_size", "mea_fwd_fp8", "mea_fwd_paged_fp8", "mea_fwd_fp8_workspace_size",
     "mea_swiglu_ffn", "mea_status_string", "mea_last_error", "mea_abi_version",
 )
@@ -86,6 +87,10 @@ def load() -> ctypes.CDLL:
         lib = ctypes.CDLL(path)
         lib.mea_fwd.argtypes = _FWD_ARGS
         lib.mea_fwd.restype = ctypes.c_int
+        lib.mea_fwd_mixed.argtypes = _FWD_ARGS[:12] + [_i32] * 4 + _FWD_ARGS[12:]
+        lib.mea_fwd_mixed.restype = ctypes.c_int
+        lib.mea_fwd_mixed_workspace_size.argtypes = [_i32] * 10
+        lib.mea_fwd_mixed_workspace_size.restype = _sz
         lib.mea_fwd_noalloc.argtypes = _FWD_ARGS[:19] + [_vp]   # no workspace, workspace_bytes
         lib.mea_fwd_noalloc.restype = ctypes.c_int
         lib.mea_fwd_splitkv.argtypes = _FWD_ARGS + [_i32]
@@ -124,6 +129,21 @@ def mea_fwd(q, k, v, out, lse, seqstart_q, seqstart_k, num_seqs, total_q, total_
     return load().mea_fwd(q, k, v, out, lse, seqstart_q, seqstart_k, num_seqs, total_q, total_k,
                           max_seqlen_q, max_seqlen_k, Hq, Hkv, D, dtype, causal, alibi_slopes,
                           scale, workspace, workspace_bytes, stream)
+
+
+def mea_fwd_mixed(q, k, v, out, lse, seqstart_q, seqstart_k, num_seqs, total_q, total_k, max_seqlen_q,
+                  max_seqlen_k, num_prefill_seqs, prefill_total_q, prefill_total_k, decode_max_seqlen_k, Hq, Hkv, D,
+                  dtype, causal, alibi_slopes, scale, workspace, workspace_bytes, stream) -> int:
+    return load().mea_fwd_mixed(q, k, v, out, lse, seqstart_q, seqstart_k, num_seqs, total_q, total_k,
+                                max_seqlen_q, max_seqlen_k, num_prefill_seqs, prefill_total_q, prefill_total_k,
+                                decode_max_seqlen_k, Hq, Hkv, D, dtype, causal, alibi_slopes, scale, workspace,
+                                workspace_bytes, stream)
+
+
+def mea_fwd_mixed_workspace_size(num_seqs, total_k, max_seqlen_q, max_seqlen_k, num_prefill_seqs, prefill_total_k,
+                                 decode_max_seqlen_k, Hq, Hkv, D) -> int:
+    return load().mea_fwd_mixed_workspace_size(num_seqs, total_k, max_seqlen_q, max_seqlen_k, num_prefill_seqs,
+                                               prefill_total_k, decode_max_seqlen_k, Hq, Hkv, D)
 
 
 def mea_fwd_noalloc(q, k, v, out, lse, seqstart_q, seqstart_k, num_seqs, total_q, total_k, max_seqlen_q,

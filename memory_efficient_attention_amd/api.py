@@ -89,6 +89,19 @@ class BlockDiagonalMask:
     def max_seqlen_kv(self) -> int:
         return max(self.kv_seqlen, default=0)
 
+    def mixed_split(self) -> Optional[Tuple[int, int, int, int]]:
+        """For a batch of prefills followed by decode steps (one query each),
+        the way a serving engine lays out a mixed batch, ``(num_prefill_seqs,
+        prefill_total_q, prefill_total_k, decode_max_seqlen_k)``; None when the
+        batch has no such tail of decode steps or no prefill before it."""
+        n = self.num_seqs
+        i = n
+        while i > 0 and self.q_seqlen[i - 1] == 1:
+            i -= 1
+        if i == n or max(self.q_seqlen[:i], default=0) <= 1:
+            return None
+        return i, self.q_seqstart[i], self.kv_seqstart[i], max(self.kv_seqlen[i:])
+
     def seqstart_tensors(self, device) -> Tuple[torch.Tensor, torch.Tensor]:
         """int32 device copies of the sequence offsets (cached per device)."""
         key = str(torch.device(device))
@@ -170,11 +183,16 @@ def attention_packed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                      alibi_slopes: Optional[torch.Tensor] = None, scale: Optional[float] = None,
                      return_lse: bool = False, out: Optional[torch.Tensor] = None,
                      lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                     chunk_keys: Optional[int] = None, stream: Optional[torch.cuda.Stream] = None):
+                     chunk_keys: Optional[int] = None, mixed: Optional[Tuple[int, int, int, int]] = None,
+                     stream: Optional[torch.cuda.Stream] = None):
     """Packed call: q ``[Tq, Hq, D]``, k/v ``[Tk, Hkv, D]`` (contiguous device
     tensors), int32 device ``seqstart_q/k`` ``[n + 1]``.  Returns ``out`` or
     ``(out, lse)`` with lse ``[Hq, Tq]`` float32.  ``chunk_keys`` forces the
-    decode split length (only for max_seqlen_q == 1)."""
+    decode split length (only for max_seqlen_q == 1).  ``mixed`` =
+    ``(num_prefill_seqs, prefill_total_q, prefill_total_k,
+    decode_max_seqlen_k)`` serves a batch of prefills followed by one-query
+    decode steps with both kinds of kernels (mea_fwd_mixed; see
+    ``BlockDiagonalMask.mixed_split``)."""
     if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
         raise ValueError("packed q, k, v must be [tokens, heads, D]")
     Tq, Hq, D = q.shape
@@ -208,20 +226,29 @@ def attention_packed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     scale = float(np.float32(scale))
-    ws_bytes = _native.mea_fwd_workspace_size(num_seqs, Tk, max_seqlen_q, max_seqlen_k, Hq, Hkv, D,
-                                              int(chunk_keys or 0))
+    if mixed is not None:
+        if chunk_keys is not None:
+            raise ValueError("chunk_keys and mixed are exclusive")
+        n_pre, pre_q, pre_k, dec_max_k = (int(x) for x in mixed)
+        ws_bytes = _native.mea_fwd_mixed_workspace_size(num_seqs, Tk, int(max_seqlen_q), int(max_seqlen_k), n_pre,
+                                                        pre_k, dec_max_k, Hq, Hkv, D)
+    else:
+        ws_bytes = _native.mea_fwd_workspace_size(num_seqs, Tk, max_seqlen_q, max_seqlen_k, Hq, Hkv, D,
+                                                  int(chunk_keys or 0))
     workspace = _workspace(workspace, ws_bytes, dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
-    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(seqstart_q), _ptr(seqstart_k),
-            num_seqs, Tq, Tk, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, D, _dtype_code(q.dtype),
-            int(bool(causal)), _ptr(slopes), scale, _ptr(workspace),
+    head = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(seqstart_q), _ptr(seqstart_k),
+            num_seqs, Tq, Tk, int(max_seqlen_q), int(max_seqlen_k))
+    tail = (Hq, Hkv, D, _dtype_code(q.dtype), int(bool(causal)), _ptr(slopes), scale, _ptr(workspace),
             ws_bytes, stream.cuda_stream)
     with torch.cuda.device(dev):
-        if chunk_keys is None:
-            st = _native.mea_fwd(*args)
+        if mixed is not None:
+            st = _native.mea_fwd_mixed(*head, n_pre, pre_q, pre_k, dec_max_k, *tail)
+        elif chunk_keys is None:
+            st = _native.mea_fwd(*head, *tail)
         else:
-            st = _native.mea_fwd_splitkv(*args, int(chunk_keys))
+            st = _native.mea_fwd_splitkv(*head, *tail, int(chunk_keys))
     if st != _native.MEA_OK:
         raise MeaError(st, _native.mea_last_error())
     return (out, lse) if return_lse else out
@@ -360,9 +387,9 @@ class _PackedAttention(torch.autograd.Function):
     (keeping out and lse), backward through ``mea_bwd``."""
 
     @staticmethod
-    def forward(ctx, q, k, v, seqstart_q, seqstart_k, max_seqlen_q, max_seqlen_k, causal, slopes, scale):
+    def forward(ctx, q, k, v, seqstart_q, seqstart_k, max_seqlen_q, max_seqlen_k, causal, slopes, scale, mixed):
         out, lse = attention_packed(q, k, v, seqstart_q, seqstart_k, max_seqlen_q, max_seqlen_k,
-                                    causal=causal, alibi_slopes=slopes, scale=scale, return_lse=True)
+                                    causal=causal, alibi_slopes=slopes, scale=scale, return_lse=True, mixed=mixed)
         ctx.save_for_backward(q, k, v, out, lse, seqstart_q, seqstart_k)
         ctx.meta = (max_seqlen_q, max_seqlen_k, causal, slopes, scale)
         ctx.mark_non_differentiable(lse)
@@ -375,7 +402,7 @@ class _PackedAttention(torch.autograd.Function):
         dq, dk, dv = attention_backward_packed(q, k, v, out, lse, dout.contiguous(), seqstart_q, seqstart_k,
                                                max_seqlen_q, max_seqlen_k, causal=causal,
                                                alibi_slopes=slopes, scale=scale)
-        return dq, dk, dv, None, None, None, None, None, None, None
+        return dq, dk, dv, None, None, None, None, None, None, None, None
 
 
 def attention_packed_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, q_scale: float,
@@ -601,11 +628,11 @@ def memory_efficient_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
     if torch.is_grad_enabled() and (q.requires_grad or k.requires_grad or v.requires_grad):
         out, lse = _PackedAttention.apply(qp.contiguous(), kp.contiguous(), vp.contiguous(), ssq, ssk,
                                           mask.max_seqlen_q, mask.max_seqlen_kv, mask.causal,
-                                          alibi_slopes, scale)
+                                          alibi_slopes, scale, mask.mixed_split())
         return (out.view(q.shape), lse) if return_lse else out.view(q.shape)
     res = attention_packed(qp, kp, vp, ssq, ssk, mask.max_seqlen_q, mask.max_seqlen_kv,
                            causal=mask.causal, alibi_slopes=alibi_slopes, scale=scale,
-                           return_lse=return_lse)
+                           return_lse=return_lse, mixed=mask.mixed_split())
     if return_lse:
         return res[0].view(q.shape), res[1]
     return res.view(q.shape)

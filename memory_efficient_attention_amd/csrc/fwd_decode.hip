@@ -4,7 +4,9 @@
 // once, so the kernels are built to keep as many bytes in flight per CU as
 // possible and to spend little else.
 //
-// Work split: the concatenated key axis [0, total_k) of all sequences is cut
+// Work split: the concatenated key axis [0, total_k) of all sequences (from
+// dc_key_base = seqstart_k[dc_seq_base] when only the sequences from
+// dc_seq_base on are served: the decode part of a mixed batch) is cut
 // into pieces of W keys, W chosen so that the launch is one round of
 // equal-sized workgroups on the chip (equal pieces leave no long tail, unlike
 // per-sequence chunks of unequal length).  A piece that spans the end of one
@@ -110,9 +112,9 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void fwd_decode_partial_ke
 
   // the piece: keys [k0, k1) of the concatenated key axis
   const int W = a.chunk_keys;
-  const int k0 = piece * W, k1 = min(a.total_k, k0 + W);
+  const int k0 = a.dc_key_base + piece * W, k1 = min(a.total_k, k0 + W);
   // first sequence that owns a key >= k0: smallest b with seqstart_k[b + 1] > k0
-  int b = 0;
+  int b = a.dc_seq_base;
   {
     int hi = a.num_seqs - 1;
     while (b < hi) {
@@ -130,7 +132,7 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void fwd_decode_partial_ke
   // this segment: keys [c0, c1) of sequence b; its partial goes to slot
   // `slot` of the sequence (slot 0 = the piece holding the sequence's first key)
   const int c0 = max(k0, sk0) - sk0, c1 = min(k1, sk1) - sk0;
-  const int slot = piece - sk0 / W;
+  const int slot = piece - (sk0 - a.dc_key_base) / W;
   const int qpos = Lk - 1;  // the single query is the sequence's last position
 
   const int hl = hs * 16 + q;  // query head within the group (= product column)
@@ -473,7 +475,7 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void fwd_decode_partial_ke
     }
     const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
     const int hq = (g0 + h2) * a.group + hs * 16 + qc;
-    const size_t prow = ((size_t)b * a.max_chunks + slot) * a.Hq + hq;
+    const size_t prow = ((size_t)(b - a.dc_seq_base) * a.max_chunks + slot) * a.Hq + hq;
     float* dst = a.ws_o + prow * D + part * FP;
 #pragma unroll
     for (int e = 0; e < FP; ++e) {
@@ -505,14 +507,14 @@ __global__ __launch_bounds__(256) void fwd_decode_combine_kernel(FwdArgs a) {
   const int lane = threadIdx.x & 63;
   const int grp = lane / LPR, f0 = (lane % LPR) * 8;
   const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int b = blockIdx.y;
+  const int b = a.dc_seq_base + (int)blockIdx.y;
   if (h >= a.Hq) return;
   const int sq0 = a.seqstart_q[b], Lq = a.seqstart_q[b + 1] - sq0;
   if (Lq == 0) return;
-  const int sk0 = a.seqstart_k[b], sk1 = a.seqstart_k[b + 1];
+  const int sk0 = a.seqstart_k[b] - a.dc_key_base, sk1 = a.seqstart_k[b + 1] - a.dc_key_base;
   // partial slots of sequence b: one per piece of the key axis its keys touch
   const int nch = sk1 > sk0 ? (sk1 - 1) / a.chunk_keys - sk0 / a.chunk_keys + 1 : 0;
-  const size_t row0 = (size_t)b * a.max_chunks * a.Hq + h;  // partial row of chunk 0
+  const size_t row0 = (size_t)(b - a.dc_seq_base) * a.max_chunks * a.Hq + h;  // partial row of chunk 0
   const float* lse_p = a.ws_lse + row0;                        // chunk c at [c * Hq]
   float M = kNegInf;
   for (int ch = lane; ch < nch; ch += 64) M = __builtin_fmaxf(M, lse_p[(size_t)ch * a.Hq]);
@@ -583,7 +585,7 @@ static hipError_t launch_decode_d(const FwdArgs& a, bool alibi, hipStream_t stre
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((fwd_decode_combine_kernel<D, BF16>), dim3((a.Hq + 3) / 4, a.num_seqs), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((fwd_decode_combine_kernel<D, BF16>), dim3((a.Hq + 3) / 4, a.num_seqs - a.dc_seq_base), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -610,8 +612,8 @@ hipError_t launch_decode_fp8(const FwdArgs& a, bool out_bf16, bool alibi, hipStr
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (out_bf16) hipLaunchKernelGGL((fwd_decode_combine_kernel<128, true>), dim3((a.Hq + 3) / 4, a.num_seqs), dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL((fwd_decode_combine_kernel<128, false>), dim3((a.Hq + 3) / 4, a.num_seqs), dim3(256), 0, stream, a);
+  if (out_bf16) hipLaunchKernelGGL((fwd_decode_combine_kernel<128, true>), dim3((a.Hq + 3) / 4, a.num_seqs - a.dc_seq_base), dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL((fwd_decode_combine_kernel<128, false>), dim3((a.Hq + 3) / 4, a.num_seqs - a.dc_seq_base), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

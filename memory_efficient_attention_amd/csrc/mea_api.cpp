@@ -124,20 +124,73 @@ struct PagedKv {
 
 // fp8 (OCP e4m3) q, k, v with per-tensor scales: the values are q_scale * q8
 // etc.  q_scale * k_scale folds into the score scale, v_scale into the output.
+struct Fp8Scales {
+  float q, k, v;
+};
+
+// A mixed batch: sequences [0, n_pre) are prefills (any query count) and
+// sequences [n_pre, num_seqs) decode steps of exactly one query each;
+// pre_q = seqstart_q[n_pre], pre_k = seqstart_k[n_pre]; dec_max_k bounds the
+// key count of the decode sequences.
+struct MixedSplit {
+  int32_t n_pre, pre_q, pre_k, dec_max_k;
+};
+
+// How one forward call is carried out: a prefill part (sequences [0, n) on the
+// prefill kernels) and a decode part (sequences [seq_base, num_seqs), keys
+// [key_base, total_k), on the split-KV kernels), each with its workspace
+// region.
+struct FwdPlan {
+  bool pre = false, dec = false;
+  int32_t pre_n = 0, pre_k = 0;
+  int32_t dec_base = 0, dec_key_base = 0, dec_n = 0, dec_keys = 0, dec_max_k = 0;
+  DecodeSplit split{0, 0};
+  size_t pre_bytes = 0, dec_bytes = 0, dec_off = 0, total = 0;
+};
+
+FwdPlan fwd_plan(int32_t num_seqs, int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq,
+                 int32_t Hkv, int32_t D, int32_t chunk_keys, bool forced_split, bool fp8, const MixedSplit* mixed) {
+  FwdPlan p;
+  if (mixed != nullptr) {
+    p.pre = mixed->n_pre > 0;
+    p.pre_n = mixed->n_pre;
+    p.pre_k = mixed->pre_k;
+    p.dec = mixed->n_pre < num_seqs;
+    p.dec_base = mixed->n_pre;
+    p.dec_key_base = mixed->pre_k;
+    p.dec_n = num_seqs - mixed->n_pre;
+    p.dec_keys = total_k - mixed->pre_k;
+    p.dec_max_k = mixed->dec_max_k;
+  } else if (max_seqlen_q == 1) {
+    p.dec = true;
+    p.dec_n = num_seqs;
+    p.dec_keys = total_k;
+    p.dec_max_k = max_seqlen_k;
+  } else {
+    p.pre = true;
+    p.pre_n = num_seqs;
+    p.pre_k = total_k;
+  }
+  if (p.pre) p.pre_bytes = prefill_ws_bytes(p.pre_n, p.pre_k, Hkv, D);
+  if (p.dec) {
+    p.split = forced_split ? DecodeSplit{gcd_int(Hkv, mea::kDcKvPerWgMax), chunk_keys}
+                           : decode_split(p.dec_keys, Hq, Hkv, fp8);
+    p.dec_bytes = decode_ws_bytes(p.dec_n, p.dec_keys, p.dec_max_k, Hq, D, p.split.chunk);
+  }
+  p.dec_off = p.pre_bytes > 0 && p.dec_bytes > 0 ? align256(p.pre_bytes) : 0;
+  p.total = p.dec_bytes > 0 ? p.dec_off + p.dec_bytes : p.pre_bytes;
+  return p;
+}
+
 size_t fwd_ws_size(int32_t num_seqs, int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq,
                    int32_t Hkv, int32_t D, int32_t chunk_keys, bool fp8) {
   if (num_seqs <= 0 || total_k < 0 || max_seqlen_q <= 0 || max_seqlen_k < 0 || Hq <= 0 || Hkv <= 0 ||
       Hq % Hkv != 0 || (D != 64 && D != 128) || chunk_keys < 0 ||
       (chunk_keys > 0 && chunk_keys % mea::kDcPieceAlign != 0))
     return 0;
-  if (max_seqlen_q != 1) return prefill_ws_bytes(num_seqs, total_k, Hkv, D);
-  const int32_t chunk = chunk_keys > 0 ? chunk_keys : decode_split(total_k, Hq, Hkv, fp8).chunk;
-  return decode_ws_bytes(num_seqs, total_k, max_seqlen_k, Hq, D, chunk);
+  return fwd_plan(num_seqs, total_k, max_seqlen_q, max_seqlen_k, Hq, Hkv, D, chunk_keys, chunk_keys > 0, fp8,
+                  nullptr).total;
 }
-
-struct Fp8Scales {
-  float q, k, v;
-};
 
 mea_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse,
                       const int32_t* seqstart_q, const int32_t* seqstart_k, int32_t num_seqs,
@@ -145,7 +198,8 @@ mea_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, fl
                       int32_t Hkv, int32_t D, mea_dtype_t dtype, int32_t causal,
                       const float* alibi_slopes, float scale, void* workspace,
                       size_t workspace_bytes, void* stream, int32_t chunk_keys, bool forced_split,
-                      const PagedKv* paged = nullptr, const Fp8Scales* fp8 = nullptr) {
+                      const PagedKv* paged = nullptr, const Fp8Scales* fp8 = nullptr,
+                      const MixedSplit* mixed = nullptr) {
   g_last_error[0] = '\0';
   // q and out are read/written only when total_q > 0, k and v only when total_k > 0
   if (((q == nullptr || out == nullptr) && total_q > 0) || ((k == nullptr || v == nullptr) && total_k > 0))
@@ -200,6 +254,19 @@ mea_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, fl
   // key/value rows of one sequence are addressed with 32-bit byte offsets
   if ((long long)max_seqlen_k * Hkv * D * 2 >= (1ll << 31))
     return fail(MEA_ERR_UNSUPPORTED, "max_seqlen_k * Hkv * D * 2 bytes must stay below 2^31");
+  if (mixed != nullptr) {
+    const int32_t n_dec = num_seqs - mixed->n_pre;
+    if (mixed->n_pre < 0 || n_dec < 0 || mixed->pre_q < 0 || mixed->pre_q > total_q || mixed->pre_k < 0 ||
+        mixed->pre_k > total_k || mixed->dec_max_k < 0 || mixed->dec_max_k > max_seqlen_k)
+      return fail(MEA_ERR_INVALID, "mixed batch: need 0 <= num_prefill_seqs <= num_seqs, 0 <= prefill_total_q <= "
+                  "total_q, 0 <= prefill_total_k <= total_k and 0 <= decode_max_seqlen_k <= max_seqlen_k (got %d, %d, "
+                  "%d, %d)", mixed->n_pre, mixed->pre_q, mixed->pre_k, mixed->dec_max_k);
+    if (total_q - mixed->pre_q != n_dec)
+      return fail(MEA_ERR_INVALID, "mixed batch: the %d decode sequences must hold one query each, but total_q - "
+                  "prefill_total_q = %d", n_dec, total_q - mixed->pre_q);
+    if (mixed->pre_q > 0 && max_seqlen_q == 0)
+      return fail(MEA_ERR_INVALID, "mixed batch: prefill_total_q=%d > 0 but max_seqlen_q == 0", mixed->pre_q);
+  }
   if (num_seqs == 0 || total_q == 0) return MEA_OK;
 
   mea::FwdArgs a{};
@@ -233,49 +300,52 @@ mea_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, fl
   const bool alibi = alibi_slopes != nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
-  hipError_t err;
-  if (max_seqlen_q == 1) {
-    const DecodeSplit sp = forced_split ? DecodeSplit{gcd_int(Hkv, mea::kDcKvPerWgMax), chunk_keys}
-                                        : decode_split(total_k, Hq, Hkv, fp8 != nullptr);
-    const int32_t chunk = sp.chunk;
-    const size_t need = decode_ws_bytes(num_seqs, total_k, max_seqlen_k, Hq, D, chunk);
-    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
-      return fail(MEA_ERR_INVALID, "workspace of %zu bytes is smaller than the %zu bytes required", workspace_bytes, need);
-    if (need > 0 && !aligned(workspace, 256)) return fail(MEA_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
-    a.chunk_keys = chunk;
-    a.dc_pieces = need > 0 ? (int32_t)(((long long)total_k + chunk - 1) / chunk) : 0;
-    a.max_chunks = need > 0 ? decode_slots(max_seqlen_k, chunk) : 0;
-    a.head_slices = (a.group + mea::kDcHeadsPerWg - 1) / mea::kDcHeadsPerWg;
-    a.heads_per_wg = mea::kDcHeadsPerWg;
-    a.kv_per_wg = sp.kv_per_wg;
-    a.ws_o = static_cast<float*>(workspace);
-    a.ws_lse = a.ws_o + (size_t)num_seqs * a.max_chunks * Hq * D;
-    if ((long long)a.dc_pieces * decode_head_groups(Hq, Hkv, sp.kv_per_wg) > 0x7ffffff8ll)  // the grid is padded to a multiple of 8
-      return fail(MEA_ERR_UNSUPPORTED, "too many decode workgroups (%d pieces of %d keys)", a.dc_pieces, chunk);
-    err = fp8 != nullptr ? mea::launch_decode_fp8(a, bf16, alibi, s) : mea::launch_decode(a, D, bf16, alibi, s);
-  } else {
-    const size_t need = prefill_ws_bytes(num_seqs, total_k, Hkv, D);
-    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
-      return fail(MEA_ERR_INVALID, "workspace of %zu bytes is smaller than the %zu bytes required", workspace_bytes, need);
-    if (need > 0 && !aligned(workspace, 256)) return fail(MEA_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  const FwdPlan plan = fwd_plan(num_seqs, total_k, max_seqlen_q, max_seqlen_k, Hq, Hkv, D, chunk_keys, forced_split,
+                                fp8 != nullptr, mixed);
+  if (plan.total > 0 && (workspace == nullptr || workspace_bytes < plan.total))
+    return fail(MEA_ERR_INVALID, "workspace of %zu bytes is smaller than the %zu bytes required", workspace_bytes,
+                plan.total);
+  if (plan.total > 0 && !aligned(workspace, 256)) return fail(MEA_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  mea::FwdArgs ap = a, ad = a;  // the prefill part's and the decode part's arguments
+  if (plan.dec) {
+    const int32_t chunk = plan.split.chunk;
+    ad.chunk_keys = chunk;
+    ad.dc_pieces = plan.dec_bytes > 0 ? (int32_t)(((long long)plan.dec_keys + chunk - 1) / chunk) : 0;
+    ad.max_chunks = plan.dec_bytes > 0 ? decode_slots(plan.dec_max_k, chunk) : 0;
+    ad.head_slices = (a.group + mea::kDcHeadsPerWg - 1) / mea::kDcHeadsPerWg;
+    ad.heads_per_wg = mea::kDcHeadsPerWg;
+    ad.kv_per_wg = plan.split.kv_per_wg;
+    ad.dc_seq_base = plan.dec_base;
+    ad.dc_key_base = plan.dec_key_base;
+    ad.ws_o = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + plan.dec_off);
+    ad.ws_lse = ad.ws_o + (size_t)plan.dec_n * ad.max_chunks * Hq * D;
+    if ((long long)ad.dc_pieces * decode_head_groups(Hq, Hkv, plan.split.kv_per_wg) > 0x7ffffff8ll)  // padded to 8
+      return fail(MEA_ERR_UNSUPPORTED, "too many decode workgroups (%d pieces of %d keys)", ad.dc_pieces, chunk);
+  }
+  if (plan.pre) {
     if ((long long)max_seqlen_k / mea::kPfBN + 1 > 65535)
       return fail(MEA_ERR_UNSUPPORTED, "max_seqlen_k=%d needs more than 65535 key tiles", max_seqlen_k);
-    a.ws_vt = static_cast<uint16_t*>(workspace);
-    if (need > 0)
-      a.ws_vflag = reinterpret_cast<int32_t*>(
-          static_cast<uint8_t*>(workspace) + align256(prefill_slots(num_seqs, total_k, Hkv) * (size_t)D * mea::kPfBN * 2));
-    a.heads_per_wg = gcd_int(a.group, mea::kPfGroupWaves);
-    a.head_slices = a.group / a.heads_per_wg;
-    const int bt = mea::kPfGroups * 32 * (mea::kPfGroupWaves / a.heads_per_wg);
+    ap.num_seqs = plan.pre_n;
+    ap.ws_vt = static_cast<uint16_t*>(workspace);
+    if (plan.pre_bytes > 0)
+      ap.ws_vflag = reinterpret_cast<int32_t*>(
+          static_cast<uint8_t*>(workspace) + align256(prefill_slots(plan.pre_n, plan.pre_k, Hkv) * (size_t)D * mea::kPfBN * 2));
+    ap.heads_per_wg = gcd_int(a.group, mea::kPfGroupWaves);
+    ap.head_slices = a.group / ap.heads_per_wg;
+    const int bt = mea::kPfGroups * 32 * (mea::kPfGroupWaves / ap.heads_per_wg);
     const long long tiles = (max_seqlen_q + bt - 1) / bt;
-    const long long items = (long long)Hkv * a.head_slices * num_seqs * tiles;
+    const long long items = (long long)Hkv * ap.head_slices * plan.pre_n * tiles;
     if (items > (1ll << 31) - 8)
       return fail(MEA_ERR_UNSUPPORTED, "%lld prefill work items exceed the grid limit", items);
-    a.pf_max_tiles = (int32_t)tiles;
-    a.pf_items = (int32_t)items;
-    err = fp8 != nullptr ? mea::launch_prefill_fp8(a, bf16, causal != 0, alibi, max_seqlen_k, s)
-                         : mea::launch_prefill(a, D, bf16, causal != 0, alibi, max_seqlen_k, s);
+    ap.pf_max_tiles = (int32_t)tiles;
+    ap.pf_items = (int32_t)items;
   }
+  hipError_t err = hipSuccess;
+  if (plan.pre && !(mixed != nullptr && mixed->pre_q == 0))
+    err = fp8 != nullptr ? mea::launch_prefill_fp8(ap, bf16, causal != 0, alibi, max_seqlen_k, s)
+                         : mea::launch_prefill(ap, D, bf16, causal != 0, alibi, max_seqlen_k, s);
+  if (err == hipSuccess && plan.dec)
+    err = fp8 != nullptr ? mea::launch_decode_fp8(ad, bf16, alibi, s) : mea::launch_decode(ad, D, bf16, alibi, s);
   if (err != hipSuccess) return fail(MEA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
   return MEA_OK;
 }
@@ -435,6 +505,29 @@ mea_status_t mea_fwd(const void* q, const void* k, const void* v, void* out, flo
   return fwd_impl(q, k, v, out, lse, seqstart_q, seqstart_k, num_seqs, total_q, total_k, max_seqlen_q,
                   max_seqlen_k, Hq, Hkv, D, dtype, causal, alibi_slopes, scale, workspace,
                   workspace_bytes, stream, 0, false);
+}
+
+mea_status_t mea_fwd_mixed(const void* q, const void* k, const void* v, void* out, float* lse,
+                           const int32_t* seqstart_q, const int32_t* seqstart_k, int32_t num_seqs, int32_t total_q,
+                           int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t num_prefill_seqs,
+                           int32_t prefill_total_q, int32_t prefill_total_k, int32_t decode_max_seqlen_k, int32_t Hq,
+                           int32_t Hkv, int32_t D, mea_dtype_t dtype, int32_t causal, const float* alibi_slopes,
+                           float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  const MixedSplit mixed{num_prefill_seqs, prefill_total_q, prefill_total_k, decode_max_seqlen_k};
+  return fwd_impl(q, k, v, out, lse, seqstart_q, seqstart_k, num_seqs, total_q, total_k, max_seqlen_q,
+                  max_seqlen_k, Hq, Hkv, D, dtype, causal, alibi_slopes, scale, workspace, workspace_bytes, stream, 0,
+                  false, nullptr, nullptr, &mixed);
+}
+
+size_t mea_fwd_mixed_workspace_size(int32_t num_seqs, int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                    int32_t num_prefill_seqs, int32_t prefill_total_k, int32_t decode_max_seqlen_k,
+                                    int32_t Hq, int32_t Hkv, int32_t D) {
+  if (num_seqs <= 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || Hq <= 0 || Hkv <= 0 ||
+      Hq % Hkv != 0 || (D != 64 && D != 128) || num_prefill_seqs < 0 || num_prefill_seqs > num_seqs ||
+      prefill_total_k < 0 || prefill_total_k > total_k || decode_max_seqlen_k < 0)
+    return 0;
+  const MixedSplit mixed{num_prefill_seqs, 0, prefill_total_k, decode_max_seqlen_k};
+  return fwd_plan(num_seqs, total_k, max_seqlen_q, max_seqlen_k, Hq, Hkv, D, 0, false, false, &mixed).total;
 }
 
 mea_status_t mea_fwd_noalloc(const void* q, const void* k, const void* v, void* out, float* lse,

@@ -53,6 +53,8 @@ struct FwdArgs {
   int32_t pf_max_tiles;      // prefill: query tiles of the longest sequence
   int32_t pf_items;          // prefill: head slices * num_seqs * pf_max_tiles
   float out_scale;           // fp8 inputs: the V scale, applied to the output (else 1)
+  int32_t dc_seq_base;       // decode: first sequence served (a mixed batch's decode part: the sequences after its prefills)
+  int32_t dc_key_base;       // decode: seqstart_k[dc_seq_base], where the split key axis starts
 };
 
 // Everything a backward launch needs; passed by value as the kernel argument.

@@ -48,7 +48,7 @@ def test_every_kernel_stub_is_defined():
 
 
 def test_version_and_strings():
-    assert _native.mea_abi_version() == 9
+    assert _native.mea_abi_version() == 10
     for st in range(4):
         assert _native.mea_status_string(st).startswith("MEA_")
     assert "unknown" in _native.mea_status_string(99)
@@ -366,3 +366,35 @@ def test_noalloc_rejects_calls_beyond_its_scratch():
     # malformed arguments are rejected by the usual validation, still before any device call
     st = _native.mea_fwd_noalloc(P, P, P, P, P, P, P, 2, 10, 10, 5, 5, 6, 4, 64, MEA_F16, 0, None, 0.125, None)
     assert st == MEA_ERR_INVALID
+
+
+def test_mixed_workspace_size():
+    """mea_fwd_mixed: the prefill part's V^T images and flags, then (256-byte
+    aligned) the decode part's partials sized for the decode keys alone."""
+    mws = _native.mea_fwd_mixed_workspace_size
+    r256 = lambda x: -(-x // 256) * 256
+    # 3 prefills (201 tokens, 437 keys) + 3 decode steps (1933 keys, longest 1000), Hq 8, Hkv 2, D 128
+    pre = _native.mea_fwd_workspace_size(3, 437, 130, 1000, 8, 2, 128, 0)
+    slots = (437 // 64 + 3) * 2
+    assert pre == r256(slots * 128 * 128) + r256(slots * 4)
+    W = _native.mea_default_chunk_keys(1933, 8, 2)
+    dec = 3 * (-(-1000 // W) + 1) * 8 * 129 * 4
+    assert mws(6, 437 + 1933, 130, 1000, 3, 437, 1000, 8, 2, 128) == r256(pre) + dec
+    assert mws(6, 2370, 130, 1000, 0, 0, 1000, 8, 2, 128) == _native.mea_fwd_workspace_size(6, 2370, 1, 1000, 8, 2,
+                                                                                           128, 0)
+    assert mws(6, 2370, 130, 1000, 7, 0, 1000, 8, 2, 128) == 0          # more prefills than sequences
+    assert mws(6, 2370, 130, 1000, 3, 437, 1000, 6, 4, 128) == 0        # Hq % Hkv != 0
+
+
+@pytest.mark.parametrize("mixed, needle", [
+    ((7, 0, 0, 0), "num_prefill_seqs"),
+    ((2, 2, 5, 0), "one query each"),
+    ((2, 3, 5, 99), "decode_max_seqlen_k"),
+    ((2, -1, 5, 0), "prefill_total_q"),
+])
+def test_mixed_rejected_before_launch(mixed, needle):
+    n_pre, pre_q, pre_k, dmk = mixed
+    st = _native.mea_fwd_mixed(P, P, P, P, P, P, P, 4, 5, 40, 4, 20, n_pre, pre_q, pre_k, dmk, 8, 2, 64,
+                               MEA_F16, 1, None, 0.125, P, 1 << 20, None)
+    assert st == MEA_ERR_INVALID
+    assert needle in _native.mea_last_error()

@@ -110,3 +110,15 @@ def test_workspace_checks():
         _workspace(torch.empty(64, 128, dtype=torch.uint8).t(), 16, dev)
     with pytest.raises(ValueError, match="must be on"):
         _workspace(torch.empty(64, dtype=torch.uint8, device="meta"), 16, dev)
+
+
+def test_mixed_split():
+    """A batch of prefills followed by one-query decode steps is recognised
+    (the layout the mixed entry point serves); anything else is not."""
+    m = BlockDiagonalCausalMask.from_seqlens([130, 7, 64, 1, 1, 1], [130, 7, 300, 900, 33, 1000])
+    assert m.mixed_split() == (3, 201, 437, 1000)
+    assert BlockDiagonalMask.from_seqlens([1, 1, 1], [10, 20, 30]).mixed_split() is None     # decode only
+    assert BlockDiagonalMask.from_seqlens([10, 20], [10, 20]).mixed_split() is None          # prefill only
+    assert BlockDiagonalMask.from_seqlens([1, 50, 1], [9, 50, 9]).mixed_split() == (2, 51, 59, 9)
+    assert BlockDiagonalMask.from_seqlens([1, 1, 1, 1], [9, 8, 7, 6]).mixed_split() is None
+    assert BlockDiagonalMask.from_seqlens([0, 2, 1], [5, 2, 7]).mixed_split() == (2, 2, 7, 7)

@@ -57,7 +57,13 @@ def _fwd_guarded(inp, fn_name="packed", chunk_keys=None, page_size=64, fp8=False
     out_dtype = inp.q.dtype
     out = Guarded((Tq, Hq, D), out_dtype)
     lse = Guarded((Hq, Tq), torch.float32)
-    if fp8:
+    mixed = None
+    if fn_name == "mixed":
+        from memory_efficient_attention_amd import BlockDiagonalMask
+        mixed = BlockDiagonalMask.from_seqlens(inp.seqlens_q, inp.seqlens_k).mixed_split()
+        ws_n = _native.mea_fwd_mixed_workspace_size(len(inp.seqlens_q), Tk, inp.max_seqlen_q, inp.max_seqlen_k,
+                                                    mixed[0], mixed[2], mixed[3], Hq, Hkv, D)
+    elif fp8:
         ws_n = _native.mea_fwd_fp8_workspace_size(len(inp.seqlens_q), Tk, inp.max_seqlen_q, inp.max_seqlen_k, Hq, Hkv, D)
     else:
         ws_n = _native.mea_fwd_workspace_size(len(inp.seqlens_q), Tk, inp.max_seqlen_q, inp.max_seqlen_k, Hq, Hkv, D,
@@ -78,9 +84,9 @@ def _fwd_guarded(inp, fn_name="packed", chunk_keys=None, page_size=64, fp8=False
             attention_paged_fp8(f8.q8.to(dev), pk.k_cache.to(dev), pk.v_cache.to(dev), f8.q_scale, f8.k_scale,
                                 f8.v_scale, pk.block_table.to(dev), ssq, ssk, inp.max_seqlen_q, inp.max_seqlen_k,
                                 out_dtype=out_dtype, total_k=Tk, **kw)
-    elif fn_name == "packed":
+    elif fn_name in ("packed", "mixed"):
         attention_packed(inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), ssq, ssk, inp.max_seqlen_q, inp.max_seqlen_k,
-                         chunk_keys=chunk_keys, **kw)
+                         chunk_keys=chunk_keys, mixed=mixed, **kw)
     else:
         pk = to_paged(inp, page_size, seed=1)
         attention_paged(inp.q.to(dev), pk.k_cache.to(dev), pk.v_cache.to(dev), pk.block_table.to(dev), ssq, ssk,
@@ -99,6 +105,7 @@ FWD_CASES = [
     ("fp8_prefill", [130, 7, 200], None, 8, 2, 128, "bf16", True, False, "packed", None, True),
     ("fp8_decode", [1, 1, 1], [3000, 65, 1000], 16, 8, 128, "bf16", False, False, "packed", None, True),
     ("fp8_paged_decode", [1, 1, 1], [3000, 65, 1000], 16, 8, 128, "bf16", False, False, "paged", None, True),
+    ("mixed", [130, 7, 1, 1, 1], [130, 7, 3000, 65, 1000], 16, 2, 128, "bf16", True, True, "mixed", None, False),
 ]
 
 
