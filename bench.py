@@ -27,9 +27,13 @@ seeded dO) at 2.5x the forward's unmasked FLOPs (five products against two),
 ``decode_paged_fp8`` the decode workload quantised the same way (packed, and
 in the shuffled 64-key pages through mea_fwd_paged_fp8), ``swiglu_ffn`` the SwiGLU
 feed-forward layer of the same block on the same 137,663 tokens (d_model
-4096, d_ff 11008, bf16; 6 * T * d_model * d_ff FLOPs), and ``prefill_4x2048``
+4096, d_ff 11008, bf16; 6 * T * d_model * d_ff FLOPs), ``prefill_4x2048``
 the 4 x 2048-token causal ALiBi GQA prefill (32 query / 8 key-value heads,
-D = 128, bf16) with its own roofline.  ``cpu_baseline`` also times the oracle
+D = 128, bf16) with its own roofline, and ``mixed`` a serving engine's mixed
+batch (8 prefills U[128, 4096] then 56 decode steps over U[1024, 32768]
+keys, 32/8 heads) through mea_fwd_mixed, with its prefill part (TFLOP/s) and
+decode part (GB/s) timed on their own and the whole batch through the
+prefill kernels for comparison.  ``cpu_baseline`` also times the oracle
 on samples of the decode workload and on the small parity workloads, and
 records the host's CPU model and core count.
 
@@ -121,29 +125,40 @@ def measured_traffic(kernel: str):
 class Call:
     """Pre-bound launch of one workload (buffers allocated once, outside the timed region)."""
 
-    def __init__(self, inp, dev):
+    def __init__(self, inp, dev, mixed=None):
+        """mixed: (num_prefill_seqs, prefill_total_q, prefill_total_k,
+        decode_max_seqlen_k) to call mea_fwd_mixed instead of mea_fwd."""
         import torch
         from memory_efficient_attention_amd import _native
-        self.inp = inp
+        self.inp, self.mixed = inp, mixed
         self.q, self.k, self.v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
         self.ssq, self.ssk = inp.seqstart_q.to(dev), inp.seqstart_k.to(dev)
         self.slopes = None if inp.alibi_slopes is None else inp.alibi_slopes.to(dev)
         self.out = torch.empty_like(self.q)
         self.lse = torch.empty((inp.Hq, inp.total_q), dtype=torch.float32, device=dev)
-        self.ws_bytes = _native.mea_fwd_workspace_size(len(inp.seqlens_q), inp.total_k, inp.max_seqlen_q,
-                                                       inp.max_seqlen_k, inp.Hq, inp.Hkv, inp.D, 0)
+        if mixed is None:
+            self.ws_bytes = _native.mea_fwd_workspace_size(len(inp.seqlens_q), inp.total_k, inp.max_seqlen_q,
+                                                           inp.max_seqlen_k, inp.Hq, inp.Hkv, inp.D, 0)
+        else:
+            self.ws_bytes = _native.mea_fwd_mixed_workspace_size(len(inp.seqlens_q), inp.total_k, inp.max_seqlen_q,
+                                                                 inp.max_seqlen_k, mixed[0], mixed[2], mixed[3],
+                                                                 inp.Hq, inp.Hkv, inp.D)
         self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=dev)
         self.dtype = _native.MEA_BF16 if inp.dtype == "bf16" else _native.MEA_F16
         self.native = _native
 
     def __call__(self, stream):
         inp = self.inp
-        st = self.native.mea_fwd(
-            self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.out.data_ptr(),
-            self.lse.data_ptr(), self.ssq.data_ptr(), self.ssk.data_ptr(), len(inp.seqlens_q),
-            inp.total_q, inp.total_k, inp.max_seqlen_q, inp.max_seqlen_k, inp.Hq, inp.Hkv, inp.D, self.dtype,
-            int(inp.causal), None if self.slopes is None else self.slopes.data_ptr(), inp.scale,
-            self.ws.data_ptr() if self.ws_bytes else None, self.ws_bytes, stream.cuda_stream)
+        head = (self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.out.data_ptr(),
+                self.lse.data_ptr(), self.ssq.data_ptr(), self.ssk.data_ptr(), len(inp.seqlens_q),
+                inp.total_q, inp.total_k, inp.max_seqlen_q, inp.max_seqlen_k)
+        tail = (inp.Hq, inp.Hkv, inp.D, self.dtype, int(inp.causal),
+                None if self.slopes is None else self.slopes.data_ptr(), inp.scale,
+                self.ws.data_ptr() if self.ws_bytes else None, self.ws_bytes, stream.cuda_stream)
+        if self.mixed is None:
+            st = self.native.mea_fwd(*head, *tail)
+        else:
+            st = self.native.mea_fwd_mixed(*head, *self.mixed, *tail)
         if st != 0:
             raise RuntimeError(f"mea_fwd: {self.native.mea_status_string(st)}: {self.native.mea_last_error()}")
 
@@ -320,6 +335,56 @@ class FfnCall:
                                         stream.cuda_stream)
         if st != 0:
             raise RuntimeError(f"mea_swiglu_ffn: {self.native.mea_status_string(st)}: {self.native.mea_last_error()}")
+
+
+def mixed_setup(seed, dev):
+    """The mixed serving workload (8 prefills U[128, 4096], then 56 decode
+    steps over U[1024, 32768] keys, 32/8 heads, D 128, bf16, causal): the
+    mea_fwd_mixed call, its prefill part and its decode part each called on
+    its own (the same tensors, as sub-batches), and mea_fwd on the whole batch
+    (every sequence through the prefill kernels)."""
+    from memory_efficient_attention_amd import BlockDiagonalCausalMask
+    from mea_workloads import mixed_case, prefix
+    inp = mixed_case(seed)
+    split = BlockDiagonalCausalMask.from_seqlens(inp.seqlens_q, inp.seqlens_k).mixed_split()
+    n_pre = split[0]
+    pre = prefix(inp, n_pre)
+    dec = suffix(inp, n_pre)
+    return {"inp": inp, "pre": pre, "dec": dec, "split": split, "mixed": Call(inp, dev, mixed=split),
+            "whole": Call(inp, dev), "pre_call": Call(pre, dev), "dec_call": Call(dec, dev)}
+
+
+def suffix(inp, n):
+    """Sequences n .. end of ``inp`` as their own batch (views of the same tensors)."""
+    import dataclasses
+    from mea_workloads import seqstart_from_lengths
+    sq, sk = inp.seqstart_q.tolist(), inp.seqstart_k.tolist()
+    return dataclasses.replace(inp, q=inp.q[sq[n]:], k=inp.k[sk[n]:], v=inp.v[sk[n]:],
+                               seqstart_q=seqstart_from_lengths(inp.seqlens_q[n:]),
+                               seqstart_k=seqstart_from_lengths(inp.seqlens_k[n:]),
+                               seqlens_q=inp.seqlens_q[n:], seqlens_k=inp.seqlens_k[n:], bmghk=None)
+
+
+def mixed_timings(c, stream, reps):
+    pre_flops = unmasked_flops(c["pre"])
+    dec_bytes = algorithmic_bytes(c["dec"])
+    ms = time_calls(c["mixed"], stream, reps)
+    whole_ms = time_calls(c["whole"], stream, reps)
+    pms = time_calls(c["pre_call"], stream, reps)
+    dms = time_calls(c["dec_call"], stream, reps)
+    ptf = pre_flops / (pms * 1e-3) / 1e12
+    dgb = dec_bytes / (dms * 1e-3) / 1e9
+    inp = c["inp"]
+    return {"ms": round(ms, 4), "ms_all_through_prefill_kernels": round(whole_ms, 4),
+            "speedup": round(whole_ms / ms, 3),
+            "config": {"prefills": c["split"][0], "prefill_tokens": c["split"][1],
+                       "decodes": len(inp.seqlens_q) - c["split"][0], "decode_kv_tokens": c["dec"].total_k,
+                       "Hq": inp.Hq, "Hkv": inp.Hkv, "D": inp.D, "dtype": inp.dtype, "mask": "block-diagonal causal"},
+            "prefill_part": {"ms": round(pms, 4), "value": round(ptf, 2), "unit": "TFLOP/s",
+                             "frac": round(ptf / PEAK_MFMA_BF16_TFLOPS, 4), "unmasked_flops": pre_flops},
+            "decode_part": {"ms": round(dms, 4), "value": round(dgb, 1), "unit": "GB/s",
+                            "frac": round(dgb / PEAK_HBM_GBS, 4), "algorithmic_bytes": dec_bytes},
+            "parts_ms_sum": round(pms + dms, 4)}
 
 
 BWD_GEMMS = 2.5   # backward algorithmic FLOPs / forward's: Q K^T, dO V^T, P^T dO, dS K, dS^T Q vs Q K^T, P V
@@ -610,6 +675,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-ffn", action="store_true")
+    ap.add_argument("--no-mixed", action="store_true")
     ap.add_argument("--write-traffic", metavar="DIR", default=None,
                     help="write profiles/hbm_traffic.json from the rocprofv3 counter runs under DIR and exit "
                          "(no GPU needed)")
@@ -664,6 +730,9 @@ def main():
         ffn_call = FfnCall(dev, args.seed)
     cfg3 = generate(PREFILL_4X2048, seed=args.seed)
     cfg3_call = Call(cfg3, dev)
+    mixed_calls = None
+    if not args.no_mixed:
+        mixed_calls = mixed_setup(args.seed, dev)
     torch.cuda.synchronize()
     print(f"[bench] inputs generated and resident in HBM in {time.perf_counter() - t_gen:.1f} s",
           file=sys.stderr, flush=True)
@@ -746,6 +815,10 @@ def main():
                                 "kernel": "mea_bwd call: bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel "
                                           "<128,bf16,causal>"},
                    "algorithmic_flops": int(BWD_GEMMS * pre_flops)}
+
+    mixed_res = None
+    if mixed_calls is not None:
+        mixed_res = mixed_timings(mixed_calls, stream, max(5, K // 2))
 
     fp8_res = None
     if fp8_call is not None:  # the prefill workload with q, k, v in e4m3 and per-tensor scales
@@ -831,6 +904,7 @@ def main():
         },
         "prefill_alibi": alibi_res,
         "prefill_4x2048": cfg3_res,
+        "mixed": mixed_res,
         "backward": bwd_res,
         "prefill_fp8": fp8_res,
         "decode_fp8": fp8_dec_res,
