@@ -279,9 +279,10 @@ MEA_EXPORT mea_status_t mea_fwd_paged(const void* q, const void* k_cache, const 
  *     mea_default_chunk_keys(total_k, Hq, Hkv)) -- float32 partial outputs
  *     and log-sum-exps; 0 when total_k or max_seqlen_k is 0;
  *   max_seqlen_q > 1 (prefill): with S = (total_k / 64 + num_seqs) * Hkv,
- *     round256(S * D * 128) + round256(S * 4) -- one transposed 16-bit copy
- *     of every 64-key tile of V and one int32 flag per copy (round256 rounds
- *     up to a multiple of 256; 0 when total_k == 0).
+ *     round256(S * D * 128) + round256(S * 4) + 256 -- one transposed 16-bit
+ *     copy of every 64-key tile of V, one int32 flag per copy, and the work
+ *     counters of the prefill workgroups (round256 rounds up to a multiple of
+ *     256; 0 when total_k == 0).
  */
 MEA_EXPORT size_t mea_fwd_workspace_size(int32_t num_seqs, int32_t total_k, int32_t max_seqlen_q,
                                          int32_t max_seqlen_k, int32_t Hq, int32_t Hkv, int32_t D,

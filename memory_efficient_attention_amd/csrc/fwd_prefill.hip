@@ -115,11 +115,25 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
     const int bt = kPfGroups * 32 * (kPfGroupWaves / a.heads_per_wg);
     vcand = a.head_slices * ((lq + bt - 1) / bt);
   }
-  for (int vi = 0;; ++vi) {  // VBF: candidate vi; otherwise one pass
-  // ---- work item: XCD-aware remap of the linear workgroup index (VBF:
-  // candidate vi of (vb, vg), or -1 when it reads no flagged tile)
-  const int per_xcd = (int)gridDim.x >> 3;
-  int w = ((int)blockIdx.x & 7) * per_xcd + ((int)blockIdx.x >> 3);
+  // Persistent workgroups (a.pf_tickets set): the work items of XCD x =
+  // blockIdx mod 8 are x * per_xcd .. + per_xcd - 1; its n workgroups start
+  // with items 0 .. n - 1 of that run and then draw tickets n, n + 1, ...
+  // from the XCD's counter, the next ticket fetched while an item runs.
+  // Otherwise one item per workgroup, by the XCD-aware remap of blockIdx.
+  const bool persistent = !VBF && a.pf_tickets != nullptr;
+  const int xcd = (int)blockIdx.x & 7;
+  const int per_xcd = persistent ? (a.pf_items + 7) / 8 : (int)gridDim.x >> 3;
+  int ticket = (int)blockIdx.x >> 3;
+  __shared__ int next_ticket;
+  for (int vi = 0;; ++vi) {  // VBF: candidate vi; persistent: item vi of this workgroup; otherwise one pass
+  // ---- work item (VBF: candidate vi of (vb, vg), or -1 when it reads no
+  // flagged tile)
+  int w = xcd * per_xcd + ticket;
+  int ticket_ahead = 0;
+  if (persistent) {
+    if (ticket >= per_xcd) return;  // uniform over the workgroup
+    if (threadIdx.x == 0) ticket_ahead = atomicAdd(a.pf_tickets + xcd, 1) + ((int)gridDim.x >> 3);
+  }
   if constexpr (VBF) {
     if (vi >= vcand) return;
     const int lq = a.seqstart_q[vb + 1] - a.seqstart_q[vb];
@@ -149,7 +163,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
   const int tc = kPfGroupWaves / a.heads_per_wg;  // 32-token chunks per group
   const int BT = kPfGroups * 32 * tc;             // tokens per workgroup
   const int ntiles = (Lq + BT - 1) / BT;
-  if (t_rev >= ntiles) return;
+  if (t_rev >= ntiles) {  // uniform over the workgroup: an empty item
+    if (!persistent) return;
+    if (threadIdx.x == 0) next_ticket = ticket_ahead;
+    __syncthreads();
+    ticket = next_ticket;
+    __syncthreads();
+    continue;
+  }
   const int t0 = (ntiles - 1 - t_rev) * BT;    // longest causal tiles launch first
   const int off = Lk - Lq;                     // query row r sits at key position r + off
 
@@ -470,8 +491,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
       *(u32x4*)(a.out + ((size_t)(sq0 + tok0 + row) * a.Hq + head) * D + ch * 8) = val;
     }
   }
-  if constexpr (!VBF) break;
-  __syncthreads();  // VBF: the next item reuses the LDS
+  if (!VBF && !persistent) break;
+  if (persistent && threadIdx.x == 0) next_ticket = ticket_ahead;
+  __syncthreads();  // the next item reuses the LDS
+  if (persistent) {
+    ticket = next_ticket;
+    __syncthreads();  // every wave has read next_ticket before it is written again
+  }
   }
 #endif
 }
@@ -490,6 +516,7 @@ __global__ __launch_bounds__(kVtThreads) void vt_images_kernel(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int BN = kPfBN;
   const int g = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
+  if (a.pf_tickets != nullptr && g == 0 && i == 0 && b == 0 && threadIdx.x < 8) a.pf_tickets[threadIdx.x] = 0;
   const int sk0 = a.seqstart_k[b], Lk = a.seqstart_k[b + 1] - sk0;
   if (i * BN >= Lk) return;  // uniform over the workgroup
   const int tid = threadIdx.x;
@@ -561,16 +588,39 @@ static hipError_t launch_prefill_d(const FwdArgs& a, bool causal, bool alibi, di
   return e;
 }
 
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 template <int D, bool BF16, bool PAGED, bool FP8 = false>
 static hipError_t launch_prefill_dp(const FwdArgs& a, bool causal, bool alibi, int max_seqlen_k,
                                     hipStream_t stream) {
-  if (max_seqlen_k > 0) {
-    const dim3 vgrid(a.Hkv, (max_seqlen_k + kPfBN - 1) / kPfBN, a.num_seqs);
+  if (max_seqlen_k > 0 || a.pf_tickets != nullptr) {
+    // (with no keys at all the pre-pass only zeroes the tickets)
+    const dim3 vgrid(a.Hkv, max(1, (max_seqlen_k + kPfBN - 1) / kPfBN), a.num_seqs);
     hipLaunchKernelGGL((vt_images_kernel<D, BF16, PAGED, FP8>), vgrid, dim3(kVtThreads), 0, stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const dim3 grid((unsigned)(((long long)a.pf_items + 7) / 8 * 8));
+  // persistent: one workgroup per compute unit (8 XCDs), as long as there are
+  // at least as many items; otherwise one workgroup per item
+  const long long per_item = ((long long)a.pf_items + 7) / 8 * 8;
+  const long long cus = (long long)device_cus() / 8 * 8;
+  const dim3 grid((unsigned)(a.pf_tickets != nullptr && per_item > cus ? cus : per_item));
+  if (a.pf_tickets != nullptr && per_item <= cus) {
+    FwdArgs b = a;
+    b.pf_tickets = nullptr;
+    return launch_prefill_d<D, BF16, PAGED, FP8>(b, causal, alibi, grid, stream);
+  }
   return launch_prefill_d<D, BF16, PAGED, FP8>(a, causal, alibi, grid, stream);
 }
 

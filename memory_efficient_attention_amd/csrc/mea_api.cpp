@@ -99,11 +99,15 @@ size_t decode_ws_bytes(int32_t num_seqs, int32_t total_k, int32_t max_seqlen_k, 
 }
 
 // Prefill: one 16-bit V^T image of D x 64 keys per key/value head and key
-// tile, then one int32 flag per image (1: the image stayed bfloat16);
+// tile, then one int32 flag per image (1: the image stayed bfloat16), then
+// the work counters of the persistent prefill workgroups;
 // sequence b's tiles start at slot seqstart_k[b] / 64 + b, so total_k / 64 +
 // num_seqs slots per head cover every sequence.  Each part is 256-byte
 // aligned.
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// The prefill's work counters (8 int32, one per XCD) after the flags.
+constexpr size_t kPfTicketBytes = 256;
 
 size_t prefill_slots(int32_t num_seqs, int32_t total_k, int32_t Hkv) {
   return ((size_t)total_k / mea::kPfBN + (size_t)num_seqs) * (size_t)Hkv;
@@ -112,7 +116,7 @@ size_t prefill_slots(int32_t num_seqs, int32_t total_k, int32_t Hkv) {
 size_t prefill_ws_bytes(int32_t num_seqs, int32_t total_k, int32_t Hkv, int32_t D) {
   if (total_k == 0) return 0;
   const size_t slots = prefill_slots(num_seqs, total_k, Hkv);
-  return align256(slots * (size_t)D * mea::kPfBN * 2) + align256(slots * sizeof(int32_t));
+  return align256(slots * (size_t)D * mea::kPfBN * 2) + align256(slots * sizeof(int32_t)) + kPfTicketBytes;
 }
 
 // Paged K/V cache: block_table[b * max_blocks + i] is the page holding keys
@@ -327,9 +331,13 @@ mea_status_t fwd_impl(const void* q, const void* k, const void* v, void* out, fl
       return fail(MEA_ERR_UNSUPPORTED, "max_seqlen_k=%d needs more than 65535 key tiles", max_seqlen_k);
     ap.num_seqs = plan.pre_n;
     ap.ws_vt = static_cast<uint16_t*>(workspace);
-    if (plan.pre_bytes > 0)
-      ap.ws_vflag = reinterpret_cast<int32_t*>(
-          static_cast<uint8_t*>(workspace) + align256(prefill_slots(plan.pre_n, plan.pre_k, Hkv) * (size_t)D * mea::kPfBN * 2));
+    if (plan.pre_bytes > 0) {
+      const size_t slots = prefill_slots(plan.pre_n, plan.pre_k, Hkv);
+      uint8_t* ws = static_cast<uint8_t*>(workspace);
+      ap.ws_vflag = reinterpret_cast<int32_t*>(ws + align256(slots * (size_t)D * mea::kPfBN * 2));
+      ap.pf_tickets = reinterpret_cast<int32_t*>(ws + align256(slots * (size_t)D * mea::kPfBN * 2) +
+                                                 align256(slots * sizeof(int32_t)));
+    }
     ap.heads_per_wg = gcd_int(a.group, mea::kPfGroupWaves);
     ap.head_slices = a.group / ap.heads_per_wg;
     const int bt = mea::kPfGroups * 32 * (mea::kPfGroupWaves / ap.heads_per_wg);

@@ -55,6 +55,7 @@ struct FwdArgs {
   float out_scale;           // fp8 inputs: the V scale, applied to the output (else 1)
   int32_t dc_seq_base;       // decode: first sequence served (a mixed batch's decode part: the sequences after its prefills)
   int32_t dc_key_base;       // decode: seqstart_k[dc_seq_base], where the split key axis starts
+  int32_t* pf_tickets;       // prefill: 8 work counters (one per XCD), zeroed by the V pre-pass; nullptr: one item per workgroup
 };
 
 // Everything a backward launch needs; passed by value as the kernel argument.

@@ -158,12 +158,13 @@ def test_empty_problem_is_a_noop(kw):
 def test_workspace_size():
     ws = _native.mea_fwd_workspace_size
     # prefill: one D x 64 16-bit V^T image per key/value head and tile slot,
-    # then one int32 flag per image, each part rounded up to 256 bytes
+    # then one int32 flag per image, each part rounded up to 256 bytes, then
+    # 256 bytes of work counters
     r256 = lambda x: -(-x // 256) * 256
     slots = (365 // 64 + 4) * 8
-    assert ws(4, 365, 200, 200, 8, 8, 64, 0) == r256(slots * 64 * 128) + r256(slots * 4)
+    assert ws(4, 365, 200, 200, 8, 8, 64, 0) == r256(slots * 64 * 128) + r256(slots * 4) + 256
     slots = (137663 // 64 + 64) * 8
-    assert ws(64, 137663, 4085, 4085, 32, 8, 128, 0) == r256(slots * 128 * 128) + r256(slots * 4)
+    assert ws(64, 137663, 4085, 4085, 32, 8, 128, 0) == r256(slots * 128 * 128) + r256(slots * 4) + 256
     assert ws(4, 0, 200, 0, 8, 8, 64, 0) == 0
     # decode: float32 partials per (sequence, partial slot, query head); the
     # key axis is cut into pieces of W keys, ~256 (piece, head group)
@@ -305,7 +306,7 @@ def test_fp8_workspace_size():
     ws = _native.mea_fwd_fp8_workspace_size
     # prefill-shaped: the V^T tile images (and flags) of the 16-bit prefill path
     slots = (137663 // 64 + 64) * 8
-    assert ws(64, 137663, 4094, 4094, 32, 8, 128) == -(-slots * 128 * 128 // 256) * 256 + -(-slots * 4 // 256) * 256
+    assert ws(64, 137663, 4094, 4094, 32, 8, 128) == -(-slots * 128 * 128 // 256) * 256 + -(-slots * 4 // 256) * 256 + 256
     # decode-shaped: float32 partials, num_seqs x slots x Hq x (D + 1) floats,
     # slots = ceil(max_seqlen_k / W) + 1 for pieces of W keys.  16-bit: two
     # groups of 4 key/value heads, W = 1101299 * 2 / 256 -> 8608 (a multiple
@@ -376,7 +377,7 @@ def test_mixed_workspace_size():
     # 3 prefills (201 tokens, 437 keys) + 3 decode steps (1933 keys, longest 1000), Hq 8, Hkv 2, D 128
     pre = _native.mea_fwd_workspace_size(3, 437, 130, 1000, 8, 2, 128, 0)
     slots = (437 // 64 + 3) * 2
-    assert pre == r256(slots * 128 * 128) + r256(slots * 4)
+    assert pre == r256(slots * 128 * 128) + r256(slots * 4) + 256
     W = _native.mea_default_chunk_keys(1933, 8, 2)
     dec = 3 * (-(-1000 // W) + 1) * 8 * 129 * 4
     assert mws(6, 437 + 1933, 130, 1000, 3, 437, 1000, 8, 2, 128) == r256(pre) + dec
