@@ -80,6 +80,35 @@ def test_varlen_causal_gqa_64seq_bf16_full_size_sampled(alibi):
 
 
 @pytest.mark.parametrize("alibi", [False, True])
+def test_persistent_and_per_item_grids_agree(alibi):
+    """The full 64-sequence batch has enough work items for the persistent
+    grid (one workgroup per compute unit drawing items); its first 8
+    sequences alone run one workgroup per item.  An item's arithmetic does not
+    depend on the grid, so the two agree bit for bit on those rows."""
+    import dataclasses
+    import math
+    inp = generate("varlen_causal_gqa_64seq_h32kv8_d128_bf16", alibi=alibi)
+    n = 8
+    sq, sk = inp.seqstart_q.tolist(), inp.seqstart_k.tolist()
+    sub = dataclasses.replace(inp, q=inp.q[:sq[n]], k=inp.k[:sk[n]], v=inp.v[:sk[n]],
+                              seqstart_q=inp.seqstart_q[:n + 1].clone(), seqstart_k=inp.seqstart_k[:n + 1].clone(),
+                              seqlens_q=inp.seqlens_q[:n], seqlens_k=inp.seqlens_k[:n])
+    # the grids the launcher picks: persistent from 32 items per compute unit
+    cus = torch.cuda.get_device_properties(0).multi_processor_count // 8 * 8
+    group = inp.Hq // inp.Hkv
+    slices = group // math.gcd(group, 4)
+    bt = 2 * 32 * (4 // math.gcd(group, 4))
+    items = lambda x: inp.Hkv * slices * len(x.seqlens_q) * -(-x.max_seqlen_q // bt)
+    assert items(inp) >= 32 * cus > items(sub), (items(inp), items(sub), cus)
+    _log(f"grids alibi={alibi}: {items(inp)} items persistent, {items(sub)} per item")
+    out, lse = run_gpu(inp)
+    out_s, lse_s = run_gpu(sub)
+    assert not torch.isnan(out_s).any()
+    assert torch.equal(out[:sq[n]], out_s)
+    assert torch.equal(lse[:, :sq[n]], lse_s)
+
+
+@pytest.mark.parametrize("alibi", [False, True])
 def test_varlen_causal_gqa_first_sequences_full(alibi):
     inp = generate("varlen_causal_gqa_64seq_h32kv8_d128_bf16", alibi=alibi, num_seqs=6)
     _log(f"varlen first 6 seqs alibi={alibi} T={inp.total_q}")
