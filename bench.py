@@ -513,21 +513,23 @@ COPY_BYTES = 1 << 30   # calibration copy: 1 GiB read + 1 GiB written per launch
 # Parts whose counter runs make up each reported traffic figure: the kernels of
 # one call (warm-up included, averaged per dispatch) and the parts that ran them.
 TRAFFIC_PARTS = {
+    # (the last two template arguments of fwd_prefill_kernel: the bfloat16-V
+    # second launch, and persistent workgroups)
     "fwd_prefill": ("prefill", ["vt_images_kernel<128, true, false, false>",
-                                "fwd_prefill_kernel<128, true, true, false, false, false, false>",
-                                "fwd_prefill_kernel<128, true, true, false, false, false, true>"]),
+                                "fwd_prefill_kernel<128, true, true, false, false, false, false, true>",
+                                "fwd_prefill_kernel<128, true, true, false, false, false, true, false>"]),
     "fwd_prefill_alibi": ("prefill_alibi", ["vt_images_kernel<128, true, false, false>",
-                                            "fwd_prefill_kernel<128, true, true, true, false, false, false>",
-                                            "fwd_prefill_kernel<128, true, true, true, false, false, true>"]),
+                                            "fwd_prefill_kernel<128, true, true, true, false, false, false, true>",
+                                            "fwd_prefill_kernel<128, true, true, true, false, false, true, false>"]),
     "fwd_prefill_4x2048": ("prefill_4x2048", ["vt_images_kernel<128, true, false, false>",
-                                              "fwd_prefill_kernel<128, true, true, true, false, false, false>",
-                                              "fwd_prefill_kernel<128, true, true, true, false, false, true>"]),
+                                              "fwd_prefill_kernel<128, true, true, true, false, false, false, false>",
+                                              "fwd_prefill_kernel<128, true, true, true, false, false, true, false>"]),
     "fwd_decode": ("decode", ["fwd_decode_partial_kernel<128, true, false, false, false>",
                               "fwd_decode_combine_kernel<128, true>"]),
     "bwd": ("backward", ["bwd_prep_kernel<128, true>", "bwd_dkdv_kernel<128, true, true, false>",
                          "bwd_dq_kernel<128, true, true, false>"]),
     "fwd_prefill_fp8": ("prefill_fp8", ["vt_images_kernel<128, true, false, true>",
-                                        "fwd_prefill_kernel<128, true, true, false, false, true, false>"]),
+                                        "fwd_prefill_kernel<128, true, true, false, false, true, false, true>"]),
     "fwd_decode_fp8": ("decode_fp8", ["fwd_decode_partial_kernel<128, true, false, false, true>",
                                       "fwd_decode_combine_kernel<128, true>"]),
     "ffn": ("ffn", ["ffn_gemm_kernel<true, true>", "ffn_gemm_kernel<true, false>"]),
