@@ -108,6 +108,30 @@ def test_persistent_and_per_item_grids_agree(alibi):
     assert torch.equal(lse[:, :sq[n]], lse_s)
 
 
+@pytest.mark.parametrize("D,dtype,alibi", [(64, "fp16", False), (128, "bf16", True)])
+def test_persistent_many_short_and_empty_sequences(D, dtype, alibi):
+    """240 sequences, one of 2,048 queries and the rest U[0, 150) with every
+    17th empty: 240 x 32 query-tile slots per key/value head is enough for the
+    persistent grid, and almost all of them lie past their sequence's end, so
+    the workgroups draw long runs of empty items between the real ones.
+    Inputs have std 0.5: with a few keys a
+    row's output is close to one V row, and |out| stays below 4, where half a
+    bfloat16 ulp (at most 2^-7) is within the 1e-2 bound."""
+    import numpy as np
+    rng = np.random.default_rng(91)
+    lq = [int(x) for x in rng.integers(0, 150, size=240)]
+    lq = [0 if i % 17 == 3 else L for i, L in enumerate(lq)]
+    lq[100] = 2048
+    lk = [L + int(e) for L, e in zip(lq, rng.integers(0, 40, size=240))]
+    inp = random_case(4500 + D, lq, lk, Hq=32, Hkv=8, D=D, dtype=dtype, causal=True, alibi=alibi, std=0.5)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count // 8 * 8
+    assert 8 * len(lq) * (2048 // 64) >= 32 * cus      # persistent grid (one head slice, 64-token tiles)
+    _log(f"persistent short sequences D={D} {dtype} alibi={alibi}: T={inp.total_q}")
+    out, lse = run_gpu(inp)
+    ref_out, ref_lse = oracle_full(inp)
+    _log(f"  {compare(out, lse, ref_out, ref_lse, dtype, 'persistent short sequences')}")
+
+
 @pytest.mark.parametrize("alibi", [False, True])
 def test_varlen_causal_gqa_first_sequences_full(alibi):
     inp = generate("varlen_causal_gqa_64seq_h32kv8_d128_bf16", alibi=alibi, num_seqs=6)
