@@ -559,6 +559,138 @@ def _counter_means(path, counter):
     return {k: sums[k] / counts[k] for k in sums}, counts
 
 
+TRACE_SUMMARY_FILE = os.path.join(ROOT, "profiles", "bench_default_kernel_stats.md")
+
+
+def _trace_label(name, grid, segment):
+    """Workload of one dispatch of the default run, from its kernel, grid and the
+    run's segment: 0 = before the backward, 1 = backward, 2 = the mixed batch,
+    3 = fp8, 4 = SwiGLU.  Pre-passes, bfloat16-V second launches and combines
+    take the label of their call's main kernel (None here)."""
+    if name.startswith(("vt_images_kernel", "fwd_decode_combine_kernel")) or \
+            (name.startswith("fwd_prefill_kernel") and name.endswith("true, false>")):
+        return None
+    if name.startswith("bwd_"):
+        return "backward"
+    if name.startswith("ffn_gemm_kernel"):
+        return "SwiGLU feed-forward"
+    if name.startswith("fwd_prefill_kernel"):
+        args = [x.strip() for x in name[name.index("<") + 1:-1].split(",")]
+        alibi, fp8, persist = args[3] == "true", args[5] == "true", args[7] == "true"
+        if fp8:
+            return "fp8 prefill"
+        if segment == 2:
+            return "mixed batch, all through the prefill kernels" if persist else "mixed batch: prefill part"
+        if alibi:
+            return "prefill + ALiBi" if persist else "4 x 2048 prefill + ALiBi"
+        return "prefill (64 sequences)"
+    if name.startswith("fwd_decode_partial_kernel"):
+        args = [x.strip() for x in name[name.index("<") + 1:-1].split(",")]
+        paged, fp8 = args[3] == "true", args[4] == "true"
+        if segment == 2:
+            return "mixed batch: decode part"
+        return ("fp8 " if fp8 else "") + ("decode, 64-key pages" if paged else "decode")
+    return "other"
+
+
+def trace_summary(root, bench_json=None):
+    """profiles/bench_default_kernel_stats.md from the kernel trace of one
+    rocprofv3 --kernel-trace run of the default bench (and its JSON line)."""
+    import csv
+    import glob
+    import statistics
+    files = glob.glob(os.path.join(root, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no kernel_trace.csv under {root}")
+    rows = []
+    for f in files:
+        with open(f, newline="") as fh:
+            rows += list(csv.DictReader(fh))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    disp = []
+    segment = 0
+    for r in rows:
+        name = r["Kernel_Name"]
+        name = name[name.find("::") + 2:] if "mea::" in name else name
+        name = name.split("(")[0].strip()
+        if not name.startswith(("fwd_", "bwd_", "vt_images", "ffn_")):
+            continue
+        if name.startswith("bwd_"):
+            segment = 1
+        elif segment == 1:
+            segment = 2
+        if name.startswith("vt_images_kernel") and name.endswith("true>"):
+            segment = 3
+        if name.startswith("ffn_"):
+            segment = 4
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        disp.append([name, _trace_label(name, r.get("Grid_Size_X") or r.get("Grid_Size"), segment), us])
+    # pre-passes take the label of the next main kernel, the rest of the previous
+    for i, d in enumerate(disp):
+        if d[1] is None and d[0].startswith("vt_images_kernel"):
+            d[1] = next((e[1] for e in disp[i + 1:] if e[1] is not None), "other")
+    last = "other"
+    for d in disp:
+        if d[1] is None:
+            d[1] = last
+        last = d[1]
+    groups = {}
+    for name, label, us in disp:
+        groups.setdefault((label, name), []).append(us)
+    lines = ["# Kernel-trace statistics of the default bench run (MI355X, gfx950, one GPU)", "",
+             "Command (repository root, `TMPDIR=/tmp`), then the summary:", "",
+             "    rocprofv3 --kernel-trace --stats -d gpurun_out/kt_bench -o kt --output-format csv -- "
+             "python3 bench.py > gpurun_out/kt_bench.json",
+             "    python3 bench.py --trace-summary gpurun_out/kt_bench --trace-json gpurun_out/kt_bench.json", "",
+             "Every dispatch of the run, grouped by the workload it served (the bench's fixed call order:",
+             "the step's prefill and decode, the ALiBi prefill, the 4 x 2048 prefill, paged decode,",
+             "backward, the mixed batch, fp8, SwiGLU). Warm-up calls are included; \"steady\" leaves",
+             "out each group's first two calls. `__amd_rocclr_copyBuffer` (input upload, CPU",
+             "baseline copies) is outside every timed region and not listed.", "",
+             "| workload | kernel | calls | mean µs | median µs | steady mean µs |",
+             "|---|---|---:|---:|---:|---:|"]
+    order = []
+    for name, label, _ in disp:
+        if (label, name) not in order:
+            order.append((label, name))
+    steady = {}
+    for label, name in order:
+        v = groups[(label, name)]
+        st = v[2:] if len(v) > 4 else v
+        steady[(label, name)] = statistics.mean(st)
+        lines.append(f"| {label} | `{name}` | {len(v)} | {statistics.mean(v):.1f} | {statistics.median(v):.1f} | "
+                     f"{steady[(label, name)]:.1f} |")
+    if bench_json is not None:
+        with open(bench_json) as fh:
+            rec = json.loads(fh.read().strip().splitlines()[-1])
+        per_call = {}
+        for (label, name), us in steady.items():
+            per_call[label] = per_call.get(label, 0.0) + us
+        pairs = [("prefill (64 sequences)", rec["roofline"].get("launch_ms")),
+                 ("decode", rec.get("decode", {}).get("ms")),
+                 ("prefill + ALiBi", (rec.get("prefill_alibi") or {}).get("ms")),
+                 ("4 x 2048 prefill + ALiBi", (rec.get("prefill_4x2048") or {}).get("ms")),
+                 ("decode, 64-key pages", (rec.get("decode_paged") or {}).get("ms")),
+                 ("backward", (rec.get("backward") or {}).get("ms")),
+                 ("mixed batch: prefill part", ((rec.get("mixed") or {}).get("prefill_part") or {}).get("ms")),
+                 ("mixed batch: decode part", ((rec.get("mixed") or {}).get("decode_part") or {}).get("ms")),
+                 ("fp8 prefill", (rec.get("prefill_fp8") or {}).get("ms")),
+                 ("fp8 decode", (rec.get("decode_fp8") or {}).get("ms")),
+                 ("fp8 decode, 64-key pages", (rec.get("decode_paged_fp8") or {}).get("ms")),
+                 ("SwiGLU feed-forward", (rec.get("swiglu_ffn") or {}).get("ms"))]
+        lines += ["", "Per call: the steady means of a call's kernels summed, against the bench line's HIP-event",
+                  "time of the same call in the same (profiled) run:", "",
+                  "| call | kernels, steady (µs) | bench line (µs) |", "|---|---:|---:|"]
+        for label, ms in pairs:
+            if label in per_call and ms is not None:
+                lines.append(f"| {label} | {per_call[label]:.1f} | {ms * 1e3:.1f} |")
+        lines += ["", f"The bench line of this run: prefill {rec['value']} {rec['unit']} "
+                      f"(frac {rec['roofline']['frac']}), {rec['ms_per_step']} ms per step."]
+    with open(TRACE_SUMMARY_FILE, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(TRACE_SUMMARY_FILE)
+
+
 def write_traffic(root):
     """profiles/hbm_traffic.json from the FETCH_SIZE / WRITE_SIZE runs under
     root: each counter scaled by what it reads for the copy of known size."""
@@ -681,6 +813,11 @@ def main():
     ap.add_argument("--write-traffic", metavar="DIR", default=None,
                     help="write profiles/hbm_traffic.json from the rocprofv3 counter runs under DIR and exit "
                          "(no GPU needed)")
+    ap.add_argument("--trace-summary", metavar="DIR", default=None,
+                    help="write profiles/bench_default_kernel_stats.md from the rocprofv3 kernel trace of a "
+                         "default run under DIR and exit (no GPU needed)")
+    ap.add_argument("--trace-json", metavar="FILE", default=None,
+                    help="with --trace-summary: the JSON line that profiled run printed")
     ap.add_argument("--part", choices=["all", "prefill", "decode", "decode_paged", "backward", "prefill_fp8",
                                        "decode_fp8", "decode_paged_fp8", "ffn", "prefill_alibi", "prefill_4x2048",
                                        "copy"],
@@ -690,6 +827,9 @@ def main():
     args = ap.parse_args()
     if args.write_traffic is not None:
         write_traffic(args.write_traffic)
+        return
+    if args.trace_summary is not None:
+        trace_summary(args.trace_summary, args.trace_json)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
