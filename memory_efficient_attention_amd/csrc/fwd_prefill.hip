@@ -616,14 +616,15 @@ static hipError_t launch_prefill_dp(const FwdArgs& a, bool causal, bool alibi, i
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  // persistent: one workgroup per compute unit (8 XCDs) when there are at
-  // least kPersistItemsPerCu items per unit; otherwise one workgroup per item.
+  // persistent: one workgroup per compute unit (8 XCDs; the grid is a
+  // multiple of 8, at least 8) when there are at least kPersistItemsPerCu
+  // items per unit; otherwise one workgroup per item.
   // (64 sequences of U[128, 4096] tokens, 128 items per unit: persistent 1.4 %
   // faster; 4 x 2048 tokens, 4 items per unit: one per item 11 % faster.)
   constexpr long long kPersistItemsPerCu = 32;
   const long long per_item = ((long long)a.pf_items + 7) / 8 * 8;
   const long long cus = (long long)device_cus() / 8 * 8;
-  if (a.pf_tickets != nullptr && per_item >= kPersistItemsPerCu * cus)
+  if (a.pf_tickets != nullptr && cus >= 8 && per_item >= kPersistItemsPerCu * cus)
     return launch_prefill_d<D, BF16, PAGED, FP8, true>(a, causal, alibi, dim3((unsigned)cus), stream);
   return launch_prefill_d<D, BF16, PAGED, FP8, false>(a, causal, alibi, dim3((unsigned)per_item), stream);
 }
