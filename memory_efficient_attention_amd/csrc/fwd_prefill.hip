@@ -38,9 +38,11 @@
 // the LDS tile, so the transposition and conversion happen once per tile
 // instead of once per workgroup that reads it.
 //
-// Grid: one linear index, remapped so that the 8 XCDs each take a contiguous
-// run of (head slice, sequence, tile) work items: the workgroups working on
-// one sequence's K/V at the same time share one XCD's L2.
+// Grid: the 8 XCDs each take a contiguous run of the (head slice, sequence,
+// tile) work items, so the workgroups working on one sequence's K/V at the
+// same time share one XCD's L2.  Large batches (at least 32 items per compute
+// unit) run persistent workgroups, one per compute unit, that draw the items
+// of their XCD's run from a counter; smaller ones one workgroup per item.
 #include "mea_common.h"
 #include "mea_launch.h"
 #include "mea_tiles.h"
