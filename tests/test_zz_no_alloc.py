@@ -56,6 +56,11 @@ PAIRS = [
      ([1, 1], [700, 64], 32, 8, 128, "bf16", False, False)),
     (([37, 120, 8, 200], None, 8, 8, 64, "fp16", False, False),
      ([1, 1, 1], [1000, 7, 64], 8, 2, 64, "fp16", False, True)),
+    # the first call has 8 x 20 x 64 = 10,240 work items, enough for the
+    # persistent prefill grid (work counters in the fixed scratch), and needs
+    # 11 MB of it
+    (([4096] + [3] * 19, None, 32, 8, 128, "bf16", True, False),
+     ([300, 17, 65], None, 32, 8, 128, "bf16", True, False)),
 ]
 
 
