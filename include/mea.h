@@ -43,8 +43,10 @@
  *
  * Ownership: every pointer argument is caller-owned DEVICE memory (q, k, v,
  * out, lse, seqstart_q, seqstart_k, alibi_slopes, workspace).  The library
- * allocates no memory, keeps no pointer after a call returns, and has no
- * global mutable state apart from the thread-local error text.
+ * allocates no memory in a call, keeps no caller pointer after a call
+ * returns, and has no global mutable state apart from the thread-local error
+ * text, per-device caches of the compute-unit count and of the address of
+ * mea_fwd_noalloc's fixed scratch array, and that array (see there).
  *
  * Execution: the work is enqueued on `stream` (a hipStream_t; NULL = the null
  * stream) and the call returns without synchronising.  Faults during
