@@ -562,8 +562,8 @@ def _counter_means(path, counter):
 TRACE_SUMMARY_FILE = os.path.join(ROOT, "profiles", "bench_default_kernel_stats.md")
 
 
-def _trace_label(name, grid, segment):
-    """Workload of one dispatch of the default run, from its kernel, grid and the
+def _trace_label(name, segment):
+    """Workload of one dispatch of the default run, from its kernel and the
     run's segment: 0 = before the backward, 1 = backward, 2 = the mixed batch,
     3 = fp8, 4 = SwiGLU.  Pre-passes, bfloat16-V second launches and combines
     take the label of their call's main kernel (None here)."""
@@ -624,7 +624,7 @@ def trace_summary(root, bench_json=None):
         if name.startswith("ffn_"):
             segment = 4
         us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-        disp.append([name, _trace_label(name, r.get("Grid_Size_X") or r.get("Grid_Size"), segment), us])
+        disp.append([name, _trace_label(name, segment), us])
     # pre-passes take the label of the next main kernel, the rest of the previous
     for i, d in enumerate(disp):
         if d[1] is None and d[0].startswith("vt_images_kernel"):
