@@ -199,3 +199,34 @@ def test_out_of_range_entries_read_as_zeros(ci):
         inz = dataclasses.replace(inp, k=_zero_blocks(inp.k, inp, bad, ps), v=_zero_blocks(inp.v, inp, bad, ps))
         ref_out, ref_lse = oracle_full(inz)
     _log(f"  {compare(got_out, got_lse, ref_out, ref_lse, dt, f'out-of-range entries {ci}')}")
+
+
+# ---------------------------------------------------------------- persistent prefill grid on pages
+def _many_short_sequences(seed, dtype, alibi):
+    """240 sequences, one of 2,048 queries, the rest U[0, 150) with every 17th
+    empty: 240 x 32 query-tile slots per key/value head, enough for the
+    persistent prefill grid.  std 0.5 keeps |out| below 4 (a few keys make a
+    row's output close to one V row), where half a bfloat16 ulp is within the
+    1e-2 bound."""
+    rng = np.random.default_rng(91)
+    lq = [int(x) for x in rng.integers(0, 150, size=240)]
+    lq = [0 if i % 17 == 3 else L for i, L in enumerate(lq)]
+    lq[100] = 2048
+    lk = [L + int(e) for L, e in zip(lq, rng.integers(0, 40, size=240))]
+    return random_case(seed, lq, lk, Hq=32, Hkv=8, D=128, dtype=dtype, causal=True, alibi=alibi, std=0.5)
+
+
+def test_paged_persistent_prefill():
+    inp = _many_short_sequences(4620, "bf16", True)
+    _log(f"paged persistent prefill: T={inp.total_q}, page 128")
+    out, lse = run_paged(inp, 128, seed=5)
+    ref_out, ref_lse = oracle_full(inp)
+    _log(f"  {compare(out, lse, ref_out, ref_lse, 'bf16', 'paged persistent prefill')}")
+
+
+def test_paged_fp8_persistent_prefill():
+    inp = _many_short_sequences(4630, "bf16", False)
+    _log(f"paged fp8 persistent prefill: T={inp.total_q}, page 64")
+    out, lse, f = run_paged_fp8(inp, 64, seed=6)
+    ref_out, ref_lse = oracle_fp8(inp, f)
+    _log(f"  {compare(out, lse, ref_out, ref_lse, 'bf16', 'paged fp8 persistent prefill')}")
