@@ -108,8 +108,9 @@ def test_persistent_and_per_item_grids_agree(alibi):
     assert torch.equal(lse[:, :sq[n]], lse_s)
 
 
-@pytest.mark.parametrize("D,dtype,alibi", [(64, "fp16", False), (128, "bf16", True)])
-def test_persistent_many_short_and_empty_sequences(D, dtype, alibi):
+@pytest.mark.parametrize("D,dtype,causal,alibi", [(64, "fp16", True, False), (128, "bf16", True, True),
+                                                 (128, "bf16", False, False), (64, "bf16", False, True)])
+def test_persistent_many_short_and_empty_sequences(D, dtype, causal, alibi):
     """240 sequences, one of 2,048 queries and the rest U[0, 150) with every
     17th empty: 240 x 32 query-tile slots per key/value head is enough for the
     persistent grid, and almost all of them lie past their sequence's end, so
@@ -123,10 +124,11 @@ def test_persistent_many_short_and_empty_sequences(D, dtype, alibi):
     lq = [0 if i % 17 == 3 else L for i, L in enumerate(lq)]
     lq[100] = 2048
     lk = [L + int(e) for L, e in zip(lq, rng.integers(0, 40, size=240))]
-    inp = random_case(4500 + D, lq, lk, Hq=32, Hkv=8, D=D, dtype=dtype, causal=True, alibi=alibi, std=0.5)
+    inp = random_case(4500 + D + 7 * int(causal), lq, lk, Hq=32, Hkv=8, D=D, dtype=dtype, causal=causal, alibi=alibi,
+                      std=0.5)
     cus = torch.cuda.get_device_properties(0).multi_processor_count // 8 * 8
     assert 8 * len(lq) * (2048 // 64) >= 32 * cus      # persistent grid (one head slice, 64-token tiles)
-    _log(f"persistent short sequences D={D} {dtype} alibi={alibi}: T={inp.total_q}")
+    _log(f"persistent short sequences D={D} {dtype} causal={causal} alibi={alibi}: T={inp.total_q}")
     out, lse = run_gpu(inp)
     ref_out, ref_lse = oracle_full(inp)
     _log(f"  {compare(out, lse, ref_out, ref_lse, dtype, 'persistent short sequences')}")

@@ -97,6 +97,27 @@ def test_bf16_v_out_of_half_range_packed(ci):
     _log(f"  {_check(out.cpu(), lse.cpu(), inp, f'range packed {ci}')}")
 
 
+def test_bf16_v_out_of_half_range_persistent():
+    """The planted sequences in a batch large enough for the persistent
+    prefill grid (240 sequences, one of 2,048 queries: 240 x 32 query-tile
+    slots per key/value head): the second launch recomputes the items of the
+    flagged tiles after the persistent workgroups have written them."""
+    import numpy as np
+    from memory_efficient_attention_amd import attention_packed
+    rng = np.random.default_rng(93)
+    lq = [300, 200, 130, 2048] + [int(x) for x in rng.integers(1, 150, size=236)]
+    inp = _plant(random_case(4300, lq, None, Hq=32, Hkv=8, D=128, dtype="bf16", causal=True, alibi=True), seed=30)
+    _log(f"range persistent: T={inp.total_q}")
+    dev = "cuda"
+    q = inp.q.to(dev)
+    out, lse = attention_packed(q, inp.k.to(dev), inp.v.to(dev), inp.seqstart_q.to(dev), inp.seqstart_k.to(dev),
+                                inp.max_seqlen_q, inp.max_seqlen_k, causal=True,
+                                alibi_slopes=inp.alibi_slopes.to(dev), scale=inp.scale, return_lse=True,
+                                out=torch.full_like(q, float("nan")))
+    torch.cuda.synchronize()
+    _log(f"  {_check(out.cpu(), lse.cpu(), inp, 'range persistent')}")
+
+
 @pytest.mark.parametrize("ci", [0, 2, 4])
 def test_bf16_v_out_of_half_range_paged(ci):
     from memory_efficient_attention_amd import attention_paged
