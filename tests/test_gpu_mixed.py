@@ -84,3 +84,25 @@ def test_mixed_full_size_sampled():
     n_pre = _mask(inp).mixed_split()[1]
     rows += [(t, h) for t in range(n_pre, inp.total_q, 7) for h in (0, inp.Hq - 1)]   # decode rows
     _log(f"  {compare_rows(out, lse, inp, sorted(set(rows)), 'mixed full size')}")
+
+
+def test_mixed_with_a_persistent_prefill_part():
+    """240 prefills (one of 2,048 queries, the rest U[2, 150), enough query-tile
+    slots for the persistent prefill grid) followed by 24 decode steps over
+    U[1, 3000] keys: the persistent workgroups on the first sequences, then the
+    split-KV kernels from the decode part's sequence and key bases.  std 0.5
+    keeps |out| below 4 (half a bfloat16 ulp within the 1e-2 bound)."""
+    import numpy as np
+    rng = np.random.default_rng(97)
+    lq = [int(x) for x in rng.integers(2, 150, size=240)]
+    lq[100] = 2048
+    lk = [L + int(e) for L, e in zip(lq, rng.integers(0, 40, size=240))]
+    lq += [1] * 24
+    lk += [int(x) for x in rng.integers(1, 3000, size=24)]
+    inp = random_case(5200, lq, lk, Hq=32, Hkv=8, D=128, dtype="bf16", causal=True, alibi=True, std=0.5)
+    split = _mask(inp).mixed_split()
+    assert split[0] == 240
+    _log(f"mixed, persistent prefill part: Tq={inp.total_q} Tk={inp.total_k} split={split}")
+    out, lse = run_mixed(inp)
+    ref_out, ref_lse = oracle_full(inp)
+    _log(f"  {compare(out, lse, ref_out, ref_lse, 'bf16', 'mixed persistent')}")
