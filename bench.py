@@ -639,9 +639,9 @@ def trace_summary(root, bench_json=None):
         groups.setdefault((label, name), []).append(us)
     lines = ["# Kernel-trace statistics of the default bench run (MI355X, gfx950, one GPU)", "",
              "Command (repository root, `TMPDIR=/tmp`), then the summary:", "",
-             "    rocprofv3 --kernel-trace --stats -d gpurun_out/kt_bench -o kt --output-format csv -- "
-             "python3 bench.py > gpurun_out/kt_bench.json",
-             "    python3 bench.py --trace-summary gpurun_out/kt_bench --trace-json gpurun_out/kt_bench.json", "",
+             "    rocprofv3 --kernel-trace --stats -d DIR -o kt --output-format csv -- python3 bench.py > DIR.json",
+             "    python3 bench.py --trace-summary DIR --trace-json DIR.json", "",
+             "(DIR: any output directory.)", "",
              "Every dispatch of the run, grouped by the workload it served (the bench's fixed call order:",
              "the step's prefill and decode, the ALiBi prefill, the 4 x 2048 prefill, paged decode,",
              "backward, the mixed batch, fp8, SwiGLU). Warm-up calls are included; \"steady\" leaves",
@@ -832,7 +832,7 @@ def main():
         trace_summary(args.trace_summary, args.trace_json)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU only: there is no multi-GPU path "
               f"(asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     if int(os.environ.get("WORLD_SIZE", "1")) != 1:
