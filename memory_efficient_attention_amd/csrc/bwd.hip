@@ -105,7 +105,8 @@ __device__ __forceinline__ void store_rows(const uint16_t* tile, uint16_t* dst, 
 #pragma unroll
   for (int i = 0; i < 32 / RPI; ++i) {
     const int row = i * RPI + lane / chunks, ch = lane % chunks;
-    if (row < nrows) *(u32x4*)(dst + (size_t)row * stride + ch * 8) = *(const u32x4*)(tile + row * (D + 8) + ch * 8);
+    if (row < nrows)
+      __builtin_nontemporal_store(*(const u32x4*)(tile + row * (D + 8) + ch * 8), (u32x4*)(dst + (size_t)row * stride + ch * 8));
   }
 }
 

@@ -204,7 +204,7 @@ __global__ __launch_bounds__(kFfThreads) void ffn_gemm_kernel(FfnArgs p) {
       const int row = i * kRowsPerStore + lane / kChunks, ch = lane % kChunks;
       const int grow = m0 + 64 * wm + 32 * mb + row;
       if (grow < p.rows)
-        *(u32x4*)(p.c + (size_t)grow * p.n + col0 + ch * 8) = *(const u32x4*)(st + row * kOutPitch + ch * 8);
+        __builtin_nontemporal_store(*(const u32x4*)(st + row * kOutPitch + ch * 8), (u32x4*)(p.c + (size_t)grow * p.n + col0 + ch * 8));
     }
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_wave_barrier();

@@ -495,7 +495,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
     const int row = i * RPI + lane / kOutChunks, ch = lane % kOutChunks;
     if (tok0 + row < Lq) {
       const u32x4 val = *(const u32x4*)(ot + row * (D + 8) + ch * 8);
-      *(u32x4*)(a.out + ((size_t)(sq0 + tok0 + row) * a.Hq + head) * D + ch * 8) = val;
+      __builtin_nontemporal_store(val, (u32x4*)(a.out + ((size_t)(sq0 + tok0 + row) * a.Hq + head) * D + ch * 8));
     }
   }
   if (!VBF && !persistent) break;
