@@ -15,9 +15,11 @@
 // Either way a wave keeps 128 float32 accumulators and issues 32 MFMAs per
 // k-step.  Operand tiles go HBM -> LDS by buffer loads with an LDS
 // destination into two stage buffers (a request one k-step ahead, one barrier
-// per k-step); rows of 64 values are 128 bytes with their 16-byte chunks
-// XOR-swizzled so that the 16 rows a fragment read touches hit 16 different
-// bank groups.  Rows past `rows` read zeros and are never stored.
+// per k-step, placed before the k-step's last 8 products so that they run
+// while the next stage's first fragments are read); rows of 64 values are 128
+// bytes with their 16-byte chunks XOR-swizzled so that the 16 rows a fragment
+// read touches hit 16 different bank groups.  Rows past `rows` read zeros and
+// are never stored.
 //
 // Work order: groups of 4 row tiles walk every column tile before the next
 // group starts, remapped so that each XCD takes a contiguous run of
@@ -126,55 +128,77 @@ __global__ __launch_bounds__(kFfThreads) void ffn_gemm_kernel(FfnArgs p) {
 #pragma unroll
     for (int j = 0; j < 2 * NB / (GATED ? 1 : 2); ++j) acc[i][j] = f32x16{};
 
-  // Fragments of sub-step kk are read one sub-step ahead into the other half
-  // of a register double buffer, so each read has 8 products' time to land.
+  // Fragments of sub-step kk + 1 are read into the other half of a register
+  // double buffer while the products of sub-step kk run.  The barrier that
+  // publishes stage ks + 1 sits before the last sub-step's products of stage
+  // ks, whose fragments are then in registers: after it those products keep
+  // the matrix pipe busy while the first fragments of stage ks + 1 arrive.
   constexpr int NJ = 2 * NB / (GATED ? 1 : 2);  // B fragments per sub-step
-  auto read_frags = [&](const uint8_t* A, const uint8_t* B, int kk, u32x4 (&af)[2], u32x4 (&bf)[NJ]) {
+  constexpr int KK = kBK / 16;                  // sub-steps per k-step
+  constexpr int NR = 2 + NJ;                    // fragment reads per sub-step
+  constexpr int NP = 2 * NJ;                    // products per sub-step
+  static_assert(NR <= NP, "reads interleave with products");
+  u32x4 af[2][2], bf[2][NJ];
+  auto read_frags = [&](const uint8_t* A, const uint8_t* B, int kk, int slot) {
     const int c = 2 * kk + hi;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       const int r = 64 * wm + 32 * mb + l32;
-      af[mb] = *(const u32x4*)(A + r * kRowBytes + ff_pos(r, c) * 16);
+      af[slot][mb] = *(const u32x4*)(A + r * kRowBytes + ff_pos(r, c) * 16);
     }
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       // GATED: j < 2 gate columns 64 wn + 32 j, j >= 2 up columns 128 + 64 wn + 32 (j - 2)
       const int r = GATED ? (j < 2 ? 64 * wn + 32 * j : 128 + 64 * wn + 32 * (j - 2)) + l32
                           : 128 * wn + 32 * j + l32;
-      bf[j] = *(const u32x4*)(B + r * kRowBytes + ff_pos(r, c) * 16);
+      bf[slot][j] = *(const u32x4*)(B + r * kRowBytes + ff_pos(r, c) * 16);
     }
   };
-  auto compute = [&](int ks) {
-    const uint8_t* A = smem + (ks & 1) * kStageBytes;
-    const uint8_t* B = A + kTileBytes;
-    u32x4 af[2][2], bf[2][NJ];
-    read_frags(A, B, 0, af[0], bf[0]);
+  auto products = [&](int slot) {
 #pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      if (kk + 1 < kBK / 16) read_frags(A, B, kk + 1, af[(kk + 1) & 1], bf[(kk + 1) & 1]);
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
+      for (int mb = 0; mb < 2; ++mb) acc[mb][j] = mfma_32x32x16<BF16>(af[slot][mb], bf[slot][j], acc[mb][j]);
+  };
+  // one product, one read in turn, then the remaining products
+  auto interleave = [&]() {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) acc[mb][j] = mfma_32x32x16<BF16>(af[kk & 1][mb], bf[kk & 1][j], acc[mb][j]);
+    for (int i = 0; i < NR; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    // order: reads of sub-steps 0 and 1, then (products of kk, reads of kk + 2),
-    // so every read is issued a full sub-step of products before its use
-    constexpr int NR = 2 + NJ;  // reads per sub-step
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * NR, 0);
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NJ, 0);
-      if (kk + 2 < kBK / 16) __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
-    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NP - NR, 0);
   };
 
   const int nks = p.k / kBK;
   issue(0);
-  for (int ks = 0; ks < nks; ++ks) {
+  if (nks > 1) {
+    issue(1);
+    __builtin_amdgcn_s_waitcnt(vmcnt_at_most(2 * kLoads));  // stage 0 landed, stage 1 may be in flight
+  } else {
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();  // stage ks landed everywhere; every wave is done with stage ks - 1
-    if (ks + 1 < nks) issue(ks + 1);
-    compute(ks);
+  }
+  __syncthreads();
+  read_frags(smem, smem + kTileBytes, 0, 0);
+  for (int ks = 0; ks < nks; ++ks) {
+    const uint8_t* A = smem + (ks & 1) * kStageBytes;
+    const uint8_t* B = A + kTileBytes;
+#pragma unroll
+    for (int kk = 0; kk + 1 < KK; ++kk) {
+      read_frags(A, B, kk + 1, (kk + 1) & 1);
+      products(kk & 1);
+    }
+#pragma unroll
+    for (int kk = 0; kk + 1 < KK; ++kk) interleave();
+    // the last sub-step's fragments are in registers and this wave's share of
+    // stage ks + 1 has landed; after the barrier nobody reads stage ks again
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (ks + 2 < nks) issue(ks + 2);
+    const uint8_t* An = smem + ((ks + 1) & 1) * kStageBytes;
+    read_frags(An, An + kTileBytes, 0, 0);  // past the last stage: unused LDS reads
+    products((KK - 1) & 1);
+    interleave();
   }
   __syncthreads();
 
