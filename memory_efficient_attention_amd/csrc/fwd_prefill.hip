@@ -286,7 +286,32 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
   f32x16 o[D / 32];
 #pragma unroll
   for (int d = 0; d < D / 32; ++d) o[d] = f32x16{};
-  float m_run = kNegInf, l_run = 0.f;
+  float m_run = kNegInf;
+  // Row sums of P.  Where the vector phase is the longer one (ALiBi adds a
+  // bias to every score; fp8 halves the Q K^T products), they run on the
+  // matrix cores, as a
+  // 16x16x32 product of a selector with each 16-key chunk of the P operand.
+  // Lane n + 16 u of the P operand holds 8 weights of query n + 16 (u % 2);
+  // selector row 0 takes the lanes of query n (u = 0, 2), row 1 those of
+  // query n + 16 (u = 1, 3), so lane n < 16 accumulates the row sum of query
+  // n in register 0 and of query n + 16 in register 1: the sum of the weights
+  // P V used, in float32 (within 2^-11 of the sum of the unrounded ones).
+  // bfloat16 weights (VBF) would leave the sum within only 2^-9, too coarse
+  // for the log-sum-exp.  Otherwise each lane adds its float32 weights
+  // (l_run), which keeps the matrix phase of bf16/fp16 without ALiBi at its
+  // 32 products (4 more measured 3 % slower there; 2-3 % faster with ALiBi or fp8).
+  constexpr bool kRowSumMfma = (ALIBI || FP8) && !VBF;
+  f32x4 lacc = {};
+  float l_run = 0.f;
+  u32x4 sel = {0u, 0u, 0u, 0u};
+  if (((lane & 15) == 0 && (lane & 16) == 0) || ((lane & 15) == 1 && (lane & 16) != 0))
+    sel = u32x4{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};  // halves 1.0
+  auto rowsums = [&](const u32x4 (&pf)[4]) {
+    if constexpr (kRowSumMfma) {
+#pragma unroll
+      for (int ch = 0; ch < 4; ++ch) lacc = mfma_16x16x32<false>(sel, pf[ch], lacc);
+    }
+  };
 
   // S^T = K Q^T for tile t, K fragments straight from LDS
   auto qk = [&](int t, f32x16 (&s)[2]) {
@@ -356,7 +381,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
     if (__any(mx > m_run + kRescaleThreshold)) {
       const float m_new = __builtin_fmaxf(m_run, mx);
       const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
-      l_run *= alpha;
+      if constexpr (!kRowSumMfma) {
+        l_run *= alpha;
+      } else {  // lane n < 16 holds the sums of queries n and n + 16 (lanes n and n + 16)
+        lacc[0] *= alpha;
+        lacc[1] *= __shfl(alpha, (lane & 15) + 16);
+      }
 #pragma unroll
       for (int d = 0; d < D / 32; ++d) o[d] *= alpha;
       m_run = m_new;
@@ -378,7 +408,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
           p0 = fast_exp2(__builtin_fmaf(s[kb][r], c, -m_use));
           p1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], c, -m_use));
         }
-        lsum += p0 + p1;
+        if constexpr (!kRowSumMfma) lsum += p0 + p1;
         pf[2 * kb + r / 8][(r % 8) / 2] = VBF ? pack_out_x2<true>(p0, p1) : pack_f16x2(p0, p1);
       }
   };
@@ -419,6 +449,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
     float lsum = 0.f;
     probs(s, pf, lsum);
     l_run += lsum;
+    rowsums(pf);
   };
   auto request = [&](int j) {
     if (j + 1 < nkt) issue_k(j + 1);
@@ -471,7 +502,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
 
   // ---- epilogue: normalise, round, stage the wave's 32 x D tile through LDS
   // so that every global store writes whole 16-byte runs of a row.
-  const float l_tot = halfwave_sum(l_run);
+  // the row sum of this lane's query l32 sits in lane l32 % 16, register l32 / 16
+  float l_tot;
+  if constexpr (!kRowSumMfma) {
+    l_tot = halfwave_sum(l_run);
+  } else {
+    const float ls0 = __shfl(lacc[0], l32 & 15), ls1 = __shfl(lacc[1], l32 & 15);
+    l_tot = l32 < 16 ? ls0 : ls1;
+  }
   float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if constexpr (FP8) inv *= a.out_scale;
   uint16_t* ot = reinterpret_cast<uint16_t*>(smem) + wave * 32 * (D + 8);  // [32][D + 8]

@@ -104,6 +104,19 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(u32x4 a, u32x4 b, f32x16 c) {
   }
 }
 
+// 16x16x32 matrix-core products, float32 accumulate.  Lane l holds row (or
+// column) l % 16 of a 16 x 32 operand and 8 k-values of group l / 16 (both
+// operands share the assignment); accumulator register r of lane l is element
+// (4*(l/16) + r, l%16).
+template <bool BF16>
+__device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+}
+
 typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
