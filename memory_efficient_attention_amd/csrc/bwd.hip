@@ -230,10 +230,10 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
     }
   }
 
-  auto issue = [&](int st) {
+  auto stage_buf = [&](int st) { return smem + L::offStage + (st % L::slots) * L::stageBytes; };
+  auto issue = [&](int st, uint8_t* buf) {
     const int hh = st % a.group, qb = qb_last - st / a.group;
     const int h = g * a.group + hh;
-    uint8_t* buf = smem + L::offStage + (st % L::slots) * L::stageBytes;
     if (wave < 2) {
       const float* src = (wave == 0 ? a.ws_lse2 : a.ws_dsum) + (size_t)h * a.total_q + sq0;
       load_lds4(buf_rsrc(src, (uint32_t)Lq * 4), buf + L::offL + wave * (kBwRows * 4), (uint32_t)lane * 4,
@@ -250,10 +250,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
 
   const float c = a.scale_log2;
   const int sb = grp;  // this wave's 32-row half of every stage
-  auto compute = [&](int st) {
+  auto compute = [&](int st, const uint8_t* buf) {
     const int hh = st % a.group, qb = qb_last - st / a.group;
     const int h = g * a.group + hh;
-    const uint8_t* buf = smem + L::offStage + (st % L::slots) * L::stageBytes;
     float slope2 = 0.f;
     if constexpr (ALIBI) slope2 = a.slopes[h] * kLog2e;
     const int kd0 = my_key - (qb * kBwRows + off);  // key position minus the stage's first query position
@@ -328,12 +327,19 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
   // st and is done with tile st - 1, whose buffer tile st + 1 takes), request
   // tile st + 1, compute st.
   if (nst > 0) {
-    issue(0);
+    // the stage being read and the one being filled as restrict pointers:
+    // the compiler then knows that the transposed LDS reads of stage st do
+    // not touch the DMA of stage st + 1 in flight, and does not wait for it
+    // before them
+    auto step = [&](int st, uint8_t* __restrict__ next, const uint8_t* __restrict__ cur) {
+      if (st + 1 < nst) issue(st + 1, next);
+      compute(st, cur);
+    };
+    issue(0, stage_buf(0));
     for (int st = 0; st < nst; ++st) {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      if (st + 1 < nst) issue(st + 1);
-      compute(st);
+      step(st, stage_buf(st + 1), stage_buf(st));
     }
     __syncthreads();  // every wave is done with the buffers before the epilogue reuses LDS
   }
@@ -453,8 +459,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
     row_voff[i] = (uint32_t)r * rs_k + (uint32_t)kt_pos<D>(r, lane % L::chunks) * 16u;
   }
 
-  auto issue = [&](int t) {
-    uint8_t* buf = smem + (t % L::slots) * L::bufBytes;
+  auto ring_buf = [&](int t) { return smem + (t % L::slots) * L::bufBytes; };
+  auto issue = [&](int t, uint8_t* buf) {
     const int rsoff = t * kBwKeyTile * (int)rs_k;
 #pragma unroll
     for (int i = 0; i < L::loads; ++i) {
@@ -468,8 +474,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int d = 0; d < ND; ++d) dq[d] = f32x16{};
 
-  auto compute = [&](int t) {
-    const uint8_t* buf = smem + (t % L::slots) * L::bufBytes;
+  auto compute = [&](int t, const uint8_t* buf) {
     const int j0 = t * kBwKeyTile;
     const int jlane = j0 + 8 * hi;  // key of register 0 in block 0
     const bool need_mask = (j0 + kBwKeyTile > Lk) || (CAUSAL && j0 + kBwKeyTile - 1 > tok0 + off);
@@ -533,17 +538,36 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
 
   // ---- a ring of 3 tile buffers, tiles requested two ahead, one barrier per
   // tile (as in the dK/dV kernel)
-  constexpr int kWaitNext = vmcnt_at_most(2 * L::loads);
+  constexpr int kWaitNextLds = (2 * L::loads) | (7 << 4);  // vmcnt(2 loads), lgkmcnt(0)
   if (nkt > 0) {
-    issue(0);
-    if (nkt > 1) issue(1);
-    for (int t = 0; t < nkt; ++t) {
-      if (t + 1 < nkt) __builtin_amdgcn_s_waitcnt(kWaitNext);
-      else __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (t + 2 < nkt) issue(t + 2);
-      compute(t);
-    }
+    // restrict pointers, as in the dK/dV kernel: no wait for the DMA of tile
+    // t + 2 before the transposed reads of tile t
+    // the three ring slots as restrict pointers, and the loop unrolled by
+    // three so that each step's slots are fixed: the compiler then knows that
+    // the transposed reads of tile t touch neither the DMA of tile t + 1 nor
+    // that of tile t + 2 in flight
+    auto ring = [&](uint8_t* __restrict__ b0, uint8_t* __restrict__ b1, uint8_t* __restrict__ b2) {
+      auto step = [&](int t, uint8_t* next, const uint8_t* cur) {
+        // tile t landed (tile t + 1 may stay in flight across the barrier:
+        // __syncthreads would wait for it) and this wave's reads of tile
+        // t - 1, whose slot tile t + 2 takes, are done
+        if (t + 1 < nkt) __builtin_amdgcn_s_waitcnt(kWaitNextLds);
+        else __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (t + 2 < nkt) issue(t + 2, next);
+        compute(t, cur);
+      };
+      issue(0, b0);
+      if (nkt > 1) issue(1, b1);
+      for (int t = 0; t < nkt; t += 3) {
+        step(t, b2, b0);
+        if (t + 1 < nkt) step(t + 1, b0, b1);
+        if (t + 2 < nkt) step(t + 2, b1, b2);
+      }
+    };
+    ring(ring_buf(0), ring_buf(1), ring_buf(2));
     __syncthreads();  // every wave is done with the ring before the epilogue reuses LDS
   }
 
