@@ -108,8 +108,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
     __shared__ int first_flagged;
     vb = (int)blockIdx.x / a.Hkv;
     vg = (int)blockIdx.x % a.Hkv;
-    const int sk = a.seqstart_k[vb], lk = a.seqstart_k[vb + 1] - sk;
-    const int lq = a.seqstart_q[vb + 1] - a.seqstart_q[vb];
+    const int sk = load_const(a.seqstart_k, vb), lk = load_const(a.seqstart_k, vb + 1) - sk;
+    const int lq = load_const(a.seqstart_q, vb + 1) - load_const(a.seqstart_q, vb);
     const int ntk = (lk + BN - 1) / BN;
     if (threadIdx.x == 0) first_flagged = ntk;
     __syncthreads();
@@ -132,19 +132,29 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
   const int per_xcd = persistent ? (a.pf_items + 7) / 8 : (int)gridDim.x >> 3;
   int ticket = (int)blockIdx.x >> 3;
   __shared__ int next_ticket;
+  // the next ticket, before the offset of the first round (lane 0 of wave 0;
+  // declared outside the item loop so that no reset of it at the top of the
+  // loop has to wait for the previous atomic, or for the stores in flight)
+  int ticket_raw = 0;
   for (int vi = 0;; ++vi) {  // VBF: candidate vi; persistent: item vi of this workgroup; otherwise one pass
   // ---- work item (VBF: candidate vi of (vb, vg), or -1 when it reads no
   // flagged tile)
   int w = xcd * per_xcd + ticket;
-  int ticket_ahead = 0;
   if (persistent) {
     if (ticket >= per_xcd) return;  // uniform over the workgroup
-    if (threadIdx.x == 0) ticket_ahead = atomicAdd(a.pf_tickets + xcd, 1) + ((int)gridDim.x >> 3);
+    if (threadIdx.x == 0) {
+      // lane 0 alone; the lane-dependent offset (0 there) keeps the compiler
+      // from aggregating the atomic over the wave, whose result it would
+      // broadcast at once: the returned ticket stays in flight while the item
+      // runs and is waited for where it is used
+      const int lane_zero = (int)__builtin_amdgcn_mbcnt_lo(~0u, 0u);
+      ticket_raw = atomicAdd(a.pf_tickets + xcd + lane_zero, 1);
+    }
   }
   if constexpr (VBF) {
     if (vi >= vcand) return;
-    const int lq = a.seqstart_q[vb + 1] - a.seqstart_q[vb];
-    const int lk = a.seqstart_k[vb + 1] - a.seqstart_k[vb];
+    const int lq = load_const(a.seqstart_q, vb + 1) - load_const(a.seqstart_q, vb);
+    const int lk = load_const(a.seqstart_k, vb + 1) - load_const(a.seqstart_k, vb);
     const int bt = kPfGroups * 32 * (kPfGroupWaves / a.heads_per_wg);
     const int nt = (lq + bt - 1) / bt;
     const int t_r = vi % nt, h_s = vi / nt;
@@ -165,14 +175,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
   const int grp = wave >> 2;                 // 0 leads, 1 trails by one phase
   const int wq = wave & 3;                   // wave within its group
   const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-  const int sq0 = a.seqstart_q[b], Lq = a.seqstart_q[b + 1] - sq0;
-  const int sk0 = a.seqstart_k[b], Lk = a.seqstart_k[b + 1] - sk0;
+  const int sq0 = load_const(a.seqstart_q, b), Lq = load_const(a.seqstart_q, b + 1) - sq0;
+  const int sk0 = load_const(a.seqstart_k, b), Lk = load_const(a.seqstart_k, b + 1) - sk0;
   const int tc = kPfGroupWaves / a.heads_per_wg;  // 32-token chunks per group
   const int BT = kPfGroups * 32 * tc;             // tokens per workgroup
   const int ntiles = (Lq + BT - 1) / BT;
   if (t_rev >= ntiles) {  // uniform over the workgroup: an empty item
     if (!persistent) return;
-    if (threadIdx.x == 0) next_ticket = ticket_ahead;
+    if (threadIdx.x == 0) next_ticket = ticket_raw + ((int)gridDim.x >> 3);
     __syncthreads();
     ticket = next_ticket;
     __syncthreads();
@@ -537,7 +547,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_prefill_kernel(FwdArgs a) {
     }
   }
   if (!VBF && !persistent) break;
-  if (persistent && threadIdx.x == 0) next_ticket = ticket_ahead;
+  if (persistent && threadIdx.x == 0) next_ticket = ticket_raw + ((int)gridDim.x >> 3);
   __syncthreads();  // the next item reuses the LDS
   if (persistent) {
     ticket = next_ticket;

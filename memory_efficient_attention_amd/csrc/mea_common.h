@@ -141,6 +141,14 @@ __device__ __forceinline__ f32x4 mfma_16x16x128_fp8(u32x4 alo, u32x4 ahi, u32x4 
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// p[i] read through the constant address space: with a wave-uniform i it
+// becomes a scalar load (scalar cache and counter, so it neither waits for
+// nor holds up the vector-memory operations in flight).  Only for arrays that
+// no kernel of the launch writes.
+__device__ __forceinline__ int32_t load_const(const int32_t* p, int i) {
+  return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
+
 // The other half-wave's value of x (lane l <-> lane l ^ 32), combined.
 __device__ __forceinline__ float halfwave_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
